@@ -1,0 +1,104 @@
+"""Seeded workload generator: determinism, bf16 rounding, calibration, margin and planting."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from workloads import bf16_bits_from_f32, build_workload, get_config
+
+
+def oracle_query_fn(dtype):
+    return lambda h, w: oracle.query_encoder(oracle.decode_values(h, dtype), oracle.decode_values(w, dtype))
+
+
+def oracle_logits_fn(dtype):
+    return lambda q, keys, bias: oracle.block_logits(q, oracle.decode_values(keys, dtype), bias)
+
+
+def test_bf16_rounding_is_nearest_even():
+    # 1 + 2^-8 is exactly halfway between 1 and 1 + 2^-7: ties to even (1.0)
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], dtype=np.float32)
+    bits = bf16_bits_from_f32(x)
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F81]
+
+
+def test_same_seed_same_bytes():
+    a = build_workload("ragged_s", seed=3)
+    b = build_workload("ragged_s", seed=3)
+    c = build_workload("ragged_s", seed=4)
+    assert np.array_equal(a.ctx, b.ctx)
+    assert np.array_equal(a.w_q, b.w_q)
+    for r in range(a.n_req):
+        assert np.array_equal(a.keys[r], b.keys[r])
+        ka, va = a.kv_prefill(r)
+        kb, vb = b.kv_prefill(r)
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    assert not np.array_equal(a.w_q, c.w_q)
+
+
+def test_shapes_and_schedule():
+    wl = build_workload("ragged_s", seed=0)
+    cfg = wl.cfg
+    assert (wl.ctx % 64 == 0).all()
+    assert len(set(wl.phase.tolist())) == cfg.n_req
+    for r in range(cfg.n_req):
+        steps = wl.refresh_steps[r]
+        assert steps == sorted(steps)
+        in_range = [t for t in steps if t >= 0]
+        assert all((t + wl.phase[r]) % 64 == 0 for t in in_range)
+        # at step 0 some refresh is in force
+        assert steps[0] <= 0
+        assert wl.hidden[r].shape == (len(steps), cfg.d_model)
+        assert wl.keys[r].shape == (cfg.n_idx, wl.n_blocks[r], cfg.d_idx)
+    # staggered: at most one request refreshes per step
+    for t in range(cfg.steps):
+        assert len(wl.refreshes_at(t)) <= 1
+
+
+def test_tiny_is_fp32_and_calibrated():
+    wl = build_workload("tiny", seed=0)
+    assert wl.w_q.dtype == np.float32 and wl.keys[0].dtype == np.float32
+    assert wl.refresh_steps == [[0]]
+
+
+@pytest.mark.parametrize("name", ["ctx128k_s", "ctx512k_s", "ragged_s"])
+def test_margin_conditioning(name):
+    wl = build_workload(name, seed=1)
+    dt = wl.cfg.dtype
+    rep = wl.condition(oracle_query_fn(dt), oracle_logits_fn(dt))
+    assert rep.min_abs_logit >= 2e-3
+    # recompute independently: no logit within the margin at any refresh
+    w = oracle.decode_values(wl.w_q, dt)
+    for r in range(wl.n_req):
+        keys = oracle.decode_values(wl.keys[r], dt)
+        for k in range(len(wl.refresh_steps[r])):
+            res = oracle.refresh(oracle.decode_values(wl.hidden[r][k], dt), w, keys, wl.bias[r])
+            assert np.abs(res.z).min() >= 2e-3
+
+
+def test_realised_density_near_target():
+    wl = build_workload(get_config("ctx128k").scaled(name="dens", ctx=("fixed", 262144), steps=64), seed=2)
+    dt = wl.cfg.dtype
+    w = oracle.decode_values(wl.w_q, dt)
+    res = oracle.refresh(oracle.decode_values(wl.hidden[0][0], dt), w, oracle.decode_values(wl.keys[0], dt),
+                         wl.bias[0])
+    frac = res.count / wl.n_blocks[0]
+    assert abs(frac - 0.10) < 0.02, frac
+
+
+def test_planted_blocks_recalled_small():
+    wl = build_workload("ctx1m_s", seed=5)
+    dt = wl.cfg.dtype
+    rep = wl.condition(oracle_query_fn(dt), oracle_logits_fn(dt))
+    assert rep.planted_rows == wl.cfg.n_idx * sum(len(p) for p in wl.planted)
+    assert rep.min_planted_logit >= 1.0, rep.min_planted_logit
+    w = oracle.decode_values(wl.w_q, dt)
+    for r in range(wl.n_req):
+        keys = oracle.decode_values(wl.keys[r], dt)
+        for k in range(len(wl.refresh_steps[r])):
+            res = oracle.refresh(oracle.decode_values(wl.hidden[r][k], dt), w, keys, wl.bias[r])
+            assert set(wl.planted[r].tolist()) <= set(res.ids.tolist())
+            # every indexer keeps every planted block
+            assert res.s[:, wl.planted[r]].all()
+        assert (wl.planted[r] < (wl.ctx[r] - wl.cfg.window) // 64).all()
