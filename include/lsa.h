@@ -1,0 +1,231 @@
+/*
+ * lsa.h -- C interface of the Lookahead Sparse Attention (LSA) decode path,
+ * hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages on "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long
+ * Context via Lookahead Sparse Attention"; the zhichai.net explainer, section 2
+ * "Core Idea of LSA", gives the loop as five steps):
+ *   every tau = 64 decode steps a Query Encoder projects the current hidden
+ *   state, three independent indexers score every 64-token KV block against
+ *   frozen precomputed block keys (KIComp), blocks whose sigmoid score is above
+ *   0.5 are selected, the three selections are OR-unioned, the selected blocks
+ *   are moved from a host-memory cold pool into GPU memory, and the next 64
+ *   decode steps attend over those blocks plus the recent local window.
+ *
+ * Three calls carry the loop:
+ *   lsa_index_refresh   score, threshold, OR-union and compact (device, async)
+ *   lsa_gather_blocks   make one request's hot pool hold a new selection
+ *                       (host planning + one copy kernel, async)
+ *   lsa_sparse_decode   one decode step over window + loaded blocks (device, async)
+ *
+ * Conventions for every call:
+ *   - All buffers belong to the caller.  "dev" = device memory (hipMalloc),
+ *     "host" = ordinary host memory, "pinned" = page-locked host memory
+ *     (hipHostMalloc).  The library allocates nothing on these paths.
+ *   - Arguments are validated before anything is enqueued: on any non-OK
+ *     status nothing was enqueued and no caller state was changed.  The
+ *     message of the last failure on the calling thread is lsa_last_error().
+ *   - Launch failures return LSA_ERR_HIP; faults inside kernels surface at the
+ *     caller's next synchronisation, as for any asynchronous HIP work.
+ *   - A workspace serves one call at a time: calls that overlap in time must
+ *     use distinct workspaces.
+ *   - bf16 tensors are raw bfloat16 bit patterns (uint16); f32 are IEEE floats.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lsa_status;
+#define LSA_OK 0
+#define LSA_ERR_INVALID (-1)     /* a pointer, size or layout argument is wrong */
+#define LSA_ERR_UNSUPPORTED (-2) /* a shape or dtype this build has no kernel for */
+#define LSA_ERR_CAPACITY (-3)    /* the hot pool cannot hold the selection */
+#define LSA_ERR_WORKSPACE (-4)   /* workspace missing or smaller than the query said */
+#define LSA_ERR_HIP (-5)         /* a HIP runtime call failed (message has the HIP error) */
+
+typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
+
+#define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
+#define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
+#define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
+#define LSA_ABI_VERSION 1
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* lsa_last_error(void);
+
+/* LSA_ABI_VERSION of the built library. */
+int32_t lsa_abi_version(void);
+
+/* sizeof the argument structs below, so a binding can check its own layout:
+ * which = 0 refresh args, 1 gather args, 2 decode args. Returns 0 for others. */
+size_t lsa_struct_size(int32_t which);
+
+/* --------------------------------------------------------------------------------------
+ * KV block format.
+ *
+ * A block holds the keys and values of 64 consecutive tokens of the single KV
+ * head, laid out for the decode kernel's matrix-core operands:
+ *     K  [64][D]  row-major (token t's key is D contiguous elements)
+ *     Vt [D][64]  the values transposed (element d of every token is contiguous)
+ * so a block is 2*64*D elements = lsa_block_bytes(dtype, D) bytes (32 KiB for
+ * bf16, D = 128).  The cold pool, the hot pool and each request's window ring
+ * are arrays of such blocks.  The window ring of capacity C tokens (a multiple
+ * of 64) holds token p in ring block (p % C) / 64, row p % 64.
+ * ------------------------------------------------------------------------------------ */
+
+/* Bytes of one block; 0 if dtype or head_dim is not supported (D in {64, 128}). */
+size_t lsa_block_bytes(int32_t dtype, int32_t head_dim);
+
+/* Host-side packing of token-major K and V into blocks (used to build the cold
+ * pool and the initial window ring).
+ *   k_tok, v_tok  host [n_tokens][head_dim]: tokens pos0 .. pos0+n_tokens-1
+ *   dst           host or pinned, n_dst_blocks blocks; token p goes to block
+ *                 (p / 64) % n_dst_blocks, row p % 64
+ * Rows of dst blocks that receive no token are left untouched.  n_threads <= 0
+ * picks a thread count.  Pure host code: no HIP call. */
+lsa_status lsa_pack_blocks(int32_t dtype, int32_t head_dim, const void* k_tok, const void* v_tok,
+                           int64_t pos0, int64_t n_tokens, void* dst, int64_t n_dst_blocks,
+                           int32_t n_threads);
+
+/* --------------------------------------------------------------------------------------
+ * (1) Index refresh.
+ *
+ * For request r with B_r blocks and indexers i < n_idx (zhichai.net explainer,
+ * sections 2-4; 1kpapers report page, Summary):
+ *   q[i]     = W_q[i] h                        Query Encoder, fp32 accumulation,
+ *                                              kept in fp32 (never rounded)
+ *   z[i][b]  = q[i] . keys[i][b] + bias[i]      dual-encoder block logit (fp32)
+ *   s[i][b]  = z[i][b] > 0                      sigmoid(z) > 0.5, decided on z
+ *   u[b]     = OR_i s[i][b]                     OR-mode union
+ *   sel_ids  = ascending b with u[b], sel_count = their number
+ * ------------------------------------------------------------------------------------ */
+typedef struct lsa_refresh_args {
+    int32_t n_req;             /* requests in this call, 1..LSA_MAX_REFRESH_REQ */
+    int32_t d_model;           /* hidden size: multiple of 256, <= 16384 */
+    int32_t d_idx;             /* index dim: 128 or 256 */
+    int32_t n_idx;             /* indexers: 1..4 (the method uses 3) */
+    int32_t dtype;             /* lsa_dtype of hidden, w_q and keys */
+    int32_t reserved0;         /* must be 0 */
+    const void* hidden;        /* dev: request r, indexer i reads d_model elements at
+                                  r*hidden_req_stride + i*hidden_idx_stride */
+    int64_t hidden_req_stride; /* elements between requests (>= d_model) */
+    int64_t hidden_idx_stride; /* elements between indexers; 0 = one shared hidden state */
+    const void* w_q;           /* dev [n_idx][d_idx][d_model]; row j projects onto output j */
+    const void* keys;          /* dev; request r's keys [n_idx][B_r][d_idx] start at element
+                                  n_idx*d_idx*blk_off[r] */
+    const int64_t* blk_off;    /* host [n_req+1]: blk_off[0] = 0, B_r = blk_off[r+1]-blk_off[r],
+                                  1 <= B_r <= 2^24 */
+    const float* bias;         /* dev [n_req][n_idx] */
+    int32_t* sel_ids;          /* dev: request r's ascending ids written at sel_ids + blk_off[r]
+                                  (capacity B_r) */
+    int32_t* sel_count;        /* dev [n_req] */
+    uint64_t* masks;           /* dev or NULL.  Request r's n_idx+1 bit planes of W_r =
+                                  ceil(B_r/64) words start at word (n_idx+1)*M_r, where M_r is
+                                  the sum of W_r' over r' < r; plane i < n_idx holds s[i],
+                                  plane n_idx holds u; block b is bit b%64 of word b/64 */
+    void* workspace;           /* dev, workspace_bytes >= lsa_index_refresh_workspace() */
+    size_t workspace_bytes;
+} lsa_refresh_args;
+
+lsa_status lsa_index_refresh_workspace(const lsa_refresh_args* a, size_t* bytes);
+lsa_status lsa_index_refresh(const lsa_refresh_args* a, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * (2) Block gather: after a refresh, make the hot pool of ONE request hold exactly
+ * its new selection (zhichai.net explainer, section 2 steps 3 and 5: the selected
+ * blocks are moved from the CPU cold pool to the GPU and the loaded set is
+ * refreshed).
+ *
+ * Host part: blocks that left the selection free their slots, blocks that
+ * entered take free slots, blocks that stayed keep theirs.  Device part: one
+ * kernel on `stream` copies the entering blocks cold -> hot and writes the
+ * request's block table: n_sel entries (block id, slot), ascending by block id.
+ *
+ * Ordering contract (the caller's, with events):
+ *   - before the call, `stream` must wait for the last decode step that read the
+ *     previous selection (slots of leaving blocks are overwritten);
+ *   - decode steps that use the new selection must wait for `stream`;
+ *   - `stage` is read by the copy kernel: do not reuse it until `stream` has
+ *     passed this call.
+ * State (slot_of_block, free_slots, n_free) is updated only on LSA_OK.
+ * ------------------------------------------------------------------------------------ */
+typedef struct lsa_gather_args {
+    int64_t n_blocks;          /* blocks of this request */
+    int32_t n_slots_total;     /* slots in the whole hot pool (bounds check of slot ids) */
+    int32_t block_bytes;       /* lsa_block_bytes(dtype, D) */
+    const void* cold;          /* pinned host or dev: [n_blocks][block_bytes] */
+    void* hot;                 /* dev: [n_slots_total][block_bytes] */
+    const int32_t* new_ids;    /* host [n_new], ascending, each < n_blocks */
+    int32_t n_new;
+    int32_t stage_ints;        /* capacity of `stage` in int32, >= 4*n_new */
+    int32_t* slot_of_block;    /* host [n_blocks]: slot holding block b, or -1 (in/out) */
+    int32_t* free_slots;       /* host [capacity]: stack of this request's free slots (in/out) */
+    int32_t* n_free;           /* host: entries in free_slots (in/out) */
+    int32_t capacity;          /* this request's slot count (free_slots capacity) */
+    int32_t reserved1;         /* must be 0 */
+    int32_t* stage;            /* pinned: copy list (source block, slot) pairs, then the table */
+    int32_t* table_dev;        /* dev [capacity][2]: (block id, slot) pairs, ascending */
+    int32_t* n_copied;         /* host out: blocks copied */
+    int32_t* n_kept;           /* host out: blocks that stayed resident */
+} lsa_gather_args;
+
+lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * (3) Sparse decode: one decode step for n_req requests (zhichai.net explainer,
+ * section 2 step 4).  For request r with L = seq_len[r] tokens (the current token
+ * is position L-1) and ws = max(0, L - window[r]):
+ *   attended T = {p : ws <= p < L}  U  {p < ws : p/64 is in the request's table}
+ *   out[r][h] = sum_{p in T} softmax_p(scale * q[r][h] . K[p]) V[p]
+ * All n_heads query heads share the single KV head.  Window tokens come from the
+ * ring, selected-block tokens from the hot pool via the table.  When k_new and
+ * v_new are given, the current token's K/V are taken from them and also written
+ * into the ring (slot (L-1) % win_cap), so the call both appends and attends.
+ * Work is split over all compute units (split-K over tiles of 64 tokens) and the
+ * partial softmax states are combined by log-sum-exp.
+ * ------------------------------------------------------------------------------------ */
+typedef struct lsa_decode_args {
+    int32_t n_req;             /* 1..LSA_MAX_DECODE_REQ */
+    int32_t n_heads;           /* query heads, 1..16, sharing one KV head */
+    int32_t head_dim;          /* 64 or 128 */
+    int32_t dtype;             /* lsa_dtype of q, k_new, v_new, ring and pool */
+    int32_t win_cap;           /* ring capacity in tokens, multiple of 64, >= every window[r] */
+    float scale;               /* softmax scale (usually 1/sqrt(head_dim)) */
+    const void* q;             /* dev [n_req][n_heads][head_dim] */
+    const void* k_new;         /* dev [n_req][head_dim] or NULL (ring already holds token L-1) */
+    const void* v_new;         /* dev [n_req][head_dim] or NULL (both or neither) */
+    void* ring;                /* dev: request r's ring of win_cap/64 blocks at byte
+                                  r*(win_cap/64)*block_bytes */
+    const void* pool;          /* dev: hot pool [n_slots_total][block_bytes] */
+    int32_t n_slots_total;     /* slots in the hot pool */
+    int32_t reserved0;         /* must be 0 */
+    const int32_t* table;      /* dev: request r's (block id, slot) pairs start at pair tbl_off[r] */
+    const int32_t* tbl_off;    /* host [n_req] */
+    const int32_t* n_sel;      /* host [n_req]: entries in request r's table (ascending block id) */
+    const int32_t* seq_len;    /* host [n_req]: L, >= 1 */
+    const int32_t* window;     /* host [n_req]: W, 1..win_cap */
+    float* out;                /* dev [n_req][n_heads][head_dim] fp32 */
+    void* workspace;           /* dev, workspace_bytes >= lsa_sparse_decode_workspace() */
+    size_t workspace_bytes;
+    int32_t max_groups;        /* 0 = all compute units; else cap on work-groups (tests) */
+    int32_t reserved1;         /* must be 0 */
+    hipEvent_t ev_attn_begin;  /* optional: recorded on stream right before the attention kernel */
+    hipEvent_t ev_attn_end;    /* optional: recorded right after it (before the merge kernel) */
+} lsa_decode_args;
+
+lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes);
+lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

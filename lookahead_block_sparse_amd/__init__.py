@@ -1,0 +1,297 @@
+"""Python binding of liblsa.so, the MI355X (gfx950) Lookahead Sparse Attention decode path.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels and host planner.  The functions carry the C names:
+
+    lsa_index_refresh_workspace / lsa_index_refresh
+    lsa_gather_blocks
+    lsa_sparse_decode_workspace / lsa_sparse_decode
+    lsa_pack_blocks, lsa_block_bytes
+
+Device buffers are torch tensors on a ROCm device (raw bit patterns are fine:
+bf16 data may live in int16/uint16 tensors); host-side planner state is NumPy.
+Importing fails with an error if the built library is missing; build it with
+``python -m lookahead_block_sparse_amd._build``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
+from pathlib import Path
+from typing import Optional, Sequence
+
+import numpy as np
+
+_LIB_PATH = Path(__file__).resolve().parent / "liblsa.so"
+
+LSA_OK = 0
+LSA_ERR_INVALID = -1
+LSA_ERR_UNSUPPORTED = -2
+LSA_ERR_CAPACITY = -3
+LSA_ERR_WORKSPACE = -4
+LSA_ERR_HIP = -5
+LSA_F32 = 0
+LSA_BF16 = 1
+BLOCK_TOKENS = 64
+MAX_REFRESH_REQ = 64
+MAX_DECODE_REQ = 64
+ABI_VERSION = 1
+
+_STATUS_NAMES = {
+    LSA_ERR_INVALID: "LSA_ERR_INVALID",
+    LSA_ERR_UNSUPPORTED: "LSA_ERR_UNSUPPORTED",
+    LSA_ERR_CAPACITY: "LSA_ERR_CAPACITY",
+    LSA_ERR_WORKSPACE: "LSA_ERR_WORKSPACE",
+    LSA_ERR_HIP: "LSA_ERR_HIP",
+}
+
+EXPORTED_SYMBOLS = (
+    "lsa_last_error",
+    "lsa_abi_version",
+    "lsa_struct_size",
+    "lsa_block_bytes",
+    "lsa_pack_blocks",
+    "lsa_index_refresh_workspace",
+    "lsa_index_refresh",
+    "lsa_gather_blocks",
+    "lsa_sparse_decode_workspace",
+    "lsa_sparse_decode",
+)
+
+
+class LSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class RefreshArgs(Structure):
+    _fields_ = [
+        ("n_req", c_int32), ("d_model", c_int32), ("d_idx", c_int32), ("n_idx", c_int32),
+        ("dtype", c_int32), ("reserved0", c_int32),
+        ("hidden", c_void_p), ("hidden_req_stride", c_int64), ("hidden_idx_stride", c_int64),
+        ("w_q", c_void_p), ("keys", c_void_p), ("blk_off", POINTER(c_int64)), ("bias", c_void_p),
+        ("sel_ids", c_void_p), ("sel_count", c_void_p), ("masks", c_void_p),
+        ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+    ]
+
+
+class GatherArgs(Structure):
+    _fields_ = [
+        ("n_blocks", c_int64), ("n_slots_total", c_int32), ("block_bytes", c_int32),
+        ("cold", c_void_p), ("hot", c_void_p), ("new_ids", c_void_p), ("n_new", c_int32),
+        ("stage_ints", c_int32), ("slot_of_block", c_void_p), ("free_slots", c_void_p),
+        ("n_free", c_void_p), ("capacity", c_int32), ("reserved1", c_int32), ("stage", c_void_p),
+        ("table_dev", c_void_p), ("n_copied", c_void_p), ("n_kept", c_void_p),
+    ]
+
+
+class DecodeArgs(Structure):
+    _fields_ = [
+        ("n_req", c_int32), ("n_heads", c_int32), ("head_dim", c_int32), ("dtype", c_int32),
+        ("win_cap", c_int32), ("scale", c_float),
+        ("q", c_void_p), ("k_new", c_void_p), ("v_new", c_void_p), ("ring", c_void_p), ("pool", c_void_p),
+        ("n_slots_total", c_int32), ("reserved0", c_int32),
+        ("table", c_void_p), ("tbl_off", c_void_p), ("n_sel", c_void_p), ("seq_len", c_void_p),
+        ("window", c_void_p), ("out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("max_groups", c_int32), ("reserved1", c_int32),
+        ("ev_attn_begin", c_void_p), ("ev_attn_end", c_void_p),
+    ]
+
+
+def _load():
+    # liblsa.so needs libamdhip64.so.7.  PyTorch ships its own copy under that soname; importing
+    # torch first makes the library bind to the runtime torch already uses, so device memory,
+    # streams and events are shared by one HIP runtime in the process.
+    import torch  # noqa: F401
+
+    if not _LIB_PATH.exists():
+        raise ImportError(
+            f"{_LIB_PATH} is missing: the LSA path has no fallback; build it with "
+            "`python -m lookahead_block_sparse_amd._build`")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    lib.lsa_last_error.restype = c_char_p
+    lib.lsa_abi_version.restype = c_int32
+    lib.lsa_struct_size.restype = c_size_t
+    lib.lsa_struct_size.argtypes = [c_int32]
+    lib.lsa_block_bytes.restype = c_size_t
+    lib.lsa_block_bytes.argtypes = [c_int32, c_int32]
+    lib.lsa_pack_blocks.restype = c_int32
+    lib.lsa_pack_blocks.argtypes = [c_int32, c_int32, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_int64, c_int32]
+    lib.lsa_index_refresh_workspace.restype = c_int32
+    lib.lsa_index_refresh_workspace.argtypes = [POINTER(RefreshArgs), POINTER(c_size_t)]
+    lib.lsa_index_refresh.restype = c_int32
+    lib.lsa_index_refresh.argtypes = [POINTER(RefreshArgs), c_void_p]
+    lib.lsa_gather_blocks.restype = c_int32
+    lib.lsa_gather_blocks.argtypes = [POINTER(GatherArgs), c_void_p]
+    lib.lsa_sparse_decode_workspace.restype = c_int32
+    lib.lsa_sparse_decode_workspace.argtypes = [POINTER(DecodeArgs), POINTER(c_size_t)]
+    lib.lsa_sparse_decode.restype = c_int32
+    lib.lsa_sparse_decode.argtypes = [POINTER(DecodeArgs), c_void_p]
+    if lib.lsa_abi_version() != ABI_VERSION:
+        raise ImportError(f"liblsa.so ABI {lib.lsa_abi_version()} != binding ABI {ABI_VERSION}")
+    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs)):
+        if lib.lsa_struct_size(i) != ctypes.sizeof(st):
+            raise ImportError(f"{st.__name__}: binding layout {ctypes.sizeof(st)} B != library {lib.lsa_struct_size(i)} B")
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int) -> None:
+    if status != LSA_OK:
+        raise LSAError(status, LIB.lsa_last_error().decode(errors="replace"))
+
+
+def _ptr(x) -> Optional[int]:
+    """Address of a torch tensor, NumPy array, int address or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(dtype) -> int:
+    """'bf16' / 'f32' names, or an integer code passed through for the library to validate."""
+    if isinstance(dtype, (int, np.integer)):
+        return int(dtype)
+    if dtype == "bf16":
+        return LSA_BF16
+    if dtype == "f32":
+        return LSA_F32
+    raise ValueError(f"dtype {dtype!r}")
+
+
+def _i32(a) -> np.ndarray:
+    out = np.ascontiguousarray(a, dtype=np.int32)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+def lsa_block_bytes(dtype, head_dim: int) -> int:
+    return int(LIB.lsa_block_bytes(_dtype_code(dtype), int(head_dim)))
+
+
+def lsa_pack_blocks(dtype, head_dim: int, k_tok, v_tok, pos0: int, n_tokens: int, dst, n_dst_blocks: int,
+                    n_threads: int = 0) -> None:
+    _check(LIB.lsa_pack_blocks(_dtype_code(dtype), int(head_dim), _ptr(k_tok), _ptr(v_tok), int(pos0),
+                               int(n_tokens), _ptr(dst), int(n_dst_blocks), int(n_threads)))
+
+
+def _refresh_args(*, dtype, d_model, d_idx, n_idx, hidden, hidden_req_stride, hidden_idx_stride, w_q, keys,
+                  blk_off, bias, sel_ids, sel_count, masks, workspace, workspace_bytes):
+    blk = np.ascontiguousarray(blk_off, dtype=np.int64)
+    a = RefreshArgs()
+    a.n_req = len(blk) - 1
+    a.d_model, a.d_idx, a.n_idx, a.dtype = int(d_model), int(d_idx), int(n_idx), _dtype_code(dtype)
+    a.reserved0 = 0
+    a.hidden = _ptr(hidden)
+    a.hidden_req_stride = int(hidden_req_stride)
+    a.hidden_idx_stride = int(hidden_idx_stride)
+    a.w_q, a.keys, a.bias = _ptr(w_q), _ptr(keys), _ptr(bias)
+    a.blk_off = blk.ctypes.data_as(POINTER(c_int64))
+    a.sel_ids, a.sel_count, a.masks = _ptr(sel_ids), _ptr(sel_count), _ptr(masks)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace_bytes)
+    return a, blk
+
+
+def lsa_index_refresh_workspace(*, dtype, d_model, d_idx, n_idx, blk_off) -> int:
+    a, keep = _refresh_args(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx, hidden=None,
+                            hidden_req_stride=d_model, hidden_idx_stride=0, w_q=None, keys=None, blk_off=blk_off,
+                            bias=None, sel_ids=None, sel_count=None, masks=None, workspace=None, workspace_bytes=0)
+    out = c_size_t(0)
+    _check(LIB.lsa_index_refresh_workspace(ctypes.byref(a), ctypes.byref(out)))
+    return int(out.value)
+
+
+def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_off, bias, sel_ids, sel_count,
+                      workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a, keep = _refresh_args(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx, hidden=hidden,
+                            hidden_req_stride=d_model if hidden_req_stride is None else hidden_req_stride,
+                            hidden_idx_stride=hidden_idx_stride, w_q=w_q, keys=keys, blk_off=blk_off, bias=bias,
+                            sel_ids=sel_ids, sel_count=sel_count, masks=masks, workspace=workspace,
+                            workspace_bytes=ws_bytes)
+    _check(LIB.lsa_index_refresh(ctypes.byref(a), _stream(stream)))
+
+
+def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_ids, slot_of_block, free_slots,
+                      n_free, capacity, stage, table_dev, stream=None):
+    """Returns (n_copied, n_kept).  slot_of_block, free_slots, n_free: int32 NumPy arrays updated in place."""
+    ids = _i32(new_ids)
+    for name, arr in (("slot_of_block", slot_of_block), ("free_slots", free_slots), ("n_free", n_free)):
+        if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
+            raise TypeError(f"{name} must be a C-contiguous int32 NumPy array (updated in place)")
+    n_copied = np.zeros(1, dtype=np.int32)
+    n_kept = np.zeros(1, dtype=np.int32)
+    a = GatherArgs()
+    a.n_blocks, a.n_slots_total, a.block_bytes = int(n_blocks), int(n_slots_total), int(block_bytes)
+    a.cold, a.hot = _ptr(cold), _ptr(hot)
+    a.new_ids, a.n_new = _ptr(ids), len(ids)
+    a.stage_ints = int(stage.numel()) if stage is not None else 0
+    a.slot_of_block, a.free_slots, a.n_free = _ptr(slot_of_block), _ptr(free_slots), _ptr(n_free)
+    a.capacity, a.reserved1 = int(capacity), 0
+    a.stage, a.table_dev = _ptr(stage), _ptr(table_dev)
+    a.n_copied, a.n_kept = _ptr(n_copied), _ptr(n_kept)
+    _check(LIB.lsa_gather_blocks(ctypes.byref(a), _stream(stream)))
+    return int(n_copied[0]), int(n_kept[0])
+
+
+def _decode_args(*, dtype, n_heads, head_dim, win_cap, scale, q, k_new, v_new, ring, pool, n_slots_total, table,
+                 tbl_off, n_sel, seq_len, window, out, workspace, max_groups, ev_begin, ev_end):
+    host = [_i32(tbl_off), _i32(n_sel), _i32(seq_len), _i32(window)]
+    a = DecodeArgs()
+    a.n_req = len(host[2])
+    a.n_heads, a.head_dim, a.dtype, a.win_cap = int(n_heads), int(head_dim), _dtype_code(dtype), int(win_cap)
+    a.scale = float(scale if scale is not None else 1.0 / np.sqrt(head_dim))
+    a.q, a.k_new, a.v_new, a.ring, a.pool = _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(ring), _ptr(pool)
+    a.n_slots_total, a.reserved0 = int(n_slots_total), 0
+    a.table = _ptr(table)
+    a.tbl_off, a.n_sel, a.seq_len, a.window = (_ptr(h) for h in host)
+    a.out = _ptr(out)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.max_groups, a.reserved1 = int(max_groups), 0
+    a.ev_attn_begin = ev_begin.cuda_event if ev_begin is not None else None
+    a.ev_attn_end = ev_end.cuda_event if ev_end is not None else None
+    return a, host
+
+
+def lsa_sparse_decode_workspace(*, dtype, n_heads, head_dim, win_cap, n_req, max_groups=0) -> int:
+    a, keep = _decode_args(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap, scale=None, q=None,
+                           k_new=None, v_new=None, ring=None, pool=None, n_slots_total=0, table=None,
+                           tbl_off=[0] * n_req, n_sel=[0] * n_req, seq_len=[1] * n_req, window=[1] * n_req,
+                           out=None, workspace=None, max_groups=max_groups, ev_begin=None, ev_end=None)
+    out = c_size_t(0)
+    _check(LIB.lsa_sparse_decode_workspace(ctypes.byref(a), ctypes.byref(out)))
+    return int(out.value)
+
+
+def lsa_sparse_decode(*, dtype, n_heads, head_dim, win_cap, q, ring, out, workspace, tbl_off, n_sel, seq_len,
+                      window, pool=None, n_slots_total=0, table=None, k_new=None, v_new=None, scale=None,
+                      max_groups=0, ev_attn_begin=None, ev_attn_end=None, stream=None) -> None:
+    a, keep = _decode_args(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap, scale=scale, q=q,
+                           k_new=k_new, v_new=v_new, ring=ring, pool=pool, n_slots_total=n_slots_total,
+                           table=table, tbl_off=tbl_off, n_sel=n_sel, seq_len=seq_len, window=window, out=out,
+                           workspace=workspace, max_groups=max_groups, ev_begin=ev_attn_begin, ev_end=ev_attn_end)
+    _check(LIB.lsa_sparse_decode(ctypes.byref(a), _stream(stream)))
+
+
+__all__ = [n for n in dir() if n.startswith("lsa_") or n.startswith("LSA_")] + [
+    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs"]

@@ -1,0 +1,615 @@
+// Block-sparse flash-decode over the recent window and the loaded blocks (zhichai.net explainer of
+// "FlashMemory-DeepSeek-V4", section 2 step 4: the decode steps attend only over the loaded blocks;
+// section 1: the recent window).
+//
+// Work unit: a tile = one 64-token block (a hot-pool slot or a window-ring block).  Request r has
+// n_sel[r] block tiles (its table, ascending block id) followed by the ring tiles that hold window
+// tokens.  The tiles of all requests are concatenated and cut into G equal contiguous ranges, one per
+// work-group (split-K, balanced whatever the request mix).  Inside a group the 4 waves take the tiles
+// of each request segment round-robin and keep their own online-softmax state; at the end of a
+// segment the waves are combined in LDS and the group writes one partial (m, l, o) per segment.  The
+// merge kernel combines a request's partials by log-sum-exp.
+//
+// Matrix cores (bf16): per tile and wave, S^T = K Q^T is 16 v_mfma_f32_16x16x32_bf16 (rows = tokens,
+// columns = the 16 query heads) and O^T += V^T P^T another 16.  The token order inside each S^T
+// sub-tile is chosen so that the S^T accumulator a lane holds is exactly the P operand it feeds to the
+// V^T P^T product (no cross-lane movement of P), and V is stored transposed in the block so each lane's
+// operand is one contiguous 16-byte load.  fp32 inputs use v_mfma_f32_16x16x4_f32 with the same
+// accumulator layout.
+#include <cmath>
+
+#include "lsa_internal.hpp"
+
+namespace lsa {
+namespace {
+
+constexpr int kMaxReq = LSA_MAX_DECODE_REQ;
+constexpr int kWaves = 4;
+constexpr int kHeads = 16;  // query heads per MFMA column block (n_heads <= 16 padded with zeros)
+
+struct DecodeParams {
+    const void* q;
+    const void* k_new;
+    const void* v_new;
+    char* ring;
+    long long ring_req_bytes;
+    const char* pool;
+    const int2* table;
+    float* part_o;   // [P][16][D]
+    float* part_ml;  // [P][16][2]
+    int n_req, n_heads, n_chunks, win_cap, n_slots, total_tiles, n_groups;
+    float scale_log2;
+    int tile_prefix[kMaxReq + 1];
+    int seq_len[kMaxReq];
+    int ws[kMaxReq];
+    int tbl_off[kMaxReq];
+    int n_sel[kMaxReq];
+    int ring_first[kMaxReq];
+};
+
+struct MergeParams {
+    const float* part_o;
+    const float* part_ml;
+    float* out;
+    int n_heads;
+    int w_lo[kMaxReq];
+    int w_hi[kMaxReq];
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------------------------------
+// bf16 operands.  Lane l: lr = l % 16, lg = l / 16.
+//   S^T sub-tile j (16 tokens), k-step ks: A = K[token][32ks + 8lg .. +8], token = tokK(j, lr)
+//   accumulator element i of sub-tile j is token tokC(j, lg, i)
+//   O^T += V^T P^T, k-step kk (32 tokens), d-tile dt: A = Vt[16dt + lr][32kk + 8lg .. +8],
+//   B = P[h = lr][32kk + 8lg .. +8] = the lane's own accumulator values of sub-tiles 2kk, 2kk+1.
+template <int D>
+struct Bf16Ops {
+    static constexpr int KS = D / 32;
+    static constexpr int DT = D / 16;
+    static constexpr int EB = 2;
+    struct Frag {
+        bf16x8 k[4][KS];
+        bf16x8 v[DT][2];
+    };
+    struct QReg {
+        bf16x8 b[KS];
+    };
+    __device__ static int tokK(int j, int lr) { return 32 * (j >> 1) + 8 * (lr >> 2) + 4 * (j & 1) + (lr & 3); }
+    __device__ static int tokC(int j, int lg, int i) { return 32 * (j >> 1) + 8 * lg + 4 * (j & 1) + i; }
+
+    __device__ static void load_q(QReg& q, const uint16_t* qr, int n_heads, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (lr < n_heads)
+                q.b[ks] = *reinterpret_cast<const bf16x8*>(qr + lr * D + 32 * ks + 8 * lg);
+            else
+                q.b[ks] = bf16x8{};
+        }
+    }
+    __device__ static void load(Frag& f, const char* base, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                f.k[j][ks] = *reinterpret_cast<const bf16x8*>(base + ((size_t)tokK(j, lr) * D + 32 * ks + 8 * lg) * EB);
+        const char* vt = base + 64 * D * EB;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                f.v[dt][kk] = *reinterpret_cast<const bf16x8*>(vt + ((size_t)(16 * dt + lr) * 64 + 32 * kk + 8 * lg) * EB);
+    }
+    // Replace the current token (row cur of this tile) by k_new / v_new.
+    __device__ static void patch(Frag& f, int cur, const uint16_t* kn, const uint16_t* vn, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (tokK(j, lr) == cur)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    f.k[j][ks] = *reinterpret_cast<const bf16x8*>(kn + 32 * ks + 8 * lg);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int e = cur - (32 * kk + 8 * lg);
+            if (e >= 0 && e < 8) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const uint16_t bits = vn[16 * dt + lr];
+                    __bf16 val = __builtin_bit_cast(__bf16, bits);
+#pragma unroll
+                    for (int ee = 0; ee < 8; ++ee)
+                        if (ee == e) f.v[dt][kk][ee] = val;
+                }
+            }
+        }
+    }
+    __device__ static void qk(const Frag& f, const QReg& q, f32x4 s[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[j][ks], q.b[ks], acc, 0, 0, 0);
+            s[j] = acc;
+        }
+    }
+    __device__ static void pv(const Frag& f, const float p[16], f32x4 o[DT]) {
+        bf16x8 pb[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[kk][e] = (__bf16)p[8 * kk + e];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[dt][kk], pb[kk], o[dt], 0, 0, 0);
+    }
+    __device__ static void write_current(char* base, int cur, const uint16_t* kn, const uint16_t* vn, int lane) {
+        // K row: D*2 bytes = D/8 lanes of 16 bytes; Vt column: D values of 2 bytes
+        if (lane < D / 8)
+            *reinterpret_cast<uint4*>(base + ((size_t)cur * D + 8 * lane) * EB) = *reinterpret_cast<const uint4*>(kn + 8 * lane);
+        char* vt = base + 64 * D * EB;
+        for (int d = lane; d < D; d += 64) *reinterpret_cast<uint16_t*>(vt + ((size_t)d * 64 + cur) * EB) = vn[d];
+    }
+};
+
+// ------------------------------------------------------------------------------------------
+// fp32 operands (v_mfma_f32_16x16x4_f32).  S^T sub-tile j: token 16j + lr in A rows, element i of the
+// accumulator is token 16j + 4lg + i.  O^T k-step (j, i): A = Vt[16dt + lr][16j + 4lg + i],
+// B = P[lr][16j + 4lg + i] = the lane's own accumulator element.
+template <int D>
+struct F32Ops {
+    static constexpr int KS = D / 4;
+    static constexpr int DT = D / 16;
+    static constexpr int EB = 4;
+    struct Frag {
+        float k[4][KS];
+        float v[DT][16];
+    };
+    struct QReg {
+        float b[KS];
+    };
+    __device__ static int tokC(int j, int lg, int i) { return 16 * j + 4 * lg + i; }
+
+    __device__ static void load_q(QReg& q, const float* qr, int n_heads, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) q.b[ks] = lr < n_heads ? qr[lr * D + 4 * ks + lg] : 0.f;
+    }
+    __device__ static void load(Frag& f, const char* base, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+        const float* k = reinterpret_cast<const float*>(base);
+        const float* vt = k + 64 * D;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) f.k[j][ks] = k[(16 * j + lr) * D + 4 * ks + lg];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                f.v[dt][jj] = vt[(16 * dt + lr) * 64 + 16 * (jj >> 2) + 4 * lg + (jj & 3)];
+    }
+    __device__ static void patch(Frag& f, int cur, const float* kn, const float* vn, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (16 * j + lr == cur)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) f.k[j][ks] = kn[4 * ks + lg];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            if (16 * (jj >> 2) + 4 * lg + (jj & 3) == cur)
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) f.v[dt][jj] = vn[16 * dt + lr];
+    }
+    __device__ static void qk(const Frag& f, const QReg& q, f32x4 s[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.k[j][ks], q.b[ks], acc, 0, 0, 0);
+            s[j] = acc;
+        }
+    }
+    __device__ static void pv(const Frag& f, const float p[16], f32x4 o[DT]) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[dt][jj], p[jj], o[dt], 0, 0, 0);
+    }
+    __device__ static void write_current(char* base, int cur, const float* kn, const float* vn, int lane) {
+        float* k = reinterpret_cast<float*>(base);
+        float* vt = k + 64 * D;
+        for (int d = lane; d < D; d += 64) {
+            k[cur * D + d] = kn[d];
+            vt[d * 64 + cur] = vn[d];
+        }
+    }
+};
+
+struct TileDesc {
+    const char* base;
+    unsigned long long mask;  // valid tokens of the tile
+    int cur;                  // row of the current token to take from k_new/v_new, or -1
+};
+
+// ------------------------------------------------------------------------------------------
+template <typename Ops, typename T, int D>
+__global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
+    constexpr int DT = D / 16;
+    __shared__ float s_o[kWaves][kHeads][D];
+    __shared__ float s_m[kWaves][kHeads];
+    __shared__ float s_l[kWaves][kHeads];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int w = blockIdx.x;
+    const long long T_ = p.total_tiles, G = p.n_groups;
+    const int a = (int)((long long)w * T_ / G);
+    const int b = (int)((long long)(w + 1) * T_ / G);
+    const size_t block_bytes = (size_t)2 * 64 * D * Ops::EB;
+
+    int r = 0;
+    while (r + 1 < p.n_req && p.tile_prefix[r + 1] <= a) ++r;
+
+    for (; r < p.n_req && p.tile_prefix[r] < b; ++r) {
+        const int P0 = p.tile_prefix[r];
+        const int lo = max(a, P0) - P0;
+        const int hi = min(b, p.tile_prefix[r + 1]) - P0;
+        const int L = p.seq_len[r];
+        const int ws = p.ws[r];
+        const int n_sel = p.n_sel[r];
+        const int2* tbl = p.table + p.tbl_off[r];
+        char* ring_r = p.ring + (size_t)r * p.ring_req_bytes;
+        const T* kn = p.k_new ? static_cast<const T*>(p.k_new) + (size_t)r * D : nullptr;
+        const T* vn = p.v_new ? static_cast<const T*>(p.v_new) + (size_t)r * D : nullptr;
+        const int cur_slot = (L - 1) % p.win_cap;
+        const int cur_chunk = cur_slot >> 6;
+        const int cur_row = cur_slot & 63;
+
+        typename Ops::QReg q;
+        Ops::load_q(q, static_cast<const T*>(p.q) + (size_t)r * p.n_heads * D, p.n_heads, lane);
+
+        float m_run = -INFINITY, l_run = 0.f;
+        f32x4 o[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        const int first = lo + wave;
+        const int count = first < hi ? (hi - first + kWaves - 1) / kWaves : 0;
+
+        for (int k0 = 0; k0 < count; k0 += 64) {
+            const int kn_ = min(64, count - k0);
+            // table entries of this wave's block tiles k0 .. k0+63 (one per lane)
+            int2 ent = make_int2(0, -1);
+            {
+                const int j = first + kWaves * (k0 + lane);
+                if (lane < kn_ && j < n_sel) ent = tbl[j];
+            }
+            auto desc = [&](int k) -> TileDesc {
+                TileDesc d;
+                d.cur = -1;
+                const int j = first + kWaves * (k0 + k);
+                if (j < n_sel) {
+                    const int blk = __builtin_amdgcn_readlane(ent.x, k);
+                    const int slot = __builtin_amdgcn_readlane(ent.y, k);
+                    const int nv = min(64, max(0, ws - 64 * blk));
+                    const bool ok = slot >= 0 && slot < p.n_slots && nv > 0;
+                    d.mask = !ok ? 0ull : (nv >= 64 ? ~0ull : ((1ull << nv) - 1ull));
+                    d.base = p.pool + (size_t)(ok ? slot : 0) * block_bytes;
+                } else {
+                    const int c = (p.ring_first[r] + (j - n_sel)) % p.n_chunks;
+                    d.base = ring_r + (size_t)c * block_bytes;
+                    const int s = 64 * c + lane;
+                    int back = (L - 1 - s) % p.win_cap;
+                    if (back < 0) back += p.win_cap;
+                    const int pos = L - 1 - back;
+                    d.mask = __ballot(pos >= ws);
+                    if (kn && c == cur_chunk) d.cur = cur_row;
+                }
+                return d;
+            };
+            auto compute = [&](typename Ops::Frag& f, const TileDesc& d) {
+                f32x4 s[4];
+                Ops::qk(f, q, s);
+                float sv[16];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = Ops::tokC(j, lg, i);
+                        const float v = ((d.mask >> t) & 1ull) ? s[j][i] * p.scale_log2 : -INFINITY;
+                        sv[4 * j + i] = v;
+                        mx = fmaxf(mx, v);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float m_new = fmaxf(m_run, mx);
+                const float corr = fast_exp2(m_run - m_new);
+                float ps = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    sv[e] = fast_exp2(sv[e] - m_new);
+                    ps += sv[e];
+                }
+                l_run = l_run * corr + ps;
+                m_run = m_new;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+                Ops::pv(f, sv, o);
+            };
+            auto fetch = [&](typename Ops::Frag& f, const TileDesc& d) {
+                if (d.mask == 0ull) return;
+                Ops::load(f, d.base, lane);
+                if (d.cur >= 0) Ops::patch(f, d.cur, kn, vn, lane);
+            };
+            auto finish = [&](const TileDesc& d) {
+                if (d.cur >= 0) Ops::write_current(const_cast<char*>(d.base), d.cur, kn, vn, lane);
+            };
+
+            typename Ops::Frag fa, fb;
+            TileDesc da = desc(0), db;
+            fetch(fa, da);
+            for (int k = 0; k < kn_; k += 2) {
+                if (k + 1 < kn_) {
+                    db = desc(k + 1);
+                    fetch(fb, db);
+                }
+                if (da.mask) {
+                    compute(fa, da);
+                    finish(da);
+                }
+                if (k + 1 >= kn_) break;
+                if (k + 2 < kn_) {
+                    da = desc(k + 2);
+                    fetch(fa, da);
+                }
+                if (db.mask) {
+                    compute(fb, db);
+                    finish(db);
+                }
+            }
+        }
+
+        // ---- combine the 4 waves of this segment ----
+        float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+        l_tot += __shfl_xor(l_tot, 32, 64);
+        if (lg == 0) {
+            s_m[wave][lr] = m_run;
+            s_l[wave][lr] = l_tot;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_o[wave][lr][16 * dt + 4 * lg + i] = o[dt][i];
+        __syncthreads();
+        const int pidx = w + r;
+        for (int e = threadIdx.x; e < kHeads * D; e += 256) {
+            const int h = e / D, d = e % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v][h]);
+            float acc = 0.f, lsum = 0.f;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                const float mv = s_m[v][h];
+                const float sc = mv == -INFINITY ? 0.f : fast_exp2(mv - M);
+                acc += sc * s_o[v][h][d];
+                lsum += sc * s_l[v][h];
+            }
+            p.part_o[((size_t)pidx * kHeads + h) * D + d] = acc;
+            if (d == 0) {
+                p.part_ml[((size_t)pidx * kHeads + h) * 2 + 0] = M;
+                p.part_ml[((size_t)pidx * kHeads + h) * 2 + 1] = lsum;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// One group per (request, head).  Combines the partials of groups w_lo..w_hi (index w + r).
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+    constexpr int SUB = 256 / D;  // partial subsets per thread column
+    __shared__ float s_acc[SUB][D];
+    __shared__ float s_l[SUB];
+    __shared__ float s_M;
+    const int r = blockIdx.x / p.n_heads;
+    const int h = blockIdx.x % p.n_heads;
+    const int d = threadIdx.x % D;
+    const int sub = threadIdx.x / D;
+    const int w0 = p.w_lo[r], w1 = p.w_hi[r];
+    if (threadIdx.x == 0) {
+        float M = -INFINITY;
+        for (int w = w0; w <= w1; ++w) M = fmaxf(M, p.part_ml[((size_t)(w + r) * kHeads + h) * 2]);
+        s_M = M;
+    }
+    __syncthreads();
+    const float M = s_M;
+    float acc = 0.f, lsum = 0.f;
+    for (int w = w0 + sub; w <= w1; w += SUB) {
+        const size_t pi = (size_t)(w + r) * kHeads + h;
+        const float m = p.part_ml[pi * 2];
+        const float sc = m == -INFINITY ? 0.f : fast_exp2(m - M);
+        acc += sc * p.part_o[pi * D + d];
+        lsum += sc * p.part_ml[pi * 2 + 1];
+    }
+    s_acc[sub][d] = acc;
+    if (d == 0) s_l[sub] = lsum;
+    __syncthreads();
+    if (sub == 0) {
+        float a = 0.f, l = 0.f;
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+            a += s_acc[s][d];
+            l += s_l[s];
+        }
+        p.out[((size_t)r * p.n_heads + h) * D + d] = a / l;
+    }
+}
+
+struct DecodePlan {
+    int G = 0;
+    int total_tiles = 0;
+    size_t part_o_off = 0, part_ml_off = 0, total = 0;
+};
+
+lsa_status decode_check(const lsa_decode_args* a) {
+    LSA_CHECK_ARG(a != nullptr, "lsa_sparse_decode: null args");
+    LSA_CHECK_ARG(a->n_req >= 1 && a->n_req <= kMaxReq, "lsa_sparse_decode: n_req=%d outside 1..%d", a->n_req, kMaxReq);
+    LSA_CHECK_SUP(dtype_ok(a->dtype), "lsa_sparse_decode: dtype %d", a->dtype);
+    LSA_CHECK_SUP(a->head_dim == 64 || a->head_dim == 128, "lsa_sparse_decode: head_dim=%d (64 or 128)", a->head_dim);
+    LSA_CHECK_SUP(a->n_heads >= 1 && a->n_heads <= kHeads, "lsa_sparse_decode: n_heads=%d (1..16)", a->n_heads);
+    LSA_CHECK_ARG(a->win_cap >= 64 && a->win_cap % 64 == 0, "lsa_sparse_decode: win_cap=%d (multiple of 64)", a->win_cap);
+    LSA_CHECK_ARG(a->reserved0 == 0 && a->reserved1 == 0, "lsa_sparse_decode: reserved fields must be 0");
+    LSA_CHECK_ARG(a->max_groups >= 0, "lsa_sparse_decode: max_groups=%d", a->max_groups);
+    LSA_CHECK_ARG(a->tbl_off && a->n_sel && a->seq_len && a->window, "lsa_sparse_decode: null host array");
+    LSA_CHECK_ARG((a->k_new == nullptr) == (a->v_new == nullptr), "lsa_sparse_decode: give both k_new and v_new or neither");
+    LSA_CHECK_ARG(a->n_slots_total >= 0, "lsa_sparse_decode: n_slots_total=%d", a->n_slots_total);
+    return LSA_OK;
+}
+
+lsa_status decode_plan(const lsa_decode_args* a, DecodePlan* P, bool sizing_only) {
+    lsa_status st = decode_check(a);
+    if (st != LSA_OK) return st;
+    long long T = 0;
+    if (!sizing_only) {
+        const int n_chunks = a->win_cap / 64;
+        for (int r = 0; r < a->n_req; ++r) {
+            const int L = a->seq_len[r], W = a->window[r];
+            LSA_CHECK_ARG(L >= 1, "lsa_sparse_decode: seq_len[%d]=%d", r, L);
+            LSA_CHECK_ARG(W >= 1 && W <= a->win_cap, "lsa_sparse_decode: window[%d]=%d outside 1..win_cap", r, W);
+            LSA_CHECK_ARG(a->n_sel[r] >= 0 && a->tbl_off[r] >= 0, "lsa_sparse_decode: n_sel/tbl_off[%d] negative", r);
+            const int ws = std::max(0, L - W);
+            const int ring = std::min(n_chunks, (L - 1) / 64 - ws / 64 + 1);
+            T += (long long)a->n_sel[r] + ring;
+        }
+        LSA_CHECK_ARG(T < (1ll << 30), "lsa_sparse_decode: too many tiles");
+    }
+    DeviceInfo dev;
+    st = current_device(&dev);
+    if (st != LSA_OK) return st;
+    const int g_max = a->max_groups > 0 ? std::min(a->max_groups, dev.cu_count) : dev.cu_count;
+    P->total_tiles = (int)T;
+    P->G = sizing_only ? g_max : (int)std::max<long long>(1, std::min<long long>(g_max, (T + kWaves - 1) / kWaves));
+    const int n_part = g_max + a->n_req;
+    size_t off = 0;
+    P->part_o_off = off;
+    off = align_up(off + (size_t)n_part * kHeads * a->head_dim * sizeof(float), 256);
+    P->part_ml_off = off;
+    off = align_up(off + (size_t)n_part * kHeads * 2 * sizeof(float), 256);
+    P->total = off;
+    return LSA_OK;
+}
+
+template <typename Ops, typename T, int D>
+lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStream_t stream) {
+    DecodeParams dp{};
+    char* ws = static_cast<char*>(a->workspace);
+    dp.q = a->q;
+    dp.k_new = a->k_new;
+    dp.v_new = a->v_new;
+    dp.ring = static_cast<char*>(a->ring);
+    const size_t bb = lsa_block_bytes(a->dtype, a->head_dim);
+    dp.ring_req_bytes = (long long)(a->win_cap / 64) * (long long)bb;
+    dp.pool = static_cast<const char*>(a->pool);
+    dp.table = reinterpret_cast<const int2*>(a->table);
+    dp.part_o = reinterpret_cast<float*>(ws + P.part_o_off);
+    dp.part_ml = reinterpret_cast<float*>(ws + P.part_ml_off);
+    dp.n_req = a->n_req;
+    dp.n_heads = a->n_heads;
+    dp.n_chunks = a->win_cap / 64;
+    dp.win_cap = a->win_cap;
+    dp.n_slots = a->n_slots_total;
+    dp.total_tiles = P.total_tiles;
+    dp.n_groups = P.G;
+    dp.scale_log2 = a->scale * 1.4426950408889634f;
+    int pre = 0;
+    for (int r = 0; r < a->n_req; ++r) {
+        const int L = a->seq_len[r], W = a->window[r];
+        const int wsr = std::max(0, L - W);
+        const int ring = std::min(dp.n_chunks, (L - 1) / 64 - wsr / 64 + 1);
+        dp.tile_prefix[r] = pre;
+        dp.seq_len[r] = L;
+        dp.ws[r] = wsr;
+        dp.tbl_off[r] = a->tbl_off[r];
+        dp.n_sel[r] = a->n_sel[r];
+        dp.ring_first[r] = (wsr / 64) % dp.n_chunks;
+        pre += a->n_sel[r] + ring;
+    }
+    dp.tile_prefix[a->n_req] = pre;
+
+    MergeParams mp{};
+    mp.part_o = dp.part_o;
+    mp.part_ml = dp.part_ml;
+    mp.out = a->out;
+    mp.n_heads = a->n_heads;
+    // groups whose tile range meets request r's tiles
+    {
+        const long long TT = P.total_tiles, G = P.G;
+        int wcur = 0;
+        for (int r = 0; r < a->n_req; ++r) {
+            const long long t0 = dp.tile_prefix[r], t1 = dp.tile_prefix[r + 1];  // t1 > t0 always
+            while ((long long)(wcur + 1) * TT / G <= t0) ++wcur;  // group whose range holds t0
+            int wend = wcur;
+            while ((long long)(wend + 1) * TT / G < t1) ++wend;   // group whose range holds t1-1
+            mp.w_lo[r] = wcur;
+            mp.w_hi[r] = wend;
+        }
+    }
+
+    if (a->ev_attn_begin) LSA_HIP(hipEventRecord(a->ev_attn_begin, stream));
+    hipLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, dp);
+    LSA_HIP(hipGetLastError());
+    if (a->ev_attn_end) LSA_HIP(hipEventRecord(a->ev_attn_end, stream));
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(a->n_req * a->n_heads), dim3(256), 0, stream, mp);
+    LSA_HIP(hipGetLastError());
+    return LSA_OK;
+}
+
+}  // namespace
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes) {
+    DecodePlan P;
+    lsa_status st = decode_plan(a, &P, true);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(bytes != nullptr, "lsa_sparse_decode_workspace: bytes is null");
+    *bytes = P.total;
+    return LSA_OK;
+}
+
+extern "C" lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream) {
+    lsa_status st = decode_check(a);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(a->q && a->ring && a->out, "lsa_sparse_decode: null device pointer");
+    bool any_sel = false;
+    for (int r = 0; r < a->n_req; ++r) any_sel |= a->n_sel[r] > 0;
+    LSA_CHECK_ARG(!any_sel || (a->pool && a->table && a->n_slots_total > 0),
+                  "lsa_sparse_decode: selected blocks but no pool/table");
+    DecodePlan P;
+    st = decode_plan(a, &P, false);
+    if (st != LSA_OK) return st;
+    if (a->workspace == nullptr || a->workspace_bytes < P.total)
+        return fail(LSA_ERR_WORKSPACE, "lsa_sparse_decode: workspace of %zu bytes, need %zu",
+                    a->workspace ? a->workspace_bytes : (size_t)0, P.total);
+    LSA_CHECK_ARG(((uintptr_t)a->q % 16) == 0 && ((uintptr_t)a->ring % 16) == 0 &&
+                      (a->pool == nullptr || ((uintptr_t)a->pool % 16) == 0) &&
+                      (a->k_new == nullptr || ((uintptr_t)a->k_new % 16) == 0) &&
+                      (a->table == nullptr || ((uintptr_t)a->table % 8) == 0),
+                  "lsa_sparse_decode: q, ring, pool, k_new must be 16-byte aligned, table 8-byte aligned");
+    if (a->dtype == LSA_BF16) {
+        if (a->head_dim == 128) return launch_decode<Bf16Ops<128>, uint16_t, 128>(a, P, stream);
+        return launch_decode<Bf16Ops<64>, uint16_t, 64>(a, P, stream);
+    }
+    if (a->head_dim == 128) return launch_decode<F32Ops<128>, float, 128>(a, P, stream);
+    return launch_decode<F32Ops<64>, float, 64>(a, P, stream);
+}

@@ -1,0 +1,202 @@
+// Cold pool -> hot pool block gather for one request (zhichai.net explainer of "FlashMemory-DeepSeek-V4",
+// section 2 step 3: the selected blocks are moved from the CPU cold pool to the GPU; step 5: the loaded
+// set is refreshed).
+//
+// Host: diff the new ascending selection against the request's resident set, free the slots of blocks
+// that left, give free slots to blocks that entered, and write the copy list and the new block table
+// into the caller's pinned staging buffer.  Device: one kernel copies every entering 64-token block
+// (one contiguous block-format record) from the cold pool into its slot and copies the table.  The cold
+// pool may be pinned host memory (the kernel reads it over the host link, zero-copy) or device memory.
+#include <algorithm>
+#include <vector>
+
+#include "lsa_internal.hpp"
+
+namespace lsa {
+namespace {
+
+struct GatherParams {
+    const char* cold;
+    char* hot;
+    const int* copies;  // (source block, slot) pairs, device-visible
+    const int* tsrc;    // table pairs, device-visible
+    int* tdst;
+    int n_copies;
+    int n_table;
+    int block_bytes;
+};
+
+// Each group copies blocks g, g + G, ...: 256 threads x 16-byte vectors, all loads of a block in
+// flight before its stores.
+__global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
+    const int per_thread = p.block_bytes / (16 * 256);  // 16-byte vectors per thread per block
+    for (int c = blockIdx.x; c < p.n_copies; c += gridDim.x) {
+        const int src = p.copies[2 * c];
+        const int dst = p.copies[2 * c + 1];
+        const uint4* s = reinterpret_cast<const uint4*>(p.cold + (size_t)src * p.block_bytes);
+        uint4* d = reinterpret_cast<uint4*>(p.hot + (size_t)dst * p.block_bytes);
+        uint4 buf[8];
+        for (int k0 = 0; k0 < per_thread; k0 += 8) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k0 + k < per_thread) buf[k] = s[(k0 + k) * 256 + threadIdx.x];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k0 + k < per_thread) d[(k0 + k) * 256 + threadIdx.x] = buf[k];
+        }
+    }
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < 2 * p.n_table; e += gridDim.x * 256) p.tdst[e] = p.tsrc[e];
+}
+
+// Device-visible address of a buffer that is either device memory or pinned host memory.
+lsa_status device_view(const void* ptr, const char* what, const void** out, bool* is_host) {
+    hipPointerAttribute_t attr{};
+    hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(LSA_ERR_INVALID, "lsa_gather_blocks: %s is neither device nor pinned host memory", what);
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+        *out = ptr;
+        *is_host = false;
+        return LSA_OK;
+    }
+    if (attr.type == hipMemoryTypeHost) {
+        void* dptr = nullptr;
+        e = hipHostGetDevicePointer(&dptr, const_cast<void*>(ptr), 0);
+        if (e != hipSuccess || dptr == nullptr) {
+            (void)hipGetLastError();
+            return fail(LSA_ERR_INVALID, "lsa_gather_blocks: %s is host memory that is not mapped for the device", what);
+        }
+        *out = dptr;
+        *is_host = true;
+        return LSA_OK;
+    }
+    return fail(LSA_ERR_INVALID, "lsa_gather_blocks: %s has memory type %d (need device or pinned host)", what,
+                (int)attr.type);
+}
+
+}  // namespace
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream) {
+    LSA_CHECK_ARG(a != nullptr, "lsa_gather_blocks: null args");
+    LSA_CHECK_ARG(a->reserved1 == 0, "lsa_gather_blocks: reserved1 must be 0");
+    LSA_CHECK_ARG(a->n_blocks >= 1 && a->n_blocks <= (1ll << 30), "lsa_gather_blocks: n_blocks=%lld", (long long)a->n_blocks);
+    LSA_CHECK_ARG(a->block_bytes > 0 && a->block_bytes % 4096 == 0,
+                  "lsa_gather_blocks: block_bytes=%d (multiple of 4096)", a->block_bytes);
+    LSA_CHECK_ARG(a->n_new >= 0 && (a->n_new == 0 || a->new_ids), "lsa_gather_blocks: n_new=%d / new_ids", a->n_new);
+    LSA_CHECK_ARG(a->slot_of_block && a->free_slots && a->n_free && a->n_copied && a->n_kept,
+                  "lsa_gather_blocks: null host state pointer");
+    LSA_CHECK_ARG(a->capacity >= 0 && a->n_slots_total >= a->capacity, "lsa_gather_blocks: capacity=%d n_slots_total=%d",
+                  a->capacity, a->n_slots_total);
+    LSA_CHECK_ARG(*a->n_free >= 0 && *a->n_free <= a->capacity, "lsa_gather_blocks: n_free=%d outside 0..capacity",
+                  *a->n_free);
+    LSA_CHECK_ARG(a->cold && a->hot && a->table_dev && a->stage, "lsa_gather_blocks: null buffer");
+    for (int k = 0; k < a->n_new; ++k) {
+        LSA_CHECK_ARG(a->new_ids[k] >= 0 && a->new_ids[k] < a->n_blocks, "lsa_gather_blocks: new_ids[%d]=%d out of range",
+                      k, a->new_ids[k]);
+        LSA_CHECK_ARG(k == 0 || a->new_ids[k] > a->new_ids[k - 1], "lsa_gather_blocks: new_ids not strictly ascending at %d", k);
+    }
+    if (a->n_new > a->capacity)
+        return fail(LSA_ERR_CAPACITY, "lsa_gather_blocks: %d selected blocks exceed the %d hot slots", a->n_new, a->capacity);
+    LSA_CHECK_ARG(a->stage_ints >= 4 * a->n_new, "lsa_gather_blocks: stage holds %d ints, need %d", a->stage_ints,
+                  4 * a->n_new);
+
+    // ---- plan (no caller state touched yet) ----
+    std::vector<int> leave, enter;
+    int kept = 0, resident = 0;
+    {
+        int j = 0;
+        for (long long b = 0; b < a->n_blocks; ++b) {
+            const bool wanted = j < a->n_new && a->new_ids[j] == b;
+            if (wanted) ++j;
+            const int s = a->slot_of_block[b];
+            if (s >= 0) {
+                LSA_CHECK_ARG(s < a->n_slots_total, "lsa_gather_blocks: slot_of_block[%lld]=%d out of range", b, s);
+                ++resident;
+                if (wanted) ++kept;
+                else leave.push_back((int)b);
+            } else {
+                LSA_CHECK_ARG(s == -1, "lsa_gather_blocks: slot_of_block[%lld]=%d (want -1 or a slot)", b, s);
+                if (wanted) enter.push_back((int)b);
+            }
+        }
+    }
+    LSA_CHECK_ARG(resident + *a->n_free == a->capacity,
+                  "lsa_gather_blocks: %d resident blocks + %d free slots != capacity %d", resident, *a->n_free,
+                  a->capacity);
+    const int avail = *a->n_free + (int)leave.size();
+    if ((int)enter.size() > avail)
+        return fail(LSA_ERR_CAPACITY, "lsa_gather_blocks: %zu entering blocks, %d slots available", enter.size(), avail);
+
+    const void* cold_dev = nullptr;
+    const void* stage_dev = nullptr;
+    bool cold_host = false, stage_host = false;
+    lsa_status st = device_view(a->cold, "cold", &cold_dev, &cold_host);
+    if (st != LSA_OK) return st;
+    st = device_view(a->stage, "stage", &stage_dev, &stage_host);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(stage_host, "lsa_gather_blocks: stage must be pinned host memory");
+
+    // Simulate slot assignment on a copy of the free stack, fill the staging buffer.
+    std::vector<int> freestack(a->free_slots, a->free_slots + *a->n_free);
+    for (int b : leave) freestack.push_back(a->slot_of_block[b]);
+    std::vector<int> new_slot(enter.size());
+    for (size_t k = 0; k < enter.size(); ++k) {
+        new_slot[k] = freestack.back();
+        freestack.pop_back();
+        LSA_CHECK_ARG(new_slot[k] >= 0 && new_slot[k] < a->n_slots_total, "lsa_gather_blocks: free slot %d out of range",
+                      new_slot[k]);
+    }
+    int* stage = a->stage;
+    const int n_copies = (int)enter.size();
+    for (int k = 0; k < n_copies; ++k) {
+        stage[2 * k] = enter[k];
+        stage[2 * k + 1] = new_slot[k];
+    }
+    int* table = stage + 2 * n_copies;
+    {
+        size_t e = 0;
+        for (int k = 0; k < a->n_new; ++k) {
+            const int b = a->new_ids[k];
+            int s = a->slot_of_block[b];
+            if (s < 0) {
+                while (enter[e] != b) ++e;  // enter is ascending, a subsequence of new_ids
+                s = new_slot[e];
+            }
+            table[2 * k] = b;
+            table[2 * k + 1] = s;
+        }
+    }
+
+    if (n_copies > 0 || a->n_new > 0) {
+        DeviceInfo dev;
+        st = current_device(&dev);
+        if (st != LSA_OK) return st;
+        GatherParams gp{};
+        gp.cold = static_cast<const char*>(cold_dev);
+        gp.hot = static_cast<char*>(a->hot);
+        gp.copies = static_cast<const int*>(stage_dev);
+        gp.tsrc = static_cast<const int*>(stage_dev) + 2 * n_copies;
+        gp.tdst = a->table_dev;
+        gp.n_copies = n_copies;
+        gp.n_table = a->n_new;
+        gp.block_bytes = a->block_bytes;
+        const int want = std::max(n_copies, (2 * a->n_new + 255) / 256);
+        const int grid = std::max(1, std::min(want, dev.cu_count * 4));
+        hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, stream, gp);
+        LSA_HIP(hipGetLastError());
+    }
+
+    // ---- commit caller state ----
+    for (int b : leave) a->slot_of_block[b] = -1;
+    for (size_t k = 0; k < enter.size(); ++k) a->slot_of_block[enter[k]] = new_slot[k];
+    std::copy(freestack.begin(), freestack.end(), a->free_slots);
+    *a->n_free = (int)freestack.size();
+    *a->n_copied = n_copies;
+    *a->n_kept = kept;
+    return LSA_OK;
+}

@@ -1,0 +1,224 @@
+"""Device state of a batch of requests running the LSA decode loop on one GPU.
+
+An LSASession owns the buffers the three library calls work on and issues the
+calls in the order the loop needs them.  It moves data (uploads, the device to
+host copy of each new selection) and keeps the host-side residency state; all
+arithmetic of the path happens inside liblsa.so.
+
+Layouts:
+  * W_q                [n_idx][d_idx][d_model]
+  * keys               request r at element n_idx*d_idx*blk_off[r], [n_idx][B_r][d_idx]
+  * cold pool          per request B_r blocks (library block format), pinned host
+                       memory, or device memory when cold_on_device=True
+  * hot pool           sum of the per-request capacities, slots of request r are
+                       slot_base[r] .. slot_base[r] + capacity[r] - 1
+  * window ring        [R][win_cap/64] blocks
+  * block table        request r's (block id, slot) pairs at pair slot_base[r]
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (
+    BLOCK_TOKENS,
+    lsa_block_bytes,
+    lsa_gather_blocks,
+    lsa_index_refresh,
+    lsa_index_refresh_workspace,
+    lsa_pack_blocks,
+    lsa_sparse_decode,
+    lsa_sparse_decode_workspace,
+)
+
+
+def _raw_tensor(arr: np.ndarray, device) -> torch.Tensor:
+    """Upload the raw bytes of a uint16 (bf16 bits) or float32 array."""
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(arr.view(np.int16))
+    elif arr.dtype == np.float32:
+        t = torch.from_numpy(arr)
+    else:
+        raise TypeError(f"unexpected dtype {arr.dtype}")
+    return t.to(device)
+
+
+class LSASession:
+    def __init__(self, *, dtype: str, n_idx: int, d_model: int, d_idx: int, n_heads: int, head_dim: int,
+                 win_cap: int, n_blocks: Sequence[int], w_q: np.ndarray, keys: Sequence[np.ndarray],
+                 capacity: Optional[Sequence[int]] = None, cold_on_device: bool = False,
+                 with_masks: bool = False, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
+                 max_groups: int = 0):
+        self.dtype = dtype
+        self.n_idx, self.d_model, self.d_idx = n_idx, d_model, d_idx
+        self.n_heads, self.head_dim, self.win_cap = n_heads, head_dim, win_cap
+        self.device = torch.device(device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.max_groups = max_groups
+        self.n_req = len(n_blocks)
+        self.n_blocks = np.asarray(n_blocks, dtype=np.int64)
+        self.blk_off = np.concatenate([[0], np.cumsum(self.n_blocks)]).astype(np.int64)
+        self.block_bytes = lsa_block_bytes(dtype, head_dim)
+        if self.block_bytes == 0:
+            raise ValueError("unsupported dtype/head_dim")
+        self.elt = 2 if dtype == "bf16" else 4
+        self.cold_on_device = cold_on_device
+
+        with torch.cuda.stream(self.stream):
+            self.w_q = _raw_tensor(w_q, self.device)
+            self.keys = _raw_tensor(np.concatenate([np.ascontiguousarray(k).reshape(-1) for k in keys]), self.device)
+            total_blocks = int(self.blk_off[-1])
+            self.sel_ids = torch.zeros(total_blocks, dtype=torch.int32, device=self.device)
+            self.sel_count = torch.zeros(self.n_req, dtype=torch.int32, device=self.device)
+            self.word_off = np.concatenate([[0], np.cumsum((self.n_blocks + 63) // 64)]).astype(np.int64)
+            self.masks = (torch.zeros(int(self.word_off[-1]) * (n_idx + 1), dtype=torch.int64, device=self.device)
+                          if with_masks else None)
+            ws = lsa_index_refresh_workspace(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx,
+                                             blk_off=self.blk_off)
+            self.refresh_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
+            self.sel_ids_h = torch.empty(total_blocks, dtype=torch.int32, pin_memory=True)
+            self.sel_count_h = torch.empty(self.n_req, dtype=torch.int32, pin_memory=True)
+
+            # hot pool and residency state
+            cap = np.asarray(capacity if capacity is not None else self.n_blocks, dtype=np.int64)
+            self.capacity = cap
+            self.slot_base = np.concatenate([[0], np.cumsum(cap)]).astype(np.int64)
+            self.n_slots = int(self.slot_base[-1])
+            self.hot = torch.empty(max(1, self.n_slots) * self.block_bytes, dtype=torch.uint8, device=self.device)
+            self.table = torch.zeros(max(1, self.n_slots) * 2, dtype=torch.int32, device=self.device)
+            self.slot_of_block = [np.full(int(b), -1, dtype=np.int32) for b in self.n_blocks]
+            self.free_slots = [np.arange(self.slot_base[r + 1] - 1, self.slot_base[r] - 1, -1, dtype=np.int32)
+                               for r in range(self.n_req)]
+            self.n_free = [np.array([int(c)], dtype=np.int32) for c in cap]
+            self.stage = [torch.empty(max(4, 4 * int(c)), dtype=torch.int32, pin_memory=True) for c in cap]
+            self.n_sel = np.zeros(self.n_req, dtype=np.int32)
+            self.sel_host: List[np.ndarray] = [np.zeros(0, dtype=np.int32) for _ in range(self.n_req)]
+
+            # cold pools and rings
+            self.cold: List[Optional[torch.Tensor]] = [None] * self.n_req
+            n_chunks = win_cap // BLOCK_TOKENS
+            self.ring = torch.zeros(self.n_req * n_chunks * self.block_bytes, dtype=torch.uint8, device=self.device)
+            ws = lsa_sparse_decode_workspace(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap,
+                                             n_req=self.n_req, max_groups=max_groups)
+            self.decode_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        self.last_decode_event: Optional[torch.cuda.Event] = None
+        # record an event after each decode so a gather on another stream can wait for it
+        self.track_decode = False
+
+    # ---------------------------------------------------------------------------------------
+    def load_prefill(self, r: int, k_tok: np.ndarray, v_tok: np.ndarray) -> None:
+        """Pack request r's prefill K/V ([N_r][D] raw) into its cold pool and window ring."""
+        n = int(self.n_blocks[r]) * BLOCK_TOKENS
+        assert k_tok.shape[0] == n and v_tok.shape[0] == n
+        k_tok = np.ascontiguousarray(k_tok)
+        v_tok = np.ascontiguousarray(v_tok)
+        cold_h = torch.empty(int(self.n_blocks[r]) * self.block_bytes, dtype=torch.uint8,
+                             pin_memory=not self.cold_on_device)
+        lsa_pack_blocks(self.dtype, self.head_dim, k_tok, v_tok, 0, n, cold_h, int(self.n_blocks[r]))
+        if self.cold_on_device:
+            with torch.cuda.stream(self.stream):
+                self.cold[r] = cold_h.to(self.device)
+        else:
+            self.cold[r] = cold_h
+        n_chunks = self.win_cap // BLOCK_TOKENS
+        ring_h = np.zeros(n_chunks * self.block_bytes, dtype=np.uint8)
+        w = min(self.win_cap, n)
+        lsa_pack_blocks(self.dtype, self.head_dim, k_tok[n - w:], v_tok[n - w:], n - w, w, ring_h, n_chunks)
+        lo = r * n_chunks * self.block_bytes
+        with torch.cuda.stream(self.stream):
+            self.ring[lo:lo + len(ring_h)].copy_(torch.from_numpy(ring_h).to(self.device))
+
+    # ---------------------------------------------------------------------------------------
+    def refresh(self, reqs: Sequence[int], hidden: np.ndarray, bias: np.ndarray) -> Dict[int, np.ndarray]:
+        """Index refresh for requests `reqs` (hidden [len][d_model] raw, bias [len][n_idx]).
+
+        Enqueues lsa_index_refresh per contiguous run of requests, copies the selections back
+        (one synchronisation) and returns {r: ascending ids}."""
+        reqs = list(reqs)
+        bias_t = torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32).reshape(len(reqs), self.n_idx))
+        with torch.cuda.stream(self.stream):
+            hid = _raw_tensor(np.ascontiguousarray(hidden).reshape(len(reqs), self.d_model), self.device)
+            bias_d = bias_t.to(self.device)
+            runs = []
+            i = 0
+            while i < len(reqs):
+                j = i
+                while j + 1 < len(reqs) and reqs[j + 1] == reqs[j] + 1:
+                    j += 1
+                runs.append((i, j + 1))
+                i = j + 1
+            for i, j in runs:
+                r0, r1 = reqs[i], reqs[j - 1] + 1
+                self._refresh_run(r0, r1, hid[i:j], bias_d[i:j])
+            for r in reqs:
+                b0, b1 = int(self.blk_off[r]), int(self.blk_off[r + 1])
+                self.sel_ids_h[b0:b1].copy_(self.sel_ids[b0:b1], non_blocking=True)
+            self.sel_count_h.copy_(self.sel_count, non_blocking=True)
+        self.stream.synchronize()
+        out = {}
+        for r in reqs:
+            b0 = int(self.blk_off[r])
+            c = int(self.sel_count_h[r])
+            out[r] = self.sel_ids_h[b0:b0 + c].numpy().copy()
+        return out
+
+    def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor) -> None:
+        off = self.blk_off[r0:r1 + 1] - self.blk_off[r0]
+        key_elem0 = int(self.n_idx * self.d_idx * self.blk_off[r0])
+        masks = None
+        if self.masks is not None:
+            masks = self.masks[int(self.word_off[r0]) * (self.n_idx + 1):]
+        lsa_index_refresh(dtype=self.dtype, d_model=self.d_model, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
+                          w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
+                          sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
+                          workspace=self.refresh_ws, masks=masks, stream=self.stream)
+
+    def masks_of(self, r: int) -> np.ndarray:
+        """Request r's bit planes [n_idx+1][words] (after a refresh with masks enabled)."""
+        w = int(self.word_off[r + 1] - self.word_off[r])
+        base = int(self.word_off[r]) * (self.n_idx + 1)
+        m = self.masks[base:base + w * (self.n_idx + 1)].cpu().numpy().view(np.uint64)
+        return m.reshape(self.n_idx + 1, w)
+
+    # ---------------------------------------------------------------------------------------
+    def gather(self, r: int, ids: np.ndarray, stream: Optional[torch.cuda.Stream] = None):
+        """Make request r's hot pool hold exactly `ids` (returns (copied, kept))."""
+        st = stream if stream is not None else self.stream
+        if st is not self.stream:
+            if not self.track_decode:
+                raise RuntimeError("set track_decode before gathering on a side stream")
+            if self.last_decode_event is not None:
+                st.wait_event(self.last_decode_event)  # slots of leaving blocks may still be read
+        res = lsa_gather_blocks(
+            n_blocks=int(self.n_blocks[r]), n_slots_total=self.n_slots, block_bytes=self.block_bytes,
+            cold=self.cold[r], hot=self.hot, new_ids=ids, slot_of_block=self.slot_of_block[r],
+            free_slots=self.free_slots[r], n_free=self.n_free[r], capacity=int(self.capacity[r]),
+            stage=self.stage[r], table_dev=self.table[2 * int(self.slot_base[r]):], stream=st)
+        self.n_sel[r] = len(ids)
+        self.sel_host[r] = np.asarray(ids, dtype=np.int32)
+        if st is not self.stream:
+            ev = torch.cuda.Event()
+            ev.record(st)
+            self.stream.wait_event(ev)
+        return res
+
+    # ---------------------------------------------------------------------------------------
+    def decode(self, q: torch.Tensor, seq_len: Sequence[int], window: Sequence[int], out: torch.Tensor,
+               k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+               max_groups: Optional[int] = None, ev_attn_begin=None, ev_attn_end=None) -> None:
+        """One decode step for all requests of the session."""
+        lsa_sparse_decode(dtype=self.dtype, n_heads=self.n_heads, head_dim=self.head_dim, win_cap=self.win_cap,
+                          q=q, ring=self.ring, out=out, workspace=self.decode_ws,
+                          tbl_off=self.slot_base[:-1], n_sel=self.n_sel, seq_len=seq_len, window=window,
+                          pool=self.hot, n_slots_total=self.n_slots, table=self.table, k_new=k_new, v_new=v_new,
+                          max_groups=self.max_groups if max_groups is None else max_groups,
+                          ev_attn_begin=ev_attn_begin, ev_attn_end=ev_attn_end, stream=self.stream)
+        if self.track_decode:
+            # one event re-recorded every step: a later wait sees the latest decode
+            if self.last_decode_event is None:
+                self.last_decode_event = torch.cuda.Event()
+            self.last_decode_event.record(self.stream)

@@ -1,0 +1,205 @@
+"""The C-ABI library on the CPU: it loads, exports every function include/lsa.h declares,
+matches the binding's struct layouts, validates arguments before any HIP call, and packs the
+block format correctly.  No compute kernel is launched here."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import lookahead_block_sparse_amd as L
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "lsa.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(lsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L.LIB, n), f"{n} declared in lsa.h but not exported"
+    assert sorted(L.EXPORTED_SYMBOLS) == names
+
+
+def test_abi_version_and_struct_sizes():
+    assert L.LIB.lsa_abi_version() == L.ABI_VERSION
+    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs)):
+        assert L.LIB.lsa_struct_size(i) == ctypes.sizeof(st)
+    assert L.LIB.lsa_struct_size(7) == 0
+
+
+def test_block_bytes():
+    assert L.lsa_block_bytes("bf16", 128) == 2 * 64 * 128 * 2
+    assert L.lsa_block_bytes("bf16", 64) == 2 * 64 * 64 * 2
+    assert L.lsa_block_bytes("f32", 64) == 2 * 64 * 64 * 4
+    assert L.LIB.lsa_block_bytes(1, 96) == 0
+    assert L.LIB.lsa_block_bytes(7, 128) == 0
+
+
+FAKE = 1 << 40  # a non-null address that validation rejects before anything dereferences it
+
+
+def _refresh_kwargs(**over):
+    kw = dict(dtype="bf16", d_model=4096, d_idx=256, n_idx=3, blk_off=[0, 2048])
+    kw.update(over)
+    return kw
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_idx=192), L.LSA_ERR_UNSUPPORTED),
+    (dict(n_idx=5), L.LSA_ERR_UNSUPPORTED),
+    (dict(d_model=4000), L.LSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.LSA_ERR_UNSUPPORTED),
+    (dict(blk_off=[0, 0]), L.LSA_ERR_INVALID),
+    (dict(blk_off=[1, 10]), L.LSA_ERR_INVALID),
+    (dict(blk_off=list(range(0, 66))), L.LSA_ERR_INVALID),
+])
+def test_refresh_workspace_validation(over, status):
+    with pytest.raises(L.LSAError) as e:
+        L.lsa_index_refresh_workspace(**_refresh_kwargs(**over))
+    assert e.value.status == status
+    assert L.LIB.lsa_last_error().decode()
+
+
+def test_refresh_workspace_size():
+    n = L.lsa_index_refresh_workspace(**_refresh_kwargs(blk_off=[0, 16384, 32768, 49152, 65536]))
+    assert n >= 4 * 3 * 256 * 4 + 1024 * 8 + 16
+
+
+def test_refresh_rejects_small_workspace_before_any_hip_call():
+    a, keep = L._refresh_args(dtype="bf16", d_model=4096, d_idx=256, n_idx=3, hidden=FAKE, hidden_req_stride=4096,
+                              hidden_idx_stride=0, w_q=FAKE, keys=FAKE, blk_off=[0, 2048], bias=FAKE, sel_ids=FAKE,
+                              sel_count=FAKE, masks=None, workspace=FAKE, workspace_bytes=16)
+    st = L.LIB.lsa_index_refresh(ctypes.byref(a), None)
+    assert st == L.LSA_ERR_WORKSPACE
+    a.workspace = None
+    a.workspace_bytes = 1 << 30
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_WORKSPACE
+    a.workspace = FAKE
+    a.hidden = None
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+
+
+def _gather_args(n_blocks=100, capacity=8, new_ids=(1, 5, 9), slot_of_block=None, n_free=None, stage_ints=64):
+    sob = np.full(n_blocks, -1, dtype=np.int32) if slot_of_block is None else slot_of_block
+    free = np.arange(capacity, dtype=np.int32)
+    nf = np.array([capacity if n_free is None else n_free], dtype=np.int32)
+    ids = np.asarray(new_ids, dtype=np.int32)
+    outs = np.zeros(2, dtype=np.int32)
+    a = L.GatherArgs()
+    a.n_blocks, a.n_slots_total, a.block_bytes = n_blocks, capacity, 32768
+    a.cold, a.hot = FAKE, FAKE
+    a.new_ids, a.n_new = ids.ctypes.data, len(ids)
+    a.stage_ints = stage_ints
+    a.slot_of_block, a.free_slots, a.n_free = sob.ctypes.data, free.ctypes.data, nf.ctypes.data
+    a.capacity, a.reserved1 = capacity, 0
+    a.stage, a.table_dev = FAKE, FAKE
+    a.n_copied, a.n_kept = outs.ctypes.data, outs[1:].ctypes.data
+    return a, (sob, free, nf, ids, outs)
+
+
+def test_gather_capacity_error_leaves_state_untouched():
+    a, keep = _gather_args(capacity=2, new_ids=(1, 5, 9))
+    sob, free, nf = keep[0].copy(), keep[1].copy(), keep[2].copy()
+    assert L.LIB.lsa_gather_blocks(ctypes.byref(a), None) == L.LSA_ERR_CAPACITY
+    assert np.array_equal(sob, keep[0]) and np.array_equal(free, keep[1]) and np.array_equal(nf, keep[2])
+    assert "exceed" in L.LIB.lsa_last_error().decode()
+
+
+@pytest.mark.parametrize("case", ["unsorted", "dup", "range", "stage", "state", "badslot"])
+def test_gather_validation(case):
+    kw = {}
+    if case == "unsorted":
+        kw = dict(new_ids=(5, 1))
+    elif case == "dup":
+        kw = dict(new_ids=(5, 5))
+    elif case == "range":
+        kw = dict(new_ids=(1, 100))
+    elif case == "stage":
+        kw = dict(stage_ints=4)
+    elif case == "state":
+        kw = dict(n_free=3)  # 0 resident + 3 free != capacity 8
+    elif case == "badslot":
+        sob = np.full(100, -1, dtype=np.int32)
+        sob[3] = 50
+        kw = dict(slot_of_block=sob, n_free=7)
+    a, keep = _gather_args(**kw)
+    before = [x.copy() for x in keep[:3]]
+    assert L.LIB.lsa_gather_blocks(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+    for b, x in zip(before, keep[:3]):
+        assert np.array_equal(b, x)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), L.LSA_ERR_UNSUPPORTED),
+    (dict(n_heads=17), L.LSA_ERR_UNSUPPORTED),
+    (dict(win_cap=100), L.LSA_ERR_INVALID),
+    (dict(window=[9000]), L.LSA_ERR_INVALID),
+    (dict(seq_len=[0]), L.LSA_ERR_INVALID),
+    (dict(k_only=True), L.LSA_ERR_INVALID),
+    (dict(n_req=65), L.LSA_ERR_INVALID),
+])
+def test_decode_validation_before_any_hip_call(over, status):
+    n_req = over.pop("n_req", 1)
+    k_only = over.pop("k_only", False)
+    kw = dict(dtype="bf16", n_heads=16, head_dim=128, win_cap=8192, scale=None, q=FAKE, k_new=FAKE if k_only else None,
+              v_new=None, ring=FAKE, pool=None, n_slots_total=0, table=None, tbl_off=[0] * n_req, n_sel=[0] * n_req,
+              seq_len=[100] * n_req, window=[64] * n_req, out=FAKE, workspace=None, max_groups=0, ev_begin=None,
+              ev_end=None)
+    kw.update(over)
+    a, keep = L._decode_args(**kw)
+    a.workspace, a.workspace_bytes = FAKE, 1 << 30
+    assert L.LIB.lsa_sparse_decode(ctypes.byref(a), None) == status
+
+
+# ---- block format packing (pure host) ------------------------------------------------------
+def _ref_pack(k, v, pos0, n_dst):
+    """Block format written out with NumPy: K rows then V transposed, token p -> block (p//64)%n_dst."""
+    D = k.shape[1]
+    out = {}
+    for i in range(k.shape[0]):
+        p = pos0 + i
+        b = (p // 64) % n_dst
+        K, Vt = out.setdefault(b, (np.zeros((64, D), k.dtype), np.zeros((D, 64), k.dtype)))
+        K[p % 64] = k[i]
+        Vt[:, p % 64] = v[i]
+    return out
+
+
+@pytest.mark.parametrize("dtype,D,pos0,n,n_dst", [
+    ("bf16", 128, 0, 640, 10), ("bf16", 64, 0, 128, 2), ("f32", 64, 0, 256, 4),
+    ("bf16", 128, 4096 - 256, 256, 4),   # a window ring: last 256 tokens into 4 blocks
+    ("bf16", 128, 130, 256, 4),          # unaligned start wraps into the first block
+    ("f32", 128, 7, 200, 5),
+])
+def test_pack_blocks_matches_numpy(dtype, D, pos0, n, n_dst):
+    rng = np.random.default_rng(0)
+    st = np.uint16 if dtype == "bf16" else np.float32
+    k = (rng.integers(0, 60000, (n, D)) if dtype == "bf16" else rng.standard_normal((n, D))).astype(st)
+    v = (rng.integers(0, 60000, (n, D)) if dtype == "bf16" else rng.standard_normal((n, D))).astype(st)
+    bb = L.lsa_block_bytes(dtype, D)
+    dst = np.zeros(n_dst * bb, dtype=np.uint8)
+    L.lsa_pack_blocks(dtype, D, k, v, pos0, n, dst, n_dst, n_threads=3)
+    want = _ref_pack(k, v, pos0, n_dst)
+    blocks = dst.view(st).reshape(n_dst, 2, 64 * D)
+    for b, (K, Vt) in want.items():
+        got_k = blocks[b, 0].reshape(64, D)
+        got_vt = blocks[b, 1].reshape(D, 64)
+        rows = sorted({(pos0 + i) % 64 for i in range(n) if ((pos0 + i) // 64) % n_dst == b})
+        assert np.array_equal(got_k[rows], K[rows])
+        assert np.array_equal(got_vt[:, rows], Vt[:, rows])
+
+
+def test_pack_blocks_rejects_overflow():
+    k = np.zeros((200, 64), dtype=np.float32)
+    with pytest.raises(L.LSAError) as e:
+        L.lsa_pack_blocks("f32", 64, k, k, 0, 200, np.zeros(3 * 32768, np.uint8), 3)
+    assert e.value.status == L.LSA_ERR_INVALID

@@ -1,0 +1,87 @@
+"""Cold pool -> hot pool gather on the GPU: copied bytes, residency delta, slot reuse under the
+smallest capacity, and the device-memory cold pool."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import ABS_TOL, REL_TOL, attention_errors, conditioned_workload, log, make_session, run_loop
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_pool(sess, r, ids):
+    bb = sess.block_bytes
+    base = int(sess.slot_base[r])
+    table = sess.table[2 * base: 2 * (base + len(ids))].view(-1, 2).cpu().numpy()
+    assert np.array_equal(table[:, 0], ids)
+    slots = table[:, 1]
+    assert len(set(slots.tolist())) == len(slots)
+    assert ((slots >= base) & (slots < base + sess.capacity[r])).all()
+    hot = sess.hot.view(-1, bb)
+    cold = sess.cold[r].view(-1, bb)
+    got = hot[torch.as_tensor(slots, dtype=torch.long, device=hot.device)].cpu()
+    want = cold[torch.as_tensor(ids, dtype=torch.long, device=cold.device)].cpu()
+    assert torch.equal(got, want)
+    # host state agrees with the device table
+    assert np.array_equal(sess.slot_of_block[r][ids], slots)
+    assert (sess.slot_of_block[r] >= 0).sum() == len(ids)
+    return dict(zip(ids.tolist(), slots.tolist()))
+
+
+@pytest.mark.parametrize("cold_on_device", [False, True])
+def test_gather_contents_and_delta(cold_on_device):
+    log(f"gather contents cold_on_device={cold_on_device}")
+    wl = conditioned_workload("ctx1m_s", seed=11)
+    sess = make_session(wl, cold_on_device=cold_on_device, with_masks=False)
+    prev = {}
+    for r in range(wl.n_req):
+        prev[r] = {}
+    for k in range(len(wl.refresh_steps[0])):
+        reqs = list(range(wl.n_req))
+        sel = sess.refresh(reqs, np.stack([wl.hidden[r][k] for r in reqs]), wl.bias)
+        for r in reqs:
+            copied, kept = sess.gather(r, sel[r])
+            torch.cuda.synchronize()
+            old = set(prev[r])
+            new = set(sel[r].tolist())
+            assert copied == len(new - old) and kept == len(new & old)
+            cur = _check_pool(sess, r, sel[r])
+            for b in new & old:
+                assert cur[b] == prev[r][b], "a block that stayed moved"
+            prev[r] = cur
+
+
+def test_gather_slot_reuse_minimal_capacity():
+    """Capacity = the largest selection: every refresh reuses freed slots.  Outputs still match
+    the oracle around every refresh."""
+    log("gather WAR stress")
+    wl = conditioned_workload("ctx128k_s", seed=12, steps=4 * 64 + 2)
+    cfg = wl.cfg
+    refs, _ = oracle.simulate(wl, steps=[])
+    cap = [max(len(x.ids) for x in refs[r]) for r in range(wl.n_req)]
+    sess = make_session(wl, capacity=cap, with_masks=False)
+    T = cfg.steps
+    sample = sorted({t for t in range(T) if t % 64 in (0, 1, 63)})
+    gpu, sels = run_loop(wl, sess, range(T), record=sample)
+    _, outs = oracle.simulate(wl, steps=sample)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        e = attention_errors(gpu[t], ref)
+        assert e[0] <= ABS_TOL and e[1] <= REL_TOL, (t, e)
+
+
+def test_gather_capacity_overflow_is_an_error():
+    import lookahead_block_sparse_amd as L
+    log("gather overflow")
+    wl = conditioned_workload("ctx128k_s", seed=13, steps=1)
+    refs, _ = oracle.simulate(wl, steps=[])
+    n = len(refs[0][0].ids)
+    sess = make_session(wl, capacity=[n - 1], with_masks=False)
+    sel = sess.refresh([0], wl.hidden[0][:1], wl.bias[:1])
+    before = sess.slot_of_block[0].copy()
+    with pytest.raises(L.LSAError) as e:
+        sess.gather(0, sel[0])
+    assert e.value.status == L.LSA_ERR_CAPACITY
+    assert np.array_equal(before, sess.slot_of_block[0])
