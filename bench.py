@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lookahead Sparse Attention decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ctx1m] [--cold device|host]
+
+A step is one decode step of the whole batch through the full path: on the
+steps where the refresh cadence (every 64 steps) fires, the index refresh
+(query encoder, block scoring, threshold, OR-union, compaction), the copy of
+the selection to the host, the residency plan and the block gather; then the
+sparse decode (window append, split-K attention, log-sum-exp merge).  W
+untimed warm-up steps run first (they include the first refresh and the
+initial load of every selected block), then K timed steps.
+
+Default workload: 4 requests x 1,048,576-token contexts (16384 blocks of 64
+tokens each), bf16, 3 indexers (d_model 4096, d_idx 256), 16 query heads
+sharing one KV head of dim 128, an 8192-token window, 10% background + 10%
+planted relevant blocks.  Inputs are seeded synthetic data with those shapes
+and distributions.  With --cold device (default) the cold pool sits in HBM, so
+the timed region moves no host data except the selected ids; --cold host puts
+it in pinned host memory and the gather crosses the host link.
+
+Prints one JSON line.  `value` is end-to-end decode tokens/s (requests x K /
+wall time of the timed steps).  `roofline` describes the attention kernel
+(the dominant kernel): algorithmic bytes per launch / mean launch time from
+HIP events.  `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "LSA decode tokens/s at 1M ctx + index-refresh µs; % of HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="ctx1m")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold", choices=("device", "host"), default="device")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-steps", type=int, default=6, help="decode steps per request timed on the CPU")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for counter calibration)")
+    return ap.parse_args()
+
+
+def _bf16_to_f32(raw: np.ndarray) -> np.ndarray:
+    return (raw.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _planting_query(dtype):
+    """Query embeddings used only to place the planted keys (input construction)."""
+    def fn(h, w):
+        hf = _bf16_to_f32(h) if dtype == "bf16" else h
+        wf = _bf16_to_f32(w) if dtype == "bf16" else w
+        return np.stack([wf[i].astype(np.float64) @ hf.astype(np.float64) for i in range(wf.shape[0])])
+    return fn
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted((ROOT / "lookahead_block_sparse_amd" / "csrc").glob("*")):
+        h.update(f.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, khash: str):
+    """HBM traffic of the attention kernel from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    f = ROOT / "profiles" / f"attn_kernel_{workload}_traffic.json"
+    if not f.exists():
+        return None
+    d = json.loads(f.read_text())
+    if d.get("kernel_sources_sha256_16") != khash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, sels, sample_steps: int, seed: int):
+    """Time the oracle on a bounded sample of the same workload: one refresh of every request and
+    `sample_steps` decode steps per request."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cfg = wl.cfg
+    dt = cfg.dtype
+    w_q = oracle.decode_values(wl.w_q, dt)
+    t_ref = 0.0
+    refs = {}
+    for r in range(wl.n_req):
+        t0 = time.perf_counter()
+        keys = oracle.decode_values(wl.keys[r], dt)
+        res = oracle.refresh(oracle.decode_values(wl.hidden[r][0], dt), w_q, keys, wl.bias[r])
+        t_ref += time.perf_counter() - t0
+        refs[r] = res
+    rng = np.random.default_rng(seed)
+    steps = sorted(rng.choice(np.arange(1, min(cfg.steps, 64)), size=sample_steps, replace=False).tolist())
+    t_dec = 0.0
+    n = 0
+    for r in range(wl.n_req):
+        kp, vp = wl.kv_prefill(r)
+        N = int(wl.ctx[r])
+        for t in steps:
+            t0 = time.perf_counter()
+            L = N + t + 1
+            pos = oracle.token_set(L, cfg.window, refs[r].ids, cfg.block)
+            lo = pos < N
+            k = np.empty((len(pos), cfg.head_dim))
+            v = np.empty((len(pos), cfg.head_dim))
+            k[lo] = oracle.decode_values(kp[pos[lo]], dt)
+            v[lo] = oracle.decode_values(vp[pos[lo]], dt)
+            k[~lo] = oracle.decode_values(wl.k_new[pos[~lo] - N, r], dt)
+            v[~lo] = oracle.decode_values(wl.v_new[pos[~lo] - N, r], dt)
+            oracle.attention(oracle.decode_values(wl.q_dec[t, r], dt), k, v, cfg.head_dim ** -0.5)
+            t_dec += time.perf_counter() - t0
+            n += 1
+    return {
+        "value": n / t_dec,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} request-steps (steps {steps} of each of {wl.n_req} requests, selection of the "
+                  f"first refresh) and one refresh per request; float64 NumPy",
+        "refresh_us_per_request": 1e6 * t_ref / wl.n_req,
+        "seconds": t_dec + t_ref,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the LSA decode path on one GPU only; --gpus must be 1 "
+              "(sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from lookahead_block_sparse_amd.session import LSASession
+    from workloads import build_workload, get_config
+
+    def note(msg):
+        print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+    cfg = get_config(args.workload)
+    W, K = args.warmup, args.steps
+    total_steps = W + K
+    t_setup = time.perf_counter()
+    wl = build_workload(cfg, seed=args.seed, steps=max(cfg.steps, total_steps))
+    cfg = wl.cfg
+    if cfg.planted_frac > 0:
+        wl.condition(_planting_query(cfg.dtype), None)
+    note(f"workload {cfg.name}: {wl.n_req} requests, contexts {wl.ctx.tolist()[:4]}..., built")
+
+    dev = torch.device("cuda")
+    sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
+                      n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
+                      w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False)
+    for r in range(wl.n_req):
+        k, v = wl.kv_prefill(r)
+        sess.load_prefill(r, k, v)
+        if args.no_cpu_baseline:
+            wl.drop_kv(r)
+    note(f"session ready in {time.perf_counter() - t_setup:.1f}s (cold pool on {args.cold})")
+
+    def dev_raw(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    # every refresh's hidden state and the biases are device-resident before the timed region
+    hid_dev = {(r, k): dev_raw(wl.hidden[r][k]) for r in range(wl.n_req) for k in range(len(wl.refresh_steps[r]))}
+    bias_dev = torch.from_numpy(np.ascontiguousarray(wl.bias, dtype=np.float32)).to(dev)
+    q_all = dev_raw(wl.q_dec[:total_steps])
+    kn_all = dev_raw(wl.k_new[:total_steps])
+    vn_all = dev_raw(wl.v_new[:total_steps])
+    out = torch.empty((wl.n_req, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    window = np.full(wl.n_req, cfg.window, dtype=np.int32)
+
+    def mk_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    att_ev = [(mk_event(), mk_event()) for _ in range(K)]
+    call_ev = [(mk_event(), mk_event()) for _ in range(K)]
+    ref_ev = {}
+    gather_ev = {}
+    torch.cuda.synchronize()
+
+    # host-side bookkeeping of the algorithmic bytes of every timed attention launch
+    e = 2 if cfg.dtype == "bf16" else 4
+    D, H = cfg.head_dim, cfg.n_heads
+    attn_bytes = []
+    attn_tokens = []
+    gather_host_s = []
+    gather_blocks = []
+    sel_now = {}
+
+    def tokens_at(r, L):
+        ws = max(0, L - cfg.window)
+        ids = sel_now.get(r, np.zeros(0, dtype=np.int64)).astype(np.int64)
+        blk = np.minimum(64, np.maximum(0, ws - 64 * ids)).sum()
+        return int(min(L, cfg.window) + blk)
+
+    def step(t, timed_idx):
+        reqs = wl.refreshes_at(t)
+        if reqs:
+            if timed_idx is not None:
+                ref_ev[t] = (mk_event(), mk_event())
+                gather_ev[t] = (mk_event(), mk_event())
+            hid = torch.stack([hid_dev[(r, wl.refresh_index_at(r, t))] for r in reqs])
+            bias = bias_dev[reqs[0]:reqs[-1] + 1] if reqs == list(range(reqs[0], reqs[-1] + 1)) else \
+                torch.stack([bias_dev[r] for r in reqs])
+            evs = ref_ev.get(t, (None, None)) if timed_idx is not None else (None, None)
+            sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1])
+            h0 = time.perf_counter()
+            if timed_idx is not None:
+                gather_ev[t][0].record(sess.stream)
+            copied = 0
+            for r in reqs:
+                c, _ = sess.gather(r, sel[r])
+                copied += c
+                sel_now[r] = sel[r]
+            if timed_idx is not None:
+                gather_ev[t][1].record(sess.stream)
+                gather_host_s.append(time.perf_counter() - h0)
+                gather_blocks.append(copied)
+        seq_len = (wl.ctx + t + 1).astype(np.int32)
+        kw = {}
+        if timed_idx is not None:
+            kw = dict(ev_attn_begin=att_ev[timed_idx][0], ev_attn_end=att_ev[timed_idx][1])
+            call_ev[timed_idx][0].record(sess.stream)
+            toks = sum(tokens_at(r, int(seq_len[r])) for r in range(wl.n_req))
+            n_sel = int(sess.n_sel.sum())
+            attn_tokens.append(toks)
+            attn_bytes.append(toks * 2 * D * e + wl.n_req * H * D * e + 8 * n_sel)
+        sess.decode(q_all[t], seq_len, window, out, k_new=kn_all[t], v_new=vn_all[t], **kw)
+        if timed_idx is not None:
+            call_ev[timed_idx][1].record(sess.stream)
+
+    note(f"warm-up {W} steps")
+    for t in range(W):
+        step(t, None)
+    torch.cuda.synchronize()
+    note(f"timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    note(f"timed region {elapsed * 1e3:.2f} ms")
+
+    attn_ms = np.array([a.elapsed_time(b) for a, b in att_ev])
+    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
+    ref_us = np.array([1e3 * a.elapsed_time(b) for a, b in ref_ev.values()])
+    gat_us = np.array([1e3 * a.elapsed_time(b) for a, b in gather_ev.values()])
+    attn_bytes = np.array(attn_bytes, dtype=np.float64)
+    achieved = attn_bytes.sum() / (attn_ms.sum() * 1e-3) / 1e9  # GB/s
+
+    # refresh algorithmic bytes for one group of all requests
+    n_blocks_total = int(wl.n_blocks.sum())
+    ref_bytes = (cfg.n_idx * cfg.d_model * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
+                 + wl.n_req * cfg.d_model * e + 4 * sum(len(s) for s in sel_now.values()) + 4 * wl.n_req)
+
+    khash = kernel_hash()
+    res = {
+        "metric": METRIC,
+        "value": wl.n_req * K / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": elapsed * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {wl.n_req} requests x {int(wl.ctx[0])}-token context, {cfg.n_idx} indexers "
+                         f"(d_model {cfg.d_model}, d_idx {cfg.d_idx}), {cfg.n_heads} q-heads / 1 kv-head x "
+                         f"{cfg.head_dim}, window {cfg.window}, refresh every {cfg.tau} steps, "
+                         f"{int(100 * cfg.planted_frac)}% planted + background density {cfg.density}"),
+            "cold_pool": args.cold,
+            "requests": wl.n_req,
+            "context_tokens": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else wl.ctx.tolist(),
+            "seed": args.seed,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_kernel (split-K block-sparse flash-decode)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": stored_traffic(cfg.name, khash),
+            "algorithmic_bytes_per_launch": float(attn_bytes.mean()),
+            "mean_launch_us": float(attn_ms.mean() * 1e3),
+        },
+        "decode_attn_us": float(attn_ms.mean() * 1e3),
+        "decode_call_us": float(call_ms.mean() * 1e3),
+        "decode_only_tokens_per_s": wl.n_req / (call_ms.mean() * 1e-3),
+        "attended_tokens_per_step": float(np.mean(attn_tokens)),
+        "refresh_us": float(np.median(ref_us)) if len(ref_us) else None,
+        "refresh_roofline": ({"achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                              "algorithmic_bytes": ref_bytes} if len(ref_us) else None),
+        "gather_us": float(np.median(gat_us)) if len(gat_us) else None,
+        "gather_blocks_per_refresh": float(np.mean(gather_blocks)) if gather_blocks else None,
+        "gather_host_plan_ms": float(np.median(gather_host_s) * 1e3) if gather_host_s else None,
+        "kernel_sources_sha256_16": khash,
+    }
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = n
+    if not args.no_cpu_baseline:
+        note("timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(wl, sel_now, args.cpu_sample_steps, args.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

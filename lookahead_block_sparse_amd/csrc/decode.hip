@@ -413,25 +413,28 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
     }
 }
 
-// One group per (request, head).  Combines the partials of groups w_lo..w_hi (index w + r).
+// One group per (request, head).  Combines the partials of groups w_lo..w_hi (index w + r): the
+// maximum over all partials first (every thread takes a strided share, then a block reduction), then
+// the rescaled sums.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-    constexpr int SUB = 256 / D;  // partial subsets per thread column
+    constexpr int SUB = 256 / D;  // partial subsets per output element
     __shared__ float s_acc[SUB][D];
     __shared__ float s_l[SUB];
-    __shared__ float s_M;
+    __shared__ float s_max[4];
     const int r = blockIdx.x / p.n_heads;
     const int h = blockIdx.x % p.n_heads;
     const int d = threadIdx.x % D;
     const int sub = threadIdx.x / D;
     const int w0 = p.w_lo[r], w1 = p.w_hi[r];
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int w = w0; w <= w1; ++w) M = fmaxf(M, p.part_ml[((size_t)(w + r) * kHeads + h) * 2]);
-        s_M = M;
-    }
+    float mloc = -INFINITY;
+    for (int w = w0 + (int)threadIdx.x; w <= w1; w += 256)
+        mloc = fmaxf(mloc, p.part_ml[((size_t)(w + r) * kHeads + h) * 2]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = mloc;
     __syncthreads();
-    const float M = s_M;
+    const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     float acc = 0.f, lsum = 0.f;
     for (int w = w0 + sub; w <= w1; w += SUB) {
         const size_t pi = (size_t)(w + r) * kHeads + h;

@@ -133,16 +133,25 @@ class LSASession:
             self.ring[lo:lo + len(ring_h)].copy_(torch.from_numpy(ring_h).to(self.device))
 
     # ---------------------------------------------------------------------------------------
-    def refresh(self, reqs: Sequence[int], hidden: np.ndarray, bias: np.ndarray) -> Dict[int, np.ndarray]:
-        """Index refresh for requests `reqs` (hidden [len][d_model] raw, bias [len][n_idx]).
+    def refresh(self, reqs: Sequence[int], hidden: np.ndarray, bias: np.ndarray, ev_begin=None,
+                ev_end=None) -> Dict[int, np.ndarray]:
+        """Index refresh for requests `reqs` (hidden [len][d_model] raw or a device tensor, bias
+        [len][n_idx] float32 array or device tensor).
 
         Enqueues lsa_index_refresh per contiguous run of requests, copies the selections back
-        (one synchronisation) and returns {r: ascending ids}."""
+        (one synchronisation) and returns {r: ascending ids}.  ev_begin / ev_end (torch events)
+        are recorded around the refresh kernels only."""
         reqs = list(reqs)
-        bias_t = torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32).reshape(len(reqs), self.n_idx))
         with torch.cuda.stream(self.stream):
-            hid = _raw_tensor(np.ascontiguousarray(hidden).reshape(len(reqs), self.d_model), self.device)
-            bias_d = bias_t.to(self.device)
+            if isinstance(hidden, torch.Tensor):
+                hid = hidden.reshape(len(reqs), self.d_model)
+            else:
+                hid = _raw_tensor(np.ascontiguousarray(hidden).reshape(len(reqs), self.d_model), self.device)
+            if isinstance(bias, torch.Tensor):
+                bias_d = bias.reshape(len(reqs), self.n_idx)
+            else:
+                bias_d = torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32).reshape(
+                    len(reqs), self.n_idx)).to(self.device)
             runs = []
             i = 0
             while i < len(reqs):
@@ -151,9 +160,13 @@ class LSASession:
                     j += 1
                 runs.append((i, j + 1))
                 i = j + 1
+            if ev_begin is not None:
+                ev_begin.record(self.stream)
             for i, j in runs:
                 r0, r1 = reqs[i], reqs[j - 1] + 1
                 self._refresh_run(r0, r1, hid[i:j], bias_d[i:j])
+            if ev_end is not None:
+                ev_end.record(self.stream)
             for r in reqs:
                 b0, b1 = int(self.blk_off[r]), int(self.blk_off[r + 1])
                 self.sel_ids_h[b0:b1].copy_(self.sel_ids[b0:b1], non_blocking=True)
