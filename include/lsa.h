@@ -131,7 +131,8 @@ typedef struct lsa_refresh_args {
                                   ceil(B_r/64) words start at word (n_idx+1)*M_r, where M_r is
                                   the sum of W_r' over r' < r; plane i < n_idx holds s[i],
                                   plane n_idx holds u; block b is bit b%64 of word b/64 */
-    void* workspace;           /* dev, workspace_bytes >= lsa_index_refresh_workspace() */
+    void* workspace;           /* dev, 256-byte aligned, workspace_bytes >= lsa_index_refresh_workspace();
+                                  holds q and the per-request counters of one call */
     size_t workspace_bytes;
 } lsa_refresh_args;
 

@@ -103,28 +103,40 @@ struct Bf16Ops {
             for (int kk = 0; kk < 2; ++kk)
                 f.v[dt][kk] = *reinterpret_cast<const bf16x8*>(vt + ((size_t)(16 * dt + lr) * 64 + 32 * kk + 8 * lg) * EB);
     }
-    // Replace the current token (row cur of this tile) by k_new / v_new.
-    __device__ static void patch(Frag& f, int cur, const uint16_t* kn, const uint16_t* vn, int lane) {
-        const int lr = lane & 15, lg = lane >> 4;
+    // Issue point of a tile: every load of the tile (K then V) stays before this point and only the
+    // K operands must have arrived, so the V loads are still in flight during Q K^T.
+    __device__ static void pin_k(const Frag& f) {
+        if constexpr (KS == 4) {
+            asm volatile("" :: "v"(f.k[0][0]), "v"(f.k[0][1]), "v"(f.k[0][2]), "v"(f.k[0][3]), "v"(f.k[1][0]), "v"(f.k[1][1]), "v"(f.k[1][2]), "v"(f.k[1][3]), "v"(f.k[2][0]), "v"(f.k[2][1]), "v"(f.k[2][2]), "v"(f.k[2][3]), "v"(f.k[3][0]), "v"(f.k[3][1]), "v"(f.k[3][2]), "v"(f.k[3][3]) : "memory");
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (tokK(j, lr) == cur)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    f.k[j][ks] = *reinterpret_cast<const bf16x8*>(kn + 32 * ks + 8 * lg);
+                for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(f.k[j][ks]) : "memory");
+        }
+    }
+    // Partial dot product of this lane's query elements (head lr, dims 32ks + 8lg + e) with k_new.
+    __device__ static float dot_q_new(const QReg& q, const uint16_t* kn, int lane) {
+        const int lg = lane >> 4;
+        float acc = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int e = cur - (32 * kk + 8 * lg);
-            if (e >= 0 && e < 8) {
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 k = *reinterpret_cast<const bf16x8*>(kn + 32 * ks + 8 * lg);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const uint16_t bits = vn[16 * dt + lr];
-                    __bf16 val = __builtin_bit_cast(__bf16, bits);
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)q.b[ks][e], (float)k[e], acc);
+        }
+        return acc;
+    }
+    // v_new[16dt + 4lg + i]: the value entries of the output elements this lane accumulates.
+    __device__ static void load_vnew(const uint16_t* vn, int lane, float v[DT][4]) {
+        const int lg = lane >> 4;
 #pragma unroll
-                    for (int ee = 0; ee < 8; ++ee)
-                        if (ee == e) f.v[dt][kk][ee] = val;
-                }
-            }
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint2 w = *reinterpret_cast<const uint2*>(vn + 16 * dt + 4 * lg);
+            v[dt][0] = bf16_lo(w.x);
+            v[dt][1] = bf16_hi(w.x);
+            v[dt][2] = bf16_lo(w.y);
+            v[dt][3] = bf16_hi(w.y);
         }
     }
     __device__ static void qk(const Frag& f, const QReg& q, f32x4 s[4]) {
@@ -147,8 +159,8 @@ struct Bf16Ops {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[dt][kk], pb[kk], o[dt], 0, 0, 0);
     }
+    // Store the current token into ring row `cur` (K row and V^T column).
     __device__ static void write_current(char* base, int cur, const uint16_t* kn, const uint16_t* vn, int lane) {
-        // K row: D*2 bytes = D/8 lanes of 16 bytes; Vt column: D values of 2 bytes
         if (lane < D / 8)
             *reinterpret_cast<uint4*>(base + ((size_t)cur * D + 8 * lane) * EB) = *reinterpret_cast<const uint4*>(kn + 8 * lane);
         char* vt = base + 64 * D * EB;
@@ -193,18 +205,25 @@ struct F32Ops {
             for (int jj = 0; jj < 16; ++jj)
                 f.v[dt][jj] = vt[(16 * dt + lr) * 64 + 16 * (jj >> 2) + 4 * lg + (jj & 3)];
     }
-    __device__ static void patch(Frag& f, int cur, const float* kn, const float* vn, int lane) {
-        const int lr = lane & 15, lg = lane >> 4;
+    __device__ static void pin_k(const Frag& f) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (16 * j + lr == cur)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) f.k[j][ks] = kn[4 * ks + lg];
+            for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(f.k[j][ks]) : "memory");
+    }
+    __device__ static float dot_q_new(const QReg& q, const float* kn, int lane) {
+        const int lg = lane >> 4;
+        float acc = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
-            if (16 * (jj >> 2) + 4 * lg + (jj & 3) == cur)
+        for (int ks = 0; ks < KS; ++ks) acc = fmaf(q.b[ks], kn[4 * ks + lg], acc);
+        return acc;
+    }
+    __device__ static void load_vnew(const float* vn, int lane, float v[DT][4]) {
+        const int lg = lane >> 4;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) f.v[dt][jj] = vn[16 * dt + lr];
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[dt][i] = vn[16 * dt + 4 * lg + i];
     }
     __device__ static void qk(const Frag& f, const QReg& q, f32x4 s[4]) {
 #pragma unroll
@@ -234,12 +253,14 @@ struct F32Ops {
 struct TileDesc {
     const char* base;
     unsigned long long mask;  // valid tokens of the tile
-    int cur;                  // row of the current token to take from k_new/v_new, or -1
+    bool cur;                 // the ring tile whose slot receives the current token
 };
 
 // ------------------------------------------------------------------------------------------
+constexpr int kGroupsPerCU = 2;
+
 template <typename Ops, typename T, int D>
-__global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p) {
     constexpr int DT = D / 16;
     __shared__ float s_o[kWaves][kHeads][D];
     __shared__ float s_m[kWaves][kHeads];
@@ -273,7 +294,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
         const int cur_row = cur_slot & 63;
 
         typename Ops::QReg q;
-        Ops::load_q(q, static_cast<const T*>(p.q) + (size_t)r * p.n_heads * D, p.n_heads, lane);
+        const T* q_r = static_cast<const T*>(p.q) + (size_t)r * p.n_heads * D;
+        Ops::load_q(q, q_r, p.n_heads, lane);
 
         float m_run = -INFINITY, l_run = 0.f;
         f32x4 o[DT];
@@ -282,6 +304,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
 
         const int first = lo + wave;
         const int count = first < hi ? (hi - first + kWaves - 1) / kWaves : 0;
+        const char* cur_base = nullptr;
 
         for (int k0 = 0; k0 < count; k0 += 64) {
             const int kn_ = min(64, count - k0);
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
             }
             auto desc = [&](int k) -> TileDesc {
                 TileDesc d;
-                d.cur = -1;
+                d.cur = false;
                 const int j = first + kWaves * (k0 + k);
                 if (j < n_sel) {
                     const int blk = __builtin_amdgcn_readlane(ent.x, k);
@@ -310,7 +333,11 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
                     if (back < 0) back += p.win_cap;
                     const int pos = L - 1 - back;
                     d.mask = __ballot(pos >= ws);
-                    if (kn && c == cur_chunk) d.cur = cur_row;
+                    if (kn && c == cur_chunk) {
+                        // the slot still holds an old token: the current one is added after the loop
+                        d.cur = true;
+                        d.mask &= ~(1ull << cur_row);
+                    }
                 }
                 return d;
             };
@@ -331,11 +358,13 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
                 mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                 mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
                 const float m_new = fmaxf(m_run, mx);
-                const float corr = fast_exp2(m_run - m_new);
+                // a head with no valid token yet keeps (m, l, o) = (-inf, 0, 0)
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float corr = fast_exp2(m_run - m_use);
                 float ps = 0.f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    sv[e] = fast_exp2(sv[e] - m_new);
+                    sv[e] = fast_exp2(sv[e] - m_use);
                     ps += sv[e];
                 }
                 l_run = l_run * corr + ps;
@@ -344,37 +373,38 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
                 for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
                 Ops::pv(f, sv, o);
             };
-            auto fetch = [&](typename Ops::Frag& f, const TileDesc& d) {
-                if (d.mask == 0ull) return;
+            // One tile in registers per wave; latency is hidden by the second wave on each SIMD
+            // (two groups per CU), which streams its tile while this one computes.  Every tile has a
+            // valid base and nothing but the tile's own loads sits between them and the matrix
+            // products, so the products wait only for the operands they read.
+            for (int k = 0; k < kn_; ++k) {
+                const TileDesc d = desc(k);
+                typename Ops::Frag f;
                 Ops::load(f, d.base, lane);
-                if (d.cur >= 0) Ops::patch(f, d.cur, kn, vn, lane);
-            };
-            auto finish = [&](const TileDesc& d) {
-                if (d.cur >= 0) Ops::write_current(const_cast<char*>(d.base), d.cur, kn, vn, lane);
-            };
-
-            typename Ops::Frag fa, fb;
-            TileDesc da = desc(0), db;
-            fetch(fa, da);
-            for (int k = 0; k < kn_; k += 2) {
-                if (k + 1 < kn_) {
-                    db = desc(k + 1);
-                    fetch(fb, db);
-                }
-                if (da.mask) {
-                    compute(fa, da);
-                    finish(da);
-                }
-                if (k + 1 >= kn_) break;
-                if (k + 2 < kn_) {
-                    da = desc(k + 2);
-                    fetch(fa, da);
-                }
-                if (db.mask) {
-                    compute(fb, db);
-                    finish(db);
-                }
+                Ops::pin_k(f);
+                if (d.cur) cur_base = d.base;
+                if (d.mask) compute(f, d);
             }
+        }
+
+        // ---- the current token: folded into this wave's state, then appended to the ring ----
+        if (cur_base) {
+            float part = Ops::dot_q_new(q, kn, lane);
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            const float s_cur = part * p.scale_log2;
+            const float m_new = fmaxf(m_run, s_cur);
+            const float corr = fast_exp2(m_run - m_new);
+            const float pc = fast_exp2(s_cur - m_new);
+            l_run = l_run * corr + (lg == 0 ? pc : 0.f);
+            m_run = m_new;
+            float vv[DT][4];
+            Ops::load_vnew(vn, lane, vv);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[dt][i] = o[dt][i] * corr + pc * vv[dt][i];
+            Ops::write_current(const_cast<char*>(cur_base), cur_row, kn, vn, lane);
         }
 
         // ---- combine the 4 waves of this segment ----
@@ -413,19 +443,24 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(DecodeParams p) {
     }
 }
 
-// One group per (request, head).  Combines the partials of groups w_lo..w_hi (index w + r): the
-// maximum over all partials first (every thread takes a strided share, then a block reduction), then
-// the rescaled sums.
+// One group per (request, head, 32 output columns).  Combines the partials of groups w_lo..w_hi
+// (index w + r): the maximum over all partials first (strided share per thread, block reduction), then
+// the rescaled sums, 8 partial subsets in parallel per column.
+constexpr int kMergeCols = 32;
+constexpr int kMergeSub = 256 / kMergeCols;
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-    constexpr int SUB = 256 / D;  // partial subsets per output element
-    __shared__ float s_acc[SUB][D];
-    __shared__ float s_l[SUB];
+    __shared__ float s_acc[kMergeSub][kMergeCols];
+    __shared__ float s_l[kMergeSub];
     __shared__ float s_max[4];
-    const int r = blockIdx.x / p.n_heads;
-    const int h = blockIdx.x % p.n_heads;
-    const int d = threadIdx.x % D;
-    const int sub = threadIdx.x / D;
+    constexpr int NC = D / kMergeCols;
+    const int c = blockIdx.x % NC;
+    const int rh = blockIdx.x / NC;
+    const int r = rh / p.n_heads;
+    const int h = rh % p.n_heads;
+    const int d = c * kMergeCols + (int)(threadIdx.x % kMergeCols);
+    const int sub = threadIdx.x / kMergeCols;
     const int w0 = p.w_lo[r], w1 = p.w_hi[r];
     float mloc = -INFINITY;
     for (int w = w0 + (int)threadIdx.x; w <= w1; w += 256)
@@ -436,21 +471,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     __syncthreads();
     const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     float acc = 0.f, lsum = 0.f;
-    for (int w = w0 + sub; w <= w1; w += SUB) {
+#pragma unroll 4
+    for (int w = w0 + sub; w <= w1; w += kMergeSub) {
         const size_t pi = (size_t)(w + r) * kHeads + h;
         const float m = p.part_ml[pi * 2];
         const float sc = m == -INFINITY ? 0.f : fast_exp2(m - M);
         acc += sc * p.part_o[pi * D + d];
         lsum += sc * p.part_ml[pi * 2 + 1];
     }
-    s_acc[sub][d] = acc;
-    if (d == 0) s_l[sub] = lsum;
+    s_acc[sub][threadIdx.x % kMergeCols] = acc;
+    if ((threadIdx.x % kMergeCols) == 0) s_l[sub] = lsum;
     __syncthreads();
     if (sub == 0) {
         float a = 0.f, l = 0.f;
 #pragma unroll
-        for (int s = 0; s < SUB; ++s) {
-            a += s_acc[s][d];
+        for (int s = 0; s < kMergeSub; ++s) {
+            a += s_acc[s][threadIdx.x];
             l += s_l[s];
         }
         p.out[((size_t)r * p.n_heads + h) * D + d] = a / l;
@@ -498,7 +534,8 @@ lsa_status decode_plan(const lsa_decode_args* a, DecodePlan* P, bool sizing_only
     DeviceInfo dev;
     st = current_device(&dev);
     if (st != LSA_OK) return st;
-    const int g_max = a->max_groups > 0 ? std::min(a->max_groups, dev.cu_count) : dev.cu_count;
+    const int g_all = dev.cu_count * kGroupsPerCU;
+    const int g_max = a->max_groups > 0 ? std::min(a->max_groups, g_all) : g_all;
     P->total_tiles = (int)T;
     P->G = sizing_only ? g_max : (int)std::max<long long>(1, std::min<long long>(g_max, (T + kWaves - 1) / kWaves));
     const int n_part = g_max + a->n_req;
@@ -571,7 +608,7 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
     hipLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, dp);
     LSA_HIP(hipGetLastError());
     if (a->ev_attn_end) LSA_HIP(hipEventRecord(a->ev_attn_end, stream));
-    hipLaunchKernelGGL((merge_kernel<D>), dim3(a->n_req * a->n_heads), dim3(256), 0, stream, mp);
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(a->n_req * a->n_heads * (D / kMergeCols)), dim3(256), 0, stream, mp);
     LSA_HIP(hipGetLastError());
     return LSA_OK;
 }

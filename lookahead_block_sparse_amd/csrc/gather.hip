@@ -26,26 +26,27 @@ struct GatherParams {
     int block_bytes;
 };
 
-// Each group copies blocks g, g + G, ...: 256 threads x 16-byte vectors, all loads of a block in
-// flight before its stores.
+// Group g copies blocks g, g + G, ... of the copy list, one 64-token block at a time: 256 threads x
+// 16-byte vectors, every load of the block in flight before its stores.  The table is copied with one
+// grid-wide stride.  (One block per group with many groups measured faster than fewer groups that
+// copy several blocks each.)
+template <int PER>  // 16-byte vectors per thread per block (block_bytes / 4096)
 __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
-    const int per_thread = p.block_bytes / (16 * 256);  // 16-byte vectors per thread per block
-    for (int c = blockIdx.x; c < p.n_copies; c += gridDim.x) {
-        const int src = p.copies[2 * c];
-        const int dst = p.copies[2 * c + 1];
-        const uint4* s = reinterpret_cast<const uint4*>(p.cold + (size_t)src * p.block_bytes);
-        uint4* d = reinterpret_cast<uint4*>(p.hot + (size_t)dst * p.block_bytes);
-        uint4 buf[8];
-        for (int k0 = 0; k0 < per_thread; k0 += 8) {
+    const int G = gridDim.x;
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < 2 * p.n_table; e += G * 256) p.tdst[e] = p.tsrc[e];
+    constexpr int STEP = PER > 8 ? 8 : PER;
+    for (int c = blockIdx.x; c < p.n_copies; c += G) {
+        const uint4* src = reinterpret_cast<const uint4*>(p.cold + (size_t)p.copies[2 * c] * p.block_bytes);
+        uint4* dst = reinterpret_cast<uint4*>(p.hot + (size_t)p.copies[2 * c + 1] * p.block_bytes);
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (k0 + k < per_thread) buf[k] = s[(k0 + k) * 256 + threadIdx.x];
+        for (int v0 = 0; v0 < PER; v0 += STEP) {
+            uint4 b[STEP];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (k0 + k < per_thread) d[(k0 + k) * 256 + threadIdx.x] = buf[k];
+            for (int v = 0; v < STEP; ++v) b[v] = src[(v0 + v) * 256 + threadIdx.x];
+#pragma unroll
+            for (int v = 0; v < STEP; ++v) dst[(v0 + v) * 256 + threadIdx.x] = b[v];
         }
     }
-    for (int e = blockIdx.x * 256 + threadIdx.x; e < 2 * p.n_table; e += gridDim.x * 256) p.tdst[e] = p.tsrc[e];
 }
 
 // Device-visible address of a buffer that is either device memory or pinned host memory.
@@ -85,8 +86,8 @@ extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t st
     LSA_CHECK_ARG(a != nullptr, "lsa_gather_blocks: null args");
     LSA_CHECK_ARG(a->reserved1 == 0, "lsa_gather_blocks: reserved1 must be 0");
     LSA_CHECK_ARG(a->n_blocks >= 1 && a->n_blocks <= (1ll << 30), "lsa_gather_blocks: n_blocks=%lld", (long long)a->n_blocks);
-    LSA_CHECK_ARG(a->block_bytes > 0 && a->block_bytes % 4096 == 0,
-                  "lsa_gather_blocks: block_bytes=%d (multiple of 4096)", a->block_bytes);
+    LSA_CHECK_SUP(a->block_bytes == 16384 || a->block_bytes == 32768 || a->block_bytes == 65536,
+                  "lsa_gather_blocks: block_bytes=%d (16, 32 or 64 KiB: the block format's sizes)", a->block_bytes);
     LSA_CHECK_ARG(a->n_new >= 0 && (a->n_new == 0 || a->new_ids), "lsa_gather_blocks: n_new=%d / new_ids", a->n_new);
     LSA_CHECK_ARG(a->slot_of_block && a->free_slots && a->n_free && a->n_copied && a->n_kept,
                   "lsa_gather_blocks: null host state pointer");
@@ -185,9 +186,14 @@ extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t st
         gp.n_copies = n_copies;
         gp.n_table = a->n_new;
         gp.block_bytes = a->block_bytes;
-        const int want = std::max(n_copies, (2 * a->n_new + 255) / 256);
-        const int grid = std::max(1, std::min(want, dev.cu_count * 4));
-        hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, stream, gp);
+        // one group per copied block (capped), at least enough groups for the table copy
+        const int grid = std::max(1, std::min(std::max(n_copies, (2 * a->n_new + 255) / 256), dev.cu_count * 32));
+        switch (a->block_bytes / 4096) {
+            case 4: hipLaunchKernelGGL(gather_kernel<4>, dim3(grid), dim3(256), 0, stream, gp); break;
+            case 8: hipLaunchKernelGGL(gather_kernel<8>, dim3(grid), dim3(256), 0, stream, gp); break;
+            case 16: hipLaunchKernelGGL(gather_kernel<16>, dim3(grid), dim3(256), 0, stream, gp); break;
+            default: return fail(LSA_ERR_UNSUPPORTED, "lsa_gather_blocks: block_bytes=%d", a->block_bytes);
+        }
         LSA_HIP(hipGetLastError());
     }
 

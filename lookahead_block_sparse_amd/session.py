@@ -79,7 +79,7 @@ class LSASession:
                           if with_masks else None)
             ws = lsa_index_refresh_workspace(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx,
                                              blk_off=self.blk_off)
-            self.refresh_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
+            self.refresh_ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.device)
             self.sel_ids_h = torch.empty(total_blocks, dtype=torch.int32, pin_memory=True)
             self.sel_count_h = torch.empty(self.n_req, dtype=torch.int32, pin_memory=True)
 
@@ -176,6 +176,8 @@ class LSASession:
         for r in reqs:
             b0 = int(self.blk_off[r])
             c = int(self.sel_count_h[r])
+            if c < 0:
+                raise RuntimeError(f"index refresh of request {r} reported an incomplete compaction")
             out[r] = self.sel_ids_h[b0:b0 + c].numpy().copy()
         return out
 
