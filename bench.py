@@ -91,7 +91,7 @@ def stored_traffic(workload: str, khash: str):
     return d.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(wl, sels, sample_steps: int, seed: int):
+def cpu_baseline(wl, sample_steps: int, seed: int):
     """Time the oracle on a bounded sample of the same workload: one refresh of every request and
     `sample_steps` decode steps per request."""
     import oracle
@@ -154,7 +154,7 @@ def main():
 
     import torch
 
-    from lookahead_block_sparse_amd.session import LSASession
+    from lookahead_block_sparse_amd.session import DecodeLoop, LSASession
     from workloads import build_workload, get_config
 
     def note(msg):
@@ -186,7 +186,12 @@ def main():
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     # every refresh's hidden state and the biases are device-resident before the timed region
-    hid_dev = {(r, k): dev_raw(wl.hidden[r][k]) for r in range(wl.n_req) for k in range(len(wl.refresh_steps[r]))}
+    # (stacked per refresh step, in request order)
+    hid_at = {}
+    for t in range(total_steps):
+        reqs = wl.refreshes_at(t)
+        if reqs:
+            hid_at[t] = dev_raw(np.stack([wl.hidden[r][wl.refresh_index_at(r, t)] for r in reqs]))
     bias_dev = torch.from_numpy(np.ascontiguousarray(wl.bias, dtype=np.float32)).to(dev)
     q_all = dev_raw(wl.q_dec[:total_steps])
     kn_all = dev_raw(wl.k_new[:total_steps])
@@ -200,25 +205,17 @@ def main():
         return e
 
     att_ev = [(mk_event(), mk_event()) for _ in range(K)]
-    call_ev = [(mk_event(), mk_event()) for _ in range(K)]
     ref_ev = {}
     gather_ev = {}
     torch.cuda.synchronize()
 
-    # host-side bookkeeping of the algorithmic bytes of every timed attention launch
     e = 2 if cfg.dtype == "bf16" else 4
     D, H = cfg.head_dim, cfg.n_heads
-    attn_bytes = []
-    attn_tokens = []
+    loop = DecodeLoop(sess, wl.ctx, window, out)
     gather_host_s = []
     gather_blocks = []
-    sel_now = {}
-
-    def tokens_at(r, L):
-        ws = max(0, L - cfg.window)
-        ids = sel_now.get(r, np.zeros(0, dtype=np.int64)).astype(np.int64)
-        blk = np.minimum(64, np.maximum(0, ws - 64 * ids)).sum()
-        return int(min(L, cfg.window) + blk)
+    sel_hist = {}        # (request, selection version) -> ascending ids
+    step_log = []        # (t, attended entries per request, selection version per request)
 
     def step(t, timed_idx):
         reqs = wl.refreshes_at(t)
@@ -226,7 +223,7 @@ def main():
             if timed_idx is not None:
                 ref_ev[t] = (mk_event(), mk_event())
                 gather_ev[t] = (mk_event(), mk_event())
-            hid = torch.stack([hid_dev[(r, wl.refresh_index_at(r, t))] for r in reqs])
+            hid = hid_at[t]
             bias = bias_dev[reqs[0]:reqs[-1] + 1] if reqs == list(range(reqs[0], reqs[-1] + 1)) else \
                 torch.stack([bias_dev[r] for r in reqs])
             evs = ref_ev.get(t, (None, None)) if timed_idx is not None else (None, None)
@@ -238,23 +235,17 @@ def main():
             for r in reqs:
                 c, _ = sess.gather(r, sel[r])
                 copied += c
-                sel_now[r] = sel[r]
+                sel_hist[(r, int(sess.sel_version[r]))] = sess.sel_host[r]
             if timed_idx is not None:
                 gather_ev[t][1].record(sess.stream)
                 gather_host_s.append(time.perf_counter() - h0)
                 gather_blocks.append(copied)
-        seq_len = (wl.ctx + t + 1).astype(np.int32)
-        kw = {}
-        if timed_idx is not None:
-            kw = dict(ev_attn_begin=att_ev[timed_idx][0], ev_attn_end=att_ev[timed_idx][1])
-            call_ev[timed_idx][0].record(sess.stream)
-            toks = sum(tokens_at(r, int(seq_len[r])) for r in range(wl.n_req))
-            n_sel = int(sess.n_sel.sum())
-            attn_tokens.append(toks)
-            attn_bytes.append(toks * 2 * D * e + wl.n_req * H * D * e + 8 * n_sel)
-        sess.decode(q_all[t], seq_len, window, out, k_new=kn_all[t], v_new=vn_all[t], **kw)
-        if timed_idx is not None:
-            call_ev[timed_idx][1].record(sess.stream)
+        if timed_idx is None:
+            loop.step(t, q_all[t], kn_all[t], vn_all[t])
+        else:
+            ev = att_ev[timed_idx]
+            loop.step(t, q_all[t], kn_all[t], vn_all[t], ev[0], ev[1])
+            step_log.append((t, loop.n_sel.copy(), sess.sel_version.copy()))
 
     note(f"warm-up {W} steps")
     for t in range(W):
@@ -269,7 +260,21 @@ def main():
     note(f"timed region {elapsed * 1e3:.2f} ms")
 
     attn_ms = np.array([a.elapsed_time(b) for a, b in att_ev])
-    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
+    # algorithmic bytes of every timed attention launch: window tokens + tokens of the attended
+    # selected blocks (below the window start), K and V, plus q and the table entries
+    attn_bytes, attn_tokens = [], []
+    for t, n_att, ver in step_log:
+        toks = 0
+        for r in range(wl.n_req):
+            L = int(wl.ctx[r]) + t + 1
+            ws = max(0, L - cfg.window)
+            toks += min(L, cfg.window)
+            n = int(n_att[r])
+            if n > 0:
+                last = int(sel_hist[(r, int(ver[r]))][n - 1])
+                toks += 64 * (n - 1) + min(64, ws - 64 * last)
+        attn_tokens.append(toks)
+        attn_bytes.append(toks * 2 * D * e + wl.n_req * H * D * e + 8 * int(n_att.sum()))
     ref_us = np.array([1e3 * a.elapsed_time(b) for a, b in ref_ev.values()])
     gat_us = np.array([1e3 * a.elapsed_time(b) for a, b in gather_ev.values()])
     attn_bytes = np.array(attn_bytes, dtype=np.float64)
@@ -278,7 +283,7 @@ def main():
     # refresh algorithmic bytes for one group of all requests
     n_blocks_total = int(wl.n_blocks.sum())
     ref_bytes = (cfg.n_idx * cfg.d_model * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
-                 + wl.n_req * cfg.d_model * e + 4 * sum(len(s) for s in sel_now.values()) + 4 * wl.n_req)
+                 + wl.n_req * cfg.d_model * e + 4 * sum(len(x) for x in sess.sel_host) + 4 * wl.n_req)
 
     khash = kernel_hash()
     res = {
@@ -316,8 +321,6 @@ def main():
             "mean_launch_us": float(attn_ms.mean() * 1e3),
         },
         "decode_attn_us": float(attn_ms.mean() * 1e3),
-        "decode_call_us": float(call_ms.mean() * 1e3),
-        "decode_only_tokens_per_s": wl.n_req / (call_ms.mean() * 1e-3),
         "attended_tokens_per_step": float(np.mean(attn_tokens)),
         "refresh_us": float(np.median(ref_us)) if len(ref_us) else None,
         "refresh_roofline": ({"achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
@@ -340,7 +343,7 @@ def main():
         res["calib_copy_bytes"] = n
     if not args.no_cpu_baseline:
         note("timing the CPU oracle on a sample")
-        res["cpu_baseline"] = cpu_baseline(wl, sel_now, args.cpu_sample_steps, args.seed)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, args.seed)
     print(json.dumps(res), flush=True)
 
 

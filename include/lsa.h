@@ -56,7 +56,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 1
+#define LSA_ABI_VERSION 2
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -131,9 +131,14 @@ typedef struct lsa_refresh_args {
                                   ceil(B_r/64) words start at word (n_idx+1)*M_r, where M_r is
                                   the sum of W_r' over r' < r; plane i < n_idx holds s[i],
                                   plane n_idx holds u; block b is bit b%64 of word b/64 */
-    void* workspace;           /* dev, 256-byte aligned, workspace_bytes >= lsa_index_refresh_workspace();
-                                  holds q and the per-request counters of one call */
+    void* workspace;           /* dev, 256-byte aligned, workspace_bytes >= lsa_index_refresh_workspace(),
+                                  zero-filled before its first use and then left to the library:
+                                  it holds q and per-word counts, tagged with a number unique to
+                                  each call, so nothing is cleared between calls (a captured graph
+                                  that replays one call is therefore not supported) */
     size_t workspace_bytes;
+    hipEvent_t ev_begin;       /* optional, used only when both are set: they receive the start and */
+    hipEvent_t ev_end;         /* end time of the refresh kernel's dispatch */
 } lsa_refresh_args;
 
 lsa_status lsa_index_refresh_workspace(const lsa_refresh_args* a, size_t* bytes);
@@ -218,8 +223,8 @@ typedef struct lsa_decode_args {
     size_t workspace_bytes;
     int32_t max_groups;        /* 0 = all compute units; else cap on work-groups (tests) */
     int32_t reserved1;         /* must be 0 */
-    hipEvent_t ev_attn_begin;  /* optional: recorded on stream right before the attention kernel */
-    hipEvent_t ev_attn_end;    /* optional: recorded right after it (before the merge kernel) */
+    hipEvent_t ev_attn_begin;  /* optional, used only when both are set: they receive the start and */
+    hipEvent_t ev_attn_end;    /* end time of the attention kernel's dispatch (the merge is outside) */
 } lsa_decode_args;
 
 lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes);

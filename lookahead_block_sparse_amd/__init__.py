@@ -11,7 +11,7 @@ kernels and host planner.  The functions carry the C names:
 Device buffers are torch tensors on a ROCm device (raw bit patterns are fine:
 bf16 data may live in int16/uint16 tensors); host-side planner state is NumPy.
 Importing fails with an error if the built library is missing; build it with
-``python -m lookahead_block_sparse_amd._build``.
+``python lookahead_block_sparse_amd/_build.py``.
 """
 
 from __future__ import annotations
@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -75,6 +75,7 @@ class RefreshArgs(Structure):
         ("w_q", c_void_p), ("keys", c_void_p), ("blk_off", POINTER(c_int64)), ("bias", c_void_p),
         ("sel_ids", c_void_p), ("sel_count", c_void_p), ("masks", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+        ("ev_begin", c_void_p), ("ev_end", c_void_p),
     ]
 
 
@@ -110,7 +111,7 @@ def _load():
     if not _LIB_PATH.exists():
         raise ImportError(
             f"{_LIB_PATH} is missing: the LSA path has no fallback; build it with "
-            "`python -m lookahead_block_sparse_amd._build`")
+            "`python lookahead_block_sparse_amd/_build.py`")
     lib = ctypes.CDLL(str(_LIB_PATH))
     lib.lsa_last_error.restype = c_char_p
     lib.lsa_abi_version.restype = c_int32
@@ -221,13 +222,16 @@ def lsa_index_refresh_workspace(*, dtype, d_model, d_idx, n_idx, blk_off) -> int
 
 
 def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_off, bias, sel_ids, sel_count,
-                      workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, stream=None) -> None:
+                      workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, ev_begin=None,
+                      ev_end=None, stream=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a, keep = _refresh_args(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx, hidden=hidden,
                             hidden_req_stride=d_model if hidden_req_stride is None else hidden_req_stride,
                             hidden_idx_stride=hidden_idx_stride, w_q=w_q, keys=keys, blk_off=blk_off, bias=bias,
                             sel_ids=sel_ids, sel_count=sel_count, masks=masks, workspace=workspace,
                             workspace_bytes=ws_bytes)
+    a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
+    a.ev_end = ev_end.cuda_event if ev_end is not None else None
     _check(LIB.lsa_index_refresh(ctypes.byref(a), _stream(stream)))
 
 

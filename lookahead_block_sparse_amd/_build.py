@@ -1,6 +1,6 @@
 """Build liblsa.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m lookahead_block_sparse_amd._build
+    python lookahead_block_sparse_amd/_build.py
 
 Objects go to lookahead_block_sparse_amd/_build/, the library to
 lookahead_block_sparse_amd/liblsa.so.  Every call recompiles.

@@ -16,6 +16,8 @@
 // V^T P^T product (no cross-lane movement of P), and V is stored transposed in the block so each lane's
 // operand is one contiguous 16-byte load.  fp32 inputs use v_mfma_f32_16x16x4_f32 with the same
 // accumulator layout.
+#include <hip/hip_ext.h>
+
 #include <cmath>
 
 #include "lsa_internal.hpp"
@@ -444,50 +446,69 @@ __global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p)
 }
 
 // One group per (request, head, 32 output columns).  Combines the partials of groups w_lo..w_hi
-// (index w + r): the maximum over all partials first (strided share per thread, block reduction), then
-// the rescaled sums, 8 partial subsets in parallel per column.
+// (index w + r) in one pass: 16 partial subsets per column, each with a running maximum (4 partials
+// loaded at once), then the subsets are rescaled to the common maximum in LDS.
 constexpr int kMergeCols = 32;
-constexpr int kMergeSub = 256 / kMergeCols;
+constexpr int kMergeThreads = 512;
+constexpr int kMergeSub = kMergeThreads / kMergeCols;
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     __shared__ float s_acc[kMergeSub][kMergeCols];
-    __shared__ float s_l[kMergeSub];
-    __shared__ float s_max[4];
+    __shared__ float s_l[kMergeSub][kMergeCols];
+    __shared__ float s_m[kMergeSub][kMergeCols];
     constexpr int NC = D / kMergeCols;
     const int c = blockIdx.x % NC;
     const int rh = blockIdx.x / NC;
     const int r = rh / p.n_heads;
     const int h = rh % p.n_heads;
-    const int d = c * kMergeCols + (int)(threadIdx.x % kMergeCols);
+    const int col = threadIdx.x % kMergeCols;
+    const int d = c * kMergeCols + col;
     const int sub = threadIdx.x / kMergeCols;
     const int w0 = p.w_lo[r], w1 = p.w_hi[r];
-    float mloc = -INFINITY;
-    for (int w = w0 + (int)threadIdx.x; w <= w1; w += 256)
-        mloc = fmaxf(mloc, p.part_ml[((size_t)(w + r) * kHeads + h) * 2]);
+    float m = -INFINITY, acc = 0.f, lsum = 0.f;
+    for (int w = w0 + sub; w <= w1; w += 4 * kMergeSub) {
+        float m4[4], o4[4], l4[4];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
-    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = mloc;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-    float acc = 0.f, lsum = 0.f;
-#pragma unroll 4
-    for (int w = w0 + sub; w <= w1; w += kMergeSub) {
-        const size_t pi = (size_t)(w + r) * kHeads + h;
-        const float m = p.part_ml[pi * 2];
-        const float sc = m == -INFINITY ? 0.f : fast_exp2(m - M);
-        acc += sc * p.part_o[pi * D + d];
-        lsum += sc * p.part_ml[pi * 2 + 1];
+        for (int u = 0; u < 4; ++u) {
+            const int wu = min(w + u * kMergeSub, w1);  // clamped: the extra reads are discarded
+            const size_t pi = (size_t)(wu + r) * kHeads + h;
+            m4[u] = p.part_ml[pi * 2];
+            l4[u] = p.part_ml[pi * 2 + 1];
+            o4[u] = p.part_o[pi * D + d];
+        }
+        float mx = m;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (w + u * kMergeSub <= w1) mx = fmaxf(mx, m4[u]);
+        if (mx != -INFINITY) {
+            const float corr = fast_exp2(m - mx);  // m = -inf gives 0
+            acc *= corr;
+            lsum *= corr;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float sc = w + u * kMergeSub <= w1 ? fast_exp2(m4[u] - mx) : 0.f;
+                acc += sc * o4[u];
+                lsum += sc * l4[u];
+            }
+            m = mx;
+        }
     }
-    s_acc[sub][threadIdx.x % kMergeCols] = acc;
-    if ((threadIdx.x % kMergeCols) == 0) s_l[sub] = lsum;
+    s_acc[sub][col] = acc;
+    s_l[sub][col] = lsum;
+    s_m[sub][col] = m;
     __syncthreads();
     if (sub == 0) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kMergeSub; ++s) M = fmaxf(M, s_m[s][col]);
         float a = 0.f, l = 0.f;
 #pragma unroll
         for (int s = 0; s < kMergeSub; ++s) {
-            a += s_acc[s][threadIdx.x];
-            l += s_l[s];
+            const float ms = s_m[s][col];
+            const float sc = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+            a += sc * s_acc[s][col];
+            l += sc * s_l[s][col];
         }
         p.out[((size_t)r * p.n_heads + h) * D + d] = a / l;
     }
@@ -604,11 +625,15 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
         }
     }
 
-    if (a->ev_attn_begin) LSA_HIP(hipEventRecord(a->ev_attn_begin, stream));
-    hipLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, dp);
+    if (a->ev_attn_begin && a->ev_attn_end) {
+        // the events take the dispatch's own start and end timestamps: no extra packets on the stream
+        hipExtLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, a->ev_attn_begin,
+                              a->ev_attn_end, 0, dp);
+    } else {
+        hipLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, dp);
+    }
     LSA_HIP(hipGetLastError());
-    if (a->ev_attn_end) LSA_HIP(hipEventRecord(a->ev_attn_end, stream));
-    hipLaunchKernelGGL((merge_kernel<D>), dim3(a->n_req * a->n_heads * (D / kMergeCols)), dim3(256), 0, stream, mp);
+    hipLaunchKernelGGL((merge_kernel<D>), dim3(a->n_req * a->n_heads * (D / kMergeCols)), dim3(kMergeThreads), 0, stream, mp);
     LSA_HIP(hipGetLastError());
     return LSA_OK;
 }

@@ -7,6 +7,8 @@
 // into the caller's pinned staging buffer.  Device: one kernel copies every entering 64-token block
 // (one contiguous block-format record) from the cold pool into its slot and copies the table.  The cold
 // pool may be pinned host memory (the kernel reads it over the host link, zero-copy) or device memory.
+#include <emmintrin.h>
+
 #include <algorithm>
 #include <vector>
 
@@ -107,23 +109,50 @@ extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t st
                   4 * a->n_new);
 
     // ---- plan (no caller state touched yet) ----
-    std::vector<int> leave, enter;
+    // 64 blocks at a time: a word of wanted bits (from new_ids) against a word of resident bits (from
+    // slot_of_block); only the set bits of the two differences are visited.
+    const long long n_words = (a->n_blocks + 63) / 64;
+    thread_local std::vector<unsigned long long> want;
+    want.assign((size_t)n_words, 0ull);
+    for (int k = 0; k < a->n_new; ++k) want[a->new_ids[k] >> 6] |= 1ull << (a->new_ids[k] & 63);
+    thread_local std::vector<int> leave, enter;
+    leave.clear();
+    enter.clear();
     int kept = 0, resident = 0;
     {
-        int j = 0;
-        for (long long b = 0; b < a->n_blocks; ++b) {
-            const bool wanted = j < a->n_new && a->new_ids[j] == b;
-            if (wanted) ++j;
-            const int s = a->slot_of_block[b];
-            if (s >= 0) {
-                LSA_CHECK_ARG(s < a->n_slots_total, "lsa_gather_blocks: slot_of_block[%lld]=%d out of range", b, s);
-                ++resident;
-                if (wanted) ++kept;
-                else leave.push_back((int)b);
+        // resident bits = sign bits of slot_of_block, four entries per SSE2 movemask; any entry below
+        // -1 or at/above n_slots_total sets a lane of `bad`
+        const int* sob = a->slot_of_block;
+        const __m128i lo = _mm_set1_epi32(-1), hi = _mm_set1_epi32(a->n_slots_total - 1);
+        __m128i bad = _mm_setzero_si128();
+        for (long long wi = 0; wi < n_words; ++wi) {
+            const long long b0 = 64 * wi;
+            unsigned long long neg = 0ull;
+            if (b0 + 64 <= a->n_blocks) {
+                for (int i = 0; i < 16; ++i) {
+                    const __m128i v = _mm_loadu_si128(reinterpret_cast<const __m128i*>(sob + b0 + 4 * i));
+                    neg |= (unsigned long long)_mm_movemask_ps(_mm_castsi128_ps(v)) << (4 * i);
+                    bad = _mm_or_si128(bad, _mm_or_si128(_mm_cmplt_epi32(v, lo), _mm_cmpgt_epi32(v, hi)));
+                }
             } else {
-                LSA_CHECK_ARG(s == -1, "lsa_gather_blocks: slot_of_block[%lld]=%d (want -1 or a slot)", b, s);
-                if (wanted) enter.push_back((int)b);
+                neg = ~0ull;
+                for (long long b = b0; b < a->n_blocks; ++b) {
+                    const int sv = sob[b];
+                    if (sv >= 0) neg &= ~(1ull << (b - b0));
+                    if (sv < -1 || sv >= a->n_slots_total) bad = _mm_set1_epi32(-1);
+                }
             }
+            const unsigned long long res = ~neg, w = want[wi];
+            resident += __builtin_popcountll(res);
+            kept += __builtin_popcountll(res & w);
+            for (unsigned long long x = res & ~w; x; x &= x - 1) leave.push_back((int)(b0 + __builtin_ctzll(x)));
+            for (unsigned long long x = w & ~res; x; x &= x - 1) enter.push_back((int)(b0 + __builtin_ctzll(x)));
+        }
+        if (_mm_movemask_epi8(bad)) {
+            for (long long b = 0; b < a->n_blocks; ++b)
+                LSA_CHECK_ARG(sob[b] >= -1 && sob[b] < a->n_slots_total,
+                              "lsa_gather_blocks: slot_of_block[%lld]=%d (want -1 or a slot below %d)", b, sob[b],
+                              a->n_slots_total);
         }
     }
     LSA_CHECK_ARG(resident + *a->n_free == a->capacity,
@@ -143,9 +172,10 @@ extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t st
     LSA_CHECK_ARG(stage_host, "lsa_gather_blocks: stage must be pinned host memory");
 
     // Simulate slot assignment on a copy of the free stack, fill the staging buffer.
-    std::vector<int> freestack(a->free_slots, a->free_slots + *a->n_free);
+    thread_local std::vector<int> freestack, new_slot;
+    freestack.assign(a->free_slots, a->free_slots + *a->n_free);
     for (int b : leave) freestack.push_back(a->slot_of_block[b]);
-    std::vector<int> new_slot(enter.size());
+    new_slot.resize(enter.size());
     for (size_t k = 0; k < enter.size(); ++k) {
         new_slot[k] = freestack.back();
         freestack.pop_back();

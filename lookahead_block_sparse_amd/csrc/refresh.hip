@@ -2,52 +2,61 @@
 // ordered compaction of the loaded-block list (zhichai.net explainer of "FlashMemory-DeepSeek-V4",
 // section 2 steps 2-3, section 3 (Query Encoder, frozen KIComp keys), section 4 (OR-mode union)).
 //
-// Two kernels on the caller's stream:
-//   encode_kernel  q[r][i][j] = sum_m W_q[i][j][m] h[r][i][m]: one wave per output row (i, j), the row
-//                  read once for every request of the call, fp32 accumulation, q kept in fp32.  It also
-//                  clears the score kernel's per-request counters and word slots.
-//   score_kernel   one group per 64-block word of one request, two waves per indexer.  Each wave issues
-//                  all loads of its 32 key rows at once (8 lanes per row, 16-byte loads), forms
-//                  z = q.k + bias in fp32 and turns z > 0 into a 64-bit word with a wavefront ballot;
-//                  the group ORs the indexer words into the union word.  The group publishes the union
-//                  word and counts itself on its request's counter; the group that counts last scans the
-//                  request's word popcounts and writes the ascending ids and the count.  Groups never wait
-//                  for each other: the last one only reads words whose writers have all finished.
-// Cross-group values travel in 64-bit words written with device-scope atomic stores and carrying a
-// "written" flag, read with device-scope atomic loads, so no memory fence is needed.  Atomics on one
-// address serialize on this GPU, hence one counter per request instead of one for the whole launch.
+// One kernel of 4-wave groups, three roles in this order of group index:
+//   encode   q[r][i][j] = sum_m W_q[i][j][m] h[r][i][m]: two waves per pair of output rows, each
+//            W_q row read once for every request, fp32 accumulation, q kept in fp32.
+//   score    one wave per unit = 32 key rows of one indexer in one 64-block word.  The wave issues
+//            all loads of its rows, then waits for its q, forms z = q.k + bias in fp32, turns z > 0
+//            into 32 bits with a wavefront ballot and publishes them.  Waves never synchronise with
+//            the other waves of their group.
+//   compact  one per request: waits until every unit of the request has published, ORs the
+//            indexers' bits into the union words, takes the exclusive prefix of their popcounts
+//            (wave scans, wave totals through LDS), and every thread writes the ids of its words in
+//            ascending order; then the count.
+// A group only waits for groups with a lower index, which were dispatched before it, and every
+// wait is bounded: a wait that gives up marks the request, whose count is then written as -1.
+// Values that cross groups travel in 64-bit words whose upper half is the call's number and lower
+// half the value, stored and loaded with device-scope atomics: a word is valid for this call when
+// its tag matches, so nothing has to be cleared between calls and no fence is needed.
+#include <hip/hip_ext.h>
+
+#include <atomic>
+
 #include "lsa_internal.hpp"
 
 namespace lsa {
 namespace {
 
 constexpr int kMaxReq = LSA_MAX_REFRESH_REQ;
+constexpr int kThreads = 256;
 constexpr unsigned kSpinLimit = 1u << 16;
-constexpr unsigned long long kWritten = 1ull << 32;
+constexpr unsigned long long kTagMask = 0xffffffff00000000ull;
 
-struct EncodeParams {
+struct RefreshParams {
     const void* hidden;
     long long hidden_req_stride, hidden_idx_stride;
     const void* w_q;
-    float* q;                         // [n_req][n_idx][d_idx]
-    unsigned* counters;               // [n_req], cleared here
-    unsigned long long* words;        // [total_words][2], cleared here
-    int n_req, d_model, d_idx, n_idx, total_words;
-};
-
-struct ScoreParams {
     const void* keys;
-    const float* q;
     const float* bias;
     int* sel_ids;
     int* sel_count;
     unsigned long long* masks;
-    unsigned long long* words;  // [total_words][2]: union word halves, each (written flag << 32 | 32 bits)
-    unsigned* counters;
-    int n_req, n_idx;
+    unsigned long long* qw;   // [n_req][n_idx][d_idx]          tag | fp32 bits of q
+    unsigned long long* hw;   // [total words][n_idx][2]        tag | 32 bits of one unit
+    unsigned long long* bad;  // [n_req]                        tag when a wait of the request gave up
+    unsigned long long tag;   // call number << 32
+    int n_req, d_model, d_idx, n_idx, n_units, n_encode_groups, n_score_groups;
     long long blk_off[kMaxReq + 1];
     int word_off[kMaxReq + 1];
 };
+
+__device__ __forceinline__ void put(unsigned long long* w, unsigned long long tag, unsigned v) {
+    __hip_atomic_store(w, tag | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long get(const unsigned long long* w) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tagged(unsigned long long w, unsigned long long tag) { return (w & kTagMask) == tag; }
 
 // 16 bytes of T: 8 bf16 or 4 fp32.
 template <typename T>
@@ -99,75 +108,100 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Query Encoder.  Grid: ceil(n_idx*d_idx/4) groups of 256 threads; wave w of group g owns output row
-// 4g+w.  Lane l reads 16-byte chunks l, l+64, ... of the W_q row and of each request's hidden state.
+// Query Encoder role.  A group works on rows of one indexer: group g = i*gpi + k owns the
+// kEncRows*waves/2 rows from k*kEncRows*waves/2 on; waves 2m and 2m+1 sum the two halves of rows
+// m*kEncRows ..: each wave loads the halves of kEncRows W_q rows and the matching halves of four
+// requests' hidden states in one round (a hidden-state chunk serves every row of the wave).  Lane
+// l reads 16-byte chunks l, l+64, ... of its half.
+constexpr int kEncRows = 2;  // W_q rows per wave
+constexpr int kEncReq = 4;   // requests per round
+
 template <typename T>
-__global__ __launch_bounds__(256) void encode_kernel(EncodeParams p) {
+__device__ void encode_role(const RefreshParams& p, int g) {
     using C = Chunk<T>;
+    __shared__ float s_part[8][kEncRows][kEncReq];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (blockIdx.x == 0) {
-        for (int e = threadIdx.x; e < p.n_req; e += 256) p.counters[e] = 0u;
-    }
-    for (int e = blockIdx.x * 256 + threadIdx.x; e < 2 * p.total_words; e += gridDim.x * 256) p.words[e] = 0ull;
-    if (row >= p.n_idx * p.d_idx) return;
-    const int i = row / p.d_idx;
-    const int n_chunks = p.d_model / C::N;
-    const uint4* w = reinterpret_cast<const uint4*>(static_cast<const T*>(p.w_q) + (size_t)row * p.d_model);
+    const int wave = threadIdx.x >> 6;
+    const int quads = (int)(blockDim.x >> 7);
+    const int gpi = (p.d_idx + kEncRows * quads - 1) / (kEncRows * quads);
+    const int i = g / gpi;
+    const int j0 = ((g % gpi) * quads + (wave >> 1)) * kEncRows;
+    const int half = wave & 1;
+    const int hc = p.d_model / C::N / 2;  // 16-byte chunks per half row
+    const T* wbase = static_cast<const T*>(p.w_q) + (size_t)i * p.d_idx * p.d_model;
     const T* hid = static_cast<const T*>(p.hidden) + (size_t)i * p.hidden_idx_stride;
-    for (int r0 = 0; r0 < p.n_req; r0 += 4) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < n_chunks; c0 += 64 * 8) {
-            // unconditional loads from clamped indices (zeroed after loading) keep all in flight
-            uint4 wc[8];
-            uint4 hc[4][8];
+    for (int r0 = 0; r0 < p.n_req; r0 += kEncReq) {
+        float acc[kEncRows][kEncReq] = {};
+        for (int c0 = 0; c0 < hc; c0 += 64 * 4) {
+            // unconditional loads from clamped indices (masked after loading) keep all in flight
+            uint4 wc[kEncRows][4];
+            uint4 hv[kEncReq][4];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) wc[k] = w[min(c0 + k * 64 + lane, n_chunks - 1)];
+            for (int jj = 0; jj < kEncRows; ++jj) {
+                const uint4* w = reinterpret_cast<const uint4*>(wbase + (size_t)min(j0 + jj, p.d_idx - 1) * p.d_model) + half * hc;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint4* h = reinterpret_cast<const uint4*>(hid + (size_t)min(r0 + rr, p.n_req - 1) * p.hidden_req_stride);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) hc[rr][k] = h[min(c0 + k * 64 + lane, n_chunks - 1)];
+                for (int k = 0; k < 4; ++k) wc[jj][k] = w[min(c0 + k * 64 + lane, hc - 1)];
             }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
+            for (int rr = 0; rr < kEncReq; ++rr) {
+                const uint4* h = reinterpret_cast<const uint4*>(hid + (size_t)min(r0 + rr, p.n_req - 1) * p.hidden_req_stride) + half * hc;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float d = dot_chunks<T>(wc[k], hc[rr][k]);
-                    acc[rr] += (c0 + k * 64 + lane < n_chunks) ? d : 0.f;
-                }
+                for (int k = 0; k < 4; ++k) hv[rr][k] = h[min(c0 + k * 64 + lane, hc - 1)];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool live = c0 + k * 64 + lane < hc;
+#pragma unroll
+                for (int jj = 0; jj < kEncRows; ++jj)
+#pragma unroll
+                    for (int rr = 0; rr < kEncReq; ++rr) {
+                        const float d = dot_chunks<T>(wc[jj][k], hv[rr][k]);
+                        acc[jj][rr] += live ? d : 0.f;
+                    }
+            }
         }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const float s = wave_sum(acc[rr]);
-            if (lane == 0 && r0 + rr < p.n_req) p.q[(size_t)(r0 + rr) * p.n_idx * p.d_idx + row] = s;
+        for (int jj = 0; jj < kEncRows; ++jj)
+#pragma unroll
+            for (int rr = 0; rr < kEncReq; ++rr) {
+                const float v = wave_sum(acc[jj][rr]);
+                if (lane == 0) s_part[wave][jj][rr] = v;
+            }
+        __syncthreads();
+        if (half == 0 && lane < kEncRows * kEncReq) {
+            const int jj = lane / kEncReq, rr = lane % kEncReq;
+            const int j = j0 + jj;
+            if (j < p.d_idx && r0 + rr < p.n_req) {
+                const float q = s_part[wave][jj][rr] + s_part[wave + 1][jj][rr];
+                put(&p.qw[((size_t)(r0 + rr) * p.n_idx + i) * p.d_idx + j], p.tag, __float_as_uint(q));
+            }
         }
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// Scoring + threshold + union + compaction.  Grid: one group per word (64 blocks) over all requests;
-// blockDim = 128 * n_idx: waves 2i and 2i+1 score rows 0..31 and 32..63 of indexer i.
-constexpr int kScoreWavesPerIdx = 2;
-
+// Scoring role: wave w of score group gs takes unit 4*gs + w = (word, indexer i, half): rows
+// 32*half .. 32*half + 31 of the word's 64 blocks for indexer i.
 template <typename T, int DIDX>
-__global__ __launch_bounds__(128 * 4, 3) void score_kernel(ScoreParams p) {
+__device__ void score_role(const RefreshParams& p, int gs) {
     using C = Chunk<T>;
     constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
     constexpr int LPR = ROW_BYTES / 128;  // 16-byte loads per lane per row (8 lanes per row)
     constexpr int QPL = LPR * C::N;       // q values held per lane
     constexpr int HALF = (LPR == 8) ? 2 : 1;
     constexpr int GH = 4 / HALF;          // groups of 8 rows per pass (32 rows per wave)
+    constexpr int QW = DIDX / 64;         // q words fetched per lane
     static_assert(LPR >= 1 && LPR <= 8, "row size");
-
-    __shared__ unsigned s_half[8];
-    __shared__ int s_last;
-    __shared__ int s_scan[512];
-    __shared__ unsigned s_missing;
+    __shared__ float s_q[kThreads / 64][DIDX];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int word = blockIdx.x;
+    const int unit = 4 * gs + wave;
+    if (unit >= p.n_units) return;
+    const int word = unit / (2 * p.n_idx);
+    const int i = (unit / 2) % p.n_idx;
+    const int half = unit & 1;
     int r = 0;
     while (r + 1 < p.n_req && p.word_off[r + 1] <= word) ++r;
     const int lw = word - p.word_off[r];
@@ -175,130 +209,167 @@ __global__ __launch_bounds__(128 * 4, 3) void score_kernel(ScoreParams p) {
     const int n_blk = (int)(p.blk_off[r + 1] - b_first);
     const int b0 = lw * 64;
     const int n_valid = min(64, n_blk - b0);
-    const int n_words_r = p.word_off[r + 1] - p.word_off[r];
 
-    // ---- 32 rows of one indexer per wave ----
-    {
-        const int i = wave / kScoreWavesPerIdx;
-        const int half = wave % kScoreWavesPerIdx;
-        const int x = lane & 7;      // 16-byte column inside a 128-byte slice of the row
-        const int rsub = lane >> 3;  // row inside a group of 8 rows
-        const char* rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + (size_t)i * n_blk + b0) * ROW_BYTES;
-        const float* qv = p.q + ((size_t)r * p.n_idx + i) * DIDX;
-        const float bias = p.bias[r * p.n_idx + i];
-        unsigned bits = 0u;
+    const int x = lane & 7;      // 16-byte column inside a 128-byte slice of the row
+    const int rsub = lane >> 3;  // row inside a group of 8 rows
+    const char* rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + (size_t)i * n_blk + b0) * ROW_BYTES;
+    const unsigned long long* qrow = p.qw + ((size_t)r * p.n_idx + i) * DIDX;
+    const float bias = p.bias[r * p.n_idx + i];
+    unsigned bits = 0u;
+    bool q_ok = true;
+    float qr[QPL];
 #pragma unroll
-        for (int hh = 0; hh < HALF; ++hh) {
-            // unconditional loads (rows past the request's last block re-read its last row and are
-            // masked out below), so all of them are in flight together
-            uint4 v[GH][LPR];
+    for (int hh = 0; hh < HALF; ++hh) {
+        // unconditional loads (rows past the request's last block re-read its last row and are
+        // masked out below), so all of them are in flight together
+        uint4 v[GH][LPR];
 #pragma unroll
-            for (int g = 0; g < GH; ++g) {
-                const int rowi = min(32 * half + (hh * GH + g) * 8 + rsub, n_valid - 1);
-                const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)rowi * ROW_BYTES + x * 16);
+        for (int g = 0; g < GH; ++g) {
+            const int rowi = min(32 * half + (hh * GH + g) * 8 + rsub, n_valid - 1);
+            const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)rowi * ROW_BYTES + x * 16);
 #pragma unroll
-                for (int k = 0; k < LPR; ++k) v[g][k] = src[k * 8];
+            for (int k = 0; k < LPR; ++k) v[g][k] = src[k * 8];
+        }
+        if (hh == 0) {
+            asm volatile("" ::: "memory");  // the key loads are issued before the wait for q
+            // wait for this (request, indexer)'s q: one lane polls one word, then the wave fetches
+            // the row (lane l: words QW*l ..), checks every tag and passes the values through LDS to
+            // the lanes that use them
+            unsigned spins = 0;
+            if (lane == 0) {
+                while (!tagged(get(qrow + DIDX - 1), p.tag) && ++spins <= kSpinLimit) __builtin_amdgcn_s_sleep(8);
             }
-            float qr[QPL];
+            spins = __shfl(spins, 0, 64);
+            for (;;) {
+                bool all = true;
+#pragma unroll
+                for (int k = 0; k < QW; ++k) {
+                    const unsigned long long wq = get(qrow + QW * lane + k);
+                    all = all && tagged(wq, p.tag);
+                    s_q[wave][QW * lane + k] = __uint_as_float((unsigned)wq);
+                }
+                if (__all(all)) break;
+                if (++spins > kSpinLimit) {
+                    q_ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);
+            }
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int k = 0; k < LPR; ++k)
 #pragma unroll
-                for (int e = 0; e < C::N; ++e) qr[k * C::N + e] = qv[(k * 128 + x * 16) / (int)sizeof(T) + e];
-#pragma unroll
-            for (int g = 0; g < GH; ++g) {
-                const int rowi = 32 * half + (hh * GH + g) * 8 + rsub;
-                float acc = 0.f;
-#pragma unroll
-                for (int k = 0; k < LPR; ++k) acc += dot_chunk_f32<T>(v[g][k], qr + k * C::N);
-                acc += __shfl_xor(acc, 1, 64);
-                acc += __shfl_xor(acc, 2, 64);
-                acc += __shfl_xor(acc, 4, 64);
-                const bool keep = (rowi < n_valid) && (acc + bias > 0.f);
-                const unsigned long long m = __ballot(keep);
-                unsigned b8 = 0u;  // lanes 8j..8j+7 all hold row 8g+j: take bit 8j
-#pragma unroll
-                for (int j = 0; j < 8; ++j) b8 |= (unsigned)((m >> (8 * j)) & 1ull) << j;
-                bits |= b8 << (8 * (hh * GH + g));
-            }
+                for (int e = 0; e < C::N; ++e) qr[k * C::N + e] = s_q[wave][(k * 128 + x * 16) / (int)sizeof(T) + e];
         }
-        if (lane == 0) s_half[wave] = bits;
+#pragma unroll
+        for (int g = 0; g < GH; ++g) {
+            const int rowi = 32 * half + (hh * GH + g) * 8 + rsub;
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < LPR; ++k) acc += dot_chunk_f32<T>(v[g][k], qr + k * C::N);
+            acc += __shfl_xor(acc, 1, 64);
+            acc += __shfl_xor(acc, 2, 64);
+            acc += __shfl_xor(acc, 4, 64);
+            const bool keep = q_ok && (rowi < n_valid) && (acc + bias > 0.f);
+            const unsigned long long m = __ballot(keep);
+            unsigned b8 = 0u;  // lanes 8j..8j+7 all hold row 8g+j: take bit 8j
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b8 |= (unsigned)((m >> (8 * j)) & 1ull) << j;
+            bits |= b8 << (8 * (hh * GH + g));
+        }
     }
-    __syncthreads();
-    if (p.masks && threadIdx.x < p.n_idx) {
-        const int i = threadIdx.x;
-        const unsigned long long w64 = (unsigned long long)s_half[2 * i] | ((unsigned long long)s_half[2 * i + 1] << 32);
-        p.masks[(size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)i * n_words_r + lw] = w64;
+    if (lane == 0) {
+        if (p.masks) {
+            const int n_words_r = p.word_off[r + 1] - p.word_off[r];
+            const size_t mw = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)i * n_words_r + lw;
+            reinterpret_cast<unsigned*>(p.masks)[2 * mw + half] = bits;
+        }
+        if (!q_ok) {
+            put(&p.bad[r], p.tag, 1u);
+            __builtin_amdgcn_s_waitcnt(0);  // the mark is stored before the unit is published
+        }
+        put(&p.hw[unit], p.tag, bits);
     }
+}
 
-    // ---- union word, published; count this group on its request ----
-    if (threadIdx.x == 0) {
+// ------------------------------------------------------------------------------------------
+// Compaction role for request r: thread t owns a run of consecutive words.  Waits until every unit
+// of the request is published, then writes the ids at the exclusive prefix of the popcounts of the
+// union words.
+__device__ void compact_role(const RefreshParams& p, int r) {
+    __shared__ int s_wsum[kThreads / 64];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int n_words = p.word_off[r + 1] - p.word_off[r];
+    const int per = (n_words + kThreads - 1) / kThreads;
+    const int w0 = min(n_words, t * per);
+    const int w1 = min(n_words, w0 + per);
+    const int nh = 2 * p.n_idx;  // published units per word
+    const unsigned long long* hw = p.hw + (size_t)p.word_off[r] * nh;
+    auto union_word = [&](int w, bool* ok) {
         unsigned long long u = 0ull;
-        for (int i = 0; i < p.n_idx; ++i)
-            u |= (unsigned long long)s_half[2 * i] | ((unsigned long long)s_half[2 * i + 1] << 32);
-        if (p.masks) p.masks[(size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)p.n_idx * n_words_r + lw] = u;
-        __hip_atomic_store(&p.words[2 * word], kWritten | (u & 0xffffffffull), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.words[2 * word + 1], kWritten | (u >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);  // both halves stored before the count is taken
-        const unsigned t = atomicAdd(&p.counters[r], 1u);
-        s_last = (t == (unsigned)(n_words_r - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-
-    // ---- the last group of request r: scan the word popcounts, write ascending ids ----
-    const int nt = blockDim.x;
-    const int per = (n_words_r + nt - 1) / nt;  // consecutive words per thread
-    const int w0 = min(n_words_r, (int)threadIdx.x * per);
-    const int w1 = min(n_words_r, w0 + per);
-    const unsigned long long* words_r = p.words + 2 * (size_t)p.word_off[r];
-    auto read_word = [&](int w, bool* ok) -> unsigned long long {
-        const unsigned long long lo = __hip_atomic_load(&words_r[2 * w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long hi = __hip_atomic_load(&words_r[2 * w + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *ok = (lo & kWritten) && (hi & kWritten);
-        return (lo & 0xffffffffull) | (hi << 32);
+        for (int k = 0; k < nh; ++k) {
+            const unsigned long long h = get(hw + (size_t)w * nh + k);
+            *ok = *ok && tagged(h, p.tag);
+            u |= (unsigned long long)(unsigned)h << (32 * (k & 1));
+        }
+        return u;
     };
-    // every writer counted itself after storing, so the flags are set; check them anyway (bounded)
-    for (unsigned spins = 0;; ++spins) {
-        if (threadIdx.x == 0) s_missing = 0u;
-        __syncthreads();
-        for (int w = w0; w < w1; ++w) {
-            bool ok;
-            read_word(w, &ok);
-            if (!ok) s_missing = 1u;
-        }
-        __syncthreads();
-        if (!s_missing || spins > kSpinLimit) break;
-        __builtin_amdgcn_s_sleep(2);
-    }
+    bool failed = false;
     int cnt = 0;
-    for (int w = w0; w < w1; ++w) {
-        bool ok;
-        cnt += __popcll(read_word(w, &ok));
+    for (unsigned spins = 0;; ++spins) {
+        bool ok = true;
+        cnt = 0;
+        for (int w = w0; w < w1; ++w) cnt += __popcll(union_word(w, &ok));
+        if (__syncthreads_and(ok)) break;
+        if (spins >= kSpinLimit) {
+            failed = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(16);
     }
-    s_scan[threadIdx.x] = cnt;
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+    }
+    if (lane == 63) s_wsum[wave] = inc;
     __syncthreads();
-    for (int off = 1; off < nt; off <<= 1) {
-        const int v = (int)threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
-        __syncthreads();
-        s_scan[threadIdx.x] += v;
-        __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) {
+        base += k < wave ? s_wsum[k] : 0;
+        total += s_wsum[k];
     }
-    int pos = s_scan[threadIdx.x] - cnt;
-    int* out = p.sel_ids + b_first;
-    for (int w = w0; w < w1; ++w) {
-        bool ok;
-        unsigned long long u = read_word(w, &ok);
-        while (u) {
-            const int bit = __ffsll((long long)u) - 1;
-            out[pos++] = w * 64 + bit;
-            u &= u - 1;
+    int pos = base + inc - cnt;
+    int* out = p.sel_ids + p.blk_off[r];
+    const size_t plane = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)p.n_idx * n_words;
+    if (!failed) {
+        for (int w = w0; w < w1; ++w) {
+            bool ok = true;
+            const unsigned long long u = union_word(w, &ok);
+            if (p.masks) p.masks[plane + w] = u;
+            for (unsigned long long x = u; x; x &= x - 1) out[pos++] = w * 64 + __ffsll((long long)x) - 1;
         }
     }
-    if (threadIdx.x == nt - 1) p.sel_count[r] = s_missing ? -1 : s_scan[nt - 1];
+    if (t == 0) p.sel_count[r] = (failed || tagged(get(&p.bad[r]), p.tag)) ? -1 : total;
+}
+
+template <typename T, int DIDX>
+__global__ __launch_bounds__(kThreads, 3) void refresh_kernel(RefreshParams p) {
+    const int g = blockIdx.x;
+    if (g < p.n_encode_groups)
+        encode_role<T>(p, g);
+    else if (g < p.n_encode_groups + p.n_score_groups)
+        score_role<T, DIDX>(p, g - p.n_encode_groups);
+    else
+        compact_role(p, g - p.n_encode_groups - p.n_score_groups);
 }
 
 struct RefreshLayout {
-    size_t q_off, words_off, counters_off, total;
+    size_t qw_off, hw_off, bad_off, total;
     int total_words;
 };
 
@@ -320,61 +391,62 @@ lsa_status refresh_layout(const lsa_refresh_args* a, RefreshLayout* L) {
         LSA_CHECK_ARG(nb >= 1 && nb <= (1ll << 24), "lsa_index_refresh: request %d has %lld blocks", r, nb);
         words += (nb + 63) / 64;
     }
-    LSA_CHECK_ARG(words <= (1ll << 28), "lsa_index_refresh: too many blocks");
+    LSA_CHECK_ARG(words <= (1ll << 26), "lsa_index_refresh: too many blocks");
     L->total_words = (int)words;
     size_t off = 0;
-    L->q_off = off;
-    off = align_up(off + (size_t)a->n_req * a->n_idx * a->d_idx * sizeof(float), 256);
-    L->words_off = off;
-    off = align_up(off + (size_t)words * 2 * sizeof(unsigned long long), 256);
-    L->counters_off = off;
-    off = align_up(off + (size_t)a->n_req * sizeof(unsigned), 256);
+    L->qw_off = off;
+    off = align_up(off + (size_t)a->n_req * a->n_idx * a->d_idx * sizeof(unsigned long long), 256);
+    L->hw_off = off;
+    off = align_up(off + (size_t)words * 2 * a->n_idx * sizeof(unsigned long long), 256);
+    L->bad_off = off;
+    off = align_up(off + (size_t)a->n_req * sizeof(unsigned long long), 256);
     L->total = off;
     return LSA_OK;
 }
 
+// Call numbers tag the workspace words of a call; 0 never occurs, so a zero-filled workspace holds
+// no valid word.
+std::atomic<unsigned> g_call_number{0};
+
 template <typename T>
 lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hipStream_t stream) {
     char* ws = static_cast<char*>(a->workspace);
-    EncodeParams ep{};
-    ep.hidden = a->hidden;
-    ep.hidden_req_stride = a->hidden_req_stride;
-    ep.hidden_idx_stride = a->hidden_idx_stride;
-    ep.w_q = a->w_q;
-    ep.q = reinterpret_cast<float*>(ws + L.q_off);
-    ep.counters = reinterpret_cast<unsigned*>(ws + L.counters_off);
-    ep.words = reinterpret_cast<unsigned long long*>(ws + L.words_off);
-    ep.n_req = a->n_req;
-    ep.d_model = a->d_model;
-    ep.d_idx = a->d_idx;
-    ep.n_idx = a->n_idx;
-    ep.total_words = L.total_words;
-    const int rows = a->n_idx * a->d_idx;
-    hipLaunchKernelGGL(encode_kernel<T>, dim3((rows + 3) / 4), dim3(256), 0, stream, ep);
-    LSA_HIP(hipGetLastError());
-
-    ScoreParams sp{};
-    sp.keys = a->keys;
-    sp.q = ep.q;
-    sp.bias = a->bias;
-    sp.sel_ids = a->sel_ids;
-    sp.sel_count = a->sel_count;
-    sp.masks = reinterpret_cast<unsigned long long*>(a->masks);
-    sp.words = ep.words;
-    sp.counters = ep.counters;
-    sp.n_req = a->n_req;
-    sp.n_idx = a->n_idx;
+    unsigned call = g_call_number.fetch_add(1u) + 1u;
+    if (call == 0u) call = g_call_number.fetch_add(1u) + 1u;
+    RefreshParams rp{};
+    rp.hidden = a->hidden;
+    rp.hidden_req_stride = a->hidden_req_stride;
+    rp.hidden_idx_stride = a->hidden_idx_stride;
+    rp.w_q = a->w_q;
+    rp.keys = a->keys;
+    rp.bias = a->bias;
+    rp.sel_ids = a->sel_ids;
+    rp.sel_count = a->sel_count;
+    rp.masks = reinterpret_cast<unsigned long long*>(a->masks);
+    rp.qw = reinterpret_cast<unsigned long long*>(ws + L.qw_off);
+    rp.hw = reinterpret_cast<unsigned long long*>(ws + L.hw_off);
+    rp.bad = reinterpret_cast<unsigned long long*>(ws + L.bad_off);
+    rp.tag = (unsigned long long)call << 32;
+    rp.n_req = a->n_req;
+    rp.d_model = a->d_model;
+    rp.d_idx = a->d_idx;
+    rp.n_idx = a->n_idx;
+    rp.n_units = L.total_words * 2 * a->n_idx;
+    const int rows_per_group = kEncRows * (kThreads / 128);  // two waves per kEncRows W_q rows
+    rp.n_encode_groups = a->n_idx * ((a->d_idx + rows_per_group - 1) / rows_per_group);
+    rp.n_score_groups = (rp.n_units + kThreads / 64 - 1) / (kThreads / 64);
     int wo = 0;
     for (int r = 0; r <= a->n_req; ++r) {
-        sp.blk_off[r] = a->blk_off[r];
-        sp.word_off[r] = wo;
+        rp.blk_off[r] = a->blk_off[r];
+        rp.word_off[r] = wo;
         if (r < a->n_req) wo += (int)((a->blk_off[r + 1] - a->blk_off[r] + 63) / 64);
     }
-    const dim3 grid(L.total_words), block(64 * kScoreWavesPerIdx * a->n_idx);
-    if (a->d_idx == 256)
-        hipLaunchKernelGGL((score_kernel<T, 256>), grid, block, 0, stream, sp);
+    const dim3 grid(rp.n_encode_groups + rp.n_score_groups + a->n_req), block(kThreads);
+    auto kernel = a->d_idx == 256 ? refresh_kernel<T, 256> : refresh_kernel<T, 128>;
+    if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, rp);
     else
-        hipLaunchKernelGGL((score_kernel<T, 128>), grid, block, 0, stream, sp);
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, rp);
     LSA_HIP(hipGetLastError());
     return LSA_OK;
 }

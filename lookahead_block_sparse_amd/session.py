@@ -25,14 +25,18 @@ import torch
 
 from . import (
     BLOCK_TOKENS,
+    DecodeArgs,
+    GatherArgs,
+    LIB,
+    _check,
     lsa_block_bytes,
-    lsa_gather_blocks,
     lsa_index_refresh,
     lsa_index_refresh_workspace,
     lsa_pack_blocks,
     lsa_sparse_decode,
     lsa_sparse_decode_workspace,
 )
+import ctypes
 
 
 def _raw_tensor(arr: np.ndarray, device) -> torch.Tensor:
@@ -82,6 +86,8 @@ class LSASession:
             self.refresh_ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.device)
             self.sel_ids_h = torch.empty(total_blocks, dtype=torch.int32, pin_memory=True)
             self.sel_count_h = torch.empty(self.n_req, dtype=torch.int32, pin_memory=True)
+            self._sel_ids_np = self.sel_ids_h.numpy()
+            self._sel_count_np = self.sel_count_h.numpy()
 
             # hot pool and residency state
             cap = np.asarray(capacity if capacity is not None else self.n_blocks, dtype=np.int64)
@@ -97,6 +103,7 @@ class LSASession:
             self.stage = [torch.empty(max(4, 4 * int(c)), dtype=torch.int32, pin_memory=True) for c in cap]
             self.n_sel = np.zeros(self.n_req, dtype=np.int32)
             self.sel_host: List[np.ndarray] = [np.zeros(0, dtype=np.int32) for _ in range(self.n_req)]
+            self.sel_version = np.zeros(self.n_req, dtype=np.int64)
 
             # cold pools and rings
             self.cold: List[Optional[torch.Tensor]] = [None] * self.n_req
@@ -105,6 +112,8 @@ class LSASession:
             ws = lsa_sparse_decode_workspace(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap,
                                              n_req=self.n_req, max_groups=max_groups)
             self.decode_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        self._gargs: List[Optional[tuple]] = [None] * self.n_req
+        self._stage_ev: List[Optional[torch.cuda.Event]] = [None] * self.n_req
         self.last_decode_event: Optional[torch.cuda.Event] = None
         # record an event after each decode so a gather on another stream can wait for it
         self.track_decode = False
@@ -124,6 +133,7 @@ class LSASession:
                 self.cold[r] = cold_h.to(self.device)
         else:
             self.cold[r] = cold_h
+        self._gargs[r] = None
         n_chunks = self.win_cap // BLOCK_TOKENS
         ring_h = np.zeros(n_chunks * self.block_bytes, dtype=np.uint8)
         w = min(self.win_cap, n)
@@ -140,7 +150,7 @@ class LSASession:
 
         Enqueues lsa_index_refresh per contiguous run of requests, copies the selections back
         (one synchronisation) and returns {r: ascending ids}.  ev_begin / ev_end (torch events)
-        are recorded around the refresh kernels only."""
+        time the refresh kernel only (its dispatch, when the requests form one run)."""
         reqs = list(reqs)
         with torch.cuda.stream(self.stream):
             if isinstance(hidden, torch.Tensor):
@@ -160,28 +170,34 @@ class LSASession:
                     j += 1
                 runs.append((i, j + 1))
                 i = j + 1
-            if ev_begin is not None:
-                ev_begin.record(self.stream)
-            for i, j in runs:
-                r0, r1 = reqs[i], reqs[j - 1] + 1
-                self._refresh_run(r0, r1, hid[i:j], bias_d[i:j])
-            if ev_end is not None:
-                ev_end.record(self.stream)
-            for r in reqs:
-                b0, b1 = int(self.blk_off[r]), int(self.blk_off[r + 1])
+            if len(runs) == 1:
+                # the library times its own dispatch
+                self._refresh_run(reqs[0], reqs[-1] + 1, hid, bias_d, ev_begin, ev_end)
+            else:
+                if ev_begin is not None:
+                    ev_begin.record(self.stream)
+                for i, j in runs:
+                    r0, r1 = reqs[i], reqs[j - 1] + 1
+                    self._refresh_run(r0, r1, hid[i:j], bias_d[i:j])
+                if ev_end is not None:
+                    ev_end.record(self.stream)
+            for i, j in runs:  # one copy per contiguous run of requests
+                b0, b1 = int(self.blk_off[reqs[i]]), int(self.blk_off[reqs[j - 1] + 1])
                 self.sel_ids_h[b0:b1].copy_(self.sel_ids[b0:b1], non_blocking=True)
             self.sel_count_h.copy_(self.sel_count, non_blocking=True)
         self.stream.synchronize()
         out = {}
+        ids_h, count_h = self._sel_ids_np, self._sel_count_np
         for r in reqs:
             b0 = int(self.blk_off[r])
-            c = int(self.sel_count_h[r])
+            c = int(count_h[r])
             if c < 0:
                 raise RuntimeError(f"index refresh of request {r} reported an incomplete compaction")
-            out[r] = self.sel_ids_h[b0:b0 + c].numpy().copy()
+            out[r] = ids_h[b0:b0 + c].copy()
         return out
 
-    def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor) -> None:
+    def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor, ev_begin=None,
+                     ev_end=None) -> None:
         off = self.blk_off[r0:r1 + 1] - self.blk_off[r0]
         key_elem0 = int(self.n_idx * self.d_idx * self.blk_off[r0])
         masks = None
@@ -190,7 +206,8 @@ class LSASession:
         lsa_index_refresh(dtype=self.dtype, d_model=self.d_model, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
                           w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
                           sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
-                          workspace=self.refresh_ws, masks=masks, stream=self.stream)
+                          workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
+                          stream=self.stream)
 
     def masks_of(self, r: int) -> np.ndarray:
         """Request r's bit planes [n_idx+1][words] (after a refresh with masks enabled)."""
@@ -208,13 +225,36 @@ class LSASession:
                 raise RuntimeError("set track_decode before gathering on a side stream")
             if self.last_decode_event is not None:
                 st.wait_event(self.last_decode_event)  # slots of leaving blocks may still be read
-        res = lsa_gather_blocks(
-            n_blocks=int(self.n_blocks[r]), n_slots_total=self.n_slots, block_bytes=self.block_bytes,
-            cold=self.cold[r], hot=self.hot, new_ids=ids, slot_of_block=self.slot_of_block[r],
-            free_slots=self.free_slots[r], n_free=self.n_free[r], capacity=int(self.capacity[r]),
-            stage=self.stage[r], table_dev=self.table[2 * int(self.slot_base[r]):], stream=st)
+        if self.cold[r] is None:
+            raise RuntimeError(f"request {r} has no cold pool: call load_prefill first")
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        if self._gargs[r] is None:
+            # every field but the selection is fixed for the session: built once per request
+            a = GatherArgs()
+            a.n_blocks, a.n_slots_total, a.block_bytes = int(self.n_blocks[r]), self.n_slots, self.block_bytes
+            a.cold, a.hot = self.cold[r].data_ptr(), self.hot.data_ptr()
+            a.stage_ints = self.stage[r].numel()
+            a.slot_of_block = self.slot_of_block[r].ctypes.data
+            a.free_slots = self.free_slots[r].ctypes.data
+            a.n_free = self.n_free[r].ctypes.data
+            a.capacity, a.reserved1 = int(self.capacity[r]), 0
+            a.stage = self.stage[r].data_ptr()
+            a.table_dev = self.table.data_ptr() + 4 * 2 * int(self.slot_base[r])
+            counts = np.zeros(2, dtype=np.int32)
+            a.n_copied, a.n_kept = counts.ctypes.data, counts.ctypes.data + 4
+            self._gargs[r] = (a, counts)
+        a, counts = self._gargs[r]
+        if self._stage_ev[r] is not None:
+            self._stage_ev[r].synchronize()  # the previous copy kernel may still read stage[r]
+        a.new_ids, a.n_new = ids.ctypes.data, len(ids)
+        _check(LIB.lsa_gather_blocks(ctypes.byref(a), st.cuda_stream))
+        res = (int(counts[0]), int(counts[1]))
+        if self._stage_ev[r] is None:
+            self._stage_ev[r] = torch.cuda.Event()
+        self._stage_ev[r].record(st)
         self.n_sel[r] = len(ids)
-        self.sel_host[r] = np.asarray(ids, dtype=np.int32)
+        self.sel_host[r] = ids
+        self.sel_version[r] += 1
         if st is not self.stream:
             ev = torch.cuda.Event()
             ev.record(st)
@@ -222,13 +262,23 @@ class LSASession:
         return res
 
     # ---------------------------------------------------------------------------------------
+    def attended_entries(self, seq_len: Sequence[int], window: Sequence[int]) -> np.ndarray:
+        """Per request, the number of leading table entries whose block starts before the window
+        (the only ones that contribute; the table is ascending by block id)."""
+        out = np.empty(self.n_req, dtype=np.int32)
+        for r in range(self.n_req):
+            ws = max(0, int(seq_len[r]) - int(window[r]))
+            out[r] = np.searchsorted(self.sel_host[r], (ws + BLOCK_TOKENS - 1) // BLOCK_TOKENS, side="left")
+        return out
+
     def decode(self, q: torch.Tensor, seq_len: Sequence[int], window: Sequence[int], out: torch.Tensor,
                k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
                max_groups: Optional[int] = None, ev_attn_begin=None, ev_attn_end=None) -> None:
         """One decode step for all requests of the session."""
         lsa_sparse_decode(dtype=self.dtype, n_heads=self.n_heads, head_dim=self.head_dim, win_cap=self.win_cap,
                           q=q, ring=self.ring, out=out, workspace=self.decode_ws,
-                          tbl_off=self.slot_base[:-1], n_sel=self.n_sel, seq_len=seq_len, window=window,
+                          tbl_off=self.slot_base[:-1], n_sel=self.attended_entries(seq_len, window),
+                          seq_len=seq_len, window=window,
                           pool=self.hot, n_slots_total=self.n_slots, table=self.table, k_new=k_new, v_new=v_new,
                           max_groups=self.max_groups if max_groups is None else max_groups,
                           ev_attn_begin=ev_attn_begin, ev_attn_end=ev_attn_end, stream=self.stream)
@@ -237,3 +287,57 @@ class LSASession:
             if self.last_decode_event is None:
                 self.last_decode_event = torch.cuda.Event()
             self.last_decode_event.record(self.stream)
+
+
+class DecodeLoop:
+    """Per-step decode calls with the argument struct built once.
+
+    For a fixed session, window and stream, step(t) only rewrites the per-request lengths (prefill +
+    t + 1), the attended table entries and the q / k_new / v_new addresses, then calls
+    lsa_sparse_decode.  Events (torch.cuda.Event) may be passed per call to time the attention kernel.
+    """
+
+    def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor):
+        self.sess = sess
+        self.prefill = np.asarray(prefill, dtype=np.int64)
+        self.window = np.ascontiguousarray(window, dtype=np.int32)
+        self.seq_len = np.zeros(sess.n_req, dtype=np.int32)
+        self.n_sel = np.zeros(sess.n_req, dtype=np.int32)
+        self.tbl_off = np.ascontiguousarray(sess.slot_base[:-1], dtype=np.int32)
+        a = DecodeArgs()
+        a.n_req, a.n_heads, a.head_dim = sess.n_req, sess.n_heads, sess.head_dim
+        a.dtype = 1 if sess.dtype == "bf16" else 0
+        a.win_cap = sess.win_cap
+        a.scale = float(1.0 / np.sqrt(sess.head_dim))
+        a.ring, a.pool, a.table = sess.ring.data_ptr(), sess.hot.data_ptr(), sess.table.data_ptr()
+        a.n_slots_total, a.reserved0 = sess.n_slots, 0
+        a.tbl_off, a.n_sel = self.tbl_off.ctypes.data, self.n_sel.ctypes.data
+        a.seq_len, a.window = self.seq_len.ctypes.data, self.window.ctypes.data
+        a.out = out.data_ptr()
+        a.workspace, a.workspace_bytes = sess.decode_ws.data_ptr(), sess.decode_ws.numel()
+        a.max_groups, a.reserved1 = sess.max_groups, 0
+        self.args = a
+        self.ref = ctypes.byref(a)
+        self.stream = ctypes.c_void_p(sess.stream.cuda_stream)
+        self._bnd = np.full(sess.n_req, -1, dtype=np.int64)
+        self._ver = np.full(sess.n_req, -1, dtype=np.int64)
+
+    def step(self, t: int, q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+             ev_begin=None, ev_end=None) -> None:
+        np.add(self.prefill, t + 1, out=self.seq_len, casting="unsafe")
+        # attended table entries change only when a window start crosses a block boundary or a
+        # request's selection changes
+        bnd = (np.maximum(0, self.seq_len - self.window) + BLOCK_TOKENS - 1) // BLOCK_TOKENS
+        changed = (bnd != self._bnd) | (self.sess.sel_version != self._ver)
+        if changed.any():
+            for r in np.flatnonzero(changed):
+                self.n_sel[r] = np.searchsorted(self.sess.sel_host[r], bnd[r], side="left")
+            self._bnd = bnd
+            self._ver = self.sess.sel_version.copy()
+        a = self.args
+        a.q = q.data_ptr()
+        a.k_new = k_new.data_ptr() if k_new is not None else None
+        a.v_new = v_new.data_ptr() if v_new is not None else None
+        a.ev_attn_begin = ev_begin.cuda_event if ev_begin is not None else None
+        a.ev_attn_end = ev_end.cuda_event if ev_end is not None else None
+        _check(LIB.lsa_sparse_decode(self.ref, self.stream))
