@@ -2,17 +2,20 @@
 // ordered compaction of the loaded-block list (zhichai.net explainer of "FlashMemory-DeepSeek-V4",
 // section 2 steps 2-3, section 3 (Query Encoder, frozen KIComp keys), section 4 (OR-mode union)).
 //
-// One kernel of 4-wave groups, three roles in this order of group index:
+// One kernel of 4-wave groups, four roles in this order of group index:
 //   encode   q[r][i][j] = sum_m W_q[i][j][m] h[r][i][m]: two waves per pair of output rows, each
 //            W_q row read once for every request, fp32 accumulation, q kept in fp32.
+//   prefetch as many groups as fit beside the encode groups at the start: read the keys of the
+//            first score units and drop them, so HBM streams keys into the memory-side cache while
+//            q is computed.
 //   score    one wave per unit = 32 key rows of one indexer in one 64-block word.  The wave issues
 //            all loads of its rows, then waits for its q, forms z = q.k + bias in fp32, turns z > 0
 //            into 32 bits with a wavefront ballot and publishes them.  Waves never synchronise with
 //            the other waves of their group.
-//   compact  one per request: waits until every unit of the request has published, ORs the
-//            indexers' bits into the union words, takes the exclusive prefix of their popcounts
-//            (wave scans, wave totals through LDS), and every thread writes the ids of its words in
-//            ascending order; then the count.
+//   compact  one per 64 words of a request: waits until every unit of the request up to its words
+//            has published, ORs the indexers' bits into the union words, offsets its words by the
+//            popcounts before them and a wave scan, and writes their ids in ascending order; the
+//            last one of a request writes the count.
 // A group only waits for groups with a lower index, which were dispatched before it, and every
 // wait is bounded: a wait that gives up marks the request, whose count is then written as -1.
 // Values that cross groups travel in 64-bit words whose upper half is the call's number and lower
@@ -20,6 +23,7 @@
 // its tag matches, so nothing has to be cleared between calls and no fence is needed.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "lsa_internal.hpp"
@@ -45,9 +49,10 @@ struct RefreshParams {
     unsigned long long* hw;   // [total words][n_idx][2]        tag | 32 bits of one unit
     unsigned long long* bad;  // [n_req]                        tag when a wait of the request gave up
     unsigned long long tag;   // call number << 32
-    int n_req, d_model, d_idx, n_idx, n_units, n_encode_groups, n_score_groups;
+    int n_req, d_model, d_idx, n_idx, n_units, n_encode_groups, n_prefetch_groups, n_score_groups;
     long long blk_off[kMaxReq + 1];
     int word_off[kMaxReq + 1];
+    int cg_off[kMaxReq + 1];  // first compaction group of each request
 };
 
 __device__ __forceinline__ void put(unsigned long long* w, unsigned long long tag, unsigned v) {
@@ -181,6 +186,43 @@ __device__ void encode_role(const RefreshParams& p, int g) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Prefetch role: the groups dispatched with the encode groups read the keys of the first score
+// units and drop them.  The reads pass through the memory-side cache, so HBM streams keys while q
+// is being computed, and the score waves of those units later find them there.
+template <typename T, int DIDX>
+__device__ void prefetch_role(const RefreshParams& p, int gp) {
+    constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
+    constexpr int LPR = ROW_BYTES / 128;
+    const int lane = threadIdx.x & 63;
+    const int unit = 4 * gp + (int)(threadIdx.x >> 6);
+    if (unit >= p.n_units) return;
+    const int word = unit / (2 * p.n_idx);
+    const int i = (unit / 2) % p.n_idx;
+    const int half = unit & 1;
+    int r = 0;
+    while (r + 1 < p.n_req && p.word_off[r + 1] <= word) ++r;
+    const long long b_first = p.blk_off[r];
+    const int n_blk = (int)(p.blk_off[r + 1] - b_first);
+    const int b0 = (word - p.word_off[r]) * 64;
+    const int n_valid = min(64, n_blk - b0);
+    const char* rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + (size_t)i * n_blk + b0) * ROW_BYTES;
+    uint4 v[4][LPR];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int rowi = min(32 * half + g * 8 + (lane >> 3), n_valid - 1);
+        const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)rowi * ROW_BYTES + (lane & 7) * 16);
+#pragma unroll
+        for (int k = 0; k < LPR; ++k) v[g][k] = src[k * 8];
+    }
+    uint4 x = v[0][0];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int k = 0; k < LPR; ++k) x ^= v[g][k];
+    asm volatile("" :: "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));  // the data arrives before the wave ends
+}
+
+// ------------------------------------------------------------------------------------------
 // Scoring role: wave w of score group gs takes unit 4*gs + w = (word, indexer i, half): rows
 // 32*half .. 32*half + 31 of the word's 64 blocks for indexer i.
 template <typename T, int DIDX>
@@ -232,14 +274,10 @@ __device__ void score_role(const RefreshParams& p, int gs) {
         }
         if (hh == 0) {
             asm volatile("" ::: "memory");  // the key loads are issued before the wait for q
-            // wait for this (request, indexer)'s q: one lane polls one word, then the wave fetches
-            // the row (lane l: words QW*l ..), checks every tag and passes the values through LDS to
-            // the lanes that use them
+            // wait for this (request, indexer)'s q: the wave fetches the row (lane l: words QW*l ..)
+            // right behind its key loads, checks every tag (fetching again until all are this
+            // call's) and passes the values through LDS to the lanes that use them
             unsigned spins = 0;
-            if (lane == 0) {
-                while (!tagged(get(qrow + DIDX - 1), p.tag) && ++spins <= kSpinLimit) __builtin_amdgcn_s_sleep(8);
-            }
-            spins = __shfl(spins, 0, 64);
             for (;;) {
                 bool all = true;
 #pragma unroll
@@ -253,7 +291,7 @@ __device__ void score_role(const RefreshParams& p, int gs) {
                     q_ok = false;
                     break;
                 }
-                __builtin_amdgcn_s_sleep(16);
+                __builtin_amdgcn_s_sleep(8);
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -293,79 +331,163 @@ __device__ void score_role(const RefreshParams& p, int gs) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Compaction role for request r: thread t owns a run of consecutive words.  Waits until every unit
-// of the request is published, then writes the ids at the exclusive prefix of the popcounts of the
-// union words.
-__device__ void compact_role(const RefreshParams& p, int r) {
-    __shared__ int s_wsum[kThreads / 64];
+// Compaction role: group c of a request handles the request's words [64c, 64c + 64) (its slice).
+// All 256 threads read the union words up to the slice's end (thread t: words t, t+256, ...) until
+// every unit carries this call's tag; the popcounts of the words before the slice give its base,
+// a wave scan over the slice gives each word's offset, and the four waves write the slice's ids,
+// one word at a time per wave with one lane per bit, so each store writes a word's ids contiguously.
+// The group of the last slice writes the count.
+constexpr int kSlice = 64;
+
+__device__ void compact_role(const RefreshParams& p, int cg) {
+    __shared__ unsigned long long s_u[kSlice];
+    __shared__ int s_pos[kSlice];
+    __shared__ int s_sum[kThreads / 64];
+    __shared__ int s_total;
+    int r = 0;
+    while (r + 1 < p.n_req && p.cg_off[r + 1] <= cg) ++r;
+    const int c = cg - p.cg_off[r];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
     const int n_words = p.word_off[r + 1] - p.word_off[r];
-    const int per = (n_words + kThreads - 1) / kThreads;
-    const int w0 = min(n_words, t * per);
-    const int w1 = min(n_words, w0 + per);
+    const int s0 = c * kSlice;
+    const int s1 = min(n_words, s0 + kSlice);
     const int nh = 2 * p.n_idx;  // published units per word
     const unsigned long long* hw = p.hw + (size_t)p.word_off[r] * nh;
     auto union_word = [&](int w, bool* ok) {
+        // all loads of the word first (n_idx <= 4: at most 8 units), then the checks
+        unsigned long long h[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) h[k] = get(hw + (size_t)w * nh + min(k, nh - 1));
         unsigned long long u = 0ull;
-        for (int k = 0; k < nh; ++k) {
-            const unsigned long long h = get(hw + (size_t)w * nh + k);
-            *ok = *ok && tagged(h, p.tag);
-            u |= (unsigned long long)(unsigned)h << (32 * (k & 1));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (k < nh) {
+                *ok = *ok && tagged(h[k], p.tag);
+                u |= (unsigned long long)(unsigned)h[k] << (32 * (k & 1));
+            }
         }
         return u;
     };
+    // Runs of up to kKeep words per thread stay in registers: a word is read until all its units
+    // carry this call's tag, then kept; requests longer than 256*kKeep words are re-read.
+    constexpr int kKeep = 4;
+    const bool held = s1 <= kThreads * kKeep;
+    unsigned long long keep[kKeep] = {};
+    unsigned done = 0u;
     bool failed = false;
-    int cnt = 0;
+    bool bad = false;
     for (unsigned spins = 0;; ++spins) {
         bool ok = true;
-        cnt = 0;
-        for (int w = w0; w < w1; ++w) cnt += __popcll(union_word(w, &ok));
+        if (held) {
+#pragma unroll
+            for (int k = 0; k < kKeep; ++k) {
+                const int w = t + kThreads * k;
+                if (w < s1 && !((done >> k) & 1u)) {
+                    bool okw = true;
+                    const unsigned long long u = union_word(w, &okw);
+                    if (okw) {
+                        keep[k] = u;
+                        done |= 1u << k;
+                    } else {
+                        ok = false;
+                    }
+                }
+            }
+        } else {
+            for (int w = t; w < s1; w += kThreads) union_word(w, &ok);
+        }
+        if (t == 0) bad = tagged(get(&p.bad[r]), p.tag);
         if (__syncthreads_and(ok)) break;
         if (spins >= kSpinLimit) {
             failed = true;
+            if (t == 0) put(&p.bad[r], p.tag, 1u);
             break;
         }
-        __builtin_amdgcn_s_sleep(16);
+        __builtin_amdgcn_s_sleep(4);
     }
-    int inc = cnt;
+    // popcounts before the slice; the slice's words to LDS
+    int before = 0;
+    if (held) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += v;
-    }
-    if (lane == 63) s_wsum[wave] = inc;
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int k = 0; k < kThreads / 64; ++k) {
-        base += k < wave ? s_wsum[k] : 0;
-        total += s_wsum[k];
-    }
-    int pos = base + inc - cnt;
-    int* out = p.sel_ids + p.blk_off[r];
-    const size_t plane = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)p.n_idx * n_words;
-    if (!failed) {
-        for (int w = w0; w < w1; ++w) {
+        for (int k = 0; k < kKeep; ++k) {
+            const int w = t + kThreads * k;
+            if (w < s0)
+                before += __popcll(keep[k]);
+            else if (w < s1)
+                s_u[w - s0] = keep[k];
+        }
+    } else {
+        for (int w = t; w < s1; w += kThreads) {
             bool ok = true;
             const unsigned long long u = union_word(w, &ok);
-            if (p.masks) p.masks[plane + w] = u;
-            for (unsigned long long x = u; x; x &= x - 1) out[pos++] = w * 64 + __ffsll((long long)x) - 1;
+            if (w < s0)
+                before += __popcll(u);
+            else
+                s_u[w - s0] = u;
         }
     }
-    if (t == 0) p.sel_count[r] = (failed || tagged(get(&p.bad[r]), p.tag)) ? -1 : total;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
+    if (lane == 0) s_sum[wave] = before;
+    __syncthreads();
+    if (wave == 0) {
+        int base = 0;
+#pragma unroll
+        for (int k = 0; k < kThreads / 64; ++k) base += s_sum[k];
+        const unsigned long long u = lane < s1 - s0 ? s_u[lane] : 0ull;
+        const int cnt = __popcll(u);
+        int inc = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += v;
+        }
+        s_pos[lane] = base + inc - cnt;
+        if (lane == 63) s_total = base + inc;
+    }
+    __syncthreads();
+    if (!failed) {
+        int* out = p.sel_ids + p.blk_off[r];
+        const size_t plane = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)p.n_idx * n_words;
+        if (p.masks && t < s1 - s0) p.masks[plane + s0 + t] = s_u[t];
+        // wave w writes slice words w, w+4, ..: lane m first fetches word w + 4m, then the words go
+        // to scalars one at a time
+        constexpr int kPerWave = kSlice / (kThreads / 64);
+        const int jm = wave + (kThreads / 64) * (lane % kPerWave);
+        const unsigned long long um = jm < s1 - s0 ? s_u[jm] : 0ull;
+        const int pm = s_pos[jm < kSlice ? jm : 0];
+        const int ulo = (int)(unsigned)um, uhi = (int)(unsigned)(um >> 32);
+#pragma unroll
+        for (int m = 0; m < kPerWave; ++m) {
+            const unsigned long long u = (unsigned long long)(unsigned)__builtin_amdgcn_readlane(ulo, m) |
+                                         ((unsigned long long)(unsigned)__builtin_amdgcn_readlane(uhi, m) << 32);
+            const int at = __builtin_amdgcn_readlane(pm, m);
+            const int j = wave + (kThreads / 64) * m;
+            if ((u >> lane) & 1ull) out[at + __popcll(u & ((1ull << lane) - 1ull))] = (s0 + j) * 64 + lane;
+        }
+    }
+    if (t == 0 && s1 == n_words) p.sel_count[r] = (failed || bad) ? -1 : s_total;
 }
 
 template <typename T, int DIDX>
 __global__ __launch_bounds__(kThreads, 3) void refresh_kernel(RefreshParams p) {
-    const int g = blockIdx.x;
-    if (g < p.n_encode_groups)
+    int g = blockIdx.x;
+    if (g < p.n_encode_groups) {
         encode_role<T>(p, g);
-    else if (g < p.n_encode_groups + p.n_score_groups)
-        score_role<T, DIDX>(p, g - p.n_encode_groups);
+        return;
+    }
+    g -= p.n_encode_groups;
+    if (g < p.n_prefetch_groups) {
+        prefetch_role<T, DIDX>(p, g);
+        return;
+    }
+    g -= p.n_prefetch_groups;
+    if (g < p.n_score_groups)
+        score_role<T, DIDX>(p, g);
     else
-        compact_role(p, g - p.n_encode_groups - p.n_score_groups);
+        compact_role(p, g - p.n_score_groups);
 }
 
 struct RefreshLayout {
@@ -435,14 +557,28 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
     const int rows_per_group = kEncRows * (kThreads / 128);  // two waves per kEncRows W_q rows
     rp.n_encode_groups = a->n_idx * ((a->d_idx + rows_per_group - 1) / rows_per_group);
     rp.n_score_groups = (rp.n_units + kThreads / 64 - 1) / (kThreads / 64);
-    int wo = 0;
+    int wo = 0, co = 0;
     for (int r = 0; r <= a->n_req; ++r) {
         rp.blk_off[r] = a->blk_off[r];
         rp.word_off[r] = wo;
-        if (r < a->n_req) wo += (int)((a->blk_off[r + 1] - a->blk_off[r] + 63) / 64);
+        rp.cg_off[r] = co;
+        if (r < a->n_req) {
+            const int nw = (int)((a->blk_off[r + 1] - a->blk_off[r] + 63) / 64);
+            wo += nw;
+            co += (nw + kSlice - 1) / kSlice;
+        }
     }
-    const dim3 grid(rp.n_encode_groups + rp.n_score_groups + a->n_req), block(kThreads);
     auto kernel = a->d_idx == 256 ? refresh_kernel<T, 256> : refresh_kernel<T, 128>;
+    // prefetch groups fill the slots the encode groups leave free at the start
+    {
+        DeviceInfo dev;
+        lsa_status st = current_device(&dev);
+        if (st != LSA_OK) return st;
+        int per_cu = 0;
+        LSA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0));
+        rp.n_prefetch_groups = std::max(0, std::min(rp.n_score_groups, dev.cu_count * per_cu - rp.n_encode_groups));
+    }
+    const dim3 grid(rp.n_encode_groups + rp.n_prefetch_groups + rp.n_score_groups + co), block(kThreads);
     if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps
         hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, rp);
     else
