@@ -1,0 +1,82 @@
+"""Parity at the full workload sizes, in the benchmark's launch configuration.
+
+Each workload runs its whole decode loop through the C-ABI the way bench.py runs it (cold pool in
+HBM, no bit planes, a work-group per CU slot, DecodeLoop's per-step call); every refresh of every
+request is compared with the oracle bit for bit, and the attention output of a few sampled steps
+(always including the last one, and a refresh step where there is one) within the fp tolerance.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import ABS_TOL, REL_TOL, attention_errors, conditioned_workload, log, make_session, raw_to_torch
+
+pytestmark = pytest.mark.gpu
+
+# (workload, sampled steps besides the last one)
+FULL = [("ctx128k", [0, 63, 64, 200]), ("ctx512k", [0, 64]), ("ctx1m", [64, 191]), ("ragged", [100])]
+
+
+def _run_bench_style(wl, sess, record):
+    """The benchmark's per-step path: refreshes and gathers where the schedule says, then one
+    DecodeLoop step.  Returns ({t: out float64}, {(r, k): ids})."""
+    from lookahead_block_sparse_amd.session import DecodeLoop
+
+    cfg = wl.cfg
+    R, T = wl.n_req, cfg.steps
+    dev = sess.device
+    sels = {}
+
+    def refresh(reqs, k_of):
+        hid = torch.from_numpy(np.stack([wl.hidden[r][k_of[r]] for r in reqs]).view(np.int16)).to(dev)
+        bias = torch.from_numpy(np.stack([wl.bias[r] for r in reqs]).astype(np.float32)).to(dev)
+        got = sess.refresh(reqs, hid, bias)
+        for r in reqs:
+            sess.gather(r, got[r])
+            sels[(r, k_of[r])] = got[r]
+
+    pro = [r for r in range(R) if wl.refresh_steps[r][0] < 0]
+    if pro:
+        refresh(pro, {r: 0 for r in pro})
+    out = torch.empty((R, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    loop = DecodeLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), out)
+    outs = {}
+    for t in range(T):
+        reqs = wl.refreshes_at(t)
+        if reqs:
+            refresh(reqs, {r: wl.refresh_index_at(r, t) for r in reqs})
+        loop.step(t, raw_to_torch(wl.q_dec[t], dev), raw_to_torch(wl.k_new[t], dev), raw_to_torch(wl.v_new[t], dev))
+        if t in record:
+            outs[t] = out.double().cpu().numpy()
+    torch.cuda.synchronize()
+    return outs, sels
+
+
+@pytest.mark.parametrize("name,steps", FULL, ids=[n for n, _ in FULL])
+def test_full_size_loop_matches_oracle(name, steps):
+    wl = conditioned_workload(name, seed=11)
+    assert wl.cfg.dtype == "bf16"
+    T = wl.cfg.steps
+    sample = sorted(set([t for t in steps if t < T] + [T - 1]))
+    log(f"full size {name}: {wl.n_req} requests, {int(wl.ctx.sum())} context tokens, {T} steps, sampled {sample}")
+    sess = make_session(wl, cold_on_device=True, with_masks=False)
+    gpu, sels = _run_bench_style(wl, sess, set(sample))
+    log(f"  {name}: GPU loop done, {len(sels)} refreshes")
+    refs, outs = oracle.simulate(wl, steps=sample)
+    n_ref = 0
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (name, r, k, len(ids), len(refs[r][k].ids))
+        n_ref += 1
+    assert n_ref == sum(len(s) for s in wl.refresh_steps), (n_ref, [len(s) for s in wl.refresh_steps])
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        e = attention_errors(gpu[t], ref)
+        worst = tuple(max(a, b) for a, b in zip(worst, e))
+    log(f"  {name}: {n_ref} selections bit-exact; attention max abs {worst[0]:.3e} rel {worst[1]:.3e} "
+        f"l2 {worst[2]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
