@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--cpu-sample-steps", type=int, default=6, help="decode steps per request timed on the CPU")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no run: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
+                         "rocprofv3 pass (both taken with --calib-copy-mib) into "
+                         "profiles/attn_kernel_<workload>_traffic.json")
     return ap.parse_args()
 
 
@@ -77,6 +81,40 @@ def kernel_hash() -> str:
     for f in sorted((ROOT / "lookahead_block_sparse_amd" / "csrc").glob("*")):
         h.update(f.read_bytes())
     return h.hexdigest()[:16]
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> dict:
+    """HBM bytes per attn_kernel launch from two rocprofv3 counter passes.  Each counter is scaled
+    by what it reads for the plain device copy of calib_mib MiB in the same pass (read calib bytes,
+    write calib bytes), which takes out the counters' units and any sampling of channels."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        calib = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        attn = [float(r["Counter_Value"]) for r in rows if "attn_kernel" in r["Kernel_Name"]]
+        if not attn or not calib:
+            raise SystemExit(f"{path}: no attn_kernel or copy dispatches with {counter}")
+        return float(np.mean(attn)), max(calib), len(attn)
+
+    n = calib_mib << 20
+    f_attn, f_cal, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_attn, w_cal, n_w = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = n / (f_cal * 1024.0), n / (w_cal * 1024.0)
+    return {
+        "kernel": "attn_kernel",
+        "workload": workload,
+        "dispatches": {"fetch_pass": n_f, "write_pass": n_w},
+        "fetch_size_kib_per_dispatch": f_attn,
+        "write_size_kib_per_dispatch": w_attn,
+        "calib_copy_bytes": n,
+        "calib_fetch_size_kib": f_cal,
+        "calib_write_size_kib": w_cal,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "traffic_bytes_per_launch": f_attn * 1024.0 * f_scale + w_attn * 1024.0 * w_scale,
+        "kernel_sources_sha256_16": kernel_hash(),
+    }
 
 
 def stored_traffic(workload: str, khash: str):
@@ -148,9 +186,17 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the LSA decode path on one GPU only; --gpus must be 1 "
-              "(sharding across GPUs is described in DESIGN.md, not built)", file=sys.stderr)
+        print("bench.py: the LSA decode path runs on one GPU only; --gpus must be 1 "
+              "(sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_summary:
+        if args.calib_copy_mib <= 0:
+            raise SystemExit("--traffic-summary needs the --calib-copy-mib the counter passes ran with")
+        d = traffic_summary(*args.traffic_summary, workload=args.workload, calib_mib=args.calib_copy_mib)
+        out = ROOT / "profiles" / f"attn_kernel_{args.workload}_traffic.json"
+        out.write_text(json.dumps(d, indent=1) + "\n")
+        print(json.dumps(d))
+        return
 
     import torch
 
