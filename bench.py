@@ -284,8 +284,7 @@ def main():
             if timed_idx is not None:
                 gather_ev[t][0].record(sess.stream)
             copied = 0
-            for r in reqs:
-                c, _ = sess.gather(r, sel[r])
+            for r, (c, _) in sess.gather_many(sel).items():
                 copied += c
                 sel_hist[(r, int(sess.sel_version[r]))] = sess.sel_host[r]
             if timed_idx is not None:

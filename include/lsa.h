@@ -15,7 +15,8 @@
  * Three calls carry the loop:
  *   lsa_index_refresh   score, threshold, OR-union and compact (device, async)
  *   lsa_gather_blocks   make one request's hot pool hold a new selection
- *                       (host planning + one copy kernel, async)
+ *                       (host planning + one copy kernel, async); the _batch
+ *                       form does it for the requests of one refresh at once
  *   lsa_sparse_decode   one decode step over window + loaded blocks (device, async)
  *
  * Conventions for every call:
@@ -184,6 +185,14 @@ typedef struct lsa_gather_args {
 } lsa_gather_args;
 
 lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream);
+
+/* The gathers of n requests (1..LSA_MAX_REFRESH_REQ) after one refresh: the same as calling
+ * lsa_gather_blocks on a[0..n-1] in turn, except that every request is validated and planned
+ * before anything is enqueued (any failure: nothing enqueued, no state changed for any request)
+ * and the copies of all of them go into one kernel launch per 16 requests.  The requests must
+ * have distinct residency state and staging buffers and the same block_bytes; their hot slots must
+ * not overlap. */
+lsa_status lsa_gather_blocks_batch(const lsa_gather_args* a, int32_t n, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------
  * (3) Sparse decode: one decode step for n_req requests (zhichai.net explainer,

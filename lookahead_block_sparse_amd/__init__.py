@@ -55,6 +55,7 @@ EXPORTED_SYMBOLS = (
     "lsa_index_refresh_workspace",
     "lsa_index_refresh",
     "lsa_gather_blocks",
+    "lsa_gather_blocks_batch",
     "lsa_sparse_decode_workspace",
     "lsa_sparse_decode",
 )
@@ -127,6 +128,8 @@ def _load():
     lib.lsa_index_refresh.argtypes = [POINTER(RefreshArgs), c_void_p]
     lib.lsa_gather_blocks.restype = c_int32
     lib.lsa_gather_blocks.argtypes = [POINTER(GatherArgs), c_void_p]
+    lib.lsa_gather_blocks_batch.restype = c_int32
+    lib.lsa_gather_blocks_batch.argtypes = [POINTER(GatherArgs), c_int32, c_void_p]
     lib.lsa_sparse_decode_workspace.restype = c_int32
     lib.lsa_sparse_decode_workspace.argtypes = [POINTER(DecodeArgs), POINTER(c_size_t)]
     lib.lsa_sparse_decode.restype = c_int32

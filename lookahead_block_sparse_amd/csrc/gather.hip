@@ -1,15 +1,17 @@
-// Cold pool -> hot pool block gather for one request (zhichai.net explainer of "FlashMemory-DeepSeek-V4",
-// section 2 step 3: the selected blocks are moved from the CPU cold pool to the GPU; step 5: the loaded
-// set is refreshed).
+// Cold pool -> hot pool block gather (zhichai.net explainer of "FlashMemory-DeepSeek-V4", section 2
+// step 3: the selected blocks are moved from the CPU cold pool to the GPU; step 5: the loaded set is
+// refreshed).
 //
-// Host: diff the new ascending selection against the request's resident set, free the slots of blocks
-// that left, give free slots to blocks that entered, and write the copy list and the new block table
-// into the caller's pinned staging buffer.  Device: one kernel copies every entering 64-token block
-// (one contiguous block-format record) from the cold pool into its slot and copies the table.  The cold
-// pool may be pinned host memory (the kernel reads it over the host link, zero-copy) or device memory.
+// Host: per request, diff the new ascending selection against the resident set, free the slots of
+// blocks that left, give free slots to blocks that entered, and write the copy list and the new
+// block table into the caller's pinned staging buffer.  Device: one kernel copies every entering
+// 64-token block (one contiguous block-format record) from the cold pool into its slot and copies
+// the tables, for every request of the call.  A cold pool may be pinned host memory (the kernel
+// reads it over the host link, zero-copy) or device memory.
 #include <emmintrin.h>
 
 #include <algorithm>
+#include <cstring>
 #include <vector>
 
 #include "lsa_internal.hpp"
@@ -17,29 +19,47 @@
 namespace lsa {
 namespace {
 
-struct GatherParams {
+constexpr int kMaxBatch = 16;  // requests per copy-kernel launch
+
+struct GatherJob {
     const char* cold;
     char* hot;
     const int* copies;  // (source block, slot) pairs, device-visible
     const int* tsrc;    // table pairs, device-visible
     int* tdst;
-    int n_copies;
-    int n_table;
-    int block_bytes;
 };
 
-// Group g copies blocks g, g + G, ... of the copy list, one 64-token block at a time: 256 threads x
-// 16-byte vectors, every load of the block in flight before its stores.  The table is copied with one
-// grid-wide stride.  (One block per group with many groups measured faster than fewer groups that
-// copy several blocks each.)
+struct GatherParams {
+    int n_jobs;
+    int block_bytes;
+    int copy_off[kMaxBatch + 1];   // prefix of the jobs' copy counts
+    int table_off[kMaxBatch + 1];  // prefix of the jobs' table lengths (pairs)
+    GatherJob job[kMaxBatch];
+};
+
+// Copy c of the launch (jobs' copies concatenated) goes to group c, c + G, ...: one 64-token block
+// at a time, 256 threads x 16-byte vectors, every load of the block in flight before its stores.
+// The tables are copied with one grid-wide stride.  (One block per group with many groups measured
+// faster than fewer groups that copy several blocks each.)
 template <int PER>  // 16-byte vectors per thread per block (block_bytes / 4096)
 __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
     const int G = gridDim.x;
-    for (int e = blockIdx.x * 256 + threadIdx.x; e < 2 * p.n_table; e += G * 256) p.tdst[e] = p.tsrc[e];
+    const int n_table = p.table_off[p.n_jobs];
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < 2 * n_table; e += G * 256) {
+        int j = 0;
+        while (j + 1 < p.n_jobs && 2 * p.table_off[j + 1] <= e) ++j;
+        const int k = e - 2 * p.table_off[j];
+        p.job[j].tdst[k] = p.job[j].tsrc[k];
+    }
     constexpr int STEP = PER > 8 ? 8 : PER;
-    for (int c = blockIdx.x; c < p.n_copies; c += G) {
-        const uint4* src = reinterpret_cast<const uint4*>(p.cold + (size_t)p.copies[2 * c] * p.block_bytes);
-        uint4* dst = reinterpret_cast<uint4*>(p.hot + (size_t)p.copies[2 * c + 1] * p.block_bytes);
+    const int n_copies = p.copy_off[p.n_jobs];
+    for (int c = blockIdx.x; c < n_copies; c += G) {
+        int j = 0;
+        while (j + 1 < p.n_jobs && p.copy_off[j + 1] <= c) ++j;
+        const GatherJob& jb = p.job[j];
+        const int k = c - p.copy_off[j];
+        const uint4* src = reinterpret_cast<const uint4*>(jb.cold + (size_t)jb.copies[2 * k] * p.block_bytes);
+        uint4* dst = reinterpret_cast<uint4*>(jb.hot + (size_t)jb.copies[2 * k + 1] * p.block_bytes);
 #pragma unroll
         for (int v0 = 0; v0 < PER; v0 += STEP) {
             uint4 b[STEP];
@@ -79,12 +99,19 @@ lsa_status device_view(const void* ptr, const char* what, const void** out, bool
                 (int)attr.type);
 }
 
-}  // namespace
-}  // namespace lsa
+// Everything one request's gather decides before any state changes.
+struct GatherPlan {
+    std::vector<int> leave, enter, new_slot;
+    std::vector<int> freestack;  // slots of the blocks that left, ascending block id
+    std::vector<int> stage_buf;
+    int kept = 0;
+    const void* cold_dev = nullptr;
+    const void* stage_dev = nullptr;
+};
 
-using namespace lsa;
-
-extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream) {
+// Validate one request's arguments and plan its gather; fills the request's staging buffer (copy
+// list, then table).  Touches no caller state.
+lsa_status plan_gather(const lsa_gather_args* a, GatherPlan* P) {
     LSA_CHECK_ARG(a != nullptr, "lsa_gather_blocks: null args");
     LSA_CHECK_ARG(a->reserved1 == 0, "lsa_gather_blocks: reserved1 must be 0");
     LSA_CHECK_ARG(a->n_blocks >= 1 && a->n_blocks <= (1ll << 30), "lsa_gather_blocks: n_blocks=%lld", (long long)a->n_blocks);
@@ -115,7 +142,8 @@ extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t st
     thread_local std::vector<unsigned long long> want;
     want.assign((size_t)n_words, 0ull);
     for (int k = 0; k < a->n_new; ++k) want[a->new_ids[k] >> 6] |= 1ull << (a->new_ids[k] & 63);
-    thread_local std::vector<int> leave, enter;
+    std::vector<int>& leave = P->leave;
+    std::vector<int>& enter = P->enter;
     leave.clear();
     enter.clear();
     int kept = 0, resident = 0;
@@ -162,77 +190,129 @@ extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t st
     if ((int)enter.size() > avail)
         return fail(LSA_ERR_CAPACITY, "lsa_gather_blocks: %zu entering blocks, %d slots available", enter.size(), avail);
 
-    const void* cold_dev = nullptr;
-    const void* stage_dev = nullptr;
     bool cold_host = false, stage_host = false;
-    lsa_status st = device_view(a->cold, "cold", &cold_dev, &cold_host);
+    lsa_status st = device_view(a->cold, "cold", &P->cold_dev, &cold_host);
     if (st != LSA_OK) return st;
-    st = device_view(a->stage, "stage", &stage_dev, &stage_host);
+    st = device_view(a->stage, "stage", &P->stage_dev, &stage_host);
     if (st != LSA_OK) return st;
     LSA_CHECK_ARG(stage_host, "lsa_gather_blocks: stage must be pinned host memory");
 
-    // Simulate slot assignment on a copy of the free stack, fill the staging buffer.
-    thread_local std::vector<int> freestack, new_slot;
-    freestack.assign(a->free_slots, a->free_slots + *a->n_free);
-    for (int b : leave) freestack.push_back(a->slot_of_block[b]);
-    new_slot.resize(enter.size());
-    for (size_t k = 0; k < enter.size(); ++k) {
-        new_slot[k] = freestack.back();
-        freestack.pop_back();
+    // Slot assignment without copying the free stack: conceptually the blocks that left push their
+    // slots (ascending block id) on top of the caller's stack and each entering block (ascending)
+    // pops the top, so entering block k takes entry n_free + n_leave - 1 - k of that stack.
+    const int n_free = *a->n_free;
+    const int n_leave = (int)leave.size();
+    const int n_copies = (int)enter.size();
+    std::vector<int>& leave_slot = P->freestack;  // slots of the blocks that left, in that order
+    std::vector<int>& new_slot = P->new_slot;
+    leave_slot.resize(n_leave);
+    for (int j = 0; j < n_leave; ++j) leave_slot[j] = a->slot_of_block[leave[j]];
+    new_slot.resize(n_copies);
+    for (int k = 0; k < n_copies; ++k) {
+        const int idx = n_free + n_leave - 1 - k;
+        new_slot[k] = idx >= n_free ? leave_slot[idx - n_free] : a->free_slots[idx];
         LSA_CHECK_ARG(new_slot[k] >= 0 && new_slot[k] < a->n_slots_total, "lsa_gather_blocks: free slot %d out of range",
                       new_slot[k]);
     }
-    int* stage = a->stage;
-    const int n_copies = (int)enter.size();
+    // copy list then table, built in ordinary memory and moved to the pinned stage in one copy
+    std::vector<int>& out = P->stage_buf;
+    out.resize(2 * (size_t)(n_copies + a->n_new));
     for (int k = 0; k < n_copies; ++k) {
-        stage[2 * k] = enter[k];
-        stage[2 * k + 1] = new_slot[k];
+        out[2 * k] = enter[k];
+        out[2 * k + 1] = new_slot[k];
     }
-    int* table = stage + 2 * n_copies;
     {
-        size_t e = 0;
+        int* table = out.data() + 2 * n_copies;
+        int e = 0;
         for (int k = 0; k < a->n_new; ++k) {
             const int b = a->new_ids[k];
-            int s = a->slot_of_block[b];
-            if (s < 0) {
-                while (enter[e] != b) ++e;  // enter is ascending, a subsequence of new_ids
-                s = new_slot[e];
-            }
+            const int sl = a->slot_of_block[b];
+            const int fresh = sl < 0;  // enter is the ascending list of new ids with no slot
+            const int cand = n_copies > 0 ? new_slot[std::min(e, n_copies - 1)] : -1;  // in bounds either way
             table[2 * k] = b;
-            table[2 * k + 1] = s;
+            table[2 * k + 1] = fresh ? cand : sl;
+            e += fresh;
         }
     }
+    std::memcpy(a->stage, out.data(), out.size() * sizeof(int));
+    P->kept = kept;
+    return LSA_OK;
+}
 
-    if (n_copies > 0 || a->n_new > 0) {
-        DeviceInfo dev;
-        st = current_device(&dev);
+// Apply a planned gather to the caller's state (after its copy kernel was enqueued).
+void commit_gather(const lsa_gather_args* a, const GatherPlan& P) {
+    for (int b : P.leave) a->slot_of_block[b] = -1;
+    for (size_t k = 0; k < P.enter.size(); ++k) a->slot_of_block[P.enter[k]] = P.new_slot[k];
+    // new stack = old entries 0 .. n_free-1, then the left slots, minus the n_enter popped from the top
+    const int n_free = *a->n_free;
+    const int top = n_free + (int)P.freestack.size() - (int)P.enter.size();
+    for (int i = n_free; i < top; ++i) a->free_slots[i] = P.freestack[i - n_free];
+    *a->n_free = top;
+    *a->n_copied = (int)P.enter.size();
+    *a->n_kept = P.kept;
+}
+
+// Plan every request, then launch the copy kernel(s), then commit: all or nothing.
+lsa_status gather_batch(const lsa_gather_args* args, int n, hipStream_t stream) {
+    LSA_CHECK_ARG(args != nullptr, "lsa_gather_blocks: null args");
+    LSA_CHECK_ARG(n >= 1 && n <= LSA_MAX_REFRESH_REQ, "lsa_gather_blocks_batch: n=%d outside 1..%d", n,
+                  LSA_MAX_REFRESH_REQ);
+    for (int i = 0; i < n; ++i)
+        for (int k = 0; k < i; ++k)
+            LSA_CHECK_ARG(args[i].slot_of_block != args[k].slot_of_block && args[i].stage != args[k].stage,
+                          "lsa_gather_blocks_batch: requests %d and %d share residency state or a staging buffer", k, i);
+    thread_local std::vector<GatherPlan> plans;
+    if ((int)plans.size() < n) plans.resize(n);
+    for (int i = 0; i < n; ++i) {
+        lsa_status st = plan_gather(&args[i], &plans[i]);
         if (st != LSA_OK) return st;
+        LSA_CHECK_ARG(args[i].block_bytes == args[0].block_bytes, "lsa_gather_blocks_batch: block_bytes differ");
+    }
+    DeviceInfo dev;
+    lsa_status st = current_device(&dev);
+    if (st != LSA_OK) return st;
+    for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
+        const int nj = std::min(kMaxBatch, n - i0);
         GatherParams gp{};
-        gp.cold = static_cast<const char*>(cold_dev);
-        gp.hot = static_cast<char*>(a->hot);
-        gp.copies = static_cast<const int*>(stage_dev);
-        gp.tsrc = static_cast<const int*>(stage_dev) + 2 * n_copies;
-        gp.tdst = a->table_dev;
-        gp.n_copies = n_copies;
-        gp.n_table = a->n_new;
-        gp.block_bytes = a->block_bytes;
-        // one group per copied block (capped), at least enough groups for the table copy
-        const int grid = std::max(1, std::min(std::max(n_copies, (2 * a->n_new + 255) / 256), dev.cu_count * 32));
-        switch (a->block_bytes / 4096) {
+        gp.n_jobs = nj;
+        gp.block_bytes = args[0].block_bytes;
+        for (int j = 0; j < nj; ++j) {
+            const lsa_gather_args* a = &args[i0 + j];
+            const GatherPlan& P = plans[i0 + j];
+            const int n_copies = (int)P.enter.size();
+            gp.job[j].cold = static_cast<const char*>(P.cold_dev);
+            gp.job[j].hot = static_cast<char*>(a->hot);
+            gp.job[j].copies = static_cast<const int*>(P.stage_dev);
+            gp.job[j].tsrc = static_cast<const int*>(P.stage_dev) + 2 * n_copies;
+            gp.job[j].tdst = a->table_dev;
+            gp.copy_off[j + 1] = gp.copy_off[j] + n_copies;
+            gp.table_off[j + 1] = gp.table_off[j] + a->n_new;
+        }
+        const int n_copies = gp.copy_off[nj], n_table = gp.table_off[nj];
+        if (n_copies == 0 && n_table == 0) continue;
+        // one group per copied block (capped), at least enough groups for the table copies
+        const int grid = std::max(1, std::min(std::max(n_copies, (2 * n_table + 255) / 256), dev.cu_count * 32));
+        switch (gp.block_bytes / 4096) {
             case 4: hipLaunchKernelGGL(gather_kernel<4>, dim3(grid), dim3(256), 0, stream, gp); break;
             case 8: hipLaunchKernelGGL(gather_kernel<8>, dim3(grid), dim3(256), 0, stream, gp); break;
             case 16: hipLaunchKernelGGL(gather_kernel<16>, dim3(grid), dim3(256), 0, stream, gp); break;
-            default: return fail(LSA_ERR_UNSUPPORTED, "lsa_gather_blocks: block_bytes=%d", a->block_bytes);
+            default: return fail(LSA_ERR_UNSUPPORTED, "lsa_gather_blocks: block_bytes=%d", gp.block_bytes);
         }
         LSA_HIP(hipGetLastError());
     }
-
-    // ---- commit caller state ----
-    for (int b : leave) a->slot_of_block[b] = -1;
-    for (size_t k = 0; k < enter.size(); ++k) a->slot_of_block[enter[k]] = new_slot[k];
-    std::copy(freestack.begin(), freestack.end(), a->free_slots);
-    *a->n_free = (int)freestack.size();
-    *a->n_copied = n_copies;
-    *a->n_kept = kept;
+    for (int i = 0; i < n; ++i) commit_gather(&args[i], plans[i]);
     return LSA_OK;
+}
+
+}  // namespace
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream) {
+    return gather_batch(a, 1, stream);
+}
+
+extern "C" lsa_status lsa_gather_blocks_batch(const lsa_gather_args* a, int32_t n, hipStream_t stream) {
+    return gather_batch(a, n, stream);
 }

@@ -219,15 +219,11 @@ class LSASession:
     # ---------------------------------------------------------------------------------------
     def gather(self, r: int, ids: np.ndarray, stream: Optional[torch.cuda.Stream] = None):
         """Make request r's hot pool hold exactly `ids` (returns (copied, kept))."""
-        st = stream if stream is not None else self.stream
-        if st is not self.stream:
-            if not self.track_decode:
-                raise RuntimeError("set track_decode before gathering on a side stream")
-            if self.last_decode_event is not None:
-                st.wait_event(self.last_decode_event)  # slots of leaving blocks may still be read
+        return self.gather_many({r: ids}, stream)[r]
+
+    def _gather_args(self, r: int):
         if self.cold[r] is None:
             raise RuntimeError(f"request {r} has no cold pool: call load_prefill first")
-        ids = np.ascontiguousarray(ids, dtype=np.int32)
         if self._gargs[r] is None:
             # every field but the selection is fixed for the session: built once per request
             a = GatherArgs()
@@ -243,23 +239,41 @@ class LSASession:
             counts = np.zeros(2, dtype=np.int32)
             a.n_copied, a.n_kept = counts.ctypes.data, counts.ctypes.data + 4
             self._gargs[r] = (a, counts)
-        a, counts = self._gargs[r]
-        if self._stage_ev[r] is not None:
-            self._stage_ev[r].synchronize()  # the previous copy kernel may still read stage[r]
-        a.new_ids, a.n_new = ids.ctypes.data, len(ids)
-        _check(LIB.lsa_gather_blocks(ctypes.byref(a), st.cuda_stream))
-        res = (int(counts[0]), int(counts[1]))
-        if self._stage_ev[r] is None:
-            self._stage_ev[r] = torch.cuda.Event()
-        self._stage_ev[r].record(st)
-        self.n_sel[r] = len(ids)
-        self.sel_host[r] = ids
-        self.sel_version[r] += 1
+        return self._gargs[r]
+
+    def gather_many(self, sel: Dict[int, np.ndarray], stream: Optional[torch.cuda.Stream] = None):
+        """Gathers of several requests after one refresh, planned together and copied by one kernel
+        launch (lsa_gather_blocks_batch).  Returns {r: (copied, kept)}."""
+        st = stream if stream is not None else self.stream
         if st is not self.stream:
-            ev = torch.cuda.Event()
-            ev.record(st)
+            if not self.track_decode:
+                raise RuntimeError("set track_decode before gathering on a side stream")
+            if self.last_decode_event is not None:
+                st.wait_event(self.last_decode_event)  # slots of leaving blocks may still be read
+        reqs = list(sel)
+        ids = {r: np.ascontiguousarray(sel[r], dtype=np.int32) for r in reqs}
+        arr = (GatherArgs * len(reqs))()
+        counts = []
+        for k, r in enumerate(reqs):
+            a, c = self._gather_args(r)
+            if self._stage_ev[r] is not None:
+                self._stage_ev[r].synchronize()  # the previous copy kernel may still read stage[r]
+            a.new_ids, a.n_new = ids[r].ctypes.data, len(ids[r])
+            arr[k] = a
+            counts.append(c)
+        _check(LIB.lsa_gather_blocks_batch(arr, len(reqs), st.cuda_stream))
+        ev = torch.cuda.Event()
+        ev.record(st)
+        out = {}
+        for k, r in enumerate(reqs):
+            self._stage_ev[r] = ev
+            self.n_sel[r] = len(ids[r])
+            self.sel_host[r] = ids[r]
+            self.sel_version[r] += 1
+            out[r] = (int(counts[k][0]), int(counts[k][1]))
+        if st is not self.stream:
             self.stream.wait_event(ev)
-        return res
+        return out
 
     # ---------------------------------------------------------------------------------------
     def attended_entries(self, seq_len: Sequence[int], window: Sequence[int]) -> np.ndarray:

@@ -138,6 +138,36 @@ def test_gather_validation(case):
         assert np.array_equal(b, x)
 
 
+@pytest.mark.parametrize("n", [0, 65])
+def test_gather_batch_rejects_request_count(n):
+    a, keep = _gather_args()
+    arr = (L.GatherArgs * 1)(a)
+    assert L.LIB.lsa_gather_blocks_batch(arr, n, None) == L.LSA_ERR_INVALID
+
+
+def test_gather_batch_rejects_shared_state():
+    a, keep = _gather_args()
+    b, keep_b = _gather_args(new_ids=(2, 3))
+    b.slot_of_block = a.slot_of_block
+    arr = (L.GatherArgs * 2)(a, b)
+    before = [x.copy() for x in keep[:3]]
+    assert L.LIB.lsa_gather_blocks_batch(arr, 2, None) == L.LSA_ERR_INVALID
+    assert "share" in L.LIB.lsa_last_error().decode()
+    for x, y in zip(before, keep[:3]):
+        assert np.array_equal(x, y)
+
+
+def test_gather_batch_stops_at_first_invalid_request():
+    a, keep = _gather_args(capacity=2, new_ids=(1, 5, 9))  # overflow
+    b, keep_b = _gather_args(new_ids=(2, 3))
+    b.stage = FAKE + (1 << 20)  # its own staging buffer
+    arr = (L.GatherArgs * 2)(a, b)
+    before = [x.copy() for x in keep[:3] + keep_b[:3]]
+    assert L.LIB.lsa_gather_blocks_batch(arr, 2, None) == L.LSA_ERR_CAPACITY
+    for x, y in zip(before, keep[:3] + keep_b[:3]):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(head_dim=96), L.LSA_ERR_UNSUPPORTED),
     (dict(n_heads=17), L.LSA_ERR_UNSUPPORTED),

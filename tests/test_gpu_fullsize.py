@@ -35,8 +35,8 @@ def _run_bench_style(wl, sess, record):
         hid = torch.from_numpy(np.stack([wl.hidden[r][k_of[r]] for r in reqs]).view(np.int16)).to(dev)
         bias = torch.from_numpy(np.stack([wl.bias[r] for r in reqs]).astype(np.float32)).to(dev)
         got = sess.refresh(reqs, hid, bias)
+        sess.gather_many(got)
         for r in reqs:
-            sess.gather(r, got[r])
             sels[(r, k_of[r])] = got[r]
 
     pro = [r for r in range(R) if wl.refresh_steps[r][0] < 0]

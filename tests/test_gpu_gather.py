@@ -85,3 +85,48 @@ def test_gather_capacity_overflow_is_an_error():
         sess.gather(0, sel[0])
     assert e.value.status == L.LSA_ERR_CAPACITY
     assert np.array_equal(before, sess.slot_of_block[0])
+
+
+def test_gather_batch_matches_one_request_at_a_time():
+    """One batched call for all requests of a refresh leaves the same pools, tables and residency
+    state as one call per request, over refreshes that move blocks in and out."""
+    log("gather batch vs single")
+    wl = conditioned_workload("ctx512k_s", seed=14)
+    one = make_session(wl, cold_on_device=True, with_masks=False)
+    many = make_session(wl, cold_on_device=True, with_masks=False)
+    reqs = list(range(wl.n_req))
+    for k in range(len(wl.refresh_steps[0])):
+        hid = np.stack([wl.hidden[r][k] for r in reqs])
+        sel = one.refresh(reqs, hid, wl.bias)
+        sel_b = many.refresh(reqs, hid, wl.bias)
+        got_one = {r: one.gather(r, sel[r]) for r in reqs}
+        got_many = many.gather_many(sel_b)
+        torch.cuda.synchronize()
+        assert got_one == got_many, (k, got_one, got_many)
+        for r in reqs:
+            assert np.array_equal(one.slot_of_block[r], many.slot_of_block[r]), (k, r)
+            assert np.array_equal(one.free_slots[r][:one.n_free[r][0]], many.free_slots[r][:many.n_free[r][0]])
+            _check_pool(many, r, sel_b[r])
+        n = 2 * int(one.slot_base[-1])
+        assert torch.equal(one.table[:n], many.table[:n])
+
+
+def test_gather_batch_overflow_changes_no_request():
+    """A batch whose second request overflows its hot pool fails as a whole: the first request's
+    state and pool are untouched too."""
+    import lookahead_block_sparse_amd as L
+    log("gather batch overflow")
+    wl = conditioned_workload("ctx512k_s", seed=15, steps=1)
+    refs, _ = oracle.simulate(wl, steps=[])
+    cap = [int(wl.n_blocks[r]) for r in range(wl.n_req)]
+    cap[1] = len(refs[1][0].ids) - 1
+    sess = make_session(wl, capacity=cap, with_masks=False)
+    reqs = list(range(wl.n_req))
+    sel = sess.refresh(reqs, np.stack([wl.hidden[r][0] for r in reqs]), wl.bias)
+    before = [sess.slot_of_block[r].copy() for r in reqs]
+    with pytest.raises(L.LSAError) as e:
+        sess.gather_many(sel)
+    assert e.value.status == L.LSA_ERR_CAPACITY
+    for r in reqs:
+        assert np.array_equal(before[r], sess.slot_of_block[r]), r
+        assert sess.n_free[r][0] == sess.capacity[r]
