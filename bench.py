@@ -56,6 +56,13 @@ def parse():
     ap.add_argument("--cold", choices=("device", "host"), default="device")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-steps", type=int, default=6, help="decode steps per request timed on the CPU")
+    ap.add_argument("--tau", type=int, default=0,
+                    help="refresh cadence in steps (default: the workload's, 64); 1 scores every step")
+    ap.add_argument("--density", type=float, default=0.0,
+                    help="union density the indexer biases are set for (default: the workload's)")
+    ap.add_argument("--select", choices=("threshold", "all"), default="threshold",
+                    help="all: every block selected at one refresh before the first step, i.e. dense "
+                         "attention over the whole context through the same kernels (comparator)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="time the attention kernel with HIP events on every N-th timed step (the events "
                          "take the dispatch's own stamps but still cost stream time)")
@@ -214,11 +221,19 @@ def main():
     cfg = get_config(args.workload)
     W, K = args.warmup, args.steps
     total_steps = W + K
+    if args.tau > 0:
+        cfg = cfg.scaled(tau=args.tau)
+    if args.density > 0:
+        cfg = cfg.scaled(density=("fixed", args.density))
+    if args.select == "all":
+        cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0)  # one refresh, at step 0
     t_setup = time.perf_counter()
     wl = build_workload(cfg, seed=args.seed, steps=max(cfg.steps, total_steps))
     cfg = wl.cfg
     if cfg.planted_frac > 0:
         wl.condition(_planting_query(cfg.dtype), None)
+    if args.select == "all":
+        wl.bias[:] = 1e4  # every logit above zero: every block selected
     note(f"workload {cfg.name}: {wl.n_req} requests, contexts {wl.ctx.tolist()[:4]}..., built")
 
     dev = torch.device("cuda")
@@ -356,8 +371,11 @@ def main():
             "workload": (f"{cfg.name}: {wl.n_req} requests x {int(wl.ctx[0])}-token context, {cfg.n_idx} indexers "
                          f"(d_model {cfg.d_model}, d_idx {cfg.d_idx}), {cfg.n_heads} q-heads / 1 kv-head x "
                          f"{cfg.head_dim}, window {cfg.window}, refresh every {cfg.tau} steps, "
-                         f"{int(100 * cfg.planted_frac)}% planted + background density {cfg.density}"),
+                         f"{int(100 * cfg.planted_frac)}% planted + background density {cfg.density}"
+                         + (", every block selected (dense comparator)" if args.select == "all" else "")),
             "cold_pool": args.cold,
+            "tau": cfg.tau,
+            "select": args.select,
             "requests": wl.n_req,
             "context_tokens": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else wl.ctx.tolist(),
             "seed": args.seed,

@@ -204,3 +204,27 @@ def test_needles(where):
     o = gpu[t][0]
     close = np.allclose(o, v_star[None, :], atol=2e-2)
     assert close == attended, (where, p, ws, attended, np.abs(o - v_star).max())
+
+
+@pytest.mark.parametrize("tau,steps", [(1, 24), (16, 70)])
+def test_decode_loop_other_cadences(tau, steps):
+    """The refresh cadence is a parameter of the method (64 on the pages): refreshing every step
+    (the per-step, reactive extreme) or every 16 steps gives the oracle's selections and outputs."""
+    from workloads import get_config
+
+    cfg = get_config("ctx128k_s").scaled(tau=tau, steps=steps)
+    log(f"cadence tau={tau}, {steps} steps")
+    wl = conditioned_workload(cfg, seed=21)
+    sample = sorted({0, steps - 1} | {t for t in range(steps) if t % tau in (0, tau - 1)} if tau > 1 else set(range(steps)))
+    sess = make_session(wl, with_masks=False)
+    gpu, sels = run_loop(wl, sess, range(steps), record=sample)
+    refs, outs = oracle.simulate(wl, steps=sample)
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (tau, r, k)
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
+    log(f"  tau={tau}: {len(sels)} refreshes bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
