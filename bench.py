@@ -60,6 +60,10 @@ def parse():
                     help="refresh cadence in steps (default: the workload's, 64); 1 scores every step")
     ap.add_argument("--density", type=float, default=0.0,
                     help="union density the indexer biases are set for (default: the workload's)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="attention layers whose block loads each selection drives (own K/V and queries)")
+    ap.add_argument("--hidden-rho", type=float, default=0.0,
+                    help="correlation of successive refresh hidden states (0: independent)")
     ap.add_argument("--select", choices=("threshold", "all"), default="threshold",
                     help="all: every block selected at one refresh before the first step, i.e. dense "
                          "attention over the whole context through the same kernels (comparator)")
@@ -225,6 +229,8 @@ def main():
         cfg = cfg.scaled(tau=args.tau)
     if args.density > 0:
         cfg = cfg.scaled(density=("fixed", args.density))
+    if args.layers > 1 or args.hidden_rho:
+        cfg = cfg.scaled(n_layers=args.layers, hidden_rho=args.hidden_rho)
     if args.select == "all":
         cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0)  # one refresh, at step 0
     t_setup = time.perf_counter()
@@ -239,10 +245,14 @@ def main():
     dev = torch.device("cuda")
     sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
-                      w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False)
+                      w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False,
+                      n_layers=cfg.n_layers)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
+        for layer in range(1, cfg.n_layers):
+            kl, vl = wl.kv_prefill(r, layer)
+            sess.load_prefill(r, kl, vl, layer=layer)
         if args.no_cpu_baseline:
             wl.drop_kv(r)
     note(f"session ready in {time.perf_counter() - t_setup:.1f}s (cold pool on {args.cold})")
@@ -262,6 +272,9 @@ def main():
     q_all = dev_raw(wl.q_dec[:total_steps])
     kn_all = dev_raw(wl.k_new[:total_steps])
     vn_all = dev_raw(wl.v_new[:total_steps])
+    # layers 1..: their own queries and new tokens (layer 0 is timed)
+    layer_in = [tuple(dev_raw(a[:total_steps]) for a in (wl.q_dec_of(l), wl.k_new_of(l), wl.v_new_of(l)))
+                for l in range(1, cfg.n_layers)]
     out = torch.empty((wl.n_req, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
     window = np.full(wl.n_req, cfg.window, dtype=np.int32)
 
@@ -279,6 +292,8 @@ def main():
     e = 2 if cfg.dtype == "bf16" else 4
     D, H = cfg.head_dim, cfg.n_heads
     loop = DecodeLoop(sess, wl.ctx, window, out)
+    outs_l = [torch.empty_like(out) for _ in range(1, cfg.n_layers)]
+    loops_l = [DecodeLoop(sess, wl.ctx, window, outs_l[l - 1], layer=l) for l in range(1, cfg.n_layers)]
     gather_host_s = []
     gather_blocks = []
     sel_hist = {}        # (request, selection version) -> ascending ids
@@ -308,9 +323,13 @@ def main():
                 gather_blocks.append(copied)
         if timed_idx is None:
             loop.step(t, q_all[t], kn_all[t], vn_all[t])
+            for lp, (ql, kl, vl) in zip(loops_l, layer_in):
+                lp.step(t, ql[t], kl[t], vl[t])
         else:
             ev = att_ev.get(timed_idx, (None, None))
             loop.step(t, q_all[t], kn_all[t], vn_all[t], ev[0], ev[1])
+            for lp, (ql, kl, vl) in zip(loops_l, layer_in):
+                lp.step(t, ql[t], kl[t], vl[t])
             step_log.append((t, loop.n_sel.copy(), sess.sel_version.copy(), timed_idx in att_ev))
 
     note(f"warm-up {W} steps")
@@ -372,9 +391,13 @@ def main():
                          f"(d_model {cfg.d_model}, d_idx {cfg.d_idx}), {cfg.n_heads} q-heads / 1 kv-head x "
                          f"{cfg.head_dim}, window {cfg.window}, refresh every {cfg.tau} steps, "
                          f"{int(100 * cfg.planted_frac)}% planted + background density {cfg.density}"
-                         + (", every block selected (dense comparator)" if args.select == "all" else "")),
+                         + (", every block selected (dense comparator)" if args.select == "all" else "")
+                         + (f", {cfg.n_layers} attention layers per selection" if cfg.n_layers > 1 else "")
+                         + (f", hidden-state correlation {cfg.hidden_rho}" if cfg.hidden_rho else "")),
             "cold_pool": args.cold,
             "tau": cfg.tau,
+            "layers": cfg.n_layers,
+            "hidden_rho": cfg.hidden_rho,
             "select": args.select,
             "requests": wl.n_req,
             "context_tokens": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else wl.ctx.tolist(),

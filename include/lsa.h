@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 2
+#define LSA_ABI_VERSION 3
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -163,6 +163,12 @@ lsa_status lsa_index_refresh(const lsa_refresh_args* a, hipStream_t stream);
  *   - `stage` is read by the copy kernel: do not reuse it until `stream` has
  *     passed this call.
  * State (slot_of_block, free_slots, n_free) is updated only on LSA_OK.
+ *
+ * Several attention layers (the pages' indexers feed the block loads of the
+ * whole model: 1kpapers report page, Summary, and the explainer's section 4 with
+ * indexers at three layers): with n_layers = L > 1 the one plan and the one
+ * table serve L layers, each with its own cold and hot pool at a fixed byte
+ * stride from layer 0's, and every entering block is copied for every layer.
  * ------------------------------------------------------------------------------------ */
 typedef struct lsa_gather_args {
     int64_t n_blocks;          /* blocks of this request */
@@ -177,11 +183,15 @@ typedef struct lsa_gather_args {
     int32_t* free_slots;       /* host [capacity]: stack of this request's free slots (in/out) */
     int32_t* n_free;           /* host: entries in free_slots (in/out) */
     int32_t capacity;          /* this request's slot count (free_slots capacity) */
-    int32_t reserved1;         /* must be 0 */
+    int32_t n_layers;          /* 0 or 1: one layer; L in 2..256: layers 0..L-1 (strides below) */
     int32_t* stage;            /* pinned: copy list (source block, slot) pairs, then the table */
     int32_t* table_dev;        /* dev [capacity][2]: (block id, slot) pairs, ascending */
-    int32_t* n_copied;         /* host out: blocks copied */
+    int32_t* n_copied;         /* host out: blocks copied (per layer) */
     int32_t* n_kept;           /* host out: blocks that stayed resident */
+    int64_t cold_layer_bytes;  /* L > 1: layer l's cold pool at cold + l*cold_layer_bytes (one
+                                  allocation; >= n_blocks*block_bytes, multiple of 16) */
+    int64_t hot_layer_bytes;   /* L > 1: layer l's hot pool at hot + l*hot_layer_bytes
+                                  (>= n_slots_total*block_bytes, multiple of 16) */
 } lsa_gather_args;
 
 lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream);

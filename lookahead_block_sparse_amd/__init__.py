@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -85,8 +85,9 @@ class GatherArgs(Structure):
         ("n_blocks", c_int64), ("n_slots_total", c_int32), ("block_bytes", c_int32),
         ("cold", c_void_p), ("hot", c_void_p), ("new_ids", c_void_p), ("n_new", c_int32),
         ("stage_ints", c_int32), ("slot_of_block", c_void_p), ("free_slots", c_void_p),
-        ("n_free", c_void_p), ("capacity", c_int32), ("reserved1", c_int32), ("stage", c_void_p),
+        ("n_free", c_void_p), ("capacity", c_int32), ("n_layers", c_int32), ("stage", c_void_p),
         ("table_dev", c_void_p), ("n_copied", c_void_p), ("n_kept", c_void_p),
+        ("cold_layer_bytes", c_int64), ("hot_layer_bytes", c_int64),
     ]
 
 
@@ -253,7 +254,7 @@ def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_id
     a.new_ids, a.n_new = _ptr(ids), len(ids)
     a.stage_ints = int(stage.numel()) if stage is not None else 0
     a.slot_of_block, a.free_slots, a.n_free = _ptr(slot_of_block), _ptr(free_slots), _ptr(n_free)
-    a.capacity, a.reserved1 = int(capacity), 0
+    a.capacity, a.n_layers = int(capacity), 0
     a.stage, a.table_dev = _ptr(stage), _ptr(table_dev)
     a.n_copied, a.n_kept = _ptr(n_copied), _ptr(n_kept)
     _check(LIB.lsa_gather_blocks(ctypes.byref(a), _stream(stream)))

@@ -5,8 +5,8 @@
 // Host: per request, diff the new ascending selection against the resident set, free the slots of
 // blocks that left, give free slots to blocks that entered, and write the copy list and the new
 // block table into the caller's pinned staging buffer.  Device: one kernel copies every entering
-// 64-token block (one contiguous block-format record) from the cold pool into its slot and copies
-// the tables, for every request of the call.  A cold pool may be pinned host memory (the kernel
+// 64-token block (one contiguous block-format record) from the cold pool into its slot, for every
+// layer the selection serves, and copies the tables, for every request of the call.  A cold pool may be pinned host memory (the kernel
 // reads it over the host link, zero-copy) or device memory.
 #include <emmintrin.h>
 
@@ -27,12 +27,14 @@ struct GatherJob {
     const int* copies;  // (source block, slot) pairs, device-visible
     const int* tsrc;    // table pairs, device-visible
     int* tdst;
+    long long cold_layer_bytes, hot_layer_bytes;
+    int n_copies;       // per layer
 };
 
 struct GatherParams {
     int n_jobs;
     int block_bytes;
-    int copy_off[kMaxBatch + 1];   // prefix of the jobs' copy counts
+    int copy_off[kMaxBatch + 1];   // prefix of the jobs' copy counts (copies x layers)
     int table_off[kMaxBatch + 1];  // prefix of the jobs' table lengths (pairs)
     GatherJob job[kMaxBatch];
 };
@@ -57,9 +59,12 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
         int j = 0;
         while (j + 1 < p.n_jobs && p.copy_off[j + 1] <= c) ++j;
         const GatherJob& jb = p.job[j];
-        const int k = c - p.copy_off[j];
-        const uint4* src = reinterpret_cast<const uint4*>(jb.cold + (size_t)jb.copies[2 * k] * p.block_bytes);
-        uint4* dst = reinterpret_cast<uint4*>(jb.hot + (size_t)jb.copies[2 * k + 1] * p.block_bytes);
+        const int kl = c - p.copy_off[j];
+        const int layer = kl / jb.n_copies;
+        const int k = kl - layer * jb.n_copies;
+        const uint4* src = reinterpret_cast<const uint4*>(jb.cold + layer * jb.cold_layer_bytes +
+                                                          (size_t)jb.copies[2 * k] * p.block_bytes);
+        uint4* dst = reinterpret_cast<uint4*>(jb.hot + layer * jb.hot_layer_bytes + (size_t)jb.copies[2 * k + 1] * p.block_bytes);
 #pragma unroll
         for (int v0 = 0; v0 < PER; v0 += STEP) {
             uint4 b[STEP];
@@ -113,7 +118,15 @@ struct GatherPlan {
 // list, then table).  Touches no caller state.
 lsa_status plan_gather(const lsa_gather_args* a, GatherPlan* P) {
     LSA_CHECK_ARG(a != nullptr, "lsa_gather_blocks: null args");
-    LSA_CHECK_ARG(a->reserved1 == 0, "lsa_gather_blocks: reserved1 must be 0");
+    LSA_CHECK_ARG(a->n_layers >= 0 && a->n_layers <= 256, "lsa_gather_blocks: n_layers=%d outside 0..256", a->n_layers);
+    if (a->n_layers > 1) {
+        LSA_CHECK_ARG(a->cold_layer_bytes >= a->n_blocks * (long long)a->block_bytes && a->cold_layer_bytes % 16 == 0,
+                      "lsa_gather_blocks: cold_layer_bytes=%lld (>= n_blocks*block_bytes, multiple of 16)",
+                      (long long)a->cold_layer_bytes);
+        LSA_CHECK_ARG(a->hot_layer_bytes >= (long long)a->n_slots_total * a->block_bytes && a->hot_layer_bytes % 16 == 0,
+                      "lsa_gather_blocks: hot_layer_bytes=%lld (>= n_slots_total*block_bytes, multiple of 16)",
+                      (long long)a->hot_layer_bytes);
+    }
     LSA_CHECK_ARG(a->n_blocks >= 1 && a->n_blocks <= (1ll << 30), "lsa_gather_blocks: n_blocks=%lld", (long long)a->n_blocks);
     LSA_CHECK_SUP(a->block_bytes == 16384 || a->block_bytes == 32768 || a->block_bytes == 65536,
                   "lsa_gather_blocks: block_bytes=%d (16, 32 or 64 KiB: the block format's sizes)", a->block_bytes);
@@ -285,7 +298,11 @@ lsa_status gather_batch(const lsa_gather_args* args, int n, hipStream_t stream) 
             gp.job[j].copies = static_cast<const int*>(P.stage_dev);
             gp.job[j].tsrc = static_cast<const int*>(P.stage_dev) + 2 * n_copies;
             gp.job[j].tdst = a->table_dev;
-            gp.copy_off[j + 1] = gp.copy_off[j] + n_copies;
+            const int layers = std::max(1, a->n_layers);
+            gp.job[j].n_copies = n_copies;
+            gp.job[j].cold_layer_bytes = layers > 1 ? a->cold_layer_bytes : 0;
+            gp.job[j].hot_layer_bytes = layers > 1 ? a->hot_layer_bytes : 0;
+            gp.copy_off[j + 1] = gp.copy_off[j] + n_copies * layers;
             gp.table_off[j + 1] = gp.table_off[j] + a->n_new;
         }
         const int n_copies = gp.copy_off[nj], n_table = gp.table_off[nj];

@@ -56,13 +56,18 @@ class LSASession:
                  win_cap: int, n_blocks: Sequence[int], w_q: np.ndarray, keys: Sequence[np.ndarray],
                  capacity: Optional[Sequence[int]] = None, cold_on_device: bool = False,
                  with_masks: bool = False, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
-                 max_groups: int = 0):
+                 max_groups: int = 0, n_layers: int = 1):
         self.dtype = dtype
         self.n_idx, self.d_model, self.d_idx = n_idx, d_model, d_idx
         self.n_heads, self.head_dim, self.win_cap = n_heads, head_dim, win_cap
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.max_groups = max_groups
+        # attention layers whose block loads one selection drives: each has its own cold pool, hot
+        # pool and window ring at a fixed stride from layer 0's; slots and the table are shared
+        self.n_layers = int(n_layers)
+        if not 1 <= self.n_layers <= 256:
+            raise ValueError("n_layers must be in 1..256")
         self.n_req = len(n_blocks)
         self.n_blocks = np.asarray(n_blocks, dtype=np.int64)
         self.blk_off = np.concatenate([[0], np.cumsum(self.n_blocks)]).astype(np.int64)
@@ -94,7 +99,8 @@ class LSASession:
             self.capacity = cap
             self.slot_base = np.concatenate([[0], np.cumsum(cap)]).astype(np.int64)
             self.n_slots = int(self.slot_base[-1])
-            self.hot = torch.empty(max(1, self.n_slots) * self.block_bytes, dtype=torch.uint8, device=self.device)
+            self.hot_layer_bytes = max(1, self.n_slots) * self.block_bytes
+            self.hot = torch.empty(self.n_layers * self.hot_layer_bytes, dtype=torch.uint8, device=self.device)
             self.table = torch.zeros(max(1, self.n_slots) * 2, dtype=torch.int32, device=self.device)
             self.slot_of_block = [np.full(int(b), -1, dtype=np.int32) for b in self.n_blocks]
             self.free_slots = [np.arange(self.slot_base[r + 1] - 1, self.slot_base[r] - 1, -1, dtype=np.int32)
@@ -108,7 +114,8 @@ class LSASession:
             # cold pools and rings
             self.cold: List[Optional[torch.Tensor]] = [None] * self.n_req
             n_chunks = win_cap // BLOCK_TOKENS
-            self.ring = torch.zeros(self.n_req * n_chunks * self.block_bytes, dtype=torch.uint8, device=self.device)
+            self.ring_layer_bytes = self.n_req * n_chunks * self.block_bytes
+            self.ring = torch.zeros(self.n_layers * self.ring_layer_bytes, dtype=torch.uint8, device=self.device)
             ws = lsa_sparse_decode_workspace(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap,
                                              n_req=self.n_req, max_groups=max_groups)
             self.decode_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
@@ -119,28 +126,40 @@ class LSASession:
         self.track_decode = False
 
     # ---------------------------------------------------------------------------------------
-    def load_prefill(self, r: int, k_tok: np.ndarray, v_tok: np.ndarray) -> None:
-        """Pack request r's prefill K/V ([N_r][D] raw) into its cold pool and window ring."""
+    def load_prefill(self, r: int, k_tok: np.ndarray, v_tok: np.ndarray, layer: int = 0) -> None:
+        """Pack request r's prefill K/V ([N_r][D] raw) of one layer into its cold pool and window
+        ring."""
         n = int(self.n_blocks[r]) * BLOCK_TOKENS
         assert k_tok.shape[0] == n and v_tok.shape[0] == n
+        assert 0 <= layer < self.n_layers
         k_tok = np.ascontiguousarray(k_tok)
         v_tok = np.ascontiguousarray(v_tok)
-        cold_h = torch.empty(int(self.n_blocks[r]) * self.block_bytes, dtype=torch.uint8,
-                             pin_memory=not self.cold_on_device)
-        lsa_pack_blocks(self.dtype, self.head_dim, k_tok, v_tok, 0, n, cold_h, int(self.n_blocks[r]))
+        lb = int(self.n_blocks[r]) * self.block_bytes  # bytes of one layer's cold pool
+        if self.cold[r] is None:
+            self.cold[r] = (torch.empty(self.n_layers * lb, dtype=torch.uint8, device=self.device)
+                            if self.cold_on_device else
+                            torch.empty(self.n_layers * lb, dtype=torch.uint8, pin_memory=True))
+            self._gargs[r] = None
         if self.cold_on_device:
+            cold_h = torch.empty(lb, dtype=torch.uint8)
+            lsa_pack_blocks(self.dtype, self.head_dim, k_tok, v_tok, 0, n, cold_h, int(self.n_blocks[r]))
             with torch.cuda.stream(self.stream):
-                self.cold[r] = cold_h.to(self.device)
+                self.cold[r][layer * lb:(layer + 1) * lb].copy_(cold_h)  # from pageable memory: synchronous
         else:
-            self.cold[r] = cold_h
-        self._gargs[r] = None
+            lsa_pack_blocks(self.dtype, self.head_dim, k_tok, v_tok, 0, n, self.cold[r][layer * lb:(layer + 1) * lb],
+                            int(self.n_blocks[r]))
         n_chunks = self.win_cap // BLOCK_TOKENS
         ring_h = np.zeros(n_chunks * self.block_bytes, dtype=np.uint8)
         w = min(self.win_cap, n)
         lsa_pack_blocks(self.dtype, self.head_dim, k_tok[n - w:], v_tok[n - w:], n - w, w, ring_h, n_chunks)
-        lo = r * n_chunks * self.block_bytes
+        lo = layer * self.ring_layer_bytes + r * n_chunks * self.block_bytes
         with torch.cuda.stream(self.stream):
             self.ring[lo:lo + len(ring_h)].copy_(torch.from_numpy(ring_h).to(self.device))
+
+    def layer_views(self, layer: int):
+        """(hot pool, window ring) of one layer."""
+        h, g = self.hot_layer_bytes, self.ring_layer_bytes
+        return self.hot[layer * h:(layer + 1) * h], self.ring[layer * g:(layer + 1) * g]
 
     # ---------------------------------------------------------------------------------------
     def refresh(self, reqs: Sequence[int], hidden: np.ndarray, bias: np.ndarray, ev_begin=None,
@@ -233,7 +252,9 @@ class LSASession:
             a.slot_of_block = self.slot_of_block[r].ctypes.data
             a.free_slots = self.free_slots[r].ctypes.data
             a.n_free = self.n_free[r].ctypes.data
-            a.capacity, a.reserved1 = int(self.capacity[r]), 0
+            a.capacity, a.n_layers = int(self.capacity[r]), self.n_layers
+            a.cold_layer_bytes = int(self.n_blocks[r]) * self.block_bytes
+            a.hot_layer_bytes = self.hot_layer_bytes
             a.stage = self.stage[r].data_ptr()
             a.table_dev = self.table.data_ptr() + 4 * 2 * int(self.slot_base[r])
             counts = np.zeros(2, dtype=np.int32)
@@ -287,13 +308,14 @@ class LSASession:
 
     def decode(self, q: torch.Tensor, seq_len: Sequence[int], window: Sequence[int], out: torch.Tensor,
                k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
-               max_groups: Optional[int] = None, ev_attn_begin=None, ev_attn_end=None) -> None:
-        """One decode step for all requests of the session."""
+               max_groups: Optional[int] = None, ev_attn_begin=None, ev_attn_end=None, layer: int = 0) -> None:
+        """One decode step of one layer for all requests of the session."""
+        pool, ring = self.layer_views(layer)
         lsa_sparse_decode(dtype=self.dtype, n_heads=self.n_heads, head_dim=self.head_dim, win_cap=self.win_cap,
-                          q=q, ring=self.ring, out=out, workspace=self.decode_ws,
+                          q=q, ring=ring, out=out, workspace=self.decode_ws,
                           tbl_off=self.slot_base[:-1], n_sel=self.attended_entries(seq_len, window),
                           seq_len=seq_len, window=window,
-                          pool=self.hot, n_slots_total=self.n_slots, table=self.table, k_new=k_new, v_new=v_new,
+                          pool=pool, n_slots_total=self.n_slots, table=self.table, k_new=k_new, v_new=v_new,
                           max_groups=self.max_groups if max_groups is None else max_groups,
                           ev_attn_begin=ev_attn_begin, ev_attn_end=ev_attn_end, stream=self.stream)
         if self.track_decode:
@@ -311,7 +333,8 @@ class DecodeLoop:
     lsa_sparse_decode.  Events (torch.cuda.Event) may be passed per call to time the attention kernel.
     """
 
-    def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor):
+    def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor,
+                 layer: int = 0):
         self.sess = sess
         self.prefill = np.asarray(prefill, dtype=np.int64)
         self.window = np.ascontiguousarray(window, dtype=np.int32)
@@ -323,7 +346,8 @@ class DecodeLoop:
         a.dtype = 1 if sess.dtype == "bf16" else 0
         a.win_cap = sess.win_cap
         a.scale = float(1.0 / np.sqrt(sess.head_dim))
-        a.ring, a.pool, a.table = sess.ring.data_ptr(), sess.hot.data_ptr(), sess.table.data_ptr()
+        pool, ring = sess.layer_views(layer)
+        a.ring, a.pool, a.table = ring.data_ptr(), pool.data_ptr(), sess.table.data_ptr()
         a.n_slots_total, a.reserved0 = sess.n_slots, 0
         a.tbl_off, a.n_sel = self.tbl_off.ctypes.data, self.n_sel.ctypes.data
         a.seq_len, a.window = self.seq_len.ctypes.data, self.window.ctypes.data

@@ -226,12 +226,17 @@ def decode_step(q_t: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, seq_l
 # ------------------------------------------------------------------------------------------
 # driver over a whole workload (small sizes)
 # ------------------------------------------------------------------------------------------
-def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Sequence[int]] = None):
+def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Sequence[int]] = None,
+             layer: int = 0):
     """Run the decode loop of a workload: the refreshes and the decode steps.
 
     `wl` supplies the raw inputs (see workloads.Workload).  Returns
     (refreshes, outputs): refreshes[r] is the list of RefreshResult in refresh order,
     outputs[(r, t)] is o [H][D] for every requested step t (default: all steps).
+
+    `layer` picks the attention layer whose K/V, decode queries and new tokens are used.  The
+    selection is the same for every layer: the indexers' loads serve the whole model
+    ([1kpapers Summary]; [Explained] section 4, indexers at three layers, one OR-union).
     """
     cfg = wl.cfg
     dt = cfg.dtype
@@ -249,17 +254,18 @@ def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Seque
         refreshes[r] = res
         if not step_list:
             continue
-        kp, vp = wl.kv_prefill(r)
+        kp, vp = wl.kv_prefill(r, layer) if layer else wl.kv_prefill(r)
         kp = decode_values(kp, dt)
         vp = decode_values(vp, dt)
         n = int(wl.ctx[r])
-        k_new = decode_values(wl.k_new[:, r], dt)
-        v_new = decode_values(wl.v_new[:, r], dt)
+        k_new = decode_values(wl.k_new_of(layer)[:, r] if layer else wl.k_new[:, r], dt)
+        v_new = decode_values(wl.v_new_of(layer)[:, r] if layer else wl.v_new[:, r], dt)
+        q_all = wl.q_dec_of(layer) if layer else wl.q_dec
         for t in step_list:
             L = n + t + 1
             k_idx = governing_refresh(t, wl.refresh_steps[r])
             pos = token_set(L, cfg.window, res[k_idx].ids, cfg.block)
             kk = kv_rows(kp, k_new, n, pos)
             vv = kv_rows(vp, v_new, n, pos)
-            outputs[(r, t)] = attention(decode_values(wl.q_dec[t, r], dt), kk, vv, scale)
+            outputs[(r, t)] = attention(decode_values(q_all[t, r], dt), kk, vv, scale)
     return refreshes, outputs

@@ -325,6 +325,29 @@ def pin_block_permutation(O):
     assert sorted(perm[ids_p].tolist()) == ids.tolist()
 
 
+
+def pin_simulate_layer_uses_its_own_inputs(O):
+    """simulate(layer=l) attends with layer l's queries, new tokens and prefill K/V and with the
+    selection every layer shares: moving layer 1's arrays into layer 0's places gives the same
+    outputs at layer 0, and they differ from layer 0's own."""
+    import copy
+
+    from workloads import build_workload, get_config
+
+    wl = build_workload(get_config("tiny").scaled(n_layers=2), seed=2)
+    steps = [0, 5, 63]
+    refs1, out1 = O.simulate(wl, steps=steps, layer=1)
+    refs0, out0 = O.simulate(wl, steps=steps, layer=0)
+    moved = copy.copy(wl)
+    moved.q_dec, moved.k_new, moved.v_new = wl.q_dec_of(1), wl.k_new_of(1), wl.v_new_of(1)
+    moved._kv = {(0, 0): wl.kv_prefill(0, 1)}
+    refsm, outm = O.simulate(moved, steps=steps, layer=0)
+    for t in steps:
+        assert np.array_equal(outm[(0, t)], out1[(0, t)])
+        assert not np.allclose(out0[(0, t)], out1[(0, t)])
+    assert all(np.array_equal(a.ids, b.ids) for a, b in zip(refs0[0], refs1[0]))
+
+
 PINS = [
     pin_bf16_decode,
     pin_query_encoder_columns,
@@ -343,4 +366,5 @@ PINS = [
     pin_needles,
     pin_bias_monotone,
     pin_block_permutation,
+    pin_simulate_layer_uses_its_own_inputs,
 ]

@@ -100,7 +100,7 @@ def _gather_args(n_blocks=100, capacity=8, new_ids=(1, 5, 9), slot_of_block=None
     a.new_ids, a.n_new = ids.ctypes.data, len(ids)
     a.stage_ints = stage_ints
     a.slot_of_block, a.free_slots, a.n_free = sob.ctypes.data, free.ctypes.data, nf.ctypes.data
-    a.capacity, a.reserved1 = capacity, 0
+    a.capacity, a.n_layers = capacity, 0
     a.stage, a.table_dev = FAKE, FAKE
     a.n_copied, a.n_kept = outs.ctypes.data, outs[1:].ctypes.data
     return a, (sob, free, nf, ids, outs)

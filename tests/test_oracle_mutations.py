@@ -129,6 +129,10 @@ def _m_decode_bf16_shift(raw, dtype):
     return _orig["decode_values"](raw, dtype)
 
 
+def _m_simulate_ignores_layer(wl, steps=None, requests=None, layer=0):
+    return _orig["simulate"](wl, steps, requests, 0)
+
+
 MUTATIONS = [
     ("threshold", _m_threshold_ge),
     ("threshold", _m_threshold_prob),
@@ -151,6 +155,7 @@ MUTATIONS = [
     ("governing_refresh", _m_governing_next),
     ("governing_refresh", _m_governing_strict),
     ("decode_values", _m_decode_bf16_shift),
+    ("simulate", _m_simulate_ignores_layer),
 ]
 
 

@@ -10,3 +10,4 @@ from oracle_pins import PINS
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_pin(pin):
     pin(oracle.lsa_ref)
+

@@ -102,3 +102,35 @@ def test_planted_blocks_recalled_small():
             # every indexer keeps every planted block
             assert res.s[:, wl.planted[r]].all()
         assert (wl.planted[r] < (wl.ctx[r] - wl.cfg.window) // 64).all()
+
+
+def test_layers_have_their_own_streams_and_layer0_is_unchanged():
+    from workloads import build_workload, get_config
+
+    base = build_workload("tiny", seed=3)
+    cfg = get_config("tiny").scaled(n_layers=3)
+    wl = build_workload(cfg, seed=3)
+    assert np.array_equal(wl.q_dec, base.q_dec) and np.array_equal(wl.k_new, base.k_new)
+    assert np.array_equal(wl.kv_prefill(0)[0], base.kv_prefill(0)[0])
+    assert len(wl.layer_dec) == 2
+    for layer in (1, 2):
+        assert wl.q_dec_of(layer).shape == wl.q_dec.shape
+        assert not np.array_equal(wl.q_dec_of(layer), wl.q_dec)
+        assert not np.array_equal(wl.kv_prefill(0, layer)[1], wl.kv_prefill(0)[1])
+    assert not np.array_equal(wl.kv_prefill(0, 1)[0], wl.kv_prefill(0, 2)[0])
+
+
+def test_correlated_hidden_states():
+    """h_k = rho h_(k-1) + sqrt(1 - rho^2) eps_k: unit variance, lag-1 correlation rho; rho = 0 is
+    the independent draw."""
+    from workloads import build_workload, get_config
+    from workloads.gen import Workload  # noqa: F401
+
+    cfg = get_config("ctx128k").scaled(steps=64 * 40, hidden_rho=0.8)
+    wl = build_workload(cfg, seed=5)
+    h = (wl.hidden[0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert abs(h.var() - 1.0) < 0.02
+    c = np.mean([np.corrcoef(h[k], h[k + 1])[0, 1] for k in range(len(h) - 1)])
+    assert abs(c - 0.8) < 0.02, c
+    wl0 = build_workload(get_config("ctx128k").scaled(steps=64 * 40), seed=5)
+    assert np.array_equal((wl0.hidden[0][0].astype(np.uint32) << 16).view(np.float32), h[0].astype(np.float32))

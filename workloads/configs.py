@@ -38,6 +38,11 @@ class LSAConfig:
     planted_frac: float = 0.0
     # staggered refresh phases (at most one request refreshes per step)
     staggered: bool = False
+    # attention layers whose block loads one selection drives (each with its own K/V, decode
+    # queries and new tokens; the selection and the hidden states are shared)
+    n_layers: int = 1
+    # correlation of successive refresh hidden states: h_k = rho h_{k-1} + sqrt(1 - rho^2) eps_k
+    hidden_rho: float = 0.0
     # std of the drawn tensors
     wq_std: float = field(default=0.0)  # 0 => 1/sqrt(d_model)
     key_std: float = field(default=0.0)  # 0 => 1/sqrt(d_idx)

@@ -35,7 +35,7 @@ from .configs import LSAConfig, get_config
 
 # tensor ids used in stream keys
 _T_CTX, _T_DENS, _T_PHASE, _T_WQ, _T_KEYS, _T_HID, _T_QDEC, _T_KPRE, _T_VPRE, \
-    _T_KNEW, _T_VNEW, _T_PLANT_IDS, _T_PLANT, _T_REDRAW = range(1, 15)
+    _T_KNEW, _T_VNEW, _T_PLANT_IDS, _T_PLANT, _T_REDRAW, _T_LAYER = range(1, 16)
 
 _KV_CHUNK = 1 << 16  # tokens per independent prefill K/V stream
 
@@ -97,10 +97,11 @@ class Workload:
     refresh_steps: List[List[int]]  # per request, ascending; a negative entry is the prologue refresh
     hidden: List[np.ndarray]        # per request [n_refresh_r][d_model]
     planted: List[np.ndarray]       # per request ascending planted block ids (may be empty)
-    q_dec: np.ndarray               # [T][R][H][D]
-    k_new: np.ndarray               # [T][R][D]
-    v_new: np.ndarray               # [T][R][D]
-    _kv: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
+    q_dec: np.ndarray               # [T][R][H][D]   (layer 0)
+    k_new: np.ndarray               # [T][R][D]      (layer 0)
+    v_new: np.ndarray               # [T][R][D]      (layer 0)
+    layer_dec: List[Tuple[np.ndarray, np.ndarray, np.ndarray]] = field(default_factory=list)  # layers 1..
+    _kv: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
     report: Optional[ConditionReport] = None
 
     # ---- shapes -------------------------------------------------------------------------
@@ -116,10 +117,23 @@ class Workload:
         return np.concatenate([[0], np.cumsum(self.n_blocks)]).astype(np.int64)
 
     # ---- prefill K/V ----------------------------------------------------------------------
-    def kv_prefill(self, r: int) -> Tuple[np.ndarray, np.ndarray]:
-        """Prefill K and V of request r, token-major [N_r][D] (generated on first use)."""
-        if r in self._kv:
-            return self._kv[r]
+    @property
+    def n_layers(self) -> int:
+        return self.cfg.n_layers
+
+    def q_dec_of(self, layer: int) -> np.ndarray:
+        return self.q_dec if layer == 0 else self.layer_dec[layer - 1][0]
+
+    def k_new_of(self, layer: int) -> np.ndarray:
+        return self.k_new if layer == 0 else self.layer_dec[layer - 1][1]
+
+    def v_new_of(self, layer: int) -> np.ndarray:
+        return self.v_new if layer == 0 else self.layer_dec[layer - 1][2]
+
+    def kv_prefill(self, r: int, layer: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Prefill K and V of request r in one layer, token-major [N_r][D] (generated on first use)."""
+        if (r, layer) in self._kv:
+            return self._kv[(r, layer)]
         cfg = self.cfg
         n, d = int(self.ctx[r]), cfg.head_dim
         st = _storage_dtype(cfg.dtype)
@@ -130,7 +144,8 @@ class Workload:
         def fill(ci: int) -> None:
             c0, c1 = chunks[ci]
             for arr, tid in ((k, _T_KPRE), (v, _T_VPRE)):
-                rng = rng_for(self.seed, cfg.tag, tid, r, ci)
+                rng = (rng_for(self.seed, cfg.tag, tid, r, ci) if layer == 0 else
+                       rng_for(self.seed, cfg.tag, _T_LAYER, layer, tid, r, ci))
                 arr[c0:c1] = _normal(rng, (c1 - c0, d), 1.0, cfg.dtype)
 
         if len(chunks) == 1:
@@ -138,14 +153,15 @@ class Workload:
         else:
             with ThreadPoolExecutor(_threads()) as ex:
                 list(ex.map(fill, range(len(chunks))))
-        self._kv[r] = (k, v)
+        self._kv[(r, layer)] = (k, v)
         return k, v
 
     def drop_kv(self, r: Optional[int] = None) -> None:
         if r is None:
             self._kv.clear()
         else:
-            self._kv.pop(r, None)
+            for key in [key for key in self._kv if key[0] == r]:
+                self._kv.pop(key)
 
     # ---- schedule -------------------------------------------------------------------------
     def refreshes_at(self, t: int) -> List[int]:
@@ -301,10 +317,23 @@ def build_workload(cfg: LSAConfig | str, seed: int = 0, steps: Optional[int] = N
         _normal(rng_for(seed, cfg.tag, _T_KEYS, r), (cfg.n_idx, int(n_blocks[r]), cfg.d_idx), cfg.k_std, cfg.dtype)
         for r in range(R)
     ]
-    hidden = [
-        _normal(rng_for(seed, cfg.tag, _T_HID, r), (len(refresh_steps[r]), cfg.d_model), 1.0, cfg.dtype)
-        for r in range(R)
-    ]
+    if cfg.hidden_rho == 0.0:
+        hidden = [
+            _normal(rng_for(seed, cfg.tag, _T_HID, r), (len(refresh_steps[r]), cfg.d_model), 1.0, cfg.dtype)
+            for r in range(R)
+        ]
+    else:
+        # an AR(1) sequence of unit-variance states: consecutive refreshes see related contexts
+        rho = float(cfg.hidden_rho)
+        hidden = []
+        for r in range(R):
+            eps = _normal(rng_for(seed, cfg.tag, _T_HID, r), (len(refresh_steps[r]), cfg.d_model), 1.0, "f32")
+            h = np.empty(eps.shape, dtype=np.float64)
+            h[0] = eps[0]
+            for k in range(1, len(h)):
+                h[k] = rho * h[k - 1] + np.sqrt(1.0 - rho * rho) * eps[k]
+            h32 = h.astype(np.float32)
+            hidden.append(bf16_bits_from_f32(h32) if cfg.dtype == "bf16" else h32)
 
     planted: List[np.ndarray] = []
     for r in range(R):
@@ -320,8 +349,15 @@ def build_workload(cfg: LSAConfig | str, seed: int = 0, steps: Optional[int] = N
     k_new = _normal(rng_for(seed, cfg.tag, _T_KNEW), (T, R, cfg.head_dim), 1.0, cfg.dtype)
     v_new = _normal(rng_for(seed, cfg.tag, _T_VNEW), (T, R, cfg.head_dim), 1.0, cfg.dtype)
 
+    layer_dec = []
+    for layer in range(1, cfg.n_layers):
+        layer_dec.append(tuple(
+            _normal(rng_for(seed, cfg.tag, _T_LAYER, layer, tid), shape, 1.0, cfg.dtype)
+            for tid, shape in ((_T_QDEC, (T, R, cfg.n_heads, cfg.head_dim)), (_T_KNEW, (T, R, cfg.head_dim)),
+                               (_T_VNEW, (T, R, cfg.head_dim)))))
+
     return Workload(
         cfg=cfg, seed=seed, ctx=ctx, density=dens, phase=phase, bias=bias, w_q=w_q, keys=keys,
         refresh_steps=refresh_steps, hidden=hidden, planted=planted, q_dec=q_dec, k_new=k_new,
-        v_new=v_new,
+        v_new=v_new, layer_dec=layer_dec,
     )
