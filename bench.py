@@ -93,9 +93,11 @@ def _planting_query(dtype):
 
 
 def kernel_hash() -> str:
+    """Hash of the sources the attention kernel is built from (its counters stay valid while this
+    is unchanged)."""
     h = hashlib.sha256()
-    for f in sorted((ROOT / "lookahead_block_sparse_amd" / "csrc").glob("*")):
-        h.update(f.read_bytes())
+    for name in ("decode.hip", "lsa_internal.hpp"):
+        h.update((ROOT / "lookahead_block_sparse_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 
 
