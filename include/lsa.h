@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 3
+#define LSA_ABI_VERSION 4
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -72,21 +72,31 @@ size_t lsa_struct_size(int32_t which);
 /* --------------------------------------------------------------------------------------
  * KV block format.
  *
- * A block holds the keys and values of 64 consecutive tokens of the single KV
- * head, laid out for the decode kernel's matrix-core operands:
- *     K  [64][D]  row-major (token t's key is D contiguous elements)
- *     Vt [D][64]  the values transposed (element d of every token is contiguous)
- * so a block is 2*64*D elements = lsa_block_bytes(dtype, D) bytes (32 KiB for
- * bf16, D = 128).  The cold pool, the hot pool and each request's window ring
- * are arrays of such blocks.  The window ring of capacity C tokens (a multiple
- * of 64) holds token p in ring block (p % C) / 64, row p % 64.
+ * A block holds the keys and values of 64 consecutive tokens (rows t = 0..63) of
+ * the single KV head: 2*64*D elements = lsa_block_bytes(dtype, D) bytes (32 KiB for
+ * bf16, D = 128), keys first, then values.  The cold pool, the hot pool and each
+ * request's window ring are arrays of such blocks.  The window ring of capacity C
+ * tokens (a multiple of 64) holds token p in ring block (p % C) / 64, row p % 64.
+ *
+ * bf16: matrix-core fragment order.  Both halves are runs of 16-byte pieces (8
+ * elements); every 64 consecutive pieces (1 KiB) are the operand one 64-lane wave
+ * loads with one instruction, piece u + 16 g going to lane u + 16 g.  With KS = D/32:
+ *     key (t, d)    element ((((j*KS + ks)*4 + g)*16 + u)*8 + e)
+ *                   j = 2*(t/32) + (t/4)%2,  u = 4*((t/8)%4) + t%4,
+ *                   ks = d/32,  g = (d/8)%4,  e = d%8
+ *     value (t, d)  element 64*D + ((((c*2 + kk)*4 + g)*16 + u)*8 + e)
+ *                   c = d/16,  u = d%16,  kk = t/32,  g = (t/8)%4,  e = t%8
+ * (a value piece holds 8 consecutive tokens of one dimension, a key piece 8
+ * consecutive dimensions of one token).
+ * f32: keys row-major K[64][D] (token t's key is D contiguous elements), then
+ * values transposed Vt[D][64] (dimension d of every token contiguous).
  * ------------------------------------------------------------------------------------ */
 
 /* Bytes of one block; 0 if dtype or head_dim is not supported (D in {64, 128}). */
 size_t lsa_block_bytes(int32_t dtype, int32_t head_dim);
 
-/* Host-side packing of token-major K and V into blocks (used to build the cold
- * pool and the initial window ring).
+/* Host-side packing of token-major K and V into the block format above (used to
+ * build the cold pool and the initial window ring).
  *   k_tok, v_tok  host [n_tokens][head_dim]: tokens pos0 .. pos0+n_tokens-1
  *   dst           host or pinned, n_dst_blocks blocks; token p goes to block
  *                 (p / 64) % n_dst_blocks, row p % 64

@@ -5,17 +5,20 @@
 // Work unit: a tile = one 64-token block (a hot-pool slot or a window-ring block).  Request r has
 // n_sel[r] block tiles (its table, ascending block id) followed by the ring tiles that hold window
 // tokens.  The tiles of all requests are concatenated and cut into G equal contiguous ranges, one per
-// work-group (split-K, balanced whatever the request mix).  Inside a group the 4 waves take the tiles
-// of each request segment round-robin and keep their own online-softmax state; at the end of a
-// segment the waves are combined in LDS and the group writes one partial (m, l, o) per segment.  The
-// merge kernel combines a request's partials by log-sum-exp.
+// work-group (split-K, balanced whatever the request mix), one group of 8 waves per compute unit.
+// Inside a group the waves take the tiles of each request segment on demand from a counter in LDS and
+// keep their own online-softmax state; at the end of a segment the waves are combined in LDS and the
+// group writes one partial (m, l, o) per segment.  The merge kernel combines a request's partials by
+// log-sum-exp.  (The wave scheduler favours the oldest waves, so waves of one unit progress at very
+// different rates; taking tiles on demand lets the fast ones take more.)
 //
 // Matrix cores (bf16): per tile and wave, S^T = K Q^T is 16 v_mfma_f32_16x16x32_bf16 (rows = tokens,
 // columns = the 16 query heads) and O^T += V^T P^T another 16.  The token order inside each S^T
 // sub-tile is chosen so that the S^T accumulator a lane holds is exactly the P operand it feeds to the
-// V^T P^T product (no cross-lane movement of P), and V is stored transposed in the block so each lane's
-// operand is one contiguous 16-byte load.  fp32 inputs use v_mfma_f32_16x16x4_f32 with the same
-// accumulator layout.
+// V^T P^T product (no cross-lane movement of P).  bf16 blocks are stored in that fragment order, so
+// each operand is one 16-byte load per lane and the 64 lanes of a load read 1 KiB of whole cache lines
+// (half-line reads, as a row-major block gives, cost about a tenth of the read bandwidth).  fp32
+// inputs use v_mfma_f32_16x16x4_f32 with the same accumulator layout on row-major K and V^T.
 #include <hip/hip_ext.h>
 
 #include <cmath>
@@ -26,7 +29,9 @@ namespace lsa {
 namespace {
 
 constexpr int kMaxReq = LSA_MAX_DECODE_REQ;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;  // one work-group per CU: its waves share the segment's tiles
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStage = 1024;  // table entries staged in LDS at a time
 constexpr int kHeads = 16;  // query heads per MFMA column block (n_heads <= 16 padded with zeros)
 
 struct DecodeParams {
@@ -91,19 +96,20 @@ struct Bf16Ops {
                 q.b[ks] = bf16x8{};
         }
     }
+    // The block is stored in fragment order: operand (j, ks) of K and (dt, kk) of V^T are each 1 KiB
+    // of 16-byte pieces in lane order, so every load instruction reads whole cache lines.  The loads
+    // are non-temporal: the tile is used once per launch.
     __device__ static void load(Frag& f, const char* base, int lane) {
-        const int lr = lane & 15, lg = lane >> 4;
+        const bf16x8* kp = reinterpret_cast<const bf16x8*>(base) + lane;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                f.k[j][ks] = *reinterpret_cast<const bf16x8*>(base + ((size_t)tokK(j, lr) * D + 32 * ks + 8 * lg) * EB);
-        const char* vt = base + 64 * D * EB;
+            for (int ks = 0; ks < KS; ++ks) f.k[j][ks] = __builtin_nontemporal_load(kp + (j * KS + ks) * 64);
+        const bf16x8* vp = reinterpret_cast<const bf16x8*>(base + 64 * D * EB) + lane;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                f.v[dt][kk] = *reinterpret_cast<const bf16x8*>(vt + ((size_t)(16 * dt + lr) * 64 + 32 * kk + 8 * lg) * EB);
+            for (int kk = 0; kk < 2; ++kk) f.v[dt][kk] = __builtin_nontemporal_load(vp + (dt * 2 + kk) * 64);
     }
     // Issue point of a tile: every load of the tile (K then V) stays before this point and only the
     // K operands must have arrived, so the V loads are still in flight during Q K^T.
@@ -162,11 +168,20 @@ struct Bf16Ops {
             for (int kk = 0; kk < 2; ++kk) o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v[dt][kk], pb[kk], o[dt], 0, 0, 0);
     }
     // Store the current token into ring row `cur` (K row and V^T column).
-    __device__ static void write_current(char* base, int cur, const uint16_t* kn, const uint16_t* vn, int lane) {
-        if (lane < D / 8)
-            *reinterpret_cast<uint4*>(base + ((size_t)cur * D + 8 * lane) * EB) = *reinterpret_cast<const uint4*>(kn + 8 * lane);
-        char* vt = base + 64 * D * EB;
-        for (int d = lane; d < D; d += 64) *reinterpret_cast<uint16_t*>(vt + ((size_t)d * 64 + cur) * EB) = vn[d];
+    // Row t of the block (fragment order): the key's 8-element piece d/8 sits in operand
+    // (j, ks = d/32) at lane u + 16 (d/8 % 4); the value of dimension d is element t % 8 of the piece
+    // of operand (d/16, t/32) at lane d % 16 + 16 (t/8 % 4).
+    __device__ static void write_current(char* base, int t, const uint16_t* kn, const uint16_t* vn, int lane) {
+        uint16_t* b = reinterpret_cast<uint16_t*>(base);
+        const int j = 2 * (t >> 5) + ((t >> 2) & 1), u = 4 * ((t >> 3) & 3) + (t & 3);
+        if (lane < D / 8) {
+            const int ks = lane >> 2, g = lane & 3;
+            *reinterpret_cast<uint4*>(b + (((j * KS + ks) * 4 + g) * 16 + u) * 8) =
+                *reinterpret_cast<const uint4*>(kn + 8 * lane);
+        }
+        const int kk = t >> 5, g = (t >> 3) & 3, e = t & 7;
+        for (int d = lane; d < D; d += 64)
+            b[64 * D + ((((d >> 4) * 2 + kk) * 4 + g) * 16 + (d & 15)) * 8 + e] = vn[d];
     }
 };
 
@@ -259,14 +274,16 @@ struct TileDesc {
 };
 
 // ------------------------------------------------------------------------------------------
-constexpr int kGroupsPerCU = 2;
+constexpr int kGroupsPerCU = 1;
 
 template <typename Ops, typename T, int D>
-__global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
     constexpr int DT = D / 16;
     __shared__ float s_o[kWaves][kHeads][D];
     __shared__ float s_m[kWaves][kHeads];
     __shared__ float s_l[kWaves][kHeads];
+    __shared__ int2 s_ent[kStage];
+    __shared__ int s_next;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -304,25 +321,24 @@ __global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        const int first = lo + wave;
-        const int count = first < hi ? (hi - first + kWaves - 1) / kWaves : 0;
         const char* cur_base = nullptr;
-
-        for (int k0 = 0; k0 < count; k0 += 64) {
-            const int kn_ = min(64, count - k0);
-            // table entries of this wave's block tiles k0 .. k0+63 (one per lane)
-            int2 ent = make_int2(0, -1);
-            {
-                const int j = first + kWaves * (k0 + lane);
-                if (lane < kn_ && j < n_sel) ent = tbl[j];
+        // The segment's tiles go to the waves on demand: each wave takes the next tile from an LDS
+        // counter when it finishes one, so waves the scheduler favours take more and all of them end
+        // together.  The table entries of the segment's block tiles are staged in LDS, kStage at a time.
+        for (int c0 = lo; c0 < hi; c0 += kStage) {
+            const int c1 = min(hi, c0 + kStage);
+            for (int e = threadIdx.x; e < c1 - c0; e += kThreads) {
+                const int j = c0 + e;
+                s_ent[e] = j < n_sel ? tbl[j] : make_int2(0, -1);
             }
-            auto desc = [&](int k) -> TileDesc {
+            if (threadIdx.x == 0) s_next = c0;
+            __syncthreads();
+            auto desc = [&](int j) -> TileDesc {
                 TileDesc d;
                 d.cur = false;
-                const int j = first + kWaves * (k0 + k);
                 if (j < n_sel) {
-                    const int blk = __builtin_amdgcn_readlane(ent.x, k);
-                    const int slot = __builtin_amdgcn_readlane(ent.y, k);
+                    const int2 ent = s_ent[j - c0];
+                    const int blk = ent.x, slot = ent.y;
                     const int nv = min(64, max(0, ws - 64 * blk));
                     const bool ok = slot >= 0 && slot < p.n_slots && nv > 0;
                     d.mask = !ok ? 0ull : (nv >= 64 ? ~0ull : ((1ull << nv) - 1ull));
@@ -375,18 +391,23 @@ __global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p)
                 for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
                 Ops::pv(f, sv, o);
             };
-            // One tile in registers per wave; latency is hidden by the second wave on each SIMD
-            // (two groups per CU), which streams its tile while this one computes.  Every tile has a
-            // valid base and nothing but the tile's own loads sits between them and the matrix
-            // products, so the products wait only for the operands they read.
-            for (int k = 0; k < kn_; ++k) {
-                const TileDesc d = desc(k);
+            // One tile in registers per wave; latency is hidden by the other waves of the SIMD, which
+            // stream their tiles while this one computes.  Every tile has a valid base and nothing but
+            // the tile's own loads sits between them and the matrix products, so the products wait
+            // only for the operands they read.
+            for (;;) {
+                int j = 0;
+                if (lane == 0) j = atomicAdd(&s_next, 1);
+                j = __builtin_amdgcn_readfirstlane(j);
+                if (j >= c1) break;
+                const TileDesc d = desc(j);
                 typename Ops::Frag f;
                 Ops::load(f, d.base, lane);
                 Ops::pin_k(f);
                 if (d.cur) cur_base = d.base;
                 if (d.mask) compute(f, d);
             }
+            __syncthreads();  // every wave is done with s_ent and s_next
         }
 
         // ---- the current token: folded into this wave's state, then appended to the ring ----
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p)
             Ops::write_current(const_cast<char*>(cur_base), cur_row, kn, vn, lane);
         }
 
-        // ---- combine the 4 waves of this segment ----
+        // ---- combine the waves of this segment ----
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
         if (lg == 0) {
@@ -422,7 +443,7 @@ __global__ __launch_bounds__(256, kGroupsPerCU) void attn_kernel(DecodeParams p)
             for (int i = 0; i < 4; ++i) s_o[wave][lr][16 * dt + 4 * lg + i] = o[dt][i];
         __syncthreads();
         const int pidx = w + r;
-        for (int e = threadIdx.x; e < kHeads * D; e += 256) {
+        for (int e = threadIdx.x; e < kHeads * D; e += kThreads) {
             const int h = e / D, d = e % D;
             float M = -INFINITY;
 #pragma unroll
@@ -627,10 +648,10 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
 
     if (a->ev_attn_begin && a->ev_attn_end) {
         // the events take the dispatch's own start and end timestamps: no extra packets on the stream
-        hipExtLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, a->ev_attn_begin,
+        hipExtLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(kThreads), 0, stream, a->ev_attn_begin,
                               a->ev_attn_end, 0, dp);
     } else {
-        hipLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(256), 0, stream, dp);
+        hipLaunchKernelGGL((attn_kernel<Ops, T, D>), dim3(P.G), dim3(kThreads), 0, stream, dp);
     }
     LSA_HIP(hipGetLastError());
     hipLaunchKernelGGL((merge_kernel<D>), dim3(a->n_req * a->n_heads * (D / kMergeCols)), dim3(kMergeThreads), 0, stream, mp);

@@ -68,6 +68,28 @@ size_t lsa_block_bytes(int32_t dtype, int32_t head_dim) {
     return (size_t)2 * LSA_BLOCK_TOKENS * head_dim * elem_bytes(dtype);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Element offsets inside a bf16 block (matrix-core fragment order: every 1 KiB run is one wave's
+// 16-byte-per-lane operand load).
+inline size_t bf16_key_off(int D, int t, int d) {
+    const int KS = D / 32;
+    const int j = 2 * (t >> 5) + ((t >> 2) & 1), u = 4 * ((t >> 3) & 3) + (t & 3);
+    const int ks = d >> 5, g = (d >> 3) & 3, e = d & 7;
+    return ((((size_t)j * KS + ks) * 4 + g) * 16 + u) * 8 + e;
+}
+inline size_t bf16_value_off(int D, int t, int d) {
+    const int c = d >> 4, u = d & 15;
+    const int kk = t >> 5, g = (t >> 3) & 3, e = t & 7;
+    return (size_t)64 * D + ((((size_t)c * 2 + kk) * 4 + g) * 16 + u) * 8 + e;
+}
+
+}  // namespace
+
+extern "C" {
+
 lsa_status lsa_pack_blocks(int32_t dtype, int32_t head_dim, const void* k_tok, const void* v_tok,
                            int64_t pos0, int64_t n_tokens, void* dst, int64_t n_dst_blocks,
                            int32_t n_threads) {
@@ -98,6 +120,17 @@ lsa_status lsa_pack_blocks(int32_t dtype, int32_t head_dim, const void* k_tok, c
             const int64_t p_lo = std::max<int64_t>(pos0, pb * LSA_BLOCK_TOKENS);
             const int64_t p_hi = std::min<int64_t>(pos0 + n_tokens, (pb + 1) * LSA_BLOCK_TOKENS);
             char* blk = out + (size_t)(pb % n_dst_blocks) * bb;
+            if (dtype == LSA_BF16) {
+                uint16_t* b16 = reinterpret_cast<uint16_t*>(blk);
+                for (int64_t p = p_lo; p < p_hi; ++p) {
+                    const int t = (int)(p % LSA_BLOCK_TOKENS);
+                    const uint16_t* kr = reinterpret_cast<const uint16_t*>(k + (size_t)(p - pos0) * row_bytes);
+                    const uint16_t* vr = reinterpret_cast<const uint16_t*>(v + (size_t)(p - pos0) * row_bytes);
+                    for (int d = 0; d < D; d += 8) std::memcpy(b16 + bf16_key_off(D, t, d), kr + d, 16);
+                    for (int d = 0; d < D; ++d) b16[bf16_value_off(D, t, d)] = vr[d];
+                }
+                continue;
+            }
             char* vt = blk + (size_t)LSA_BLOCK_TOKENS * row_bytes;
             for (int64_t p = p_lo; p < p_hi; ++p) {
                 const int row = (int)(p % LSA_BLOCK_TOKENS);

@@ -191,16 +191,45 @@ def test_decode_validation_before_any_hip_call(over, status):
 
 
 # ---- block format packing (pure host) ------------------------------------------------------
+def _bf16_offsets(D):
+    """Element offsets of key (t, d) and value (t, d) inside a bf16 block, [64][D] each, written from
+    the format's definition: 16-byte pieces in matrix-core fragment order."""
+    t = np.arange(64)[:, None]
+    d = np.arange(D)[None, :]
+    KS = D // 32
+    j = 2 * (t // 32) + (t // 4) % 2
+    u = 4 * ((t // 8) % 4) + t % 4
+    koff = (((j * KS + d // 32) * 4 + (d // 8) % 4) * 16 + u) * 8 + d % 8
+    voff = 64 * D + ((((d // 16) * 2 + t // 32) * 4 + (t // 8) % 4) * 16 + d % 16) * 8 + t % 8
+    return koff, voff
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_block_format_is_a_fragment_order_permutation(D):
+    """Every element of the block has exactly one (t, d) source, and each 1 KiB run of the key half
+    is one matrix-core operand: 16 tokens (one per lane u) x 32 dimensions, 8 consecutive
+    dimensions per 16-byte piece."""
+    koff, voff = _bf16_offsets(D)
+    allo = np.concatenate([koff.ravel(), voff.ravel()])
+    assert np.array_equal(np.sort(allo), np.arange(2 * 64 * D))
+    run = koff // 512                       # 1 KiB = 512 bf16 elements
+    for r in range(64 * D // 512):
+        t, d = np.nonzero(run == r)
+        assert len(set(t.tolist())) == 16 and len(set(d.tolist())) == 32
+        assert np.all((koff[t, d] % 8) == d % 8)
+
+
 def _ref_pack(k, v, pos0, n_dst):
-    """Block format written out with NumPy: K rows then V transposed, token p -> block (p//64)%n_dst."""
+    """Blocks written out with NumPy as (K [64][D], V [64][D]) per destination block, token p ->
+    block (p//64)%n_dst, row p%64."""
     D = k.shape[1]
     out = {}
     for i in range(k.shape[0]):
         p = pos0 + i
         b = (p // 64) % n_dst
-        K, Vt = out.setdefault(b, (np.zeros((64, D), k.dtype), np.zeros((D, 64), k.dtype)))
+        K, V = out.setdefault(b, (np.zeros((64, D), k.dtype), np.zeros((64, D), k.dtype)))
         K[p % 64] = k[i]
-        Vt[:, p % 64] = v[i]
+        V[p % 64] = v[i]
     return out
 
 
@@ -219,13 +248,19 @@ def test_pack_blocks_matches_numpy(dtype, D, pos0, n, n_dst):
     dst = np.zeros(n_dst * bb, dtype=np.uint8)
     L.lsa_pack_blocks(dtype, D, k, v, pos0, n, dst, n_dst, n_threads=3)
     want = _ref_pack(k, v, pos0, n_dst)
-    blocks = dst.view(st).reshape(n_dst, 2, 64 * D)
-    for b, (K, Vt) in want.items():
-        got_k = blocks[b, 0].reshape(64, D)
-        got_vt = blocks[b, 1].reshape(D, 64)
+    blocks = dst.view(st).reshape(n_dst, 2 * 64 * D)
+    for b, (K, V) in want.items():
+        if dtype == "bf16":
+            koff, voff = _bf16_offsets(D)
+            got_k, got_v = blocks[b][koff], blocks[b][voff]
+        else:
+            got_k = blocks[b, :64 * D].reshape(64, D)
+            got_v = blocks[b, 64 * D:].reshape(D, 64).T   # f32: K row-major, then V transposed
         rows = sorted({(pos0 + i) % 64 for i in range(n) if ((pos0 + i) // 64) % n_dst == b})
         assert np.array_equal(got_k[rows], K[rows])
-        assert np.array_equal(got_vt[:, rows], Vt[:, rows])
+        assert np.array_equal(got_v[rows], V[rows])
+        untouched = sorted(set(range(64)) - set(rows))
+        assert not got_k[untouched].any() and not got_v[untouched].any()
 
 
 def test_pack_blocks_rejects_overflow():

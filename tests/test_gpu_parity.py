@@ -191,8 +191,11 @@ def test_needles(where):
         k_new[p - int(wl.ctx[0]), 0] = enc(row)
     else:
         kp[p] = enc(row)
-    wl._kv[0] = (kp, vp)
+    wl.set_kv_prefill(0, kp, vp)
     wl.k_new = k_new
+    planted = wl.kv_prefill(0)[0][p] if p < int(wl.ctx[0]) else wl.k_new[p - int(wl.ctx[0]), 0]
+    assert np.array_equal(planted, enc(row)), "the needle key was not planted"
+    assert abs(oracle.decode_values(planted, dt)[0] - big) <= 1e-2 * big
     wl.q_dec = wl.q_dec.copy()
     wl.q_dec[t, 0] = enc(q)
     sess = make_session(wl, with_masks=False)

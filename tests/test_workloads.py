@@ -134,3 +134,20 @@ def test_correlated_hidden_states():
     assert abs(c - 0.8) < 0.02, c
     wl0 = build_workload(get_config("ctx128k").scaled(steps=64 * 40), seed=5)
     assert np.array_equal((wl0.hidden[0][0].astype(np.uint32) << 16).view(np.float32), h[0].astype(np.float32))
+
+
+def test_planted_prefill_is_what_oracle_and_session_read():
+    """A test that replaces a prefill (a planted needle) must change what kv_prefill returns for that
+    request and layer, and nothing else; a wrong shape is refused."""
+    from workloads import build_workload, get_config
+
+    wl = build_workload(get_config("tiny").scaled(n_layers=2), seed=4)
+    k, v = wl.kv_prefill(0)
+    k2 = k.copy()
+    k2[5] = 0
+    other = wl.kv_prefill(0, 1)[0].copy()
+    wl.set_kv_prefill(0, k2, v)
+    assert np.array_equal(wl.kv_prefill(0)[0], k2)
+    assert np.array_equal(wl.kv_prefill(0, 1)[0], other)
+    with pytest.raises(ValueError):
+        wl.set_kv_prefill(0, k2[:-1], v)

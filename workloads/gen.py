@@ -156,6 +156,13 @@ class Workload:
         self._kv[(r, layer)] = (k, v)
         return k, v
 
+    def set_kv_prefill(self, r: int, k: np.ndarray, v: np.ndarray, layer: int = 0) -> None:
+        """Replace request r's prefill K and V in one layer (tests plant keys this way)."""
+        n, d = int(self.ctx[r]), self.cfg.head_dim
+        if k.shape != (n, d) or v.shape != (n, d):
+            raise ValueError(f"prefill of request {r} is [{n}][{d}], got {k.shape} and {v.shape}")
+        self._kv[(r, layer)] = (k, v)
+
     def drop_kv(self, r: Optional[int] = None) -> None:
         if r is None:
             self._kv.clear()
