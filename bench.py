@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--select", choices=("threshold", "all"), default="threshold",
                     help="all: every block selected at one refresh before the first step, i.e. dense "
                          "attention over the whole context through the same kernels (comparator)")
+    ap.add_argument("--reactive", action="store_true",
+                    help="reactive comparator: every block resident in HBM, the index scored at every step "
+                         "and the decode reading the selected blocks in place (refresh cadence 1, no "
+                         "gathers, no host round trip)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="time the attention kernel with HIP events on every N-th timed step (the events "
                          "take the dispatch's own stamps but still cost stream time)")
@@ -218,7 +222,7 @@ def main():
 
     import torch
 
-    from lookahead_block_sparse_amd.session import DecodeLoop, LSASession
+    from lookahead_block_sparse_amd.session import DecodeLoop, LSASession, ResidentLoop
     from workloads import build_workload, get_config
 
     def note(msg):
@@ -235,6 +239,10 @@ def main():
         cfg = cfg.scaled(n_layers=args.layers, hidden_rho=args.hidden_rho)
     if args.select == "all":
         cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0)  # one refresh, at step 0
+    if args.reactive:
+        if args.select == "all" or cfg.n_layers > 1 or args.cold != "device":
+            raise SystemExit("--reactive runs one layer with the default selection and the pool in HBM")
+        cfg = cfg.scaled(tau=1, staggered=False)
     t_setup = time.perf_counter()
     wl = build_workload(cfg, seed=args.seed, steps=max(cfg.steps, total_steps))
     cfg = wl.cfg
@@ -257,7 +265,10 @@ def main():
             sess.load_prefill(r, kl, vl, layer=layer)
         if args.no_cpu_baseline:
             wl.drop_kv(r)
-    note(f"session ready in {time.perf_counter() - t_setup:.1f}s (cold pool on {args.cold})")
+    if args.reactive:
+        sess.make_resident()  # every block in the hot pool, block b of request r at slot base + b
+    note(f"session ready in {time.perf_counter() - t_setup:.1f}s (cold pool on {args.cold}"
+         + (", every block resident" if args.reactive else "") + ")")
 
     def dev_raw(a):
         a = np.ascontiguousarray(a)
@@ -294,6 +305,7 @@ def main():
     e = 2 if cfg.dtype == "bf16" else 4
     D, H = cfg.head_dim, cfg.n_heads
     loop = DecodeLoop(sess, wl.ctx, window, out)
+    rloop = ResidentLoop(sess, wl.ctx, window, out) if args.reactive else None
     outs_l = [torch.empty_like(out) for _ in range(1, cfg.n_layers)]
     loops_l = [DecodeLoop(sess, wl.ctx, window, outs_l[l - 1], layer=l) for l in range(1, cfg.n_layers)]
     gather_host_s = []
@@ -301,7 +313,19 @@ def main():
     sel_hist = {}        # (request, selection version) -> ascending ids
     step_log = []        # (t, attended entries per request, selection version per request)
 
+    def reactive_step(t, timed_idx):
+        evs = (None, None)
+        ev = (None, None)
+        if timed_idx is not None and timed_idx in att_ev:
+            ref_ev[t] = evs = (mk_event(), mk_event())
+            ev = att_ev[timed_idx]
+        rloop.step(t, hid_at[t], bias_dev, q_all[t], kn_all[t], vn_all[t], ev_refresh=evs, ev_attn=ev)
+        if timed_idx is not None:
+            step_log.append((t, None, None, timed_idx in att_ev))
+
     def step(t, timed_idx):
+        if rloop is not None:
+            return reactive_step(t, timed_idx)
         reqs = wl.refreshes_at(t)
         if reqs:
             if timed_idx is not None:
@@ -347,22 +371,41 @@ def main():
     note(f"timed region {elapsed * 1e3:.2f} ms")
 
     attn_ms = np.array([a.elapsed_time(b) for a, b in att_ev.values()])
+    sel_at = {}
+    if rloop is not None:
+        # the selections of the event-timed steps, recomputed after the timed region (the refresh
+        # is deterministic), give their attended bytes
+        for t, _, _, timed_ev in step_log:
+            if timed_ev:
+                sel_at[t] = sess.refresh(list(range(wl.n_req)), hid_at[t], bias_dev)
+        # the table entries the decode reads: every selected block of the step
+        step_log = [(t, None, None, te) for t, _, _, te in step_log]
     # algorithmic bytes of every timed attention launch: window tokens + tokens of the attended
     # selected blocks (below the window start), K and V, plus q and the table entries
     attn_bytes, attn_tokens, with_ev = [], [], []
     for t, n_att, ver, timed_ev in step_log:
+        if rloop is not None and not timed_ev:
+            continue
         with_ev.append(timed_ev)
         toks = 0
+        n_entries = 0
         for r in range(wl.n_req):
             L = int(wl.ctx[r]) + t + 1
             ws = max(0, L - cfg.window)
             toks += min(L, cfg.window)
-            n = int(n_att[r])
+            if rloop is not None:
+                ids = sel_at[t][r]
+                n_entries += len(ids)
+                n = int(np.searchsorted(ids, (ws + 63) // 64, side="left"))
+            else:
+                ids = sel_hist[(r, int(ver[r]))] if n_att[r] > 0 else None
+                n = int(n_att[r])
+                n_entries += n
             if n > 0:
-                last = int(sel_hist[(r, int(ver[r]))][n - 1])
+                last = int(ids[n - 1])
                 toks += 64 * (n - 1) + min(64, ws - 64 * last)
         attn_tokens.append(toks)
-        attn_bytes.append(toks * 2 * D * e + wl.n_req * H * D * e + 8 * int(n_att.sum()))
+        attn_bytes.append(toks * 2 * D * e + wl.n_req * H * D * e + 8 * n_entries)
     ref_us = np.array([1e3 * a.elapsed_time(b) for a, b in ref_ev.values()])
     gat_us = np.array([1e3 * a.elapsed_time(b) for a, b in gather_ev.values()])
     attn_bytes = np.array(attn_bytes, dtype=np.float64)
@@ -373,6 +416,10 @@ def main():
     n_blocks_total = int(wl.n_blocks.sum())
     ref_bytes = (cfg.n_idx * cfg.d_model * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
                  + wl.n_req * cfg.d_model * e + 4 * sum(len(x) for x in sess.sel_host) + 4 * wl.n_req)
+    if rloop is not None:  # ids and table pairs of the recomputed selections
+        n_ids = np.mean([sum(len(v) for v in s.values()) for s in sel_at.values()]) if sel_at else 0.0
+        ref_bytes = (cfg.n_idx * cfg.d_model * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
+                     + wl.n_req * cfg.d_model * e + int(12 * n_ids) + 4 * wl.n_req)
 
     khash = kernel_hash()
     res = {
@@ -395,12 +442,15 @@ def main():
                          f"{int(100 * cfg.planted_frac)}% planted + background density {cfg.density}"
                          + (", every block selected (dense comparator)" if args.select == "all" else "")
                          + (f", {cfg.n_layers} attention layers per selection" if cfg.n_layers > 1 else "")
-                         + (f", hidden-state correlation {cfg.hidden_rho}" if cfg.hidden_rho else "")),
+                         + (f", hidden-state correlation {cfg.hidden_rho}" if cfg.hidden_rho else "")
+                         + (", reactive comparator: every block resident, scored every step" if args.reactive
+                            else "")),
             "cold_pool": args.cold,
             "tau": cfg.tau,
             "layers": cfg.n_layers,
             "hidden_rho": cfg.hidden_rho,
             "select": args.select,
+            "reactive": bool(args.reactive),
             "requests": wl.n_req,
             "context_tokens": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else wl.ctx.tolist(),
             "seed": args.seed,

@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 4
+#define LSA_ABI_VERSION 5
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -150,6 +150,15 @@ typedef struct lsa_refresh_args {
     size_t workspace_bytes;
     hipEvent_t ev_begin;       /* optional, used only when both are set: they receive the start and */
     hipEvent_t ev_end;         /* end time of the refresh kernel's dispatch */
+    int32_t* table_out;        /* dev or NULL: the decode block table for a pool that holds every
+                                  block (a fully resident pool).  Request r's pairs start at pair
+                                  blk_off[r] (capacity B_r): pair j = (sel_ids[j],
+                                  table_slot_base[r] + sel_ids[j]), written with the ids, so
+                                  lsa_sparse_decode can read them with n_sel_dev = sel_count and
+                                  tbl_off[r] = blk_off[r], with no host round trip */
+    const int32_t* table_slot_base; /* host [n_req]: slot of block 0 of request r in that pool
+                                  (block b at slot base + b); required with table_out, base + B_r
+                                  <= 2^31 - 1 */
 } lsa_refresh_args;
 
 lsa_status lsa_index_refresh_workspace(const lsa_refresh_args* a, size_t* bytes);
@@ -254,6 +263,12 @@ typedef struct lsa_decode_args {
     int32_t reserved1;         /* must be 0 */
     hipEvent_t ev_attn_begin;  /* optional, used only when both are set: they receive the start and */
     hipEvent_t ev_attn_end;    /* end time of the attention kernel's dispatch (the merge is outside) */
+    const int32_t* n_sel_dev;  /* dev [n_req] or NULL.  When set, request r's entry count is read on
+                                  the device from n_sel_dev[r] (clamped to 0..n_sel[r]; a negative
+                                  count, a failed refresh, attends no block), n_sel[r] is only its
+                                  capacity, and the split of the work over the groups is computed
+                                  by the kernels: the refresh's sel_count feeds the decode with no
+                                  host round trip */
 } lsa_decode_args;
 
 lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes);

@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -77,6 +77,7 @@ class RefreshArgs(Structure):
         ("sel_ids", c_void_p), ("sel_count", c_void_p), ("masks", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("ev_begin", c_void_p), ("ev_end", c_void_p),
+        ("table_out", c_void_p), ("table_slot_base", c_void_p),
     ]
 
 
@@ -101,6 +102,7 @@ class DecodeArgs(Structure):
         ("window", c_void_p), ("out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("max_groups", c_int32), ("reserved1", c_int32),
         ("ev_attn_begin", c_void_p), ("ev_attn_end", c_void_p),
+        ("n_sel_dev", c_void_p),
     ]
 
 
@@ -227,7 +229,7 @@ def lsa_index_refresh_workspace(*, dtype, d_model, d_idx, n_idx, blk_off) -> int
 
 def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_off, bias, sel_ids, sel_count,
                       workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, ev_begin=None,
-                      ev_end=None, stream=None) -> None:
+                      ev_end=None, table_out=None, table_slot_base=None, stream=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a, keep = _refresh_args(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx, hidden=hidden,
                             hidden_req_stride=d_model if hidden_req_stride is None else hidden_req_stride,
@@ -236,6 +238,8 @@ def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_of
                             workspace_bytes=ws_bytes)
     a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
     a.ev_end = ev_end.cuda_event if ev_end is not None else None
+    tsb = _i32(table_slot_base) if table_slot_base is not None else None
+    a.table_out, a.table_slot_base = _ptr(table_out), _ptr(tsb)
     _check(LIB.lsa_index_refresh(ctypes.byref(a), _stream(stream)))
 
 
@@ -262,7 +266,7 @@ def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_id
 
 
 def _decode_args(*, dtype, n_heads, head_dim, win_cap, scale, q, k_new, v_new, ring, pool, n_slots_total, table,
-                 tbl_off, n_sel, seq_len, window, out, workspace, max_groups, ev_begin, ev_end):
+                 tbl_off, n_sel, seq_len, window, out, workspace, max_groups, ev_begin, ev_end, n_sel_dev=None):
     host = [_i32(tbl_off), _i32(n_sel), _i32(seq_len), _i32(window)]
     a = DecodeArgs()
     a.n_req = len(host[2])
@@ -278,6 +282,7 @@ def _decode_args(*, dtype, n_heads, head_dim, win_cap, scale, q, k_new, v_new, r
     a.max_groups, a.reserved1 = int(max_groups), 0
     a.ev_attn_begin = ev_begin.cuda_event if ev_begin is not None else None
     a.ev_attn_end = ev_end.cuda_event if ev_end is not None else None
+    a.n_sel_dev = _ptr(n_sel_dev)
     return a, host
 
 
@@ -293,11 +298,12 @@ def lsa_sparse_decode_workspace(*, dtype, n_heads, head_dim, win_cap, n_req, max
 
 def lsa_sparse_decode(*, dtype, n_heads, head_dim, win_cap, q, ring, out, workspace, tbl_off, n_sel, seq_len,
                       window, pool=None, n_slots_total=0, table=None, k_new=None, v_new=None, scale=None,
-                      max_groups=0, ev_attn_begin=None, ev_attn_end=None, stream=None) -> None:
+                      max_groups=0, ev_attn_begin=None, ev_attn_end=None, n_sel_dev=None, stream=None) -> None:
     a, keep = _decode_args(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap, scale=scale, q=q,
                            k_new=k_new, v_new=v_new, ring=ring, pool=pool, n_slots_total=n_slots_total,
                            table=table, tbl_off=tbl_off, n_sel=n_sel, seq_len=seq_len, window=window, out=out,
-                           workspace=workspace, max_groups=max_groups, ev_begin=ev_attn_begin, ev_end=ev_attn_end)
+                           workspace=workspace, max_groups=max_groups, ev_begin=ev_attn_begin, ev_end=ev_attn_end,
+                           n_sel_dev=n_sel_dev)
     _check(LIB.lsa_sparse_decode(ctypes.byref(a), _stream(stream)))
 
 

@@ -44,24 +44,52 @@ struct DecodeParams {
     const int2* table;
     float* part_o;   // [P][16][D]
     float* part_ml;  // [P][16][2]
-    int n_req, n_heads, n_chunks, win_cap, n_slots, total_tiles, n_groups;
+    const int* n_sel_dev;  // optional: entry counts on the device (n_sel then holds capacities)
+    int n_req, n_heads, n_chunks, win_cap, n_slots, n_groups;
     float scale_log2;
-    int tile_prefix[kMaxReq + 1];
     int seq_len[kMaxReq];
     int ws[kMaxReq];
     int tbl_off[kMaxReq];
     int n_sel[kMaxReq];
+    int n_ring[kMaxReq];  // window tiles of each request
     int ring_first[kMaxReq];
+    int tile_prefix[kMaxReq + 1];  // host-side counts: the split computed on the host
 };
 
 struct MergeParams {
     const float* part_o;
     const float* part_ml;
     float* out;
-    int n_heads;
-    int w_lo[kMaxReq];
+    const int* n_sel_dev;
+    int n_req, n_heads, n_groups;
+    int n_sel[kMaxReq];
+    int n_ring[kMaxReq];
+    int w_lo[kMaxReq];  // host-side counts: the groups of each request, computed on the host
     int w_hi[kMaxReq];
 };
+
+// With device-side counts, the split of the tiles over the groups is computed by every group of both
+// kernels from the same inputs (with host-side counts the host computes it): request r's tiles are [pre[r], pre[r+1]) of T = pre[n_req] (its n_sel[r] block tiles, read
+// from the device when the counts live there, then its window tiles); G = min(launched groups, T)
+// groups, group w taking [w T / G, (w+1) T / G), so every group has at least one tile.
+__device__ void tile_split(const int* n_sel_dev, const int* n_sel, const int* n_ring, int n_req, int* s_ns,
+                           int* s_pre) {
+    if ((int)threadIdx.x < n_req) {
+        int ns = n_sel[threadIdx.x];
+        if (n_sel_dev) ns = min(max(n_sel_dev[threadIdx.x], 0), ns);
+        s_ns[threadIdx.x] = ns;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int pre = 0;
+        for (int r = 0; r < n_req; ++r) {
+            s_pre[r] = pre;
+            pre += s_ns[r] + n_ring[r];
+        }
+        s_pre[n_req] = pre;
+    }
+    __syncthreads();
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -284,26 +312,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
     __shared__ float s_l[kWaves][kHeads];
     __shared__ int2 s_ent[kStage];
     __shared__ int s_next;
+    __shared__ int s_ns[kMaxReq];
+    __shared__ int s_pre[kMaxReq + 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int w = blockIdx.x;
-    const long long T_ = p.total_tiles, G = p.n_groups;
+    const bool dev_counts = p.n_sel_dev != nullptr;
+    if (dev_counts) tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.n_req, s_ns, s_pre);
+    // both sources are uniform: the LDS values are moved to scalar registers
+    auto prefix = [&](int r) { return dev_counts ? __builtin_amdgcn_readfirstlane(s_pre[r]) : p.tile_prefix[r]; };
+    const long long T_ = prefix(p.n_req), G = min((long long)p.n_groups, T_);
+    if (w >= G) return;
     const int a = (int)((long long)w * T_ / G);
     const int b = (int)((long long)(w + 1) * T_ / G);
     const size_t block_bytes = (size_t)2 * 64 * D * Ops::EB;
 
     int r = 0;
-    while (r + 1 < p.n_req && p.tile_prefix[r + 1] <= a) ++r;
+    while (r + 1 < p.n_req && prefix(r + 1) <= a) ++r;
 
-    for (; r < p.n_req && p.tile_prefix[r] < b; ++r) {
-        const int P0 = p.tile_prefix[r];
+    for (; r < p.n_req && prefix(r) < b; ++r) {
+        const int P0 = prefix(r);
         const int lo = max(a, P0) - P0;
-        const int hi = min(b, p.tile_prefix[r + 1]) - P0;
+        const int hi = min(b, prefix(r + 1)) - P0;
         const int L = p.seq_len[r];
         const int ws = p.ws[r];
-        const int n_sel = p.n_sel[r];
+        const int n_sel = dev_counts ? __builtin_amdgcn_readfirstlane(s_ns[r]) : p.n_sel[r];
         const int2* tbl = p.table + p.tbl_off[r];
         char* ring_r = p.ring + (size_t)r * p.ring_req_bytes;
         const T* kn = p.k_new ? static_cast<const T*>(p.k_new) + (size_t)r * D : nullptr;
@@ -478,6 +513,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     __shared__ float s_acc[kMergeSub][kMergeCols];
     __shared__ float s_l[kMergeSub][kMergeCols];
     __shared__ float s_m[kMergeSub][kMergeCols];
+    __shared__ int s_ns[kMaxReq];
+    __shared__ int s_pre[kMaxReq + 1];
     constexpr int NC = D / kMergeCols;
     const int c = blockIdx.x % NC;
     const int rh = blockIdx.x / NC;
@@ -486,7 +523,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     const int col = threadIdx.x % kMergeCols;
     const int d = c * kMergeCols + col;
     const int sub = threadIdx.x / kMergeCols;
-    const int w0 = p.w_lo[r], w1 = p.w_hi[r];
+    // the groups whose tile ranges meet request r's tiles: the group holding tile x is the largest w
+    // with floor(w T / G) <= x, i.e. ceil((x + 1) G / T) - 1
+    int w0 = p.w_lo[r], w1 = p.w_hi[r];
+    if (p.n_sel_dev) {
+        tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.n_req, s_ns, s_pre);
+        const long long T_ = s_pre[p.n_req], G = min((long long)p.n_groups, T_);
+        auto group_of = [&](long long x) { return (int)(((x + 1) * G + T_ - 1) / T_ - 1); };
+        w0 = group_of(s_pre[r]);
+        w1 = group_of(s_pre[r + 1] - 1);
+    }
     float m = -INFINITY, acc = 0.f, lsum = 0.f;
     for (int w = w0 + sub; w <= w1; w += 4 * kMergeSub) {
         float m4[4], o4[4], l4[4];
@@ -579,7 +625,10 @@ lsa_status decode_plan(const lsa_decode_args* a, DecodePlan* P, bool sizing_only
     const int g_all = dev.cu_count * kGroupsPerCU;
     const int g_max = a->max_groups > 0 ? std::min(a->max_groups, g_all) : g_all;
     P->total_tiles = (int)T;
-    P->G = sizing_only ? g_max : (int)std::max<long long>(1, std::min<long long>(g_max, (T + kWaves - 1) / kWaves));
+    // with device-side counts the host knows only the capacities: every group is launched and the
+    // kernels use min(G, T) of them
+    P->G = sizing_only || a->n_sel_dev ? g_max
+                                       : (int)std::max<long long>(1, std::min<long long>(g_max, (T + kWaves - 1) / kWaves));
     const int n_part = g_max + a->n_req;
     size_t off = 0;
     P->part_o_off = off;
@@ -609,32 +658,32 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
     dp.n_chunks = a->win_cap / 64;
     dp.win_cap = a->win_cap;
     dp.n_slots = a->n_slots_total;
-    dp.total_tiles = P.total_tiles;
+    dp.n_sel_dev = a->n_sel_dev;
     dp.n_groups = P.G;
     dp.scale_log2 = a->scale * 1.4426950408889634f;
-    int pre = 0;
+    MergeParams mp{};
     for (int r = 0; r < a->n_req; ++r) {
         const int L = a->seq_len[r], W = a->window[r];
         const int wsr = std::max(0, L - W);
         const int ring = std::min(dp.n_chunks, (L - 1) / 64 - wsr / 64 + 1);
-        dp.tile_prefix[r] = pre;
         dp.seq_len[r] = L;
         dp.ws[r] = wsr;
         dp.tbl_off[r] = a->tbl_off[r];
         dp.n_sel[r] = a->n_sel[r];
+        dp.n_ring[r] = ring;
         dp.ring_first[r] = (wsr / 64) % dp.n_chunks;
-        pre += a->n_sel[r] + ring;
+        mp.n_sel[r] = a->n_sel[r];
+        mp.n_ring[r] = ring;
     }
-    dp.tile_prefix[a->n_req] = pre;
-
-    MergeParams mp{};
-    mp.part_o = dp.part_o;
-    mp.part_ml = dp.part_ml;
-    mp.out = a->out;
-    mp.n_heads = a->n_heads;
-    // groups whose tile range meets request r's tiles
-    {
-        const long long TT = P.total_tiles, G = P.G;
+    if (!a->n_sel_dev) {
+        int pre = 0;
+        for (int r = 0; r < a->n_req; ++r) {
+            dp.tile_prefix[r] = pre;
+            pre += dp.n_sel[r] + dp.n_ring[r];
+        }
+        dp.tile_prefix[a->n_req] = pre;
+        // groups whose tile range meets request r's tiles (P.G <= T here)
+        const long long TT = pre, G = P.G;
         int wcur = 0;
         for (int r = 0; r < a->n_req; ++r) {
             const long long t0 = dp.tile_prefix[r], t1 = dp.tile_prefix[r + 1];  // t1 > t0 always
@@ -645,6 +694,13 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
             mp.w_hi[r] = wend;
         }
     }
+    mp.part_o = dp.part_o;
+    mp.part_ml = dp.part_ml;
+    mp.out = a->out;
+    mp.n_sel_dev = a->n_sel_dev;
+    mp.n_req = a->n_req;
+    mp.n_heads = a->n_heads;
+    mp.n_groups = P.G;
 
     if (a->ev_attn_begin && a->ev_attn_end) {
         // the events take the dispatch's own start and end timestamps: no extra packets on the stream

@@ -53,6 +53,8 @@ struct RefreshParams {
     long long blk_off[kMaxReq + 1];
     int word_off[kMaxReq + 1];
     int cg_off[kMaxReq + 1];  // first compaction group of each request
+    int2* table_out;          // optional: (id, tslot[r] + id) pairs at pair blk_off[r]
+    int tslot[kMaxReq];
 };
 
 __device__ __forceinline__ void put(unsigned long long* w, unsigned long long tag, unsigned v) {
@@ -465,7 +467,12 @@ __device__ void compact_role(const RefreshParams& p, int cg) {
                                          ((unsigned long long)(unsigned)__builtin_amdgcn_readlane(uhi, m) << 32);
             const int at = __builtin_amdgcn_readlane(pm, m);
             const int j = wave + (kThreads / 64) * m;
-            if ((u >> lane) & 1ull) out[at + __popcll(u & ((1ull << lane) - 1ull))] = (s0 + j) * 64 + lane;
+            if ((u >> lane) & 1ull) {
+                const int pos = at + __popcll(u & ((1ull << lane) - 1ull));
+                const int id = (s0 + j) * 64 + lane;
+                out[pos] = id;
+                if (p.table_out) p.table_out[p.blk_off[r] + pos] = make_int2(id, p.tslot[r] + id);
+            }
         }
     }
     if (t == 0 && s1 == n_words) p.sel_count[r] = (failed || bad) ? -1 : s_total;
@@ -545,6 +552,8 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
     rp.sel_ids = a->sel_ids;
     rp.sel_count = a->sel_count;
     rp.masks = reinterpret_cast<unsigned long long*>(a->masks);
+    rp.table_out = reinterpret_cast<int2*>(a->table_out);
+    for (int r = 0; r < a->n_req; ++r) rp.tslot[r] = a->table_out ? a->table_slot_base[r] : 0;
     rp.qw = reinterpret_cast<unsigned long long*>(ws + L.qw_off);
     rp.hw = reinterpret_cast<unsigned long long*>(ws + L.hw_off);
     rp.bad = reinterpret_cast<unsigned long long*>(ws + L.bad_off);
@@ -610,6 +619,15 @@ extern "C" lsa_status lsa_index_refresh(const lsa_refresh_args* a, hipStream_t s
     LSA_CHECK_ARG(a->hidden_req_stride >= a->d_model || a->n_req == 1,
                   "lsa_index_refresh: hidden_req_stride=%lld < d_model", (long long)a->hidden_req_stride);
     LSA_CHECK_ARG(a->hidden_idx_stride >= 0, "lsa_index_refresh: negative hidden_idx_stride");
+    if (a->table_out) {
+        LSA_CHECK_ARG(a->table_slot_base != nullptr, "lsa_index_refresh: table_out without table_slot_base");
+        LSA_CHECK_ARG(((uintptr_t)a->table_out % 8) == 0, "lsa_index_refresh: table_out must be 8-byte aligned");
+        for (int r = 0; r < a->n_req; ++r) {
+            const long long base = a->table_slot_base[r], nb = a->blk_off[r + 1] - a->blk_off[r];
+            LSA_CHECK_ARG(base >= 0 && base + nb <= 0x7fffffffll,
+                          "lsa_index_refresh: table_slot_base[%d]=%lld puts slots outside int32", r, base);
+        }
+    }
     if (a->workspace == nullptr || a->workspace_bytes < L.total)
         return fail(LSA_ERR_WORKSPACE, "lsa_index_refresh: workspace of %zu bytes, need %zu",
                     a->workspace ? a->workspace_bytes : (size_t)0, L.total);

@@ -216,7 +216,7 @@ class LSASession:
         return out
 
     def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor, ev_begin=None,
-                     ev_end=None) -> None:
+                     ev_end=None, table_out: bool = False) -> None:
         off = self.blk_off[r0:r1 + 1] - self.blk_off[r0]
         key_elem0 = int(self.n_idx * self.d_idx * self.blk_off[r0])
         masks = None
@@ -226,6 +226,8 @@ class LSASession:
                           w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
                           sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
                           workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
+                          table_out=(self.table[2 * int(self.slot_base[r0]):] if table_out else None),
+                          table_slot_base=(self.slot_base[r0:r1] if table_out else None),
                           stream=self.stream)
 
     def masks_of(self, r: int) -> np.ndarray:
@@ -295,6 +297,20 @@ class LSASession:
         if st is not self.stream:
             self.stream.wait_event(ev)
         return out
+
+    def make_resident(self) -> None:
+        """Load every block of every request into the hot pool (capacity must equal the block
+        count), block b of request r at slot slot_base[r] + b: the fully resident pool that
+        ResidentLoop reads through the table the refresh writes."""
+        if not np.array_equal(self.capacity, self.n_blocks):
+            raise ValueError("a resident pool needs capacity == n_blocks for every request")
+        res = self.gather_many({r: np.arange(int(self.n_blocks[r]), dtype=np.int32) for r in range(self.n_req)})
+        self.stream.synchronize()
+        for r in range(self.n_req):
+            want = np.arange(int(self.slot_base[r]), int(self.slot_base[r + 1]), dtype=np.int32)
+            if not np.array_equal(self.slot_of_block[r], want):
+                raise RuntimeError(f"request {r}: blocks were not placed in block order (gathered before?)")
+        return res
 
     # ---------------------------------------------------------------------------------------
     def attended_entries(self, seq_len: Sequence[int], window: Sequence[int]) -> np.ndarray:
@@ -379,3 +395,39 @@ class DecodeLoop:
         a.ev_attn_begin = ev_begin.cuda_event if ev_begin is not None else None
         a.ev_attn_end = ev_end.cuda_event if ev_end is not None else None
         _check(LIB.lsa_sparse_decode(self.ref, self.stream))
+
+
+class ResidentLoop:
+    """Reactive comparator: at every step the index is refreshed with that step's hidden state and the
+    decode attends over the window and the blocks just selected, read straight from a hot pool that
+    holds every block (LSASession.make_resident).  The refresh writes the decode's block table and
+    the decode reads the per-request counts on the device, so a step makes no host round trip and
+    moves no block.  Events (torch.cuda.Event pairs) may be passed per call to time the refresh and
+    the attention kernel."""
+
+    def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor,
+                 layer: int = 0):
+        if not np.array_equal(sess.capacity, sess.n_blocks):
+            raise ValueError("ResidentLoop needs a session with capacity == n_blocks, made resident")
+        self.sess = sess
+        self.loop = DecodeLoop(sess, prefill, window, out, layer=layer)
+        a = self.loop.args
+        # capacities on the host, counts from the refresh on the device
+        self.cap = np.ascontiguousarray(sess.n_blocks, dtype=np.int32)
+        a.n_sel = self.cap.ctypes.data
+        a.n_sel_dev = sess.sel_count.data_ptr()
+
+    def step(self, t: int, hidden: torch.Tensor, bias: torch.Tensor, q: torch.Tensor, k_new: Optional[torch.Tensor],
+             v_new: Optional[torch.Tensor], ev_refresh=(None, None), ev_attn=(None, None)) -> None:
+        sess = self.sess
+        sess._refresh_run(0, sess.n_req, hidden.reshape(sess.n_req, sess.d_model),
+                          bias.reshape(sess.n_req, sess.n_idx), ev_refresh[0], ev_refresh[1], table_out=True)
+        lp = self.loop
+        np.add(lp.prefill, t + 1, out=lp.seq_len, casting="unsafe")
+        a = lp.args
+        a.q = q.data_ptr()
+        a.k_new = k_new.data_ptr() if k_new is not None else None
+        a.v_new = v_new.data_ptr() if v_new is not None else None
+        a.ev_attn_begin = ev_attn[0].cuda_event if ev_attn[0] is not None else None
+        a.ev_attn_end = ev_attn[1].cuda_event if ev_attn[1] is not None else None
+        _check(LIB.lsa_sparse_decode(lp.ref, lp.stream))

@@ -69,6 +69,23 @@ def test_refresh_workspace_validation(over, status):
     assert L.LIB.lsa_last_error().decode()
 
 
+def test_refresh_table_out_validation_before_any_hip_call():
+    """The resident block table needs a slot base per request that keeps every slot in int32."""
+    a, keep = L._refresh_args(dtype="bf16", d_model=4096, d_idx=256, n_idx=3, hidden=FAKE, hidden_req_stride=4096,
+                              hidden_idx_stride=0, w_q=FAKE, keys=FAKE, blk_off=[0, 2048, 4096], bias=FAKE,
+                              sel_ids=FAKE, sel_count=FAKE, masks=None, workspace=FAKE, workspace_bytes=16)
+    a.table_out = FAKE
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+    assert "table_slot_base" in L.LIB.lsa_last_error().decode()
+    base = np.array([0, 2**31 - 2048], dtype=np.int32)   # second request's last slot past int32
+    a.table_slot_base = base.ctypes.data
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+    base[1] = 2**31 - 2049                               # fits: only the small workspace is left
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_WORKSPACE
+    a.table_out = FAKE + 4                               # pairs must be 8-byte aligned
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+
+
 def test_refresh_workspace_size():
     n = L.lsa_index_refresh_workspace(**_refresh_kwargs(blk_off=[0, 16384, 32768, 49152, 65536]))
     assert n >= 4 * 3 * 256 * 4 + 1024 * 8 + 16

@@ -231,3 +231,53 @@ def test_decode_loop_other_cadences(tau, steps):
         worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
     log(f"  tau={tau}: {len(sels)} refreshes bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
     assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+@pytest.mark.parametrize("name", ["tiny", "ctx128k_s", "ragged_s"])
+def test_resident_reactive_loop_matches_oracle(name):
+    """The reactive comparator: every step refreshes with that step's hidden state, the refresh
+    writes the block table of a fully resident pool and the decode reads the counts on the device.
+    Every step's selection is the oracle's (cadence 1), bit for bit, the table pairs are
+    (id, slot of id), and the outputs match the oracle's within tolerance."""
+    import torch
+
+    from lookahead_block_sparse_amd.session import ResidentLoop
+    from workloads import get_config
+
+    steps = 10
+    cfg = get_config(name).scaled(tau=1, steps=steps, staggered=False)
+    log(f"resident reactive loop {name}, {steps} steps")
+    wl = conditioned_workload(cfg, seed=23)
+    R = wl.n_req
+    sess = make_session(wl, cold_on_device=True, with_masks=False)
+    sess.make_resident()
+    dev = sess.device
+    out = torch.empty((R, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    loop = ResidentLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), out)
+    bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+    gpu, sels = {}, {}
+    for t in range(steps):
+        assert wl.refreshes_at(t) == list(range(R))
+        hid = raw_to_torch(np.stack([wl.hidden[r][wl.refresh_index_at(r, t)] for r in range(R)]), dev)
+        loop.step(t, hid, bias, raw_to_torch(wl.q_dec[t], dev), raw_to_torch(wl.k_new[t], dev),
+                  raw_to_torch(wl.v_new[t], dev))
+        counts = sess.sel_count.cpu().numpy()
+        ids = sess.sel_ids.cpu().numpy()
+        table = sess.table.view(-1, 2).cpu().numpy()
+        for r in range(R):
+            b0 = int(sess.blk_off[r])
+            assert counts[r] >= 0
+            sel = ids[b0:b0 + counts[r]].copy()
+            sels[(r, wl.refresh_index_at(r, t))] = sel
+            assert np.array_equal(table[b0:b0 + counts[r], 0], sel)
+            assert np.array_equal(table[b0:b0 + counts[r], 1], sess.slot_base[r] + sel)
+        gpu[t] = out.double().cpu().numpy()
+    refs, outs = oracle.simulate(wl, steps=list(range(steps)))
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (name, r, k)
+    worst = (0.0, 0.0, 0.0)
+    for t in range(steps):
+        ref = np.stack([outs[(r, t)] for r in range(R)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
+    log(f"  {name}: {len(sels)} selections bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
