@@ -92,7 +92,20 @@ def _planting_query(dtype):
     def fn(h, w):
         hf = _bf16_to_f32(h) if dtype == "bf16" else h
         wf = _bf16_to_f32(w) if dtype == "bf16" else w
-        return np.stack([wf[i].astype(np.float64) @ hf.astype(np.float64) for i in range(wf.shape[0])])
+        hs = [hf if hf.ndim == 1 else hf[i] for i in range(wf.shape[0])]  # one per indexer (latents)
+        return np.stack([wf[i].astype(np.float64) @ hs[i].astype(np.float64) for i in range(wf.shape[0])])
+    return fn
+
+
+def _planting_latent(dtype):
+    """Latents of a low-rank workload, used only to place the planted keys (input construction)."""
+    from workloads import bf16_bits_from_f32
+
+    def fn(h, w_down):
+        hf = (_bf16_to_f32(h) if dtype == "bf16" else h).astype(np.float64)
+        wf = _bf16_to_f32(w_down) if dtype == "bf16" else w_down
+        c = np.stack([wf[i].astype(np.float64) @ hf for i in range(wf.shape[0])]).astype(np.float32)
+        return bf16_bits_from_f32(c) if dtype == "bf16" else c
     return fn
 
 
@@ -247,7 +260,7 @@ def main():
     wl = build_workload(cfg, seed=args.seed, steps=max(cfg.steps, total_steps))
     cfg = wl.cfg
     if cfg.planted_frac > 0:
-        wl.condition(_planting_query(cfg.dtype), None)
+        wl.condition(_planting_query(cfg.dtype), None, latent_fn=_planting_latent(cfg.dtype))
     if args.select == "all":
         wl.bias[:] = 1e4  # every logit above zero: every block selected
     note(f"workload {cfg.name}: {wl.n_req} requests, contexts {wl.ctx.tolist()[:4]}..., built")

@@ -17,6 +17,8 @@ from .lsa_ref import (  # noqa: F401
     governing_refresh,
     kv_rows,
     query_encoder,
+    query_latent,
+    round_bf16,
     refresh,
     simulate,
     threshold,

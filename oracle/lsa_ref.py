@@ -26,6 +26,13 @@ What the pages leave open and how it is read here:
     section 5 writes ">= 0.5"; the strict form is used.
   * one hidden state per request per refresh, shared by the indexers; one set
     of block keys per indexer.
+  * low-rank query projection ([Explained] section 4, training tricks: rank
+    r = 2048, reusing the backbone's MLA/MQA bottleneck): indexer i first forms
+    the latent c_i = A_i h (A_i is [r][d_model]), which, like any activation of
+    the backbone, is stored in the input precision (rounded to the nearest
+    bfloat16, ties to even, for bf16 inputs); the Query Encoder then projects
+    the latent, q_i = B_i c_i.  The backbone's normalisation of the latent is
+    not part of the path.
   * a refresh taken at step t_k governs steps t_k .. t_k + 63 (inclusive of t_k).
   * attended tokens: the last W tokens (the recent window, including the
     current token) plus every token of a selected block that lies before the
@@ -68,9 +75,42 @@ def decode_values(raw: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each float64 (ties to even), as float64.
+
+    A bfloat16 keeps 8 significant bits (the top half of an IEEE-754 single): x = m 2^e with
+    m in [0.5, 1) is rounded to round_half_even(m 2^8) 2^(e-8).  Values stay within the single's
+    normal range here (no subnormal or overflow handling).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 # ------------------------------------------------------------------------------------------
 # index refresh: Query Encoder -> block scores -> threshold -> OR-union -> block list
 # ------------------------------------------------------------------------------------------
+def query_latent(h: np.ndarray, w_down: np.ndarray, dtype: str) -> np.ndarray:
+    """Latent of the low-rank query projection, one per indexer.
+
+    [Explained] section 4 (training tricks): the query projection is low-rank, r = 2048, using the
+    backbone's MLA/MQA bottleneck.  w_down is [n_idx][r][d_model], h is [d_model] (shared) or
+    [n_idx][d_model].  Returns c [n_idx][r]:
+        c[i][k] = sum_m w_down[i][k][m] * h[m]
+    computed exactly, then stored like an activation of the backbone: rounded to bfloat16 for
+    bf16 inputs, to float32 for f32 inputs.  query_encoder(c, B) then gives q_i = B_i c_i.
+    """
+    w_down = np.asarray(w_down, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    n_idx = w_down.shape[0]
+    c = np.stack([w_down[i] @ (h if h.ndim == 1 else h[i]) for i in range(n_idx)])
+    if dtype == "bf16":
+        return round_bf16(c)
+    if dtype == "f32":
+        return c.astype(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
 def query_encoder(h: np.ndarray, w_q: np.ndarray) -> np.ndarray:
     """Query embeddings of the current hidden state, one per indexer.
 
@@ -241,6 +281,7 @@ def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Seque
     cfg = wl.cfg
     dt = cfg.dtype
     w_q = decode_values(wl.w_q, dt)
+    w_down = decode_values(wl.w_down, dt) if getattr(wl, "w_down", None) is not None else None
     req = range(wl.n_req) if requests is None else requests
     step_list = range(cfg.steps) if steps is None else steps
     refreshes = {}
@@ -249,8 +290,10 @@ def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Seque
     for r in req:
         keys = decode_values(wl.keys[r], dt)
         bias = np.asarray(wl.bias[r], dtype=np.float64)
-        res = [refresh(decode_values(wl.hidden[r][k], dt), w_q, keys, bias)
-               for k in range(len(wl.refresh_steps[r]))]
+        hs = [decode_values(wl.hidden[r][k], dt) for k in range(len(wl.refresh_steps[r]))]
+        if w_down is not None:  # low-rank query projection: the Query Encoder reads the latents
+            hs = [query_latent(h, w_down, dt) for h in hs]
+        res = [refresh(h, w_q, keys, bias) for h in hs]
         refreshes[r] = res
         if not step_list:
             continue

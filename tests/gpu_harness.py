@@ -34,6 +34,17 @@ def oracle_query_fn(dtype):
     return lambda h, w: oracle.query_encoder(oracle.decode_values(h, dtype), oracle.decode_values(w, dtype))
 
 
+def oracle_latent_fn(dtype):
+    """Latents of a low-rank workload as stored activations (raw), from the oracle."""
+    from workloads import bf16_bits_from_f32
+
+    def fn(h, w_down):
+        c = oracle.query_latent(oracle.decode_values(h, dtype), oracle.decode_values(w_down, dtype), dtype)
+        c32 = c.astype(np.float32)  # exact: the values are already bf16 / f32 values
+        return bf16_bits_from_f32(c32) if dtype == "bf16" else c32
+    return fn
+
+
 def oracle_logits_fn(dtype):
     return lambda q, keys, bias: oracle.block_logits(q, oracle.decode_values(keys, dtype), bias)
 
@@ -41,7 +52,7 @@ def oracle_logits_fn(dtype):
 def conditioned_workload(name_or_cfg, seed=0, steps=None):
     wl = build_workload(name_or_cfg, seed=seed, steps=steps)
     dt = wl.cfg.dtype
-    rep = wl.condition(oracle_query_fn(dt), oracle_logits_fn(dt))
+    rep = wl.condition(oracle_query_fn(dt), oracle_logits_fn(dt), latent_fn=oracle_latent_fn(dt))
     assert rep.min_abs_logit >= 2e-3, rep
     return wl
 

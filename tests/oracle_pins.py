@@ -348,6 +348,98 @@ def pin_simulate_layer_uses_its_own_inputs(O):
     assert all(np.array_equal(a.ids, b.ids) for a, b in zip(refs0[0], refs1[0]))
 
 
+# ------------------------------------------------------------------------------------------
+def _bf16_rne_bits(x32: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 with integer arithmetic on the binary32 bits: add 0x7FFF
+    plus the lowest kept bit, then drop the low 16 bits (round to nearest, ties to even)."""
+    b = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_round_bf16(O):
+    """Rounding to bfloat16: the hand-derived cases of bf16_rounding.json; every bfloat16 value
+    (bf16_values.json) is a fixed point; and on random values the result is the nearest of the
+    two bfloat16 neighbours, found by enumerating bit patterns, with ties to the even pattern."""
+    g = _golden("bf16_rounding.json")
+    x = np.array([c["x"] for c in g["cases"]], dtype=np.float64)
+    want = np.array([c["rounded"] for c in g["cases"]], dtype=np.float64)
+    got = O.round_bf16(x)
+    assert np.array_equal(got, want), (x[got != want], got[got != want])
+    vals = np.array([c["value"] for c in _golden("bf16_values.json")["cases"]], dtype=np.float64)
+    normal = np.abs(vals) >= 2.0 ** -126
+    assert np.array_equal(O.round_bf16(vals[normal]), vals[normal])
+    rng = _rng(41)
+    xs = rng.standard_normal(2000) * np.exp(rng.uniform(-20, 20, 2000))
+    got = O.round_bf16(xs)
+    lo_bits = (xs.astype(np.float32).view(np.uint32) >> 16).astype(np.uint32)   # truncation toward zero
+    for x, g1, lb in zip(xs, got, lo_bits):
+        cands = [(int(b) << 16) for b in (lb - 1, lb, lb + 1)]
+        cv = np.array(cands, dtype=np.uint32).view(np.float32).astype(np.float64)
+        dist = np.abs(cv - x)
+        best = dist.min()
+        ok = [i for i in range(3) if dist[i] == best]
+        pick = ok[0] if len(ok) == 1 else [i for i in ok if (cands[i] >> 16) % 2 == 0][0]
+        assert g1 == cv[pick], (x, g1, cv)
+
+
+def pin_query_latent(O):
+    """The low-rank latent c_i = A_i h: explicit sums with rectangular and square A_i, per-indexer
+    hidden states; for bf16 the exact sums are rounded as the binary32 bit trick rounds them (the
+    sums are integers times 2^-6, exact in binary32); for f32 the sums are kept."""
+    rng = _rng(42)
+    for r, d in ((5, 7), (6, 6)):
+        A = rng.integers(-100, 101, (3, r, d)).astype(np.float64)
+        h = rng.integers(-100, 101, (3, d)).astype(np.float64) / 64.0  # sums: up to 17-bit integers / 64
+        want = np.zeros((3, r))
+        for i in range(3):
+            for k in range(r):
+                want[i, k] = math.fsum(A[i, k, m] * h[i, m] for m in range(d))
+        assert np.array_equal(O.query_latent(h, A, "f32"), want)
+        bits = _bf16_rne_bits(want.astype(np.float32))
+        want16 = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        got16 = O.query_latent(h, A, "bf16")
+        assert np.array_equal(got16, want16), np.abs(got16 - want16).max()
+        assert not np.array_equal(want16, want)  # the case does exercise rounding
+    # one hidden state shared by the indexers
+    A = rng.integers(-4, 5, (2, 3, 4)).astype(np.float64)
+    h = rng.integers(-4, 5, 4).astype(np.float64)
+    assert np.array_equal(O.query_latent(h, A, "f32"), np.stack([A[0] @ h, A[1] @ h]))
+
+
+def pin_lowrank_query_is_product(O):
+    """Without rounding (small integers, f32 storage exact) the chain B_i (A_i h) is the Query
+    Encoder of the product matrix W_i = B_i A_i, and the refresh selects the same blocks."""
+    rng = _rng(43)
+    A = rng.integers(-3, 4, (3, 4, 9)).astype(np.float64)
+    B = rng.integers(-3, 4, (3, 5, 4)).astype(np.float64)
+    h = rng.integers(-3, 4, 9).astype(np.float64)
+    W = np.stack([B[i] @ A[i] for i in range(3)])
+    c = O.query_latent(h, A, "f32")
+    assert np.array_equal(O.query_encoder(c, B), O.query_encoder(h, W))
+    keys = rng.integers(-3, 4, (3, 40, 5)).astype(np.float64)
+    bias = np.array([0.5, -0.5, 0.25])
+    assert np.array_equal(O.refresh(c, B, keys, bias).ids, O.refresh(h, W, keys, bias).ids)
+
+
+def pin_simulate_lowrank_uses_the_latent(O):
+    """simulate() on a workload with a low-rank query projection selects what the chain selects:
+    each refresh's ids equal a direct evaluation of B_i round(A_i h) . key + bias > 0."""
+    from workloads import build_workload, get_config
+
+    wl = build_workload(get_config("tiny").scaled(q_rank=96, steps=70), seed=4)
+    assert wl.w_down is not None and wl.w_q.shape[2] == 96
+    refs, _ = O.simulate(wl, steps=[])
+    A = wl.w_down.astype(np.float64)
+    B = wl.w_q.astype(np.float64)
+    for r in range(wl.n_req):
+        keys = wl.keys[r].astype(np.float64)
+        for k, res in enumerate(refs[r]):
+            h = wl.hidden[r][k].astype(np.float64)
+            c = np.stack([(A[i] @ h).astype(np.float32).astype(np.float64) for i in range(A.shape[0])])
+            z = np.stack([keys[i] @ (B[i] @ c[i]) + float(wl.bias[r][i]) for i in range(A.shape[0])])
+            assert np.array_equal(res.ids, np.flatnonzero((z > 0).any(axis=0))), (r, k)
+
+
 PINS = [
     pin_bf16_decode,
     pin_query_encoder_columns,
@@ -367,4 +459,8 @@ PINS = [
     pin_bias_monotone,
     pin_block_permutation,
     pin_simulate_layer_uses_its_own_inputs,
+    pin_round_bf16,
+    pin_query_latent,
+    pin_lowrank_query_is_product,
+    pin_simulate_lowrank_uses_the_latent,
 ]

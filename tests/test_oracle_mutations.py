@@ -133,6 +133,45 @@ def _m_simulate_ignores_layer(wl, steps=None, requests=None, layer=0):
     return _orig["simulate"](wl, steps, requests, 0)
 
 
+def _m_round_bf16_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+
+def _m_round_bf16_half_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.floor(m * 256.0 + 0.5), e - 8)
+
+
+def _m_latent_no_rounding(h, w_down, dtype):
+    return _orig["query_latent"](h, w_down, "f32") if dtype == "bf16" else _orig["query_latent"](h, w_down, dtype)
+
+
+def _m_latent_transposed(h, w_down, dtype):
+    w = np.asarray(w_down, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    c = np.stack([w[i].T @ (h if h.ndim == 1 else h[i]) for i in range(w.shape[0])])
+    return _orig["round_bf16"](c) if dtype == "bf16" else c.astype(np.float32).astype(np.float64)
+
+
+def _m_latent_shared_hidden(h, w_down, dtype):
+    h = np.asarray(h, dtype=np.float64)
+    return _orig["query_latent"](h if h.ndim == 1 else h[0], w_down, dtype)
+
+
+def _m_simulate_ignores_latent(wl, steps=None, requests=None, layer=0):
+    """The latent skipped: the first r elements of the hidden state stand in for it."""
+    import copy
+    if getattr(wl, "w_down", None) is None:
+        return _orig["simulate"](wl, steps, requests, layer)
+    moved = copy.copy(wl)
+    rank = wl.w_down.shape[1]
+    moved.w_down = None
+    moved.hidden = [np.ascontiguousarray(h[:, :rank]) for h in wl.hidden]
+    return _orig["simulate"](moved, steps, requests, layer)
+
 MUTATIONS = [
     ("threshold", _m_threshold_ge),
     ("threshold", _m_threshold_prob),
@@ -156,6 +195,12 @@ MUTATIONS = [
     ("governing_refresh", _m_governing_strict),
     ("decode_values", _m_decode_bf16_shift),
     ("simulate", _m_simulate_ignores_layer),
+    ("round_bf16", _m_round_bf16_truncate),
+    ("round_bf16", _m_round_bf16_half_up),
+    ("query_latent", _m_latent_no_rounding),
+    ("query_latent", _m_latent_transposed),
+    ("query_latent", _m_latent_shared_hidden),
+    ("simulate", _m_simulate_ignores_latent),
 ]
 
 

@@ -43,14 +43,22 @@ class LSAConfig:
     n_layers: int = 1
     # correlation of successive refresh hidden states: h_k = rho h_{k-1} + sqrt(1 - rho^2) eps_k
     hidden_rho: float = 0.0
+    # low-rank query projection: 0 = full rank (W_q [n_idx][d_idx][d_model]); r > 0 = each indexer
+    # projects the latent c_i = A_i h (A_i [r][d_model]) with B_i [d_idx][r] (w_q holds B)
+    q_rank: int = 0
     # std of the drawn tensors
-    wq_std: float = field(default=0.0)  # 0 => 1/sqrt(d_model)
+    wq_std: float = field(default=0.0)  # 0 => 1/sqrt(input size of W_q: d_model, or q_rank)
     key_std: float = field(default=0.0)  # 0 => 1/sqrt(d_idx)
     tag: int = 0  # distinguishes the random streams of different workloads
 
     @property
+    def q_in(self) -> int:
+        """Input size of the Query Encoder's matrices: the hidden size, or the latent rank."""
+        return self.q_rank if self.q_rank > 0 else self.d_model
+
+    @property
     def w_std(self) -> float:
-        return self.wq_std if self.wq_std > 0 else self.d_model ** -0.5
+        return self.wq_std if self.wq_std > 0 else self.q_in ** -0.5
 
     @property
     def k_std(self) -> float:

@@ -35,7 +35,7 @@ from .configs import LSAConfig, get_config
 
 # tensor ids used in stream keys
 _T_CTX, _T_DENS, _T_PHASE, _T_WQ, _T_KEYS, _T_HID, _T_QDEC, _T_KPRE, _T_VPRE, \
-    _T_KNEW, _T_VNEW, _T_PLANT_IDS, _T_PLANT, _T_REDRAW, _T_LAYER = range(1, 16)
+    _T_KNEW, _T_VNEW, _T_PLANT_IDS, _T_PLANT, _T_REDRAW, _T_LAYER, _T_WDOWN = range(1, 17)
 
 _KV_CHUNK = 1 << 16  # tokens per independent prefill K/V stream
 
@@ -92,7 +92,7 @@ class Workload:
     density: np.ndarray             # [R] union density targets
     phase: np.ndarray               # [R] refresh phase phi_r
     bias: np.ndarray                # [R][n_idx] float32
-    w_q: np.ndarray                 # [n_idx][d_idx][d_model]
+    w_q: np.ndarray                 # [n_idx][d_idx][d_model], or B [n_idx][d_idx][q_rank] (low rank)
     keys: List[np.ndarray]          # per request [n_idx][B_r][d_idx]
     refresh_steps: List[List[int]]  # per request, ascending; a negative entry is the prologue refresh
     hidden: List[np.ndarray]        # per request [n_refresh_r][d_model]
@@ -101,6 +101,7 @@ class Workload:
     k_new: np.ndarray               # [T][R][D]      (layer 0)
     v_new: np.ndarray               # [T][R][D]      (layer 0)
     layer_dec: List[Tuple[np.ndarray, np.ndarray, np.ndarray]] = field(default_factory=list)  # layers 1..
+    w_down: Optional[np.ndarray] = None  # low rank: A [n_idx][q_rank][d_model], latent c_i = A_i h
     _kv: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
     report: Optional[ConditionReport] = None
 
@@ -190,11 +191,14 @@ class Workload:
         margin: float = 2e-3,
         max_rounds: int = 32,
         plant_logit: float = 2.0,
+        latent_fn: Optional[Callable[[np.ndarray, np.ndarray], np.ndarray]] = None,
     ) -> ConditionReport:
         """Place planted keys and move keys away from the decision boundary.
 
         query_fn(h_raw[d], w_raw[n_idx][d_idx][d]) -> q float64 [n_idx][d_idx]
         logits_fn(q [n_idx][d_idx], keys_raw [n_idx][B][d_idx], bias [n_idx]) -> float64 [n_idx][B]
+        latent_fn(h_raw[d], w_down_raw[n_idx][r][d]) -> latent raw [n_idx][r] (low-rank workloads
+        only: query_fn then receives the latents in place of h)
 
         Both functions come from the caller; this module evaluates neither.
 
@@ -208,9 +212,12 @@ class Workload:
         cfg = self.cfg
         rep = ConditionReport()
         queries: List[np.ndarray] = []  # per request [n_ref][n_idx][d_idx]
+        if self.w_down is not None and latent_fn is None:
+            raise ValueError("a low-rank workload needs latent_fn to condition")
         for r in range(self.n_req):
-            qs = np.stack([np.asarray(query_fn(self.hidden[r][k], self.w_q), dtype=np.float64)
-                           for k in range(len(self.refresh_steps[r]))])
+            ins = [self.hidden[r][k] if self.w_down is None else latent_fn(self.hidden[r][k], self.w_down)
+                   for k in range(len(self.refresh_steps[r]))]
+            qs = np.stack([np.asarray(query_fn(h, self.w_q), dtype=np.float64) for h in ins])
             queries.append(qs)
         for r in range(self.n_req):
             if len(self.planted[r]) == 0:
@@ -318,7 +325,10 @@ def build_workload(cfg: LSAConfig | str, seed: int = 0, steps: Optional[int] = N
             steps_r = [first - cfg.tau] + steps_r  # prologue: the refresh before step 0
         refresh_steps.append(steps_r)
 
-    w_q = _normal(rng_for(seed, cfg.tag, _T_WQ), (cfg.n_idx, cfg.d_idx, cfg.d_model), cfg.w_std, cfg.dtype)
+    w_q = _normal(rng_for(seed, cfg.tag, _T_WQ), (cfg.n_idx, cfg.d_idx, cfg.q_in), cfg.w_std, cfg.dtype)
+    # low rank: latents of unit variance from unit-variance hidden states
+    w_down = (_normal(rng_for(seed, cfg.tag, _T_WDOWN), (cfg.n_idx, cfg.q_rank, cfg.d_model), cfg.d_model ** -0.5,
+                      cfg.dtype) if cfg.q_rank > 0 else None)
     n_blocks = ctx // blk
     keys = [
         _normal(rng_for(seed, cfg.tag, _T_KEYS, r), (cfg.n_idx, int(n_blocks[r]), cfg.d_idx), cfg.k_std, cfg.dtype)
@@ -366,5 +376,5 @@ def build_workload(cfg: LSAConfig | str, seed: int = 0, steps: Optional[int] = N
     return Workload(
         cfg=cfg, seed=seed, ctx=ctx, density=dens, phase=phase, bias=bias, w_q=w_q, keys=keys,
         refresh_steps=refresh_steps, hidden=hidden, planted=planted, q_dec=q_dec, k_new=k_new,
-        v_new=v_new, layer_dec=layer_dec,
+        v_new=v_new, layer_dec=layer_dec, w_down=w_down,
     )
