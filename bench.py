@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--select", choices=("threshold", "all"), default="threshold",
                     help="all: every block selected at one refresh before the first step, i.e. dense "
                          "attention over the whole context through the same kernels (comparator)")
+    ap.add_argument("--q-rank", type=int, default=0,
+                    help="low-rank query projection: each refresh first forms the latents c_i = A_i h of "
+                         "this rank (2048 on the pages), and the Query Encoder projects them")
     ap.add_argument("--reactive", action="store_true",
                     help="reactive comparator: every block resident in HBM, the index scored at every step "
                          "and the decode reading the selected blocks in place (refresh cadence 1, no "
@@ -252,6 +255,8 @@ def main():
         cfg = cfg.scaled(n_layers=args.layers, hidden_rho=args.hidden_rho)
     if args.select == "all":
         cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0)  # one refresh, at step 0
+    if args.q_rank > 0:
+        cfg = cfg.scaled(q_rank=args.q_rank)
     if args.reactive:
         if args.select == "all" or cfg.n_layers > 1 or args.cold != "device":
             raise SystemExit("--reactive runs one layer with the default selection and the pool in HBM")
@@ -269,7 +274,7 @@ def main():
     sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False,
-                      n_layers=cfg.n_layers)
+                      n_layers=cfg.n_layers, w_down=wl.w_down)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
@@ -312,6 +317,7 @@ def main():
     ev_every = max(1, args.event_every)
     att_ev = {i: (mk_event(), mk_event()) for i in range(0, K, ev_every)}
     ref_ev = {}
+    lat_ev = {}
     gather_ev = {}
     torch.cuda.synchronize()
 
@@ -344,11 +350,14 @@ def main():
             if timed_idx is not None:
                 ref_ev[t] = (mk_event(), mk_event())
                 gather_ev[t] = (mk_event(), mk_event())
+                if sess.rank:
+                    lat_ev[t] = (mk_event(), mk_event())
             hid = hid_at[t]
             bias = bias_dev[reqs[0]:reqs[-1] + 1] if reqs == list(range(reqs[0], reqs[-1] + 1)) else \
                 torch.stack([bias_dev[r] for r in reqs])
             evs = ref_ev.get(t, (None, None)) if timed_idx is not None else (None, None)
-            sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1])
+            sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
+                               ev_latent=lat_ev.get(t, (None, None)))
             h0 = time.perf_counter()
             if timed_idx is not None:
                 gather_ev[t][0].record(sess.stream)
@@ -420,6 +429,7 @@ def main():
         attn_tokens.append(toks)
         attn_bytes.append(toks * 2 * D * e + wl.n_req * H * D * e + 8 * n_entries)
     ref_us = np.array([1e3 * a.elapsed_time(b) for a, b in ref_ev.values()])
+    lat_us = np.array([1e3 * a.elapsed_time(b) for a, b in lat_ev.values()])
     gat_us = np.array([1e3 * a.elapsed_time(b) for a, b in gather_ev.values()])
     attn_bytes = np.array(attn_bytes, dtype=np.float64)
     ev_bytes = attn_bytes[np.array(with_ev)]  # the launches the events timed, in the same order
@@ -427,12 +437,16 @@ def main():
 
     # refresh algorithmic bytes for one group of all requests
     n_blocks_total = int(wl.n_blocks.sum())
-    ref_bytes = (cfg.n_idx * cfg.d_model * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
-                 + wl.n_req * cfg.d_model * e + 4 * sum(len(x) for x in sess.sel_host) + 4 * wl.n_req)
+    # (low rank: the Query Encoder reads B and the latents of every indexer instead of W_q and h)
+    q_in_bytes = (wl.n_req * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else wl.n_req * cfg.d_model * e
+    ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
+                 + q_in_bytes + 4 * sum(len(x) for x in sess.sel_host) + 4 * wl.n_req)
+    lat_bytes = (cfg.n_idx * cfg.q_rank * cfg.d_model * e + wl.n_req * cfg.d_model * e
+                 + wl.n_req * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else 0
     if rloop is not None:  # ids and table pairs of the recomputed selections
         n_ids = np.mean([sum(len(v) for v in s.values()) for s in sel_at.values()]) if sel_at else 0.0
-        ref_bytes = (cfg.n_idx * cfg.d_model * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
-                     + wl.n_req * cfg.d_model * e + int(12 * n_ids) + 4 * wl.n_req)
+        ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
+                     + q_in_bytes + int(12 * n_ids) + 4 * wl.n_req)
 
     khash = kernel_hash()
     res = {
@@ -457,13 +471,15 @@ def main():
                          + (f", {cfg.n_layers} attention layers per selection" if cfg.n_layers > 1 else "")
                          + (f", hidden-state correlation {cfg.hidden_rho}" if cfg.hidden_rho else "")
                          + (", reactive comparator: every block resident, scored every step" if args.reactive
-                            else "")),
+                            else "")
+                         + (f", low-rank query projection r={cfg.q_rank}" if cfg.q_rank else "")),
             "cold_pool": args.cold,
             "tau": cfg.tau,
             "layers": cfg.n_layers,
             "hidden_rho": cfg.hidden_rho,
             "select": args.select,
             "reactive": bool(args.reactive),
+            "q_rank": cfg.q_rank,
             "requests": wl.n_req,
             "context_tokens": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else wl.ctx.tolist(),
             "seed": args.seed,
@@ -486,6 +502,10 @@ def main():
         "refresh_roofline": ({"achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "algorithmic_bytes": ref_bytes} if len(ref_us) else None),
+        "latent_us": float(np.median(lat_us)) if len(lat_us) else None,
+        "latent_roofline": ({"achieved": lat_bytes / (np.median(lat_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": lat_bytes / (np.median(lat_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes": lat_bytes} if len(lat_us) else None),
         "gather_us": float(np.median(gat_us)) if len(gat_us) else None,
         "gather_blocks_per_refresh": float(np.mean(gather_blocks)) if gather_blocks else None,
         "gather_host_plan_ms": float(np.median(gather_host_s) * 1e3) if gather_host_s else None,

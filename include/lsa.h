@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 5
+#define LSA_ABI_VERSION 6
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -66,7 +66,7 @@ const char* lsa_last_error(void);
 int32_t lsa_abi_version(void);
 
 /* sizeof the argument structs below, so a binding can check its own layout:
- * which = 0 refresh args, 1 gather args, 2 decode args. Returns 0 for others. */
+ * which = 0 refresh args, 1 gather args, 2 decode args, 3 latent args. Returns 0 for others. */
 size_t lsa_struct_size(int32_t which);
 
 /* --------------------------------------------------------------------------------------
@@ -163,6 +163,36 @@ typedef struct lsa_refresh_args {
 
 lsa_status lsa_index_refresh_workspace(const lsa_refresh_args* a, size_t* bytes);
 lsa_status lsa_index_refresh(const lsa_refresh_args* a, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * (1a) Low-rank query projection, first factor (zhichai.net explainer, section 4,
+ * training tricks: the query projection is low-rank, r = 2048, through the
+ * backbone's MLA/MQA bottleneck).  For request r and indexer i:
+ *   c[r][i][k] = sum_m A[i][k][m] h[r][i][m]     fp32 accumulation, then stored in
+ *                                                the input type (bf16: nearest,
+ *                                                ties to even), like any activation
+ * lsa_index_refresh then runs with hidden = c (hidden_req_stride = n_idx*rank,
+ * hidden_idx_stride = rank), d_model = rank and w_q = B [n_idx][d_idx][rank]:
+ * q_i = B_i c_i.  All asynchronous on `stream`; validation happens before any launch.
+ * ------------------------------------------------------------------------------------ */
+typedef struct lsa_latent_args {
+    int32_t n_req;             /* 1..LSA_MAX_REFRESH_REQ */
+    int32_t d_model;           /* hidden size: multiple of 256, <= 16384 */
+    int32_t rank;              /* latent size r: multiple of 256, <= 16384 */
+    int32_t n_idx;             /* indexers: 1..4 */
+    int32_t dtype;             /* lsa_dtype of hidden, w_down and latent */
+    int32_t reserved0;         /* must be 0 */
+    const void* hidden;        /* dev: request r, indexer i reads d_model elements at
+                                  r*hidden_req_stride + i*hidden_idx_stride (16-byte aligned) */
+    int64_t hidden_req_stride; /* elements between requests (>= d_model unless n_req = 1) */
+    int64_t hidden_idx_stride; /* elements between indexers; 0 = one shared hidden state */
+    const void* w_down;        /* dev [n_idx][rank][d_model]: A (16-byte aligned) */
+    void* latent;              /* dev [n_req][n_idx][rank] out (16-byte aligned) */
+    hipEvent_t ev_begin;       /* optional, used only when both are set: they receive the start and */
+    hipEvent_t ev_end;         /* end time of the kernel's dispatch */
+} lsa_latent_args;
+
+lsa_status lsa_query_latent(const lsa_latent_args* a, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------
  * (2) Block gather: after a refresh, make the hot pool of ONE request hold exactly

@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -54,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "lsa_pack_blocks",
     "lsa_index_refresh_workspace",
     "lsa_index_refresh",
+    "lsa_query_latent",
     "lsa_gather_blocks",
     "lsa_gather_blocks_batch",
     "lsa_sparse_decode_workspace",
@@ -78,6 +79,16 @@ class RefreshArgs(Structure):
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("ev_begin", c_void_p), ("ev_end", c_void_p),
         ("table_out", c_void_p), ("table_slot_base", c_void_p),
+    ]
+
+
+class LatentArgs(Structure):
+    _fields_ = [
+        ("n_req", c_int32), ("d_model", c_int32), ("rank", c_int32), ("n_idx", c_int32),
+        ("dtype", c_int32), ("reserved0", c_int32),
+        ("hidden", c_void_p), ("hidden_req_stride", c_int64), ("hidden_idx_stride", c_int64),
+        ("w_down", c_void_p), ("latent", c_void_p),
+        ("ev_begin", c_void_p), ("ev_end", c_void_p),
     ]
 
 
@@ -129,6 +140,8 @@ def _load():
     lib.lsa_index_refresh_workspace.argtypes = [POINTER(RefreshArgs), POINTER(c_size_t)]
     lib.lsa_index_refresh.restype = c_int32
     lib.lsa_index_refresh.argtypes = [POINTER(RefreshArgs), c_void_p]
+    lib.lsa_query_latent.restype = c_int32
+    lib.lsa_query_latent.argtypes = [POINTER(LatentArgs), c_void_p]
     lib.lsa_gather_blocks.restype = c_int32
     lib.lsa_gather_blocks.argtypes = [POINTER(GatherArgs), c_void_p]
     lib.lsa_gather_blocks_batch.restype = c_int32
@@ -139,7 +152,7 @@ def _load():
     lib.lsa_sparse_decode.argtypes = [POINTER(DecodeArgs), c_void_p]
     if lib.lsa_abi_version() != ABI_VERSION:
         raise ImportError(f"liblsa.so ABI {lib.lsa_abi_version()} != binding ABI {ABI_VERSION}")
-    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs)):
+    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs, LatentArgs)):
         if lib.lsa_struct_size(i) != ctypes.sizeof(st):
             raise ImportError(f"{st.__name__}: binding layout {ctypes.sizeof(st)} B != library {lib.lsa_struct_size(i)} B")
     return lib
@@ -243,6 +256,30 @@ def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_of
     _check(LIB.lsa_index_refresh(ctypes.byref(a), _stream(stream)))
 
 
+def _latent_args(*, dtype, d_model, rank, n_idx, n_req, hidden, w_down, latent, hidden_req_stride=None,
+                 hidden_idx_stride=0, ev_begin=None, ev_end=None):
+    a = LatentArgs()
+    a.n_req = int(n_req)
+    a.d_model, a.rank, a.n_idx, a.dtype, a.reserved0 = int(d_model), int(rank), int(n_idx), _dtype_code(dtype), 0
+    a.hidden = _ptr(hidden)
+    a.hidden_req_stride = int(d_model if hidden_req_stride is None else hidden_req_stride)
+    a.hidden_idx_stride = int(hidden_idx_stride)
+    a.w_down, a.latent = _ptr(w_down), _ptr(latent)
+    a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
+    a.ev_end = ev_end.cuda_event if ev_end is not None else None
+    return a
+
+
+def lsa_query_latent(*, dtype, d_model, rank, n_idx, hidden, w_down, latent, n_req=None, hidden_req_stride=None,
+                     hidden_idx_stride=0, ev_begin=None, ev_end=None, stream=None) -> None:
+    """latent [n_req][n_idx][rank] = A_i h of every request and indexer (A = w_down [n_idx][rank][d_model])."""
+    a = _latent_args(dtype=dtype, d_model=d_model, rank=rank, n_idx=n_idx,
+                     n_req=n_req if n_req is not None else hidden.shape[0], hidden=hidden, w_down=w_down,
+                     latent=latent, hidden_req_stride=hidden_req_stride, hidden_idx_stride=hidden_idx_stride,
+                     ev_begin=ev_begin, ev_end=ev_end)
+    _check(LIB.lsa_query_latent(ctypes.byref(a), _stream(stream)))
+
+
 def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_ids, slot_of_block, free_slots,
                       n_free, capacity, stage, table_dev, stream=None):
     """Returns (n_copied, n_kept).  slot_of_block, free_slots, n_free: int32 NumPy arrays updated in place."""
@@ -308,4 +345,4 @@ def lsa_sparse_decode(*, dtype, n_heads, head_dim, win_cap, q, ring, out, worksp
 
 
 __all__ = [n for n in dir() if n.startswith("lsa_") or n.startswith("LSA_")] + [
-    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs"]
+    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs", "LatentArgs"]

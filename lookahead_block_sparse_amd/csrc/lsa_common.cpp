@@ -59,6 +59,7 @@ size_t lsa_struct_size(int32_t which) {
         case 0: return sizeof(lsa_refresh_args);
         case 1: return sizeof(lsa_gather_args);
         case 2: return sizeof(lsa_decode_args);
+        case 3: return sizeof(lsa_latent_args);
         default: return 0;
     }
 }

@@ -33,6 +33,7 @@ from . import (
     lsa_index_refresh,
     lsa_index_refresh_workspace,
     lsa_pack_blocks,
+    lsa_query_latent,
     lsa_sparse_decode,
     lsa_sparse_decode_workspace,
 )
@@ -56,9 +57,13 @@ class LSASession:
                  win_cap: int, n_blocks: Sequence[int], w_q: np.ndarray, keys: Sequence[np.ndarray],
                  capacity: Optional[Sequence[int]] = None, cold_on_device: bool = False,
                  with_masks: bool = False, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
-                 max_groups: int = 0, n_layers: int = 1):
+                 max_groups: int = 0, n_layers: int = 1, w_down: Optional[np.ndarray] = None):
         self.dtype = dtype
         self.n_idx, self.d_model, self.d_idx = n_idx, d_model, d_idx
+        # low-rank query projection: w_down = A [n_idx][rank][d_model], w_q = B [n_idx][d_idx][rank];
+        # every refresh first forms the latents c_i = A_i h, and the Query Encoder reads them
+        self.rank = int(w_down.shape[1]) if w_down is not None else 0
+        self.q_in = self.rank if self.rank else d_model
         self.n_heads, self.head_dim, self.win_cap = n_heads, head_dim, win_cap
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
@@ -79,6 +84,7 @@ class LSASession:
 
         with torch.cuda.stream(self.stream):
             self.w_q = _raw_tensor(w_q, self.device)
+            self.w_down = _raw_tensor(w_down, self.device) if w_down is not None else None
             self.keys = _raw_tensor(np.concatenate([np.ascontiguousarray(k).reshape(-1) for k in keys]), self.device)
             total_blocks = int(self.blk_off[-1])
             self.sel_ids = torch.zeros(total_blocks, dtype=torch.int32, device=self.device)
@@ -86,8 +92,10 @@ class LSASession:
             self.word_off = np.concatenate([[0], np.cumsum((self.n_blocks + 63) // 64)]).astype(np.int64)
             self.masks = (torch.zeros(int(self.word_off[-1]) * (n_idx + 1), dtype=torch.int64, device=self.device)
                           if with_masks else None)
-            ws = lsa_index_refresh_workspace(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx,
+            ws = lsa_index_refresh_workspace(dtype=dtype, d_model=self.q_in, d_idx=d_idx, n_idx=n_idx,
                                              blk_off=self.blk_off)
+            self.latent = (torch.empty((self.n_req, n_idx, self.rank), dtype=torch.int16 if dtype == "bf16"
+                                       else torch.float32, device=self.device) if self.rank else None)
             self.refresh_ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=self.device)
             self.sel_ids_h = torch.empty(total_blocks, dtype=torch.int32, pin_memory=True)
             self.sel_count_h = torch.empty(self.n_req, dtype=torch.int32, pin_memory=True)
@@ -163,7 +171,7 @@ class LSASession:
 
     # ---------------------------------------------------------------------------------------
     def refresh(self, reqs: Sequence[int], hidden: np.ndarray, bias: np.ndarray, ev_begin=None,
-                ev_end=None) -> Dict[int, np.ndarray]:
+                ev_end=None, ev_latent=(None, None)) -> Dict[int, np.ndarray]:
         """Index refresh for requests `reqs` (hidden [len][d_model] raw or a device tensor, bias
         [len][n_idx] float32 array or device tensor).
 
@@ -191,7 +199,7 @@ class LSASession:
                 i = j + 1
             if len(runs) == 1:
                 # the library times its own dispatch
-                self._refresh_run(reqs[0], reqs[-1] + 1, hid, bias_d, ev_begin, ev_end)
+                self._refresh_run(reqs[0], reqs[-1] + 1, hid, bias_d, ev_begin, ev_end, ev_latent=ev_latent)
             else:
                 if ev_begin is not None:
                     ev_begin.record(self.stream)
@@ -216,13 +224,23 @@ class LSASession:
         return out
 
     def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor, ev_begin=None,
-                     ev_end=None, table_out: bool = False) -> None:
+                     ev_end=None, table_out: bool = False, ev_latent=(None, None)) -> None:
         off = self.blk_off[r0:r1 + 1] - self.blk_off[r0]
+        stride = self.d_model
+        if self.rank:
+            # the latents of these requests, then the Query Encoder reads them in place of h
+            lat = self.latent[r0:r1]
+            lsa_query_latent(dtype=self.dtype, d_model=self.d_model, rank=self.rank, n_idx=self.n_idx,
+                             n_req=r1 - r0, hidden=hid, w_down=self.w_down, latent=lat, ev_begin=ev_latent[0],
+                             ev_end=ev_latent[1], stream=self.stream)
+            hid = lat
+            stride = self.n_idx * self.rank
         key_elem0 = int(self.n_idx * self.d_idx * self.blk_off[r0])
         masks = None
         if self.masks is not None:
             masks = self.masks[int(self.word_off[r0]) * (self.n_idx + 1):]
-        lsa_index_refresh(dtype=self.dtype, d_model=self.d_model, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
+        lsa_index_refresh(dtype=self.dtype, d_model=self.q_in, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
+                          hidden_req_stride=stride, hidden_idx_stride=self.rank,
                           w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
                           sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
                           workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,

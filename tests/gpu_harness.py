@@ -71,7 +71,7 @@ def make_session(wl, capacity=None, cold_on_device=False, with_masks=True, max_g
     sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, capacity=capacity, cold_on_device=cold_on_device,
-                      with_masks=with_masks, max_groups=max_groups)
+                      with_masks=with_masks, max_groups=max_groups, w_down=wl.w_down)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)

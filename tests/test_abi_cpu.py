@@ -31,7 +31,7 @@ def test_header_functions_are_exported():
 
 def test_abi_version_and_struct_sizes():
     assert L.LIB.lsa_abi_version() == L.ABI_VERSION
-    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs)):
+    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs, L.LatentArgs)):
         assert L.LIB.lsa_struct_size(i) == ctypes.sizeof(st)
     assert L.LIB.lsa_struct_size(7) == 0
 
@@ -84,6 +84,28 @@ def test_refresh_table_out_validation_before_any_hip_call():
     assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_WORKSPACE
     a.table_out = FAKE + 4                               # pairs must be 8-byte aligned
     assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(rank=1000), L.LSA_ERR_UNSUPPORTED),
+    (dict(rank=0), L.LSA_ERR_UNSUPPORTED),
+    (dict(d_model=4000), L.LSA_ERR_UNSUPPORTED),
+    (dict(n_idx=5), L.LSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.LSA_ERR_UNSUPPORTED),
+    (dict(n_req=0), L.LSA_ERR_INVALID),
+    (dict(n_req=65), L.LSA_ERR_INVALID),
+    (dict(hidden=None), L.LSA_ERR_INVALID),
+    (dict(latent=FAKE + 8), L.LSA_ERR_INVALID),
+    (dict(hidden_req_stride=100), L.LSA_ERR_INVALID),
+    (dict(hidden_idx_stride=-4096), L.LSA_ERR_INVALID),
+])
+def test_latent_validation_before_any_hip_call(over, status):
+    kw = dict(dtype="bf16", d_model=4096, rank=2048, n_idx=3, n_req=4, hidden=FAKE, w_down=FAKE, latent=FAKE,
+              hidden_req_stride=4096, hidden_idx_stride=0)
+    kw.update(over)
+    a = L._latent_args(**kw)
+    assert L.LIB.lsa_query_latent(ctypes.byref(a), None) == status
+    assert L.LIB.lsa_last_error().decode()
 
 
 def test_refresh_workspace_size():

@@ -1,0 +1,75 @@
+"""The low-rank query projection on the GPU: the latent kernel against the oracle's latent, and a
+decode loop whose refreshes go through the latent (selections bit for bit, outputs within the
+tolerance)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import ABS_TOL, REL_TOL, attention_errors, conditioned_workload, log, make_session, raw_to_torch, run_loop
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,d_model,rank,n_req,shared", [
+    ("bf16", 4096, 2048, 4, True), ("bf16", 1024, 512, 5, False), ("f32", 512, 256, 3, False)])
+def test_latent_matches_oracle(dtype, d_model, rank, n_req, shared):
+    """c_i = A_i h: bf16 latents are the oracle's (exact sum rounded to bfloat16) up to a rounding
+    decision taken on an fp32 sum instead of the exact one, i.e. equal or one bfloat16 unit
+    apart, and equal almost everywhere; fp32 latents agree to fp32 accumulation error."""
+    from lookahead_block_sparse_amd import lsa_query_latent
+    from workloads import bf16_bits_from_f32
+
+    log(f"latent {dtype} d_model {d_model} rank {rank} requests {n_req} shared hidden {shared}")
+    rng = np.random.default_rng(7)
+    n_idx = 3
+    a32 = (rng.standard_normal((n_idx, rank, d_model)) / np.sqrt(d_model)).astype(np.float32)
+    h32 = rng.standard_normal((n_req, 1 if shared else n_idx, d_model)).astype(np.float32)
+    enc = (lambda x: bf16_bits_from_f32(x)) if dtype == "bf16" else (lambda x: x)
+    a_raw, h_raw = enc(a32), enc(h32)
+    dev = torch.device("cuda")
+    st = torch.int16 if dtype == "bf16" else torch.float32
+    out = torch.empty((n_req, n_idx, rank), dtype=st, device=dev)
+    lsa_query_latent(dtype=dtype, d_model=d_model, rank=rank, n_idx=n_idx, n_req=n_req,
+                     hidden=raw_to_torch(h_raw, dev), w_down=raw_to_torch(a_raw, dev), latent=out,
+                     hidden_req_stride=h_raw.shape[1] * d_model, hidden_idx_stride=0 if shared else d_model)
+    got_raw = out.cpu().numpy()
+    got = oracle.decode_values(got_raw.view(np.uint16) if dtype == "bf16" else got_raw, dtype)
+    A = oracle.decode_values(a_raw, dtype)
+    for r in range(n_req):
+        h = oracle.decode_values(h_raw[r, 0] if shared else h_raw[r], dtype)
+        want = oracle.query_latent(h, A, dtype)
+        if dtype == "bf16":
+            ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), np.abs(got[r])))[1] - 8)
+            diff = np.abs(got[r] - want)
+            assert (diff <= ulp).all(), diff.max()
+            assert (diff == 0).mean() >= 0.999, (diff == 0).mean()
+        else:
+            exact = np.stack([A[i] @ (h if h.ndim == 1 else h[i]) for i in range(n_idx)])
+            assert np.allclose(got[r], want, rtol=1e-5, atol=1e-5 * np.abs(exact).max())
+
+
+@pytest.mark.parametrize("name", ["ctx128k_s", "ragged_s"])
+def test_lowrank_loop_matches_oracle(name):
+    """Every refresh of a low-rank workload (rank 512) selects the oracle's blocks, bit for bit, and
+    the attention outputs at sampled steps match the oracle."""
+    from workloads import get_config
+
+    cfg = get_config(name).scaled(q_rank=512, steps=70)
+    log(f"low-rank loop {name}, rank {cfg.q_rank}")
+    wl = conditioned_workload(cfg, seed=29)
+    sess = make_session(wl, with_masks=False)
+    assert sess.rank == 512
+    sample = [0, 63, 64, 69]
+    gpu, sels = run_loop(wl, sess, range(cfg.steps), record=sample)
+    refs, outs = oracle.simulate(wl, steps=sample)
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (name, r, k)
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
+    log(f"  {name}: {len(sels)} low-rank refreshes bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
