@@ -26,3 +26,4 @@ from .lsa_ref import (  # noqa: F401
     union,
     window_start,
 )
+from .denoise_ref import denoise_window, layer_softmax, top_p_set, vote  # noqa: F401,E402
