@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 6
+#define LSA_ABI_VERSION 7
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -66,7 +66,8 @@ const char* lsa_last_error(void);
 int32_t lsa_abi_version(void);
 
 /* sizeof the argument structs below, so a binding can check its own layout:
- * which = 0 refresh args, 1 gather args, 2 decode args, 3 latent args. Returns 0 for others. */
+ * which = 0 refresh args, 1 gather args, 2 decode args, 3 latent args, 4 denoise args.
+ * Returns 0 for others. */
 size_t lsa_struct_size(int32_t which);
 
 /* --------------------------------------------------------------------------------------
@@ -303,6 +304,45 @@ typedef struct lsa_decode_args {
 
 lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes);
 lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * (4) Label denoising for the indexer's training labels (zhichai.net explainer,
+ * section 3, the three-step pipeline).  For layer l and token window w with the raw
+ * indexer logits x[b] of its B_w history blocks:
+ *   p[b]      = softmax over the row's blocks
+ *   S[l][w]   = the smallest set of blocks whose probabilities sum to >= top_p:
+ *               blocks taken by decreasing logit (equal logits: increasing block id)
+ *               until the running sum reaches top_p
+ *   label[w]  = blocks kept by at least min_votes layers; naive[w] = kept by any layer
+ * Arithmetic: exp(x - max) in fp64, held as fixed point with 48 fraction bits, so
+ * every sum is exact and independent of order; "reaches top_p" is the integer test
+ * sum >= ceil(top_p * total).  Two launches on `stream`; validation happens first.
+ * Every output row has W = ceil(max_w B_w / 64) 64-bit words (block b of window w
+ * is bit b % 64 of word w*W + b/64; bits at b >= B_w are 0).
+ * ------------------------------------------------------------------------------------ */
+typedef struct lsa_denoise_args {
+    int32_t n_layers;          /* layers that vote (21 on the pages), 1..64 */
+    int32_t n_windows;         /* token windows, 1..65536 */
+    int32_t min_votes;         /* layers that must keep a block (3 on the pages), 1..n_layers */
+    int32_t reserved0;         /* must be 0 */
+    double top_p;              /* mass a layer's set reaches (0.6 on the pages), 0 < top_p <= 1 */
+    const float* logits;       /* dev [n_layers][n_windows][logit_stride] fp32, finite; row (l, w)
+                                  holds its B_w logits first (16-byte aligned) */
+    int64_t logit_stride;      /* elements between rows, >= max B_w, multiple of 4 */
+    const int32_t* n_blk;      /* host [n_windows]: B_w, 1..16384 */
+    const int32_t* n_blk_dev;  /* dev copy of n_blk */
+    uint64_t* layer_sets;      /* dev [n_layers][n_windows][W] or NULL (then kept in the workspace) */
+    uint64_t* labels;          /* dev [n_windows][W] */
+    int32_t* n_pos;            /* dev [n_windows]: labels per window */
+    int32_t* n_naive;          /* dev [n_windows] or NULL: blocks any layer keeps */
+    void* workspace;           /* dev, workspace_bytes >= lsa_label_denoise_workspace() */
+    size_t workspace_bytes;
+    hipEvent_t ev_begin;       /* optional, used only when both are set: they receive the start and */
+    hipEvent_t ev_end;         /* end time of the top-p kernel's dispatch (the vote is outside) */
+} lsa_denoise_args;
+
+lsa_status lsa_label_denoise_workspace(const lsa_denoise_args* a, size_t* bytes);
+lsa_status lsa_label_denoise(const lsa_denoise_args* a, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -59,6 +59,8 @@ EXPORTED_SYMBOLS = (
     "lsa_gather_blocks_batch",
     "lsa_sparse_decode_workspace",
     "lsa_sparse_decode",
+    "lsa_label_denoise_workspace",
+    "lsa_label_denoise",
 )
 
 
@@ -88,6 +90,16 @@ class LatentArgs(Structure):
         ("dtype", c_int32), ("reserved0", c_int32),
         ("hidden", c_void_p), ("hidden_req_stride", c_int64), ("hidden_idx_stride", c_int64),
         ("w_down", c_void_p), ("latent", c_void_p),
+        ("ev_begin", c_void_p), ("ev_end", c_void_p),
+    ]
+
+
+class DenoiseArgs(Structure):
+    _fields_ = [
+        ("n_layers", c_int32), ("n_windows", c_int32), ("min_votes", c_int32), ("reserved0", c_int32),
+        ("top_p", ctypes.c_double), ("logits", c_void_p), ("logit_stride", c_int64),
+        ("n_blk", c_void_p), ("n_blk_dev", c_void_p), ("layer_sets", c_void_p), ("labels", c_void_p),
+        ("n_pos", c_void_p), ("n_naive", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("ev_begin", c_void_p), ("ev_end", c_void_p),
     ]
 
@@ -142,6 +154,10 @@ def _load():
     lib.lsa_index_refresh.argtypes = [POINTER(RefreshArgs), c_void_p]
     lib.lsa_query_latent.restype = c_int32
     lib.lsa_query_latent.argtypes = [POINTER(LatentArgs), c_void_p]
+    lib.lsa_label_denoise_workspace.restype = c_int32
+    lib.lsa_label_denoise_workspace.argtypes = [POINTER(DenoiseArgs), POINTER(c_size_t)]
+    lib.lsa_label_denoise.restype = c_int32
+    lib.lsa_label_denoise.argtypes = [POINTER(DenoiseArgs), c_void_p]
     lib.lsa_gather_blocks.restype = c_int32
     lib.lsa_gather_blocks.argtypes = [POINTER(GatherArgs), c_void_p]
     lib.lsa_gather_blocks_batch.restype = c_int32
@@ -152,7 +168,7 @@ def _load():
     lib.lsa_sparse_decode.argtypes = [POINTER(DecodeArgs), c_void_p]
     if lib.lsa_abi_version() != ABI_VERSION:
         raise ImportError(f"liblsa.so ABI {lib.lsa_abi_version()} != binding ABI {ABI_VERSION}")
-    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs, LatentArgs)):
+    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs, LatentArgs, DenoiseArgs)):
         if lib.lsa_struct_size(i) != ctypes.sizeof(st):
             raise ImportError(f"{st.__name__}: binding layout {ctypes.sizeof(st)} B != library {lib.lsa_struct_size(i)} B")
     return lib
@@ -280,6 +296,42 @@ def lsa_query_latent(*, dtype, d_model, rank, n_idx, hidden, w_down, latent, n_r
     _check(LIB.lsa_query_latent(ctypes.byref(a), _stream(stream)))
 
 
+def _denoise_args(*, n_layers, n_blk, top_p, min_votes, logits=None, logit_stride=0, n_blk_dev=None,
+                  layer_sets=None, labels=None, n_pos=None, n_naive=None, workspace=None, ev_begin=None,
+                  ev_end=None):
+    nb = _i32(n_blk)
+    a = DenoiseArgs()
+    a.n_layers, a.n_windows, a.min_votes, a.reserved0 = int(n_layers), len(nb), int(min_votes), 0
+    a.top_p = float(top_p)
+    a.logits, a.logit_stride = _ptr(logits), int(logit_stride)
+    a.n_blk, a.n_blk_dev = nb.ctypes.data, _ptr(n_blk_dev)
+    a.layer_sets, a.labels, a.n_pos, a.n_naive = _ptr(layer_sets), _ptr(labels), _ptr(n_pos), _ptr(n_naive)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
+    a.ev_end = ev_end.cuda_event if ev_end is not None else None
+    return a, nb
+
+
+def lsa_label_denoise_workspace(*, n_layers, n_blk, top_p=0.6, min_votes=3, with_layer_sets=False) -> int:
+    a, keep = _denoise_args(n_layers=n_layers, n_blk=n_blk, top_p=top_p, min_votes=min_votes,
+                            logit_stride=int(np.max(n_blk)), layer_sets=1 if with_layer_sets else None)
+    out = c_size_t(0)
+    _check(LIB.lsa_label_denoise_workspace(ctypes.byref(a), ctypes.byref(out)))
+    return int(out.value)
+
+
+def lsa_label_denoise(*, logits, n_blk, n_blk_dev, labels, n_pos, top_p=0.6, min_votes=3, n_naive=None,
+                      layer_sets=None, workspace=None, ev_begin=None, ev_end=None, stream=None) -> None:
+    """Label denoising of logits [n_layers][n_windows][stride] (fp32 device tensor): per-layer top-p
+    sets, then the min_votes vote; labels [n_windows][W] int64 bit words, n_pos / n_naive [n_windows]."""
+    a, keep = _denoise_args(n_layers=logits.shape[0], n_blk=n_blk, top_p=top_p, min_votes=min_votes,
+                            logits=logits, logit_stride=logits.shape[2], n_blk_dev=n_blk_dev,
+                            layer_sets=layer_sets, labels=labels, n_pos=n_pos, n_naive=n_naive,
+                            workspace=workspace, ev_begin=ev_begin, ev_end=ev_end)
+    _check(LIB.lsa_label_denoise(ctypes.byref(a), _stream(stream)))
+
+
 def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_ids, slot_of_block, free_slots,
                       n_free, capacity, stage, table_dev, stream=None):
     """Returns (n_copied, n_kept).  slot_of_block, free_slots, n_free: int32 NumPy arrays updated in place."""
@@ -345,4 +397,4 @@ def lsa_sparse_decode(*, dtype, n_heads, head_dim, win_cap, q, ring, out, worksp
 
 
 __all__ = [n for n in dir() if n.startswith("lsa_") or n.startswith("LSA_")] + [
-    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs", "LatentArgs"]
+    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs", "LatentArgs", "DenoiseArgs"]

@@ -1,0 +1,307 @@
+// Label denoising of the indexer's training labels (zhichai.net explainer of "FlashMemory-DeepSeek-
+// V4", section 3 "Training the Indexer", the three-step pipeline): per CSA layer and token window,
+// softmax over the window's history blocks and the smallest set of blocks whose probability reaches
+// top_p; then, per window, the blocks at least min_votes layers keep.
+//
+// topp_kernel: one 512-thread group per (layer, window) row of up to 16,384 logits, held in
+// registers (32 per thread, block b = thread + 512 i).  exp(x - max) is taken in fp64 and held as
+// fixed point with 48 fraction bits, so the row's sums are exact and do not depend on the order of
+// the additions, and "the running sum reaches top_p" is the integer test sum >= ceil(top_p * total).
+// Blocks are ranked by logit through an order-preserving 32-bit key (equal logits by block id): a
+// 32-step bisection on the key finds the threshold K, the largest key whose blocks at or above it
+// carry the target; every block above K is kept, and of the blocks at K (equal logits, equal
+// probabilities) as many as the remaining mass needs, lowest ids first.
+// vote_kernel: one group per window, one wave per 64-block word: each lane counts its block's bit
+// over the layers and a ballot forms the label word.
+#include <hip/hip_ext.h>
+
+#include <cmath>
+
+#include "lsa_internal.hpp"
+
+namespace lsa {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kPer = 32;                      // logits per thread
+constexpr int kMaxBlocks = kThreads * kPer;   // 16,384 blocks per row
+constexpr int kVoteThreads = 256;
+
+struct TopPParams {
+    const float* logits;
+    long long stride;
+    const int* n_blk;
+    unsigned long long* sets;  // [n_layers][n_windows][words]
+    unsigned long long mant;   // top_p = mant * 2^-shift
+    int shift;
+    int n_windows, words;
+};
+
+struct VoteParams {
+    const unsigned long long* sets;
+    unsigned long long* labels;
+    int* n_pos;
+    int* n_naive;
+    int n_layers, n_windows, words, min_votes;
+};
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned lo = __shfl_xor((unsigned)v, o, 64), hi = __shfl_xor((unsigned)(v >> 32), o, 64);
+        v += ((unsigned long long)hi << 32) | lo;
+    }
+    return v;
+}
+
+// larger logit -> larger key; -0 is folded into +0 by the caller
+__device__ __forceinline__ unsigned order_key(float x) {
+    const unsigned u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(kThreads) void topp_kernel(TopPParams p) {
+    __shared__ unsigned long long s_red[2][kWaves];
+    __shared__ float s_max[kWaves];
+    __shared__ int s_cnt[kPer][kWaves];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x;  // layer * n_windows + window
+    const int n = p.n_blk[row % p.n_windows];
+    const float* x = p.logits + (size_t)row * p.stride;
+
+    int parity = 0;
+    // block-wide exact sum: two LDS buffers in turn, so one barrier per sum
+    auto block_sum = [&](unsigned long long v) {
+        v = wave_sum_u64(v);
+        if (lane == 0) s_red[parity][wave] = v;
+        __syncthreads();
+        unsigned long long t = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) t += s_red[parity][k];
+        parity ^= 1;
+        return t;
+    };
+
+    float xv[kPer];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = threadIdx.x + kThreads * i;
+        float v = b < n ? x[b] : -INFINITY;
+        if (v == 0.f) v = 0.f;  // -0 and +0 are the same logit
+        xv[i] = v;
+        mx = fmaxf(mx, v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) s_max[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) mx = fmaxf(mx, s_max[k]);
+
+    // probabilities up to the common factor 1/total: exp(x - max) in fp64, 48 fraction bits
+    unsigned long long e[kPer];
+    unsigned key[kPer];
+    unsigned long long part = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = threadIdx.x + kThreads * i;
+        if (b < n) {
+            e[i] = __double2ull_rn(ldexp(exp((double)xv[i] - (double)mx), 48));
+            key[i] = order_key(xv[i]);
+        } else {
+            e[i] = 0ull;
+            key[i] = 0u;  // below every real logit's key (-inf maps to 0x007fffff)
+        }
+        part += e[i];
+    }
+    const unsigned long long total = block_sum(part);
+    // target = ceil(top_p * total), exactly: top_p = mant / 2^shift
+    const unsigned __int128 prod = (unsigned __int128)p.mant * total;
+    const unsigned long long target =
+        (unsigned long long)((prod + (((unsigned __int128)1 << p.shift) - 1)) >> p.shift);
+
+    // the largest key K whose blocks at or above it carry at least the target
+    unsigned K = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const unsigned cand = K | (1u << bit);
+        unsigned long long s = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) s += key[i] >= cand ? e[i] : 0ull;
+        if (block_sum(s) >= target) K = cand;
+    }
+    // mass strictly above K, and the blocks at K (equal logits: equal probabilities)
+    unsigned long long above = 0, n_tie = 0, tie_sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        above += key[i] > K ? e[i] : 0ull;
+        n_tie += key[i] == K ? 1ull : 0ull;
+        tie_sum += key[i] == K ? e[i] : 0ull;
+    }
+    above = block_sum(above);
+    n_tie = block_sum(n_tie);
+    tie_sum = block_sum(tie_sum);
+    // the tied blocks share one logit, hence one value: the sum over them / their number is exact
+    const unsigned long long ek = tie_sum / n_tie;             // > 0: the tied blocks carry mass
+    const unsigned long long need = (target - above + ek - 1) / ek;  // tied blocks to keep, <= n_tie
+
+    // ranks of the tied blocks in block-id order (only when some of them stay out): tied blocks per
+    // (i, wave) slice, then an exclusive prefix over the slices in id order
+    const bool partial = need < n_tie;
+    if (partial) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const unsigned long long tb = __ballot(key[i] == K);
+            if (lane == 0) s_cnt[i][wave] = __popcll(tb);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int run = 0;
+            for (int i = 0; i < kPer; ++i)
+                for (int v = 0; v < kWaves; ++v) {
+                    const int c = s_cnt[i][v];
+                    s_cnt[i][v] = run;
+                    run += c;
+                }
+        }
+        __syncthreads();
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        bool keep = key[i] > K;
+        const unsigned long long tb = __ballot(key[i] == K);
+        if (key[i] == K)
+            keep = !partial || (unsigned long long)(s_cnt[i][wave] + __popcll(tb & below)) < need;
+        const unsigned long long bits = __ballot(keep);
+        const int word = kWaves * i + wave;
+        if (lane == 0 && word < p.words) p.sets[(size_t)row * p.words + word] = bits;
+    }
+}
+
+__global__ __launch_bounds__(kVoteThreads) void vote_kernel(VoteParams p) {
+    __shared__ int s_pos[kVoteThreads / 64], s_naive[kVoteThreads / 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int w = blockIdx.x;
+    int pos = 0, naive = 0;
+    for (int word = wave; word < p.words; word += kVoteThreads / 64) {
+        int cnt = 0;
+        unsigned long long any = 0ull;
+        for (int l = 0; l < p.n_layers; ++l) {
+            const unsigned long long bits = p.sets[((size_t)l * p.n_windows + w) * p.words + word];
+            cnt += (int)((bits >> lane) & 1ull);
+            any |= bits;
+        }
+        const unsigned long long lab = __ballot(cnt >= p.min_votes);
+        if (lane == 0) p.labels[(size_t)w * p.words + word] = lab;
+        pos += __popcll(lab);
+        naive += __popcll(any);
+    }
+    if (lane == 0) {
+        s_pos[wave] = pos;
+        s_naive[wave] = naive;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int a = 0, b = 0;
+        for (int k = 0; k < kVoteThreads / 64; ++k) {
+            a += s_pos[k];
+            b += s_naive[k];
+        }
+        p.n_pos[w] = a;
+        if (p.n_naive) p.n_naive[w] = b;
+    }
+}
+
+struct DenoisePlan {
+    int words = 0;
+    size_t sets_bytes = 0;
+};
+
+lsa_status denoise_plan(const lsa_denoise_args* a, DenoisePlan* P) {
+    LSA_CHECK_ARG(a != nullptr, "lsa_label_denoise: null args");
+    LSA_CHECK_ARG(a->n_layers >= 1 && a->n_layers <= 64, "lsa_label_denoise: n_layers=%d outside 1..64", a->n_layers);
+    LSA_CHECK_ARG(a->n_windows >= 1 && a->n_windows <= 65536, "lsa_label_denoise: n_windows=%d outside 1..65536",
+                  a->n_windows);
+    LSA_CHECK_ARG(a->min_votes >= 1 && a->min_votes <= a->n_layers, "lsa_label_denoise: min_votes=%d outside 1..%d",
+                  a->min_votes, a->n_layers);
+    LSA_CHECK_ARG(a->reserved0 == 0, "lsa_label_denoise: reserved0 must be 0");
+    LSA_CHECK_ARG(a->top_p > 0.0 && a->top_p <= 1.0 && a->top_p >= std::ldexp(1.0, -30),
+                  "lsa_label_denoise: top_p=%g outside [2^-30, 1]", a->top_p);
+    LSA_CHECK_ARG(a->n_blk != nullptr, "lsa_label_denoise: n_blk is null");
+    int mx = 0;
+    for (int w = 0; w < a->n_windows; ++w) {
+        LSA_CHECK_SUP(a->n_blk[w] >= 1 && a->n_blk[w] <= kMaxBlocks,
+                      "lsa_label_denoise: window %d has %d blocks (1..%d)", w, a->n_blk[w], kMaxBlocks);
+        mx = std::max(mx, a->n_blk[w]);
+    }
+    LSA_CHECK_ARG(a->logit_stride >= mx, "lsa_label_denoise: logit_stride=%lld < %d blocks",
+                  (long long)a->logit_stride, mx);
+    P->words = (mx + 63) / 64;
+    P->sets_bytes = (size_t)a->n_layers * a->n_windows * P->words * sizeof(unsigned long long);
+    return LSA_OK;
+}
+
+}  // namespace
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" lsa_status lsa_label_denoise_workspace(const lsa_denoise_args* a, size_t* bytes) {
+    DenoisePlan P;
+    lsa_status st = denoise_plan(a, &P);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(bytes != nullptr, "lsa_label_denoise_workspace: bytes is null");
+    *bytes = a->layer_sets ? 0 : P.sets_bytes;
+    return LSA_OK;
+}
+
+extern "C" lsa_status lsa_label_denoise(const lsa_denoise_args* a, hipStream_t stream) {
+    DenoisePlan P;
+    lsa_status st = denoise_plan(a, &P);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(a->logits && a->n_blk_dev && a->labels && a->n_pos, "lsa_label_denoise: null device pointer");
+    LSA_CHECK_ARG(((uintptr_t)a->logits % 4) == 0 && ((uintptr_t)a->labels % 8) == 0 &&
+                      (a->layer_sets == nullptr || ((uintptr_t)a->layer_sets % 8) == 0),
+                  "lsa_label_denoise: misaligned logits, labels or layer_sets");
+    unsigned long long* sets = reinterpret_cast<unsigned long long*>(a->layer_sets);
+    if (sets == nullptr) {
+        if (a->workspace == nullptr || a->workspace_bytes < P.sets_bytes)
+            return fail(LSA_ERR_WORKSPACE, "lsa_label_denoise: workspace of %zu bytes, need %zu",
+                        a->workspace ? a->workspace_bytes : (size_t)0, P.sets_bytes);
+        LSA_CHECK_ARG(((uintptr_t)a->workspace % 8) == 0, "lsa_label_denoise: misaligned workspace");
+        sets = static_cast<unsigned long long*>(a->workspace);
+    }
+    TopPParams tp;
+    tp.logits = a->logits;
+    tp.stride = a->logit_stride;
+    tp.n_blk = a->n_blk_dev;
+    tp.sets = sets;
+    int ex = 0;
+    const double f = std::frexp(a->top_p, &ex);  // top_p = f 2^ex, f in [0.5, 1)
+    tp.mant = (unsigned long long)std::ldexp(f, 53);
+    tp.shift = 53 - ex;
+    tp.n_windows = a->n_windows;
+    tp.words = P.words;
+    const dim3 grid(a->n_layers * a->n_windows), block(kThreads);
+    if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps
+        hipExtLaunchKernelGGL(topp_kernel, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, tp);
+    else
+        hipLaunchKernelGGL(topp_kernel, grid, block, 0, stream, tp);
+    LSA_HIP(hipGetLastError());
+    VoteParams vp;
+    vp.sets = sets;
+    vp.labels = reinterpret_cast<unsigned long long*>(a->labels);
+    vp.n_pos = a->n_pos;
+    vp.n_naive = a->n_naive;
+    vp.n_layers = a->n_layers;
+    vp.n_windows = a->n_windows;
+    vp.words = P.words;
+    vp.min_votes = a->min_votes;
+    hipLaunchKernelGGL(vote_kernel, dim3(a->n_windows), dim3(kVoteThreads), 0, stream, vp);
+    LSA_HIP(hipGetLastError());
+    return LSA_OK;
+}

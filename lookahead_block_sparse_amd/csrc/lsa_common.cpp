@@ -60,6 +60,7 @@ size_t lsa_struct_size(int32_t which) {
         case 1: return sizeof(lsa_gather_args);
         case 2: return sizeof(lsa_decode_args);
         case 3: return sizeof(lsa_latent_args);
+        case 4: return sizeof(lsa_denoise_args);
         default: return 0;
     }
 }

@@ -31,7 +31,7 @@ def test_header_functions_are_exported():
 
 def test_abi_version_and_struct_sizes():
     assert L.LIB.lsa_abi_version() == L.ABI_VERSION
-    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs, L.LatentArgs)):
+    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs, L.LatentArgs, L.DenoiseArgs)):
         assert L.LIB.lsa_struct_size(i) == ctypes.sizeof(st)
     assert L.LIB.lsa_struct_size(7) == 0
 
@@ -106,6 +106,36 @@ def test_latent_validation_before_any_hip_call(over, status):
     a = L._latent_args(**kw)
     assert L.LIB.lsa_query_latent(ctypes.byref(a), None) == status
     assert L.LIB.lsa_last_error().decode()
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_layers=0), L.LSA_ERR_INVALID),
+    (dict(n_layers=65), L.LSA_ERR_INVALID),
+    (dict(min_votes=0), L.LSA_ERR_INVALID),
+    (dict(min_votes=22), L.LSA_ERR_INVALID),
+    (dict(top_p=0.0), L.LSA_ERR_INVALID),
+    (dict(top_p=1.5), L.LSA_ERR_INVALID),
+    (dict(n_blk=[100, 0]), L.LSA_ERR_UNSUPPORTED),
+    (dict(n_blk=[100, 16385]), L.LSA_ERR_UNSUPPORTED),
+    (dict(logit_stride=99), L.LSA_ERR_INVALID),
+    (dict(logits=None), L.LSA_ERR_INVALID),
+    (dict(labels=FAKE + 4), L.LSA_ERR_INVALID),
+    (dict(workspace=None), L.LSA_ERR_WORKSPACE),
+])
+def test_denoise_validation_before_any_hip_call(over, status):
+    kw = dict(n_layers=21, n_blk=[100, 64], top_p=0.6, min_votes=3, logits=FAKE, logit_stride=100,
+              n_blk_dev=FAKE, labels=FAKE, n_pos=FAKE)
+    kw.update(over)
+    a, keep = L._denoise_args(**kw)
+    assert L.LIB.lsa_label_denoise(ctypes.byref(a), None) == status
+    assert L.LIB.lsa_last_error().decode()
+
+
+def test_denoise_workspace_size():
+    # layer sets: 21 layers x 3 windows x ceil(16384 / 64) words
+    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[16384, 100, 5000]) == 21 * 3 * 256 * 8
+    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[65, 64]) == 21 * 2 * 2 * 8
+    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[65, 64], with_layer_sets=True) == 0
 
 
 def test_refresh_workspace_size():

@@ -10,6 +10,7 @@ the needed functions in.  Both the oracle side (tests) and the GPU side
 """
 
 from .configs import CONFIGS, LSAConfig, get_config
+from .denoise import DenoiseWorkload, build_denoise_workload
 from .gen import (
     Workload,
     bf16_bits_from_f32,
@@ -19,6 +20,8 @@ from .gen import (
 
 __all__ = [
     "CONFIGS",
+    "DenoiseWorkload",
+    "build_denoise_workload",
     "LSAConfig",
     "get_config",
     "Workload",
