@@ -307,7 +307,7 @@ constexpr int kGroupsPerCU = 1;
 template <typename Ops, typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
     constexpr int DT = D / 16;
-    __shared__ float s_o[kWaves][kHeads][D];
+    __shared__ float s_o[kWaves][kHeads][D + 4];  // rows padded: 16-byte stores of a wave hit all banks
     __shared__ float s_m[kWaves][kHeads];
     __shared__ float s_l[kWaves][kHeads];
     __shared__ int2 s_ent[kStage];
@@ -466,34 +466,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
         }
 
         // ---- combine the waves of this segment ----
+        // the segment's maximum per head first; each wave then scales its own state to it, so the
+        // final reduction is a plain sum over the waves
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
-        if (lg == 0) {
-            s_m[wave][lr] = m_run;
-            s_l[wave][lr] = l_tot;
-        }
+        if (lg == 0) s_m[wave][lr] = m_run;
+        __syncthreads();
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v][lr]);
+        const float sc = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+        if (lg == 0) s_l[wave][lr] = sc * l_tot;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_o[wave][lr][16 * dt + 4 * lg + i] = o[dt][i];
+            *reinterpret_cast<float4*>(&s_o[wave][lr][16 * dt + 4 * lg]) =
+                make_float4(sc * o[dt][0], sc * o[dt][1], sc * o[dt][2], sc * o[dt][3]);
         __syncthreads();
         const int pidx = w + r;
         for (int e = threadIdx.x; e < kHeads * D; e += kThreads) {
             const int h = e / D, d = e % D;
-            float M = -INFINITY;
+            float acc = 0.f;
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v) M = fmaxf(M, s_m[v][h]);
-            float acc = 0.f, lsum = 0.f;
-#pragma unroll
-            for (int v = 0; v < kWaves; ++v) {
-                const float mv = s_m[v][h];
-                const float sc = mv == -INFINITY ? 0.f : fast_exp2(mv - M);
-                acc += sc * s_o[v][h][d];
-                lsum += sc * s_l[v][h];
-            }
+            for (int v = 0; v < kWaves; ++v) acc += s_o[v][h][d];
             p.part_o[((size_t)pidx * kHeads + h) * D + d] = acc;
             if (d == 0) {
-                p.part_ml[((size_t)pidx * kHeads + h) * 2 + 0] = M;
+                float Mh = -INFINITY, lsum = 0.f;
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    Mh = fmaxf(Mh, s_m[v][h]);
+                    lsum += s_l[v][h];
+                }
+                p.part_ml[((size_t)pidx * kHeads + h) * 2 + 0] = Mh;
                 p.part_ml[((size_t)pidx * kHeads + h) * 2 + 1] = lsum;
             }
         }
