@@ -316,7 +316,9 @@ lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream);
  *   label[w]  = blocks kept by at least min_votes layers; naive[w] = kept by any layer
  * Arithmetic: exp(x - max) in fp64, held as fixed point with 48 fraction bits, so
  * every sum is exact and independent of order; "reaches top_p" is the integer test
- * sum >= ceil(top_p * total).  Two launches on `stream`; validation happens first.
+ * sum >= ceil(top_p * total).  Three launches on `stream` (top-p, top-p for rows
+ * whose boundary falls in a run of > 1,024 equal-valued logits, vote); validation
+ * happens first.
  * Every output row has W = ceil(max_w B_w / 64) 64-bit words (block b of window w
  * is bit b % 64 of word w*W + b/64; bits at b >= B_w are 0).
  * ------------------------------------------------------------------------------------ */
@@ -335,10 +337,13 @@ typedef struct lsa_denoise_args {
     uint64_t* labels;          /* dev [n_windows][W] */
     int32_t* n_pos;            /* dev [n_windows]: labels per window */
     int32_t* n_naive;          /* dev [n_windows] or NULL: blocks any layer keeps */
-    void* workspace;           /* dev, workspace_bytes >= lsa_label_denoise_workspace() */
+    void* workspace;           /* dev, 8-byte aligned, workspace_bytes >= lsa_label_denoise_workspace()
+                                  (always needed: per-row flags, plus the layer sets when
+                                  layer_sets is NULL) */
     size_t workspace_bytes;
     hipEvent_t ev_begin;       /* optional, used only when both are set: they receive the start and */
-    hipEvent_t ev_end;         /* end time of the top-p kernel's dispatch (the vote is outside) */
+    hipEvent_t ev_end;         /* end time of the top-p kernel's dispatch (the rarely busy second
+                                  top-p pass for crowded rows and the vote are outside) */
 } lsa_denoise_args;
 
 lsa_status lsa_label_denoise_workspace(const lsa_denoise_args* a, size_t* bytes);

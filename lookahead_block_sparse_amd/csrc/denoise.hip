@@ -3,14 +3,18 @@
 // softmax over the window's history blocks and the smallest set of blocks whose probability reaches
 // top_p; then, per window, the blocks at least min_votes layers keep.
 //
-// topp_kernel: one 512-thread group per (layer, window) row of up to 16,384 logits, held in
-// registers (32 per thread, block b = thread + 512 i).  exp(x - max) is taken in fp64 and held as
+// topp_kernel: one 1,024-thread group per (layer, window) row of up to 16,384 logits, held in
+// registers (16 per thread, block b = thread + 1024 i).  exp(x - max) is taken in fp64 and held as
 // fixed point with 48 fraction bits, so the row's sums are exact and do not depend on the order of
 // the additions, and "the running sum reaches top_p" is the integer test sum >= ceil(top_p * total).
-// Blocks are ranked by logit through an order-preserving 32-bit key (equal logits by block id): a
-// 32-step bisection on the key finds the threshold K, the largest key whose blocks at or above it
-// carry the target; every block above K is kept, and of the blocks at K (equal logits, equal
-// probabilities) as many as the remaining mass needs, lowest ids first.
+// Blocks are ranked by logit, equal logits by block id.  One pass builds a histogram of the mass over
+// 2,048 logit buckets below the row's maximum (exact integer sums in LDS); a scan finds the bucket
+// where the running mass reaches the target; every block of the buckets above it is kept, and the
+// blocks of that bucket (usually a handful) are ranked against each other and walked in order until
+// the target is met.  A bucket of more than 1,024 blocks (long runs of equal logits) falls back to
+// a 32-step bisection on an order-preserving key: every block above the threshold key K is kept, and
+// of the blocks at K (equal logits, equal probabilities) as many as the remaining mass needs, lowest
+// ids first.
 // vote_kernel: one group per window, one wave per 64-block word: each lane counts its block's bit
 // over the layers and a ballot forms the label word.
 #include <hip/hip_ext.h>
@@ -22,17 +26,23 @@
 namespace lsa {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kPer = 32;                      // logits per thread
+constexpr int kPer = 16;                      // logits per thread
 constexpr int kMaxBlocks = kThreads * kPer;   // 16,384 blocks per row
 constexpr int kVoteThreads = 256;
+constexpr int kBuckets = 2048;   // logit buckets below the row maximum
+constexpr float kRange = 34.f;   // exp(-34) * 2^48 < 0.5: blocks further below the maximum carry no mass
+constexpr int kCand = 1024;      // largest boundary bucket ranked directly
+constexpr int kBisThreads = 512; // crowded rows: 32 logits per thread
+constexpr int kBisPer = 32;
 
 struct TopPParams {
     const float* logits;
     long long stride;
     const int* n_blk;
     unsigned long long* sets;  // [n_layers][n_windows][words]
+    int* crowded;              // [n_layers * n_windows]: 1 when the row's boundary bucket is crowded
     unsigned long long mant;   // top_p = mant * 2^-shift
     int shift;
     int n_windows, words;
@@ -62,6 +72,203 @@ __device__ __forceinline__ unsigned order_key(float x) {
 }
 
 __global__ __launch_bounds__(kThreads) void topp_kernel(TopPParams p) {
+    __shared__ unsigned long long s_red[2][kWaves];
+    __shared__ float s_max[kWaves];
+    __shared__ unsigned long long s_hmass[kBuckets];
+    __shared__ unsigned s_hcnt[kBuckets];
+    __shared__ unsigned s_ck[kCand];
+    __shared__ int s_cid[kCand];
+    __shared__ unsigned long long s_ce[kCand];
+    __shared__ unsigned long long s_se[kCand];
+    __shared__ unsigned long long s_wsum[kWaves];
+    __shared__ int s_bstar, s_pstar;
+    __shared__ unsigned long long s_before;
+    __shared__ unsigned s_nc;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x;  // layer * n_windows + window
+    const int n = p.n_blk[row % p.n_windows];
+    const float* x = p.logits + (size_t)row * p.stride;
+
+    int parity = 0;
+    // block-wide exact sum: two LDS buffers in turn, so one barrier per sum
+    auto block_sum = [&](unsigned long long v) {
+        v = wave_sum_u64(v);
+        if (lane == 0) s_red[parity][wave] = v;
+        __syncthreads();
+        unsigned long long t = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) t += s_red[parity][k];
+        parity ^= 1;
+        return t;
+    };
+
+    float xv[kPer];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = threadIdx.x + kThreads * i;
+        float v = b < n ? x[b] : -INFINITY;
+        if (v == 0.f) v = 0.f;  // -0 and +0 are the same logit
+        xv[i] = v;
+        mx = fmaxf(mx, v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) s_max[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) mx = fmaxf(mx, s_max[k]);
+
+    // probabilities up to the common factor 1/total: exp(x - max) in fp64, 48 fraction bits
+    unsigned long long e[kPer];
+    unsigned long long part = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = threadIdx.x + kThreads * i;
+        e[i] = b < n ? __double2ull_rn(ldexp(exp((double)xv[i] - (double)mx), 48)) : 0ull;
+        part += e[i];
+    }
+    const unsigned long long total = block_sum(part);
+    // target = ceil(top_p * total), exactly: top_p = mant / 2^shift
+    const unsigned __int128 prod = (unsigned __int128)p.mant * total;
+    const unsigned long long target =
+        (unsigned long long)((prod + (((unsigned __int128)1 << p.shift) - 1)) >> p.shift);
+
+    // order-preserving key of element i (recomputed, not kept: registers are short); blocks past the
+    // row's end get 0, below every real logit's key (-inf maps to 0x007fffff)
+    auto key_of = [&](int i) { return threadIdx.x + kThreads * i < n ? order_key(xv[i]) : 0u; };
+
+    // ---- mass histogram over logit buckets below the maximum (exact sums: integer LDS atomics) ----
+    for (int k = threadIdx.x; k < kBuckets; k += kThreads) {
+        s_hmass[k] = 0ull;
+        s_hcnt[k] = 0u;
+    }
+    if (threadIdx.x == 0) s_nc = 0u;
+    __syncthreads();
+    // monotone in the logit (one fp32 subtraction and product): equal logits share a bucket and a
+    // higher logit never lands in a later bucket
+    auto bucket_of = [&](float v) {
+        const float d = (mx - v) * ((float)kBuckets / kRange);
+        return d >= (float)(kBuckets - 1) ? kBuckets - 1 : (int)d;
+    };
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int b = threadIdx.x + kThreads * i;
+        if (b < n) {
+            const int k = bucket_of(xv[i]);
+            atomicAdd(&s_hmass[k], e[i]);
+            atomicAdd(&s_hcnt[k], 1u);
+        }
+    }
+    __syncthreads();
+    // the bucket where the running mass (highest logits first) reaches the target: thread t owns
+    // buckets kPerT t .. kPerT t + kPerT - 1; an exclusive scan of the owners' sums locates it
+    {
+        constexpr int kPerT = kBuckets / kThreads;
+        unsigned long long own = 0;
+#pragma unroll
+        for (int q = 0; q < kPerT; ++q) own += s_hmass[kPerT * threadIdx.x + q];
+        unsigned long long inc = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned lo = __shfl_up((unsigned)inc, o, 64), hi = __shfl_up((unsigned)(inc >> 32), o, 64);
+            if (lane >= o) inc += ((unsigned long long)hi << 32) | lo;
+        }
+        if (lane == 63) s_wsum[wave] = inc;
+        __syncthreads();
+        unsigned long long run = inc - own;
+        for (int v = 0; v < wave; ++v) run += s_wsum[v];
+#pragma unroll
+        for (int q = 0; q < kPerT; ++q) {
+            const int k = kPerT * threadIdx.x + q;
+            const unsigned long long m = s_hmass[k];
+            if (run < target && run + m >= target) {
+                s_bstar = k;
+                s_before = run;
+            }
+            run += m;
+        }
+        __syncthreads();
+    }
+    const int bstar = s_bstar;
+    const unsigned cb = s_hcnt[bstar];
+    if (cb > (unsigned)kCand) {  // long runs of equal logits: topp_bisect_kernel takes the row
+        if (threadIdx.x == 0) p.crowded[row] = 1;
+        return;
+    }
+    if (threadIdx.x == 0) p.crowded[row] = 0;
+    int pstar = 0;
+    {
+        // the boundary bucket's blocks, ranked by (logit desc, id asc), walked until the target
+        const unsigned long long need_b = target - s_before;  // > 0, <= the bucket's mass
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int b = threadIdx.x + kThreads * i;
+            if (b < n && bucket_of(xv[i]) == bstar) {
+                const unsigned pos = atomicAdd(&s_nc, 1u);
+                s_ck[pos] = key_of(i);
+                s_cid[pos] = b;
+                s_ce[pos] = e[i];
+            }
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < (int)cb; c += kThreads) {
+            const unsigned kc = s_ck[c];
+            const int ic = s_cid[c];
+            int rank = 0;
+            for (int q = 0; q < (int)cb; ++q) rank += (s_ck[q] > kc || (s_ck[q] == kc && s_cid[q] < ic)) ? 1 : 0;
+            s_se[rank] = s_ce[c];
+        }
+        __syncthreads();
+        // first rank whose running mass reaches need_b: thread t owns ranks 2t, 2t+1
+        const int r0 = 2 * threadIdx.x;
+        const unsigned long long a0 = r0 < (int)cb ? s_se[r0] : 0ull, a1 = r0 + 1 < (int)cb ? s_se[r0 + 1] : 0ull;
+        const unsigned long long own = a0 + a1;
+        unsigned long long inc = own;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned lo = __shfl_up((unsigned)inc, o, 64), hi = __shfl_up((unsigned)(inc >> 32), o, 64);
+            if (lane >= o) inc += ((unsigned long long)hi << 32) | lo;
+        }
+        __syncthreads();  // every thread is done reading s_wsum of the bucket scan
+        if (lane == 63) s_wsum[wave] = inc;
+        __syncthreads();
+        unsigned long long run = inc - own;
+        for (int v = 0; v < wave; ++v) run += s_wsum[v];
+        if (r0 < (int)cb) {
+            if (run < need_b && run + a0 >= need_b) s_pstar = r0;
+            else if (r0 + 1 < (int)cb && run + a0 < need_b && run + a0 + a1 >= need_b) s_pstar = r0 + 1;
+        }
+        __syncthreads();
+        pstar = s_pstar;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int b = threadIdx.x + kThreads * i;
+            bool keep = false;
+            if (b < n) {
+                const int k = bucket_of(xv[i]);
+                if (k < bstar) {
+                    keep = true;
+                } else if (k == bstar) {
+                    int rank = 0;
+                    for (int q = 0; q < (int)cb; ++q)
+                        rank += (s_ck[q] > key_of(i) || (s_ck[q] == key_of(i) && s_cid[q] < b)) ? 1 : 0;
+                    keep = rank <= pstar;
+                }
+            }
+            const unsigned long long bits = __ballot(keep);
+            const int word = kWaves * i + wave;
+            if (lane == 0 && word < p.words) p.sets[(size_t)row * p.words + word] = bits;
+        }
+    }
+}
+
+
+// Rows whose boundary bucket is crowded (flagged by topp_kernel): a 32-step bisection on the key.
+__global__ __launch_bounds__(kBisThreads) void topp_bisect_kernel(TopPParams p) {
+    if (p.crowded[blockIdx.x] == 0) return;
+    constexpr int kThreads = kBisThreads, kWaves = kBisThreads / 64, kPer = kBisPer;
     __shared__ unsigned long long s_red[2][kWaves];
     __shared__ float s_max[kWaves];
     __shared__ int s_cnt[kPer][kWaves];
@@ -218,7 +425,9 @@ __global__ __launch_bounds__(kVoteThreads) void vote_kernel(VoteParams p) {
 
 struct DenoisePlan {
     int words = 0;
-    size_t sets_bytes = 0;
+    size_t sets_bytes = 0;   // layer sets, when the caller does not take them
+    size_t flags_off = 0;    // crowded-row flags in the workspace
+    size_t total = 0;        // workspace bytes
 };
 
 lsa_status denoise_plan(const lsa_denoise_args* a, DenoisePlan* P) {
@@ -242,6 +451,8 @@ lsa_status denoise_plan(const lsa_denoise_args* a, DenoisePlan* P) {
                   (long long)a->logit_stride, mx);
     P->words = (mx + 63) / 64;
     P->sets_bytes = (size_t)a->n_layers * a->n_windows * P->words * sizeof(unsigned long long);
+    P->flags_off = a->layer_sets ? 0 : align_up(P->sets_bytes, 256);
+    P->total = P->flags_off + (size_t)a->n_layers * a->n_windows * sizeof(int);
     return LSA_OK;
 }
 
@@ -255,7 +466,7 @@ extern "C" lsa_status lsa_label_denoise_workspace(const lsa_denoise_args* a, siz
     lsa_status st = denoise_plan(a, &P);
     if (st != LSA_OK) return st;
     LSA_CHECK_ARG(bytes != nullptr, "lsa_label_denoise_workspace: bytes is null");
-    *bytes = a->layer_sets ? 0 : P.sets_bytes;
+    *bytes = P.total;
     return LSA_OK;
 }
 
@@ -267,19 +478,18 @@ extern "C" lsa_status lsa_label_denoise(const lsa_denoise_args* a, hipStream_t s
     LSA_CHECK_ARG(((uintptr_t)a->logits % 4) == 0 && ((uintptr_t)a->labels % 8) == 0 &&
                       (a->layer_sets == nullptr || ((uintptr_t)a->layer_sets % 8) == 0),
                   "lsa_label_denoise: misaligned logits, labels or layer_sets");
+    if (a->workspace == nullptr || a->workspace_bytes < P.total)
+        return fail(LSA_ERR_WORKSPACE, "lsa_label_denoise: workspace of %zu bytes, need %zu",
+                    a->workspace ? a->workspace_bytes : (size_t)0, P.total);
+    LSA_CHECK_ARG(((uintptr_t)a->workspace % 8) == 0, "lsa_label_denoise: misaligned workspace");
     unsigned long long* sets = reinterpret_cast<unsigned long long*>(a->layer_sets);
-    if (sets == nullptr) {
-        if (a->workspace == nullptr || a->workspace_bytes < P.sets_bytes)
-            return fail(LSA_ERR_WORKSPACE, "lsa_label_denoise: workspace of %zu bytes, need %zu",
-                        a->workspace ? a->workspace_bytes : (size_t)0, P.sets_bytes);
-        LSA_CHECK_ARG(((uintptr_t)a->workspace % 8) == 0, "lsa_label_denoise: misaligned workspace");
-        sets = static_cast<unsigned long long*>(a->workspace);
-    }
+    if (sets == nullptr) sets = static_cast<unsigned long long*>(a->workspace);
     TopPParams tp;
     tp.logits = a->logits;
     tp.stride = a->logit_stride;
     tp.n_blk = a->n_blk_dev;
     tp.sets = sets;
+    tp.crowded = reinterpret_cast<int*>(static_cast<char*>(a->workspace) + P.flags_off);
     int ex = 0;
     const double f = std::frexp(a->top_p, &ex);  // top_p = f 2^ex, f in [0.5, 1)
     tp.mant = (unsigned long long)std::ldexp(f, 53);
@@ -291,6 +501,8 @@ extern "C" lsa_status lsa_label_denoise(const lsa_denoise_args* a, hipStream_t s
         hipExtLaunchKernelGGL(topp_kernel, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, tp);
     else
         hipLaunchKernelGGL(topp_kernel, grid, block, 0, stream, tp);
+    LSA_HIP(hipGetLastError());
+    hipLaunchKernelGGL(topp_bisect_kernel, grid, dim3(kBisThreads), 0, stream, tp);
     LSA_HIP(hipGetLastError());
     VoteParams vp;
     vp.sets = sets;

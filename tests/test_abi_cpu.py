@@ -132,10 +132,12 @@ def test_denoise_validation_before_any_hip_call(over, status):
 
 
 def test_denoise_workspace_size():
-    # layer sets: 21 layers x 3 windows x ceil(16384 / 64) words
-    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[16384, 100, 5000]) == 21 * 3 * 256 * 8
-    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[65, 64]) == 21 * 2 * 2 * 8
-    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[65, 64], with_layer_sets=True) == 0
+    # layer sets (21 layers x windows x ceil(max blocks / 64) words, 256-byte aligned) + one int flag per row
+    def al(x):
+        return (x + 255) // 256 * 256
+    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[16384, 100, 5000]) == al(21 * 3 * 256 * 8) + 21 * 3 * 4
+    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[65, 64]) == al(21 * 2 * 2 * 8) + 21 * 2 * 4
+    assert L.lsa_label_denoise_workspace(n_layers=21, n_blk=[65, 64], with_layer_sets=True) == 21 * 2 * 4
 
 
 def test_refresh_workspace_size():

@@ -33,7 +33,7 @@ def _run(dw, top_p, min_votes, with_sets=True):
     sets = torch.full((L_, W, words), -1, dtype=torch.int64, device=dev) if with_sets else None
     ws_bytes = lsa_label_denoise_workspace(n_layers=L_, n_blk=dw.n_blk, top_p=top_p, min_votes=min_votes,
                                            with_layer_sets=with_sets)
-    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device=dev)
     lsa_label_denoise(logits=logits, n_blk=dw.n_blk, n_blk_dev=n_blk_dev, labels=labels, n_pos=n_pos,
                       top_p=top_p, min_votes=min_votes, n_naive=n_naive, layer_sets=sets, workspace=ws)
     torch.cuda.synchronize()
