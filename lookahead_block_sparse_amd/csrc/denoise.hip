@@ -15,8 +15,8 @@
 // a 32-step bisection on an order-preserving key: every block above the threshold key K is kept, and
 // of the blocks at K (equal logits, equal probabilities) as many as the remaining mass needs, lowest
 // ids first.
-// vote_kernel: one group per window, one wave per 64-block word: each lane counts its block's bit
-// over the layers and a ballot forms the label word.
+// vote_kernel: one group per window, one wave per 64-block word at a time: each lane counts its
+// block's bit over the layers and a ballot forms the label word.
 #include <hip/hip_ext.h>
 
 #include <cmath>
@@ -30,7 +30,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 16;                      // logits per thread
 constexpr int kMaxBlocks = kThreads * kPer;   // 16,384 blocks per row
-constexpr int kVoteThreads = 256;
+constexpr int kVoteThreads = 1024;
 constexpr int kBuckets = 2048;   // logit buckets below the row maximum
 constexpr float kRange = 34.f;   // exp(-34) * 2^48 < 0.5: blocks further below the maximum carry no mass
 constexpr int kCand = 1024;      // largest boundary bucket ranked directly
@@ -71,7 +71,7 @@ __device__ __forceinline__ unsigned order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(kThreads) void topp_kernel(TopPParams p) {
+__global__ __launch_bounds__(kThreads, 8) void topp_kernel(TopPParams p) {
     __shared__ unsigned long long s_red[2][kWaves];
     __shared__ float s_max[kWaves];
     __shared__ unsigned long long s_hmass[kBuckets];
@@ -120,20 +120,9 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(TopPParams p) {
 #pragma unroll
     for (int k = 0; k < kWaves; ++k) mx = fmaxf(mx, s_max[k]);
 
-    // probabilities up to the common factor 1/total: exp(x - max) in fp64, 48 fraction bits
-    unsigned long long e[kPer];
-    unsigned long long part = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int b = threadIdx.x + kThreads * i;
-        e[i] = b < n ? __double2ull_rn(ldexp(exp((double)xv[i] - (double)mx), 48)) : 0ull;
-        part += e[i];
-    }
-    const unsigned long long total = block_sum(part);
-    // target = ceil(top_p * total), exactly: top_p = mant / 2^shift
-    const unsigned __int128 prod = (unsigned __int128)p.mant * total;
-    const unsigned long long target =
-        (unsigned long long)((prod + (((unsigned __int128)1 << p.shift) - 1)) >> p.shift);
+    // probabilities up to the common factor 1/total: exp(x - max) in fp64, 48 fraction bits (not
+    // kept: the histogram pass uses each once, the boundary bucket's blocks recompute theirs)
+    auto fixed_e = [&](float v) { return __double2ull_rn(ldexp(exp((double)v - (double)mx), 48)); };
 
     // order-preserving key of element i (recomputed, not kept: registers are short); blocks past the
     // row's end get 0, below every real logit's key (-inf maps to 0x007fffff)
@@ -152,16 +141,23 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(TopPParams p) {
         const float d = (mx - v) * ((float)kBuckets / kRange);
         return d >= (float)(kBuckets - 1) ? kBuckets - 1 : (int)d;
     };
+    unsigned long long part = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int b = threadIdx.x + kThreads * i;
         if (b < n) {
+            const unsigned long long e = fixed_e(xv[i]);
             const int k = bucket_of(xv[i]);
-            atomicAdd(&s_hmass[k], e[i]);
+            atomicAdd(&s_hmass[k], e);
             atomicAdd(&s_hcnt[k], 1u);
+            part += e;
         }
     }
-    __syncthreads();
+    const unsigned long long total = block_sum(part);  // its barrier also completes the histogram
+    // target = ceil(top_p * total), exactly: top_p = mant / 2^shift
+    const unsigned __int128 prod = (unsigned __int128)p.mant * total;
+    const unsigned long long target =
+        (unsigned long long)((prod + (((unsigned __int128)1 << p.shift) - 1)) >> p.shift);
     // the bucket where the running mass (highest logits first) reaches the target: thread t owns
     // buckets kPerT t .. kPerT t + kPerT - 1; an exclusive scan of the owners' sums locates it
     {
@@ -209,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void topp_kernel(TopPParams p) {
                 const unsigned pos = atomicAdd(&s_nc, 1u);
                 s_ck[pos] = key_of(i);
                 s_cid[pos] = b;
-                s_ce[pos] = e[i];
+                s_ce[pos] = fixed_e(xv[i]);
             }
         }
         __syncthreads();
@@ -388,6 +384,10 @@ __global__ __launch_bounds__(kBisThreads) void topp_bisect_kernel(TopPParams p) 
     }
 }
 
+// One group per window, one wave per 64-block word of it at a time: lane l < n_layers loads layer
+// l's word (one load per lane, all in flight together); each word is then broadcast from its lane and
+// every lane counts its own block's bit.  The window's counts are reduced in LDS (no atomics: the
+// counters of all windows share a few cache lines, where device atomics serialize).
 __global__ __launch_bounds__(kVoteThreads) void vote_kernel(VoteParams p) {
     __shared__ int s_pos[kVoteThreads / 64], s_naive[kVoteThreads / 64];
     const int lane = threadIdx.x & 63;
@@ -395,10 +395,15 @@ __global__ __launch_bounds__(kVoteThreads) void vote_kernel(VoteParams p) {
     const int w = blockIdx.x;
     int pos = 0, naive = 0;
     for (int word = wave; word < p.words; word += kVoteThreads / 64) {
+        const unsigned long long mine =
+            lane < p.n_layers ? p.sets[((size_t)lane * p.n_windows + w) * p.words + word] : 0ull;
+        const unsigned lo = (unsigned)mine, hi = (unsigned)(mine >> 32);
         int cnt = 0;
         unsigned long long any = 0ull;
         for (int l = 0; l < p.n_layers; ++l) {
-            const unsigned long long bits = p.sets[((size_t)l * p.n_windows + w) * p.words + word];
+            const unsigned long long bits =
+                ((unsigned long long)(unsigned)__builtin_amdgcn_readlane(hi, l) << 32) |
+                (unsigned)__builtin_amdgcn_readlane(lo, l);
             cnt += (int)((bits >> lane) & 1ull);
             any |= bits;
         }
