@@ -15,8 +15,8 @@
 // a 32-step bisection on an order-preserving key: every block above the threshold key K is kept, and
 // of the blocks at K (equal logits, equal probabilities) as many as the remaining mass needs, lowest
 // ids first.
-// vote_kernel: one group per window, one wave per 64-block word at a time: each lane counts its
-// block's bit over the layers and a ballot forms the label word.
+// vote_kernel: one group per window, one lane per 64-block word: a bit-sliced count of the layers'
+// words, compared with min_votes bit by bit.
 #include <hip/hip_ext.h>
 
 #include <cmath>
@@ -30,7 +30,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 16;                      // logits per thread
 constexpr int kMaxBlocks = kThreads * kPer;   // 16,384 blocks per row
-constexpr int kVoteThreads = 1024;
+constexpr int kVoteThreads = 256;
 constexpr int kBuckets = 2048;   // logit buckets below the row maximum
 constexpr float kRange = 34.f;   // exp(-34) * 2^48 < 0.5: blocks further below the maximum carry no mass
 constexpr int kCand = 1024;      // largest boundary bucket ranked directly
@@ -384,33 +384,49 @@ __global__ __launch_bounds__(kBisThreads) void topp_bisect_kernel(TopPParams p) 
     }
 }
 
-// One group per window, one wave per 64-block word of it at a time: lane l < n_layers loads layer
-// l's word (one load per lane, all in flight together); each word is then broadcast from its lane and
-// every lane counts its own block's bit.  The window's counts are reduced in LDS (no atomics: the
-// counters of all windows share a few cache lines, where device atomics serialize).
+// One group per window, one lane per 64-block word of it: the lane adds its word of every layer into
+// a bit-sliced counter (bit b of plane c[k] is bit k of block b's count; ripple-carry adds of one-bit
+// values, 7 planes count up to 64 layers), then compares the counts with min_votes plane by plane.
+// Loads of consecutive lanes are consecutive words (coalesced); the window's counts are reduced in
+// LDS (no atomics: the counters of all windows share a few cache lines, where device atomics
+// serialize).
 __global__ __launch_bounds__(kVoteThreads) void vote_kernel(VoteParams p) {
     __shared__ int s_pos[kVoteThreads / 64], s_naive[kVoteThreads / 64];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int w = blockIdx.x;
     int pos = 0, naive = 0;
-    for (int word = wave; word < p.words; word += kVoteThreads / 64) {
-        const unsigned long long mine =
-            lane < p.n_layers ? p.sets[((size_t)lane * p.n_windows + w) * p.words + word] : 0ull;
-        const unsigned lo = (unsigned)mine, hi = (unsigned)(mine >> 32);
-        int cnt = 0;
+    for (int word = threadIdx.x; word < p.words; word += kVoteThreads) {
+        unsigned long long c[7] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
         unsigned long long any = 0ull;
         for (int l = 0; l < p.n_layers; ++l) {
-            const unsigned long long bits =
-                ((unsigned long long)(unsigned)__builtin_amdgcn_readlane(hi, l) << 32) |
-                (unsigned)__builtin_amdgcn_readlane(lo, l);
-            cnt += (int)((bits >> lane) & 1ull);
-            any |= bits;
+            const unsigned long long x = p.sets[((size_t)l * p.n_windows + w) * p.words + word];
+            any |= x;
+            unsigned long long carry = x;
+#pragma unroll
+            for (int k = 0; k < 7; ++k) {
+                const unsigned long long t = c[k] & carry;
+                c[k] ^= carry;
+                carry = t;
+            }
         }
-        const unsigned long long lab = __ballot(cnt >= p.min_votes);
-        if (lane == 0) p.labels[(size_t)w * p.words + word] = lab;
+        // count >= min_votes, per bit, from the most significant plane down
+        unsigned long long gt = 0ull, eq = ~0ull;
+#pragma unroll
+        for (int k = 6; k >= 0; --k) {
+            const unsigned long long mk = ((p.min_votes >> k) & 1) ? ~0ull : 0ull;
+            gt |= eq & c[k] & ~mk;
+            eq &= ~(c[k] ^ mk);
+        }
+        const unsigned long long lab = gt | eq;
+        p.labels[(size_t)w * p.words + word] = lab;
         pos += __popcll(lab);
         naive += __popcll(any);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        pos += __shfl_xor(pos, o, 64);
+        naive += __shfl_xor(naive, o, 64);
     }
     if (lane == 0) {
         s_pos[wave] = pos;
