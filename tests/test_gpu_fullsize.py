@@ -80,3 +80,68 @@ def test_full_size_loop_matches_oracle(name, steps):
     log(f"  {name}: {n_ref} selections bit-exact; attention max abs {worst[0]:.3e} rel {worst[1]:.3e} "
         f"l2 {worst[2]:.3e}")
     assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+def test_full_size_lowrank_matches_oracle():
+    """4 x 1M context with the rank-2048 query projection, as bench.py --q-rank 2048 runs it: every
+    refresh bit-exact, sampled outputs within tolerance."""
+    from workloads import get_config
+
+    cfg = get_config("ctx1m").scaled(q_rank=2048, steps=130)
+    wl = conditioned_workload(cfg, seed=12)
+    sample = [64, 129]
+    log(f"full size low-rank ctx1m: rank {cfg.q_rank}, {cfg.steps} steps, sampled {sample}")
+    sess = make_session(wl, cold_on_device=True, with_masks=False)
+    assert sess.rank == 2048
+    gpu, sels = _run_bench_style(wl, sess, set(sample))
+    refs, outs = oracle.simulate(wl, steps=sample)
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (r, k, len(ids), len(refs[r][k].ids))
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
+    log(f"  low-rank ctx1m: {len(sels)} selections bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+def test_full_size_reactive_matches_oracle():
+    """4 x 1M context through the reactive comparator as bench.py --reactive runs it (every block
+    resident, a refresh at every step writing the block table, device-side counts): six steps, every
+    selection bit-exact, outputs of the first and last step within tolerance."""
+    from lookahead_block_sparse_amd.session import ResidentLoop
+    from workloads import get_config
+
+    steps = 6
+    cfg = get_config("ctx1m").scaled(tau=1, steps=steps, staggered=False)
+    wl = conditioned_workload(cfg, seed=13)
+    R = wl.n_req
+    log(f"full size reactive ctx1m: {steps} steps")
+    sess = make_session(wl, cold_on_device=True, with_masks=False)
+    sess.make_resident()
+    dev = sess.device
+    out = torch.empty((R, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    loop = ResidentLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), out)
+    bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+    sels, gpu = {}, {}
+    for t in range(steps):
+        hid = raw_to_torch(np.stack([wl.hidden[r][wl.refresh_index_at(r, t)] for r in range(R)]), dev)
+        loop.step(t, hid, bias, raw_to_torch(wl.q_dec[t], dev), raw_to_torch(wl.k_new[t], dev),
+                  raw_to_torch(wl.v_new[t], dev))
+        counts = sess.sel_count.cpu().numpy()
+        ids = sess.sel_ids.cpu().numpy()
+        for r in range(R):
+            b0 = int(sess.blk_off[r])
+            sels[(r, wl.refresh_index_at(r, t))] = ids[b0:b0 + counts[r]].copy()
+        if t in (0, steps - 1):
+            gpu[t] = out.double().cpu().numpy()
+    refs, outs = oracle.simulate(wl, steps=[0, steps - 1])
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (r, k)
+    worst = (0.0, 0.0, 0.0)
+    for t in (0, steps - 1):
+        ref = np.stack([outs[(r, t)] for r in range(R)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
+    log(f"  reactive ctx1m: {len(sels)} selections bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
