@@ -74,6 +74,9 @@ def parse():
                     help="measure the indexer's label-denoising pipeline instead of the decode loop: 21 "
                          "layers x --denoise-windows windows x 16,384 blocks of synthetic logits per call")
     ap.add_argument("--denoise-windows", type=int, default=64)
+    ap.add_argument("--plan", choices=("device", "host"), default="host",
+                    help="where the residency plan of a refresh is made: on the device "
+                         "(lsa_gather_plan_device, no host round trip) or on the host (lsa_gather_blocks_batch)")
     ap.add_argument("--reactive", action="store_true",
                     help="reactive comparator: every block resident in HBM, the index scored at every step "
                          "and the decode reading the selected blocks in place (refresh cadence 1, no "
@@ -371,7 +374,8 @@ def main():
     sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False,
-                      n_layers=cfg.n_layers, w_down=wl.w_down)
+                      n_layers=cfg.n_layers, w_down=wl.w_down,
+                      device_plan=(args.plan == "device" and not args.reactive))
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
@@ -420,10 +424,12 @@ def main():
 
     e = 2 if cfg.dtype == "bf16" else 4
     D, H = cfg.head_dim, cfg.n_heads
-    loop = DecodeLoop(sess, wl.ctx, window, out)
+    dplan = sess.device_plan
+    loop = DecodeLoop(sess, wl.ctx, window, out, device_counts=dplan)
     rloop = ResidentLoop(sess, wl.ctx, window, out) if args.reactive else None
     outs_l = [torch.empty_like(out) for _ in range(1, cfg.n_layers)]
-    loops_l = [DecodeLoop(sess, wl.ctx, window, outs_l[l - 1], layer=l) for l in range(1, cfg.n_layers)]
+    loops_l = [DecodeLoop(sess, wl.ctx, window, outs_l[l - 1], layer=l, device_counts=dplan)
+               for l in range(1, cfg.n_layers)]
     gather_host_s = []
     gather_blocks = []
     sel_hist = {}        # (request, selection version) -> ascending ids
@@ -453,8 +459,14 @@ def main():
             bias = bias_dev[reqs[0]:reqs[-1] + 1] if reqs == list(range(reqs[0], reqs[-1] + 1)) else \
                 torch.stack([bias_dev[r] for r in reqs])
             evs = ref_ev.get(t, (None, None)) if timed_idx is not None else (None, None)
-            sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
-                               ev_latent=lat_ev.get(t, (None, None)))
+            if dplan:
+                # refresh, plan and copy on the device: nothing comes back to the host
+                sess.refresh_device(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
+                                    ev_plan=gather_ev.get(t, (None, None)))
+            else:
+                sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
+                                   ev_latent=lat_ev.get(t, (None, None)))
+        if reqs and not dplan:
             h0 = time.perf_counter()
             if timed_idx is not None:
                 gather_ev[t][0].record(sess.stream)
@@ -475,7 +487,7 @@ def main():
             loop.step(t, q_all[t], kn_all[t], vn_all[t], ev[0], ev[1])
             for lp, (ql, kl, vl) in zip(loops_l, layer_in):
                 lp.step(t, ql[t], kl[t], vl[t])
-            step_log.append((t, loop.n_sel.copy(), sess.sel_version.copy(), timed_idx in att_ev))
+            step_log.append((t, None if dplan else loop.n_sel.copy(), sess.sel_version.copy(), timed_idx in att_ev))
 
     note(f"warm-up {W} steps")
     for t in range(W):
@@ -491,6 +503,20 @@ def main():
 
     attn_ms = np.array([a.elapsed_time(b) for a, b in att_ev.values()])
     sel_at = {}
+    if dplan:
+        # the selections in force at the event-timed steps, recomputed after the timed region (the
+        # refresh is deterministic): the governing refresh of each request
+        cache = {}
+        for t, _, _, timed_ev in step_log:
+            if not timed_ev:
+                continue
+            sel_at[t] = {}
+            for r in range(wl.n_req):
+                k = max(i for i, tk in enumerate(wl.refresh_steps[r]) if tk <= t)
+                if (r, k) not in cache:
+                    hid_rk = dev_raw(wl.hidden[r][k][None])
+                    cache[(r, k)] = sess.refresh([r], hid_rk, bias_dev[r:r + 1])[r]
+                sel_at[t][r] = cache[(r, k)]
     if rloop is not None:
         # the selections of the event-timed steps, recomputed after the timed region (the refresh
         # is deterministic), give their attended bytes
@@ -503,7 +529,7 @@ def main():
     # selected blocks (below the window start), K and V, plus q and the table entries
     attn_bytes, attn_tokens, with_ev = [], [], []
     for t, n_att, ver, timed_ev in step_log:
-        if rloop is not None and not timed_ev:
+        if (rloop is not None or dplan) and not timed_ev:
             continue
         with_ev.append(timed_ev)
         toks = 0
@@ -512,9 +538,9 @@ def main():
             L = int(wl.ctx[r]) + t + 1
             ws = max(0, L - cfg.window)
             toks += min(L, cfg.window)
-            if rloop is not None:
+            if rloop is not None or dplan:
                 ids = sel_at[t][r]
-                n_entries += len(ids)
+                n_entries += len(ids)  # the decode reads every table entry (in-window ones masked)
                 n = int(np.searchsorted(ids, (ws + 63) // 64, side="left"))
             else:
                 ids = sel_hist[(r, int(ver[r]))] if n_att[r] > 0 else None
@@ -540,6 +566,10 @@ def main():
                  + q_in_bytes + 4 * sum(len(x) for x in sess.sel_host) + 4 * wl.n_req)
     lat_bytes = (cfg.n_idx * cfg.q_rank * cfg.d_model * e + wl.n_req * cfg.d_model * e
                  + wl.n_req * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else 0
+    if dplan and sel_at:  # ids of the recomputed selections, plus the bit planes the plan reads
+        n_ids = np.mean([sum(len(v) for v in s_.values()) for s_ in sel_at.values()])
+        ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
+                     + q_in_bytes + int(4 * n_ids) + 8 * (cfg.n_idx + 1) * int(sess.word_off[-1]) + 4 * wl.n_req)
     if rloop is not None:  # ids and table pairs of the recomputed selections
         n_ids = np.mean([sum(len(v) for v in s.values()) for s in sel_at.values()]) if sel_at else 0.0
         ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
@@ -577,6 +607,7 @@ def main():
             "select": args.select,
             "reactive": bool(args.reactive),
             "q_rank": cfg.q_rank,
+            "residency_plan": "device" if dplan else ("none (resident)" if args.reactive else "host"),
             "requests": wl.n_req,
             "context_tokens": int(wl.ctx[0]) if len(set(wl.ctx.tolist())) == 1 else wl.ctx.tolist(),
             "seed": args.seed,

@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 7
+#define LSA_ABI_VERSION 8
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -66,7 +66,8 @@ const char* lsa_last_error(void);
 int32_t lsa_abi_version(void);
 
 /* sizeof the argument structs below, so a binding can check its own layout:
- * which = 0 refresh args, 1 gather args, 2 decode args, 3 latent args, 4 denoise args.
+ * which = 0 refresh args, 1 gather args, 2 decode args, 3 latent args, 4 denoise args,
+ * 5 device gather args.
  * Returns 0 for others. */
 size_t lsa_struct_size(int32_t which);
 
@@ -253,6 +254,58 @@ lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream);
  * have distinct residency state and staging buffers and the same block_bytes; their hot slots must
  * not overlap. */
 lsa_status lsa_gather_blocks_batch(const lsa_gather_args* a, int32_t n, hipStream_t stream);
+
+/* --------------------------------------------------------------------------------------
+ * (2b) The gather planned on the device (zhichai.net explainer, section 2 steps 3 and 5),
+ * for requests 0..n_req-1 right after their refresh, with no host round trip: the refresh's
+ * union bits (its masks, plane n_idx) are compared with the resident set kept in device
+ * memory; the slots of blocks that left go onto the request's device free stack, blocks
+ * that entered take slots from its top and are copied cold -> hot (every layer), and the
+ * request's block table is rewritten in ascending block id.  lsa_sparse_decode then reads
+ * the table with n_sel_dev = table_count, tbl_off[r] = slot_off[r] and n_sel[r] = the
+ * request's slot count.  A selection that does not fit a request's slots changes nothing
+ * for that request and sets its status to 1 (its table and count stay those of the last
+ * refresh that fitted).  The state (resident, slot_of_block, free_slots, n_free) belongs
+ * to the caller and is set up by lsa_residency_reset; calls that share it must be ordered
+ * on one stream.  Two launches on `stream` (plan, copy); validation happens first.
+ * ------------------------------------------------------------------------------------ */
+typedef struct lsa_device_gather_args {
+    int32_t n_req;             /* 1..LSA_MAX_REFRESH_REQ */
+    int32_t n_idx;             /* indexers of the refresh whose masks are read: 1..4 */
+    int32_t block_bytes;       /* lsa_block_bytes(dtype, D) */
+    int32_t n_layers;          /* 1..256 */
+    const int64_t* blk_off;    /* host [n_req+1], as for the refresh (B_r = blk_off[r+1]-blk_off[r]) */
+    const int32_t* slot_off;   /* host [n_req+1]: request r owns hot slots slot_off[r] .. slot_off[r+1]-1 */
+    const uint64_t* masks;     /* dev: the refresh's bit planes (lsa_refresh_args.masks layout) */
+    const int32_t* sel_count;  /* dev [n_req]: the refresh's counts; a negative count (a refresh that
+                                  gave up) changes nothing for the request and sets its status to 2 */
+    uint64_t* resident;        /* dev [sum_r ceil(B_r/64)] state: request r's words start at word
+                                  sum_{r'<r} ceil(B_r'/64); bit b = block b resident */
+    int32_t* slot_of_block;    /* dev [blk_off[n_req]] state: slot of each block, or -1 */
+    int32_t* free_slots;       /* dev [slot_off[n_req]] state: request r's stack at slot_off[r] */
+    int32_t* n_free;           /* dev [n_req] state: entries on each stack */
+    const void* const* cold;   /* host [n_req]: dev pointer to request r's cold pool (HBM) */
+    int64_t cold_layer_bytes;  /* n_layers > 1: layer l of request r's cold pool at cold[r] + l*this */
+    void* hot;                 /* dev: hot pool of slot_off[n_req] slots (per layer) */
+    int64_t hot_layer_bytes;   /* n_layers > 1: layer l's hot pool at hot + l*this */
+    int32_t* table;            /* dev: request r's (block id, slot) pairs from pair slot_off[r] */
+    int32_t* table_count;      /* dev [n_req] out: entries in r's table */
+    int32_t* copied;           /* dev [n_req] out: blocks that entered (copied once per layer) */
+    int32_t* status;           /* dev [n_req] out: 0; 1 when the selection did not fit; 2 after a
+                                  refresh that gave up */
+    void* workspace;           /* dev, workspace_bytes >= lsa_gather_plan_device_workspace() */
+    size_t workspace_bytes;
+    hipEvent_t ev_begin;       /* optional, used only when both are set: start of the plan */
+    hipEvent_t ev_end;         /* dispatch and end of the copy dispatch */
+} lsa_device_gather_args;
+
+lsa_status lsa_gather_plan_device_workspace(const lsa_device_gather_args* a, size_t* bytes);
+lsa_status lsa_gather_plan_device(const lsa_device_gather_args* a, hipStream_t stream);
+
+/* Set up the device residency state of lsa_gather_plan_device: nothing resident, every
+ * slot of request r free (free_slots at slot_off[r] holds slot_off[r+1]-1 .. slot_off[r],
+ * so the lowest slot is on top), n_free = slot count, table_count = 0, status = 0. */
+lsa_status lsa_residency_reset(const lsa_device_gather_args* a, hipStream_t stream);
 
 /* --------------------------------------------------------------------------------------
  * (3) Sparse decode: one decode step for n_req requests (zhichai.net explainer,

@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -57,6 +57,9 @@ EXPORTED_SYMBOLS = (
     "lsa_query_latent",
     "lsa_gather_blocks",
     "lsa_gather_blocks_batch",
+    "lsa_gather_plan_device_workspace",
+    "lsa_gather_plan_device",
+    "lsa_residency_reset",
     "lsa_sparse_decode_workspace",
     "lsa_sparse_decode",
     "lsa_label_denoise_workspace",
@@ -101,6 +104,17 @@ class DenoiseArgs(Structure):
         ("n_blk", c_void_p), ("n_blk_dev", c_void_p), ("layer_sets", c_void_p), ("labels", c_void_p),
         ("n_pos", c_void_p), ("n_naive", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("ev_begin", c_void_p), ("ev_end", c_void_p),
+    ]
+
+
+class DeviceGatherArgs(Structure):
+    _fields_ = [
+        ("n_req", c_int32), ("n_idx", c_int32), ("block_bytes", c_int32), ("n_layers", c_int32),
+        ("blk_off", c_void_p), ("slot_off", c_void_p), ("masks", c_void_p), ("sel_count", c_void_p),
+        ("resident", c_void_p), ("slot_of_block", c_void_p), ("free_slots", c_void_p), ("n_free", c_void_p),
+        ("cold", c_void_p), ("cold_layer_bytes", c_int64), ("hot", c_void_p), ("hot_layer_bytes", c_int64),
+        ("table", c_void_p), ("table_count", c_void_p), ("copied", c_void_p), ("status", c_void_p),
+        ("workspace", c_void_p), ("workspace_bytes", c_size_t), ("ev_begin", c_void_p), ("ev_end", c_void_p),
     ]
 
 
@@ -158,6 +172,11 @@ def _load():
     lib.lsa_label_denoise_workspace.argtypes = [POINTER(DenoiseArgs), POINTER(c_size_t)]
     lib.lsa_label_denoise.restype = c_int32
     lib.lsa_label_denoise.argtypes = [POINTER(DenoiseArgs), c_void_p]
+    for fn in ("lsa_gather_plan_device", "lsa_residency_reset"):
+        getattr(lib, fn).restype = c_int32
+        getattr(lib, fn).argtypes = [POINTER(DeviceGatherArgs), c_void_p]
+    lib.lsa_gather_plan_device_workspace.restype = c_int32
+    lib.lsa_gather_plan_device_workspace.argtypes = [POINTER(DeviceGatherArgs), POINTER(c_size_t)]
     lib.lsa_gather_blocks.restype = c_int32
     lib.lsa_gather_blocks.argtypes = [POINTER(GatherArgs), c_void_p]
     lib.lsa_gather_blocks_batch.restype = c_int32
@@ -168,7 +187,7 @@ def _load():
     lib.lsa_sparse_decode.argtypes = [POINTER(DecodeArgs), c_void_p]
     if lib.lsa_abi_version() != ABI_VERSION:
         raise ImportError(f"liblsa.so ABI {lib.lsa_abi_version()} != binding ABI {ABI_VERSION}")
-    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs, LatentArgs, DenoiseArgs)):
+    for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs, LatentArgs, DenoiseArgs, DeviceGatherArgs)):
         if lib.lsa_struct_size(i) != ctypes.sizeof(st):
             raise ImportError(f"{st.__name__}: binding layout {ctypes.sizeof(st)} B != library {lib.lsa_struct_size(i)} B")
     return lib
@@ -397,4 +416,5 @@ def lsa_sparse_decode(*, dtype, n_heads, head_dim, win_cap, q, ring, out, worksp
 
 
 __all__ = [n for n in dir() if n.startswith("lsa_") or n.startswith("LSA_")] + [
-    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs", "LatentArgs", "DenoiseArgs"]
+    "LSAError", "LIB", "BLOCK_TOKENS", "EXPORTED_SYMBOLS", "RefreshArgs", "GatherArgs", "DecodeArgs", "LatentArgs", "DenoiseArgs",
+    "DeviceGatherArgs"]

@@ -436,11 +436,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
                 j = __builtin_amdgcn_readfirstlane(j);
                 if (j >= c1) break;
                 const TileDesc d = desc(j);
+                if (d.cur) cur_base = d.base;
+                // a tile with no valid token (a table entry inside the window, which device-side counts
+                // include) is not read; the branch comes before any load of the tile
+                if (d.mask == 0) continue;
                 typename Ops::Frag f;
                 Ops::load(f, d.base, lane);
                 Ops::pin_k(f);
-                if (d.cur) cur_base = d.base;
-                if (d.mask) compute(f, d);
+                compute(f, d);
             }
             __syncthreads();  // every wave is done with s_ent and s_next
         }

@@ -61,6 +61,7 @@ size_t lsa_struct_size(int32_t which) {
         case 2: return sizeof(lsa_decode_args);
         case 3: return sizeof(lsa_latent_args);
         case 4: return sizeof(lsa_denoise_args);
+        case 5: return sizeof(lsa_device_gather_args);
         default: return 0;
     }
 }

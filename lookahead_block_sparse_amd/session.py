@@ -26,6 +26,7 @@ import torch
 from . import (
     BLOCK_TOKENS,
     DecodeArgs,
+    DeviceGatherArgs,
     GatherArgs,
     LIB,
     _check,
@@ -57,7 +58,8 @@ class LSASession:
                  win_cap: int, n_blocks: Sequence[int], w_q: np.ndarray, keys: Sequence[np.ndarray],
                  capacity: Optional[Sequence[int]] = None, cold_on_device: bool = False,
                  with_masks: bool = False, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
-                 max_groups: int = 0, n_layers: int = 1, w_down: Optional[np.ndarray] = None):
+                 max_groups: int = 0, n_layers: int = 1, w_down: Optional[np.ndarray] = None,
+                 device_plan: bool = False):
         self.dtype = dtype
         self.n_idx, self.d_model, self.d_idx = n_idx, d_model, d_idx
         # low-rank query projection: w_down = A [n_idx][rank][d_model], w_q = B [n_idx][d_idx][rank];
@@ -91,7 +93,7 @@ class LSASession:
             self.sel_count = torch.zeros(self.n_req, dtype=torch.int32, device=self.device)
             self.word_off = np.concatenate([[0], np.cumsum((self.n_blocks + 63) // 64)]).astype(np.int64)
             self.masks = (torch.zeros(int(self.word_off[-1]) * (n_idx + 1), dtype=torch.int64, device=self.device)
-                          if with_masks else None)
+                          if with_masks or device_plan else None)
             ws = lsa_index_refresh_workspace(dtype=dtype, d_model=self.q_in, d_idx=d_idx, n_idx=n_idx,
                                              blk_off=self.blk_off)
             self.latent = (torch.empty((self.n_req, n_idx, self.rank), dtype=torch.int16 if dtype == "bf16"
@@ -128,10 +130,33 @@ class LSASession:
                                              n_req=self.n_req, max_groups=max_groups)
             self.decode_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
         self._gargs: List[Optional[tuple]] = [None] * self.n_req
+        self._pargs = {}  # device-plan argument structs per run of requests
         self._stage_ev: List[Optional[torch.cuda.Event]] = [None] * self.n_req
         self.last_decode_event: Optional[torch.cuda.Event] = None
         # record an event after each decode so a gather on another stream can wait for it
         self.track_decode = False
+        # residency planned on the device (lsa_gather_plan_device): the state lives in HBM and a
+        # refresh never waits for the host
+        self.device_plan = bool(device_plan)
+        if self.device_plan:
+            if not cold_on_device:
+                raise ValueError("device planning copies from a cold pool in HBM")
+            with torch.cuda.stream(self.stream):
+                dev = self.device
+                self.resident_dev = torch.zeros(int(self.word_off[-1]), dtype=torch.int64, device=dev)
+                self.slot_of_block_dev = torch.empty(int(self.blk_off[-1]), dtype=torch.int32, device=dev)
+                self.free_dev = torch.empty(max(1, self.n_slots), dtype=torch.int32, device=dev)
+                self.n_free_dev = torch.empty(self.n_req, dtype=torch.int32, device=dev)
+                self.table_count = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
+                self.copied_dev = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
+                self.plan_status = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
+            a = self._plan_args(0, self.n_req)[0]
+            ws = ctypes.c_size_t(0)
+            _check(LIB.lsa_gather_plan_device_workspace(ctypes.byref(a), ctypes.byref(ws)))
+            self.plan_ws = torch.empty(int(ws.value), dtype=torch.uint8, device=self.device)
+            self._pargs = {}
+            a = self._plan_args(0, self.n_req)[0]
+            _check(LIB.lsa_residency_reset(ctypes.byref(a), ctypes.c_void_p(self.stream.cuda_stream)))
 
     # ---------------------------------------------------------------------------------------
     def load_prefill(self, r: int, k_tok: np.ndarray, v_tok: np.ndarray, layer: int = 0) -> None:
@@ -144,6 +169,7 @@ class LSASession:
         v_tok = np.ascontiguousarray(v_tok)
         lb = int(self.n_blocks[r]) * self.block_bytes  # bytes of one layer's cold pool
         if self.cold[r] is None:
+            self._pargs.clear()  # they hold the cold pools' addresses
             self.cold[r] = (torch.empty(self.n_layers * lb, dtype=torch.uint8, device=self.device)
                             if self.cold_on_device else
                             torch.empty(self.n_layers * lb, dtype=torch.uint8, pin_memory=True))
@@ -256,6 +282,65 @@ class LSASession:
         return m.reshape(self.n_idx + 1, w)
 
     # ---------------------------------------------------------------------------------------
+    def _plan_args(self, r0: int, r1: int):
+        """lsa_device_gather_args for requests r0 .. r1-1 (built once per run of requests)."""
+        key = (r0, r1)
+        if key not in self._pargs:
+            a = DeviceGatherArgs()
+            a.n_req, a.n_idx, a.block_bytes, a.n_layers = r1 - r0, self.n_idx, self.block_bytes, self.n_layers
+            blk = np.ascontiguousarray(self.blk_off[r0:r1 + 1] - self.blk_off[r0], dtype=np.int64)
+            slo = np.ascontiguousarray(self.slot_base[r0:r1 + 1] - self.slot_base[r0], dtype=np.int32)
+            w0, s0, b0 = int(self.word_off[r0]), int(self.slot_base[r0]), int(self.blk_off[r0])
+            a.blk_off, a.slot_off = blk.ctypes.data, slo.ctypes.data
+            a.masks = self.masks.data_ptr() + 8 * w0 * (self.n_idx + 1)
+            a.sel_count = self.sel_count.data_ptr() + 4 * r0
+            a.resident = self.resident_dev.data_ptr() + 8 * w0
+            a.slot_of_block = self.slot_of_block_dev.data_ptr() + 4 * b0
+            a.free_slots = self.free_dev.data_ptr() + 4 * s0
+            a.n_free = self.n_free_dev.data_ptr() + 4 * r0
+            cold = (ctypes.c_void_p * (r1 - r0))(*[self.cold[r].data_ptr() if self.cold[r] is not None else None
+                                                   for r in range(r0, r1)])
+            a.cold = ctypes.cast(cold, ctypes.c_void_p)
+            if self.n_layers > 1 and r1 - r0 > 1 and len(set(self.n_blocks[r0:r1].tolist())) > 1:
+                raise ValueError("device planning over several layers needs equal block counts in a run")
+            a.cold_layer_bytes = int(self.n_blocks[r0]) * self.block_bytes
+            a.hot, a.hot_layer_bytes = self.hot.data_ptr(), self.hot_layer_bytes
+            a.table = self.table.data_ptr() + 8 * s0
+            a.table_count = self.table_count.data_ptr() + 4 * r0
+            a.copied = self.copied_dev.data_ptr() + 4 * r0
+            a.status = self.plan_status.data_ptr() + 4 * r0
+            ws = getattr(self, "plan_ws", None)
+            a.workspace = ws.data_ptr() if ws is not None else None
+            a.workspace_bytes = ws.numel() if ws is not None else 0
+            self._pargs[key] = (a, blk, slo, cold)
+        return self._pargs[key]
+
+    def refresh_device(self, reqs: Sequence[int], hidden: torch.Tensor, bias: torch.Tensor, ev_begin=None,
+                       ev_end=None, ev_plan=(None, None)) -> None:
+        """Index refresh of `reqs` followed by the gather planned and run on the device
+        (lsa_gather_plan_device): nothing is copied back and nothing waits for the host.  The
+        decode then reads the tables' counts on the device (DecodeLoop(..., device_counts=True))."""
+        if not self.device_plan:
+            raise RuntimeError("the session was built without device_plan")
+        reqs = list(reqs)
+        hid = hidden.reshape(len(reqs), self.d_model)
+        bias_d = bias.reshape(len(reqs), self.n_idx)
+        i = 0
+        while i < len(reqs):
+            j = i
+            while j + 1 < len(reqs) and reqs[j + 1] == reqs[j] + 1:
+                j += 1
+            r0, r1 = reqs[i], reqs[j] + 1
+            one_run = i == 0 and j == len(reqs) - 1
+            self._refresh_run(r0, r1, hid[i:j + 1], bias_d[i:j + 1], ev_begin if one_run else None,
+                              ev_end if one_run else None)
+            a = self._plan_args(r0, r1)[0]
+            a.ev_begin = ev_plan[0].cuda_event if (ev_plan[0] is not None and one_run) else None
+            a.ev_end = ev_plan[1].cuda_event if (ev_plan[1] is not None and one_run) else None
+            _check(LIB.lsa_gather_plan_device(ctypes.byref(a), ctypes.c_void_p(self.stream.cuda_stream)))
+            i = j + 1
+        self.sel_version[reqs] += 1
+
     def gather(self, r: int, ids: np.ndarray, stream: Optional[torch.cuda.Stream] = None):
         """Make request r's hot pool hold exactly `ids` (returns (copied, kept))."""
         return self.gather_many({r: ids}, stream)[r]
@@ -368,8 +453,9 @@ class DecodeLoop:
     """
 
     def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor,
-                 layer: int = 0):
+                 layer: int = 0, device_counts: bool = False):
         self.sess = sess
+        self.device_counts = bool(device_counts)
         self.prefill = np.asarray(prefill, dtype=np.int64)
         self.window = np.ascontiguousarray(window, dtype=np.int32)
         self.seq_len = np.zeros(sess.n_req, dtype=np.int32)
@@ -388,6 +474,12 @@ class DecodeLoop:
         a.out = out.data_ptr()
         a.workspace, a.workspace_bytes = sess.decode_ws.data_ptr(), sess.decode_ws.numel()
         a.max_groups, a.reserved1 = sess.max_groups, 0
+        if self.device_counts:
+            # the tables the device planner writes: counts on the device, capacities on the host
+            if not sess.device_plan:
+                raise ValueError("device_counts needs a session with device_plan")
+            self.n_sel[:] = np.asarray(sess.capacity, dtype=np.int32)
+            a.n_sel_dev = sess.table_count.data_ptr()
         self.args = a
         self.ref = ctypes.byref(a)
         self.stream = ctypes.c_void_p(sess.stream.cuda_stream)
@@ -398,10 +490,10 @@ class DecodeLoop:
              ev_begin=None, ev_end=None) -> None:
         np.add(self.prefill, t + 1, out=self.seq_len, casting="unsafe")
         # attended table entries change only when a window start crosses a block boundary or a
-        # request's selection changes
+        # request's selection changes (device counts: the kernels mask blocks inside the window)
         bnd = (np.maximum(0, self.seq_len - self.window) + BLOCK_TOKENS - 1) // BLOCK_TOKENS
         changed = (bnd != self._bnd) | (self.sess.sel_version != self._ver)
-        if changed.any():
+        if changed.any() and not self.device_counts:
             for r in np.flatnonzero(changed):
                 self.n_sel[r] = np.searchsorted(self.sess.sel_host[r], bnd[r], side="left")
             self._bnd = bnd

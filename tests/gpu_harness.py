@@ -64,17 +64,22 @@ def raw_to_torch(arr: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(arr.astype(np.float32, copy=False)).to(device)
 
 
-def make_session(wl, capacity=None, cold_on_device=False, with_masks=True, max_groups=0):
+def make_session(wl, capacity=None, cold_on_device=False, with_masks=True, max_groups=0, device_plan=False):
     from lookahead_block_sparse_amd.session import LSASession
 
     cfg = wl.cfg
     sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, capacity=capacity, cold_on_device=cold_on_device,
-                      with_masks=with_masks, max_groups=max_groups, w_down=wl.w_down)
+                      with_masks=with_masks, max_groups=max_groups, w_down=wl.w_down, device_plan=device_plan,
+                      n_layers=wl.cfg.n_layers)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
+    for layer in range(1, wl.cfg.n_layers):
+        for r in range(wl.n_req):
+            k, v = wl.kv_prefill(r, layer)
+            sess.load_prefill(r, k, v, layer=layer)
     return sess
 
 

@@ -31,7 +31,8 @@ def test_header_functions_are_exported():
 
 def test_abi_version_and_struct_sizes():
     assert L.LIB.lsa_abi_version() == L.ABI_VERSION
-    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs, L.LatentArgs, L.DenoiseArgs)):
+    for i, st in enumerate((L.RefreshArgs, L.GatherArgs, L.DecodeArgs, L.LatentArgs, L.DenoiseArgs,
+                            L.DeviceGatherArgs)):
         assert L.LIB.lsa_struct_size(i) == ctypes.sizeof(st)
     assert L.LIB.lsa_struct_size(7) == 0
 

@@ -1,0 +1,141 @@
+"""The gather planned on the device (lsa_gather_plan_device) against the oracle: a decode loop whose
+refreshes never return to the host.  After every refresh the selection is the oracle's (bit for bit),
+the table is that selection with every slot holding its cold block (every layer), the device state
+is consistent (free stack + resident slots = the request's slots), and sampled outputs match the
+oracle; a selection that does not fit changes nothing and reports status 1."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import ABS_TOL, REL_TOL, attention_errors, conditioned_workload, log, make_session, raw_to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_state(sess, r, ids):
+    """Table == ids with slots holding their cold blocks (every layer); free + used slots = all."""
+    s0, s1 = int(sess.slot_base[r]), int(sess.slot_base[r + 1])
+    assert int(sess.plan_status[r].item()) == 0
+    cnt = int(sess.table_count[r].item())
+    table = sess.table.view(-1, 2)[s0:s0 + cnt].cpu().numpy()
+    assert cnt == len(ids) and np.array_equal(table[:, 0], ids), (r, cnt, len(ids))
+    slots = table[:, 1]
+    nf = int(sess.n_free_dev[r].item())
+    free = sess.free_dev[s0:s0 + nf].cpu().numpy()
+    assert sorted(np.concatenate([slots, free]).tolist()) == list(range(s0, s1)), r
+    sob = sess.slot_of_block_dev[int(sess.blk_off[r]):int(sess.blk_off[r + 1])].cpu().numpy()
+    assert np.array_equal(np.flatnonzero(sob >= 0), ids) and np.array_equal(sob[ids], slots)
+    bb = sess.block_bytes
+    lb = int(sess.n_blocks[r]) * bb
+    st = torch.as_tensor(slots, dtype=torch.long, device=sess.device)
+    bt = torch.as_tensor(ids, dtype=torch.long, device=sess.device)
+    for layer in range(sess.n_layers):
+        hot, _ = sess.layer_views(layer)
+        cold = sess.cold[r][layer * lb:(layer + 1) * lb]
+        assert torch.equal(hot.view(-1, bb)[st], cold.view(-1, bb)[bt]), (r, layer)
+
+
+def _run(wl, sess, sample, check=True):
+    from lookahead_block_sparse_amd.session import DecodeLoop
+
+    cfg = wl.cfg
+    R = wl.n_req
+    dev = sess.device
+    bias_all = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+    sels, gpu = {}, {}
+
+    def refresh(reqs, k_of):
+        hid = raw_to_torch(np.stack([wl.hidden[r][k_of[r]] for r in reqs]), dev)
+        sess.refresh_device(reqs, hid, torch.stack([bias_all[r] for r in reqs]))
+        if check:
+            counts = sess.sel_count.cpu().numpy()
+            ids_all = sess.sel_ids.cpu().numpy()
+            for r in reqs:
+                b0 = int(sess.blk_off[r])
+                ids = ids_all[b0:b0 + counts[r]].copy()
+                sels[(r, k_of[r])] = ids
+                _check_state(sess, r, ids)
+
+    pro = [r for r in range(R) if wl.refresh_steps[r][0] < 0]
+    if pro:
+        refresh(pro, {r: 0 for r in pro})
+    outs = [torch.empty((R, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev) for _ in range(cfg.n_layers)]
+    loops = [DecodeLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), outs[l], layer=l, device_counts=True)
+             for l in range(cfg.n_layers)]
+    for t in range(cfg.steps):
+        reqs = wl.refreshes_at(t)
+        if reqs:
+            refresh(reqs, {r: wl.refresh_index_at(r, t) for r in reqs})
+        for l in range(cfg.n_layers):
+            loops[l].step(t, raw_to_torch(wl.q_dec_of(l)[t], dev), raw_to_torch(wl.k_new_of(l)[t], dev),
+                          raw_to_torch(wl.v_new_of(l)[t], dev))
+        if t in sample:
+            for l in range(cfg.n_layers):
+                gpu[(l, t)] = outs[l].double().cpu().numpy()
+    torch.cuda.synchronize()
+    return gpu, sels
+
+
+@pytest.mark.parametrize("name,layers", [("ctx128k_s", 1), ("ragged_s", 1), ("ctx512k_s", 2)])
+def test_device_planned_loop_matches_oracle(name, layers):
+    from workloads import get_config
+
+    cfg = get_config(name).scaled(n_layers=layers, hidden_rho=0.9 if layers > 1 else 0.0)
+    wl = conditioned_workload(cfg, seed=41)
+    log(f"device-planned loop {name}, {layers} layer(s), {cfg.steps} steps")
+    sess = make_session(wl, cold_on_device=True, with_masks=False, device_plan=True)
+    sample = sorted({0, 63, 64, cfg.steps - 1})
+    gpu, sels = _run(wl, sess, sample)
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    worst = (0.0, 0.0, 0.0)
+    for layer in range(layers):
+        refs, outs = oracle.simulate(wl, steps=sample, layer=layer)
+        for (r, k), ids in sels.items():
+            assert np.array_equal(ids, refs[r][k].ids), (name, r, k)
+        for t in sample:
+            ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+            worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[(layer, t)], ref)))
+    log(f"  {name}: {len(sels)} device-planned refreshes; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+def test_device_plan_overflow_changes_nothing():
+    """With too few slots for the second refresh's selection, that refresh's plan reports status 1 and
+    the table, the resident set and the free stack stay those of the first refresh."""
+    from workloads import get_config
+
+    cfg = get_config("ctx128k_s").scaled(steps=70)
+    wl = conditioned_workload(cfg, seed=42)
+    R = wl.n_req
+    dt = cfg.dtype
+    w_q = oracle.decode_values(wl.w_q, dt)
+    counts = [[oracle.refresh(oracle.decode_values(wl.hidden[r][k], dt), w_q, oracle.decode_values(wl.keys[r], dt),
+                              wl.bias[r]).count for k in range(len(wl.refresh_steps[r]))] for r in range(R)]
+    # the refresh with the smallest selection first, the largest second; slots for the first only
+    ks = [(int(np.argmin(c)), int(np.argmax(c))) for c in counts]
+    first = [counts[r][ks[r][0]] for r in range(R)]
+    second = [counts[r][ks[r][1]] for r in range(R)]
+    cap = [max(first[r], 1) for r in range(R)]
+    assert any(second[r] > cap[r] for r in range(R)), counts
+    sess = make_session(wl, capacity=cap, cold_on_device=True, with_masks=False, device_plan=True)
+    dev = sess.device
+    bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+    sess.refresh_device(list(range(R)), raw_to_torch(np.stack([wl.hidden[r][ks[r][0]] for r in range(R)]), dev), bias)
+    torch.cuda.synchronize()
+    before = (sess.table.clone(), sess.table_count.clone(), sess.resident_dev.clone(), sess.free_dev.clone(),
+              sess.n_free_dev.clone(), sess.slot_of_block_dev.clone())
+    sess.refresh_device(list(range(R)), raw_to_torch(np.stack([wl.hidden[r][ks[r][1]] for r in range(R)]), dev), bias)
+    torch.cuda.synchronize()
+    status = sess.plan_status.cpu().numpy()
+    for r in range(R):
+        assert status[r] == (1 if second[r] > cap[r] else 0), (r, status[r], second[r], cap[r])
+    over = [r for r in range(R) if second[r] > cap[r]]
+    for r in over:
+        s0, s1 = int(sess.slot_base[r]), int(sess.slot_base[r + 1])
+        assert torch.equal(sess.table.view(-1, 2)[s0:s1], before[0].view(-1, 2)[s0:s1])
+        assert int(sess.table_count[r]) == int(before[1][r]) == first[r]
+        w0, w1 = int(sess.word_off[r]), int(sess.word_off[r + 1])
+        assert torch.equal(sess.resident_dev[w0:w1], before[2][w0:w1])
+        assert int(sess.n_free_dev[r]) == int(before[4][r])
