@@ -340,3 +340,45 @@ def test_pack_blocks_rejects_overflow():
     with pytest.raises(L.LSAError) as e:
         L.lsa_pack_blocks("f32", 64, k, k, 0, 200, np.zeros(3 * 32768, np.uint8), 3)
     assert e.value.status == L.LSA_ERR_INVALID
+
+
+def _dev_gather_args(**over):
+    blk = np.array(over.pop("blk_off", [0, 100, 164]), dtype=np.int64)
+    slo = np.array(over.pop("slot_off", [0, 50, 80]), dtype=np.int32)
+    cold = (ctypes.c_void_p * (len(blk) - 1))(*([FAKE] * (len(blk) - 1)))
+    a = L.DeviceGatherArgs()
+    a.n_req, a.n_idx, a.block_bytes, a.n_layers = len(blk) - 1, 3, 32768, 1
+    a.blk_off, a.slot_off = blk.ctypes.data, slo.ctypes.data
+    for f in ("masks", "sel_count", "resident", "slot_of_block", "free_slots", "n_free", "hot", "table",
+              "table_count", "copied", "status", "workspace"):
+        setattr(a, f, FAKE)
+    a.cold = ctypes.cast(cold, ctypes.c_void_p)
+    a.workspace_bytes = 1 << 30
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, (blk, slo, cold)
+
+
+def test_device_gather_workspace_size():
+    a, keep = _dev_gather_args()
+    n = ctypes.c_size_t(0)
+    assert L.LIB.lsa_gather_plan_device_workspace(ctypes.byref(a), ctypes.byref(n)) == L.LSA_OK
+    assert n.value >= 80 * 8 + 65 * 4
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n_req=0), L.LSA_ERR_INVALID),
+    (dict(n_idx=5), L.LSA_ERR_UNSUPPORTED),
+    (dict(block_bytes=1000), L.LSA_ERR_UNSUPPORTED),
+    (dict(n_layers=0), L.LSA_ERR_INVALID),
+    (dict(blk_off=[0, 0, 64]), L.LSA_ERR_INVALID),
+    (dict(slot_off=[1, 50, 80]), L.LSA_ERR_INVALID),
+    (dict(resident=None), L.LSA_ERR_INVALID),
+    (dict(masks=None), L.LSA_ERR_INVALID),
+    (dict(workspace_bytes=16), L.LSA_ERR_WORKSPACE),
+    (dict(hot=FAKE + 8), L.LSA_ERR_INVALID),
+])
+def test_device_gather_validation_before_any_hip_call(over, status):
+    a, keep = _dev_gather_args(**over)
+    assert L.LIB.lsa_gather_plan_device(ctypes.byref(a), None) == status
+    assert L.LIB.lsa_last_error().decode()
