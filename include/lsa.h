@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 8
+#define LSA_ABI_VERSION 9
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -243,6 +243,11 @@ typedef struct lsa_gather_args {
                                   allocation; >= n_blocks*block_bytes, multiple of 16) */
     int64_t hot_layer_bytes;   /* L > 1: layer l's hot pool at hot + l*hot_layer_bytes
                                   (>= n_slots_total*block_bytes, multiple of 16) */
+    hipEvent_t ev_begin;       /* optional (NULL): recorded with the start stamp of the copy kernel's
+                                  dispatch (of the first one, in a batch); only a[0]'s are used by
+                                  lsa_gather_blocks_batch.  With nothing to launch, recorded on the
+                                  stream at the call. */
+    hipEvent_t ev_end;         /* optional (NULL): the end stamp of the (last) copy kernel's dispatch */
 } lsa_gather_args;
 
 lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream);

@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -126,6 +126,7 @@ class GatherArgs(Structure):
         ("n_free", c_void_p), ("capacity", c_int32), ("n_layers", c_int32), ("stage", c_void_p),
         ("table_dev", c_void_p), ("n_copied", c_void_p), ("n_kept", c_void_p),
         ("cold_layer_bytes", c_int64), ("hot_layer_bytes", c_int64),
+        ("ev_begin", c_void_p), ("ev_end", c_void_p),
     ]
 
 
@@ -352,8 +353,9 @@ def lsa_label_denoise(*, logits, n_blk, n_blk_dev, labels, n_pos, top_p=0.6, min
 
 
 def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_ids, slot_of_block, free_slots,
-                      n_free, capacity, stage, table_dev, stream=None):
-    """Returns (n_copied, n_kept).  slot_of_block, free_slots, n_free: int32 NumPy arrays updated in place."""
+                      n_free, capacity, stage, table_dev, stream=None, ev_begin=None, ev_end=None):
+    """Returns (n_copied, n_kept).  slot_of_block, free_slots, n_free: int32 NumPy arrays updated in place.
+    ev_begin / ev_end (torch.cuda.Event, optional) take the copy kernel's dispatch stamps."""
     ids = _i32(new_ids)
     for name, arr in (("slot_of_block", slot_of_block), ("free_slots", free_slots), ("n_free", n_free)):
         if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
@@ -369,6 +371,8 @@ def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_id
     a.capacity, a.n_layers = int(capacity), 0
     a.stage, a.table_dev = _ptr(stage), _ptr(table_dev)
     a.n_copied, a.n_kept = _ptr(n_copied), _ptr(n_kept)
+    a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
+    a.ev_end = ev_end.cuda_event if ev_end is not None else None
     _check(LIB.lsa_gather_blocks(ctypes.byref(a), _stream(stream)))
     return int(n_copied[0]), int(n_kept[0])
 

@@ -9,9 +9,11 @@
 // layer the selection serves, and copies the tables, for every request of the call.  A cold pool may be pinned host memory (the kernel
 // reads it over the host link, zero-copy) or device memory.
 #include <emmintrin.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "lsa_internal.hpp"
@@ -284,6 +286,10 @@ lsa_status gather_batch(const lsa_gather_args* args, int n, hipStream_t stream) 
     DeviceInfo dev;
     lsa_status st = current_device(&dev);
     if (st != LSA_OK) return st;
+    LSA_CHECK_SUP(args[0].block_bytes / 4096 == 4 || args[0].block_bytes / 4096 == 8 || args[0].block_bytes / 4096 == 16,
+                  "lsa_gather_blocks: block_bytes=%d", args[0].block_bytes);
+    thread_local std::vector<std::pair<GatherParams, int>> launches;
+    launches.clear();
     for (int i0 = 0; i0 < n; i0 += kMaxBatch) {
         const int nj = std::min(kMaxBatch, n - i0);
         GatherParams gp{};
@@ -309,11 +315,22 @@ lsa_status gather_batch(const lsa_gather_args* args, int n, hipStream_t stream) 
         if (n_copies == 0 && n_table == 0) continue;
         // one group per copied block (capped), at least enough groups for the table copies
         const int grid = std::max(1, std::min(std::max(n_copies, (2 * n_table + 255) / 256), dev.cu_count * 32));
+        launches.emplace_back(gp, grid);
+    }
+    // the caller's events (a[0]'s) take the dispatch stamps of the first and the last launch
+    hipEvent_t ev0 = args[0].ev_begin, ev1 = args[0].ev_end;
+    if (launches.empty()) {
+        if (ev0) LSA_HIP(hipEventRecord(ev0, stream));
+        if (ev1) LSA_HIP(hipEventRecord(ev1, stream));
+    }
+    for (size_t k = 0; k < launches.size(); ++k) {
+        const GatherParams& gp = launches[k].first;
+        const dim3 grid(launches[k].second), block(256);
+        hipEvent_t b = k == 0 ? ev0 : nullptr, e = k + 1 == launches.size() ? ev1 : nullptr;
         switch (gp.block_bytes / 4096) {
-            case 4: hipLaunchKernelGGL(gather_kernel<4>, dim3(grid), dim3(256), 0, stream, gp); break;
-            case 8: hipLaunchKernelGGL(gather_kernel<8>, dim3(grid), dim3(256), 0, stream, gp); break;
-            case 16: hipLaunchKernelGGL(gather_kernel<16>, dim3(grid), dim3(256), 0, stream, gp); break;
-            default: return fail(LSA_ERR_UNSUPPORTED, "lsa_gather_blocks: block_bytes=%d", gp.block_bytes);
+            case 4: hipExtLaunchKernelGGL(gather_kernel<4>, grid, block, 0, stream, b, e, 0, gp); break;
+            case 8: hipExtLaunchKernelGGL(gather_kernel<8>, grid, block, 0, stream, b, e, 0, gp); break;
+            default: hipExtLaunchKernelGGL(gather_kernel<16>, grid, block, 0, stream, b, e, 0, gp); break;
         }
         LSA_HIP(hipGetLastError());
     }

@@ -367,9 +367,11 @@ class LSASession:
             self._gargs[r] = (a, counts)
         return self._gargs[r]
 
-    def gather_many(self, sel: Dict[int, np.ndarray], stream: Optional[torch.cuda.Stream] = None):
+    def gather_many(self, sel: Dict[int, np.ndarray], stream: Optional[torch.cuda.Stream] = None,
+                    ev_copy=(None, None)):
         """Gathers of several requests after one refresh, planned together and copied by one kernel
-        launch (lsa_gather_blocks_batch).  Returns {r: (copied, kept)}."""
+        launch (lsa_gather_blocks_batch).  Returns {r: (copied, kept)}.  ev_copy (a pair of
+        torch.cuda.Event) takes the copy kernel's dispatch stamps."""
         st = stream if stream is not None else self.stream
         if st is not self.stream:
             if not self.track_decode:
@@ -387,6 +389,8 @@ class LSASession:
             a.new_ids, a.n_new = ids[r].ctypes.data, len(ids[r])
             arr[k] = a
             counts.append(c)
+        arr[0].ev_begin = ev_copy[0].cuda_event if ev_copy[0] is not None else None
+        arr[0].ev_end = ev_copy[1].cuda_event if ev_copy[1] is not None else None
         _check(LIB.lsa_gather_blocks_batch(arr, len(reqs), st.cuda_stream))
         ev = torch.cuda.Event()
         ev.record(st)

@@ -130,3 +130,36 @@ def test_gather_batch_overflow_changes_no_request():
     for r in reqs:
         assert np.array_equal(before[r], sess.slot_of_block[r]), r
         assert sess.n_free[r][0] == sess.capacity[r]
+
+
+def test_gather_events_time_the_copy_kernel():
+    """Events passed to the gather take the copy kernel's dispatch stamps: the contents are those
+    of an untimed gather, the elapsed time is positive, and with nothing to copy or list the events
+    are still recorded."""
+    log("gather events")
+    wl = conditioned_workload("ctx1m_s", seed=16)
+    sess = make_session(wl, cold_on_device=True, with_masks=False)
+    reqs = list(range(wl.n_req))
+    sel = sess.refresh(reqs, np.stack([wl.hidden[r][0] for r in reqs]), wl.bias)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record(sess.stream)  # torch reads only events it has seen recorded
+    res = sess.gather_many(sel, ev_copy=ev)
+    torch.cuda.synchronize()
+    assert sum(c for c, _ in res.values()) == sum(len(sel[r]) for r in reqs) > 0
+    assert ev[0].elapsed_time(ev[1]) > 0.0
+    for r in reqs:
+        _check_pool(sess, r, sel[r])
+    # the same selection again: nothing enters, only the tables are rewritten
+    res = sess.gather_many(sel, ev_copy=ev)
+    torch.cuda.synchronize()
+    assert all(c == 0 for c, _ in res.values())
+    assert ev[0].elapsed_time(ev[1]) >= 0.0
+    # an empty selection for one request: no copy and no table entry, events recorded at the call
+    empty = {0: np.zeros(0, dtype=np.int32)}
+    res = sess.gather_many(empty, ev_copy=ev)
+    torch.cuda.synchronize()
+    assert res[0] == (0, 0)
+    assert ev[0].elapsed_time(ev[1]) >= 0.0
+    for r in reqs[1:]:
+        _check_pool(sess, r, sel[r])
