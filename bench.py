@@ -593,6 +593,12 @@ def main():
     lat_us = np.array([1e3 * a.elapsed_time(b) for a, b in lat_ev.values()])
     gat_us = np.array([1e3 * a.elapsed_time(b) for a, b in gather_ev.values()])
     copy_us = np.array([1e3 * a.elapsed_time(b) for a, b in copy_ev.values()])
+    # steady-state decode: between the start stamps of two event-timed attention launches lie the
+    # steps from the first to the one before the second, and the refresh work of the second one's
+    # step (a refresh precedes its step's decode), so windows with a refresh in (i1, i2] are left out
+    idx = sorted(att_ev)
+    steady = [(i2 - i1, 1e3 * att_ev[i1][0].elapsed_time(att_ev[i2][0])) for i1, i2 in zip(idx, idx[1:])
+              if not any(wl.refreshes_at(W + i) for i in range(i1 + 1, i2 + 1))]
     attn_bytes = np.array(attn_bytes, dtype=np.float64)
     ev_bytes = attn_bytes[np.array(with_ev)]  # the launches the events timed, in the same order
     achieved = ev_bytes.sum() / (attn_ms.sum() * 1e-3) / 1e9  # GB/s
@@ -685,6 +691,10 @@ def main():
         "decode_attn_us": float(attn_ms.mean() * 1e3),
         "attended_tokens_per_step": float(np.mean(attn_tokens)),
         "refresh_us": float(np.median(ref_us)) if len(ref_us) else None,
+        "refresh_us_p90": float(np.percentile(ref_us, 90)) if len(ref_us) else None,
+        "decode_steady": ({"tokens_per_s": wl.n_req * sum(n for n, _ in steady) / (sum(u for _, u in steady) * 1e-6),
+                           "us_per_step": sum(u for _, u in steady) / sum(n for n, _ in steady),
+                           "steps": int(sum(n for n, _ in steady))} if steady else None),
         "refresh_roofline": ({"achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "algorithmic_bytes": ref_bytes} if len(ref_us) else None),
