@@ -20,6 +20,7 @@ constexpr int kRows = 2;  // rows of A per wave
 constexpr int kReq = 4;   // requests per round
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // A is read once per call: non-temporal 16-byte loads
 __device__ __forceinline__ uint4 load_nt(const uint4* q) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
@@ -39,16 +40,16 @@ struct Elem;
 template <>
 struct Elem<uint16_t> {
     static constexpr int N = 8;  // elements per 16 bytes
-    __device__ static float dot(uint4 a, uint4 b) {
-        float s = bf16_lo(a.x) * bf16_lo(b.x);
-        s = fmaf(bf16_hi(a.x), bf16_hi(b.x), s);
-        s = fmaf(bf16_lo(a.y), bf16_lo(b.y), s);
-        s = fmaf(bf16_hi(a.y), bf16_hi(b.y), s);
-        s = fmaf(bf16_lo(a.z), bf16_lo(b.z), s);
-        s = fmaf(bf16_hi(a.z), bf16_hi(b.z), s);
-        s = fmaf(bf16_lo(a.w), bf16_lo(b.w), s);
-        return fmaf(bf16_hi(a.w), bf16_hi(b.w), s);
+    // acc + a.b over 8 bf16 pairs with the packed dot of two bf16 pairs into fp32
+    // (v_dot2_f32_bf16: the products of bf16 values are exact in fp32), 4 instructions where
+    // unpacking both operands and fusing would take 24 (the unpacking made the kernel ALU-bound)
+    __device__ static float dot_acc(uint4 a, uint4 b, float acc) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.x), bf2(b.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.y), bf2(b.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.z), bf2(b.z), acc, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(bf2(a.w), bf2(b.w), acc, false);
     }
+    __device__ static bf16x2 bf2(unsigned w) { return __builtin_bit_cast(bf16x2, w); }
     // round to nearest, ties to even: add 0x7fff plus the lowest kept bit, keep the high half
     __device__ static uint16_t store(float x) {
         const unsigned b = __float_as_uint(x);
@@ -58,11 +59,11 @@ struct Elem<uint16_t> {
 template <>
 struct Elem<float> {
     static constexpr int N = 4;
-    __device__ static float dot(uint4 a, uint4 b) {
-        float s = __uint_as_float(a.x) * __uint_as_float(b.x);
-        s = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), s);
-        s = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), s);
-        return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), s);
+    __device__ static float dot_acc(uint4 a, uint4 b, float acc) {
+        acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+        acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+        acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+        return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
     }
     __device__ static float store(float x) { return x; }
 };
@@ -103,7 +104,10 @@ __global__ __launch_bounds__(kThreads) void latent_kernel(LatentParams p) {
 #pragma unroll
                 for (int jj = 0; jj < kRows; ++jj)
 #pragma unroll
-                    for (int rr = 0; rr < kReq; ++rr) acc[jj][rr] += live ? E::dot(wc[jj][k], hv[rr][k]) : 0.f;
+                    for (int rr = 0; rr < kReq; ++rr) {
+                        const float t = E::dot_acc(wc[jj][k], hv[rr][k], acc[jj][rr]);
+                        acc[jj][rr] = live ? t : acc[jj][rr];
+                    }
             }
         }
 #pragma unroll
