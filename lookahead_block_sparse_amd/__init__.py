@@ -213,6 +213,49 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+def _nbytes(x) -> int:
+    return x.numel() * x.element_size()
+
+
+def _dev(x, name: str, min_bytes: int = 0) -> Optional[int]:
+    """Address of a buffer the kernels read or write in device memory: a contiguous CUDA tensor of at
+    least min_bytes (or a raw int address, taken as is).  A host buffer here would fault the GPU, so
+    it is refused before anything is enqueued."""
+    if x is None or isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray) or not getattr(x, "is_cuda", False):
+        raise TypeError(f"{name} must be a CUDA tensor (device memory), got {type(x).__name__}"
+                        + ("" if isinstance(x, np.ndarray) else f" on {getattr(x, 'device', '?')}"))
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _nbytes(x) < min_bytes:
+        raise ValueError(f"{name} holds {_nbytes(x)} bytes, the call needs {min_bytes}")
+    return x.data_ptr()
+
+
+def _pinned_or_dev(x, name: str, min_bytes: int = 0, pinned_only: bool = False) -> Optional[int]:
+    """Address of a buffer the kernels may read over the host link: pinned host memory (or, unless
+    pinned_only, device memory), contiguous, of at least min_bytes."""
+    if x is None or isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        raise TypeError(f"{name} must be a pinned or CUDA torch tensor, got a NumPy array")
+    if x.is_cuda:
+        if pinned_only:
+            raise TypeError(f"{name} must be pinned host memory")
+    elif not x.is_pinned():
+        raise TypeError(f"{name} is host memory that is not pinned")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _nbytes(x) < min_bytes:
+        raise ValueError(f"{name} holds {_nbytes(x)} bytes, the call needs {min_bytes}")
+    return x.data_ptr()
+
+
+def _elt(dtype) -> int:
+    return 2 if _dtype_code(dtype) == LSA_BF16 else 4
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -280,6 +323,19 @@ def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_of
                       workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, ev_begin=None,
                       ev_end=None, table_out=None, table_slot_base=None, stream=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    blk = np.asarray(blk_off, dtype=np.int64)
+    n_req, n_blk, e = len(blk) - 1, int(blk[-1]), _elt(dtype)
+    rs = d_model if hidden_req_stride is None else hidden_req_stride
+    n_words = int(((blk[1:] - blk[:-1] + 63) // 64).sum())
+    _dev(hidden, "hidden", ((n_req - 1) * rs + (n_idx - 1) * hidden_idx_stride + d_model) * e)
+    _dev(w_q, "w_q", n_idx * d_model * d_idx * e)
+    _dev(keys, "keys", n_idx * n_blk * d_idx * e)
+    _dev(bias, "bias", n_req * n_idx * 4)
+    _dev(sel_ids, "sel_ids", n_blk * 4)
+    _dev(sel_count, "sel_count", n_req * 4)
+    _dev(masks, "masks", (n_idx + 1) * n_words * 8)
+    _dev(workspace, "workspace")
+    _dev(table_out, "table_out", n_blk * 8)
     a, keep = _refresh_args(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx, hidden=hidden,
                             hidden_req_stride=d_model if hidden_req_stride is None else hidden_req_stride,
                             hidden_idx_stride=hidden_idx_stride, w_q=w_q, keys=keys, blk_off=blk_off, bias=bias,
@@ -309,6 +365,11 @@ def _latent_args(*, dtype, d_model, rank, n_idx, n_req, hidden, w_down, latent, 
 def lsa_query_latent(*, dtype, d_model, rank, n_idx, hidden, w_down, latent, n_req=None, hidden_req_stride=None,
                      hidden_idx_stride=0, ev_begin=None, ev_end=None, stream=None) -> None:
     """latent [n_req][n_idx][rank] = A_i h of every request and indexer (A = w_down [n_idx][rank][d_model])."""
+    nr, e = (n_req if n_req is not None else hidden.shape[0]), _elt(dtype)
+    rs = d_model if hidden_req_stride is None else hidden_req_stride
+    _dev(hidden, "hidden", ((nr - 1) * rs + (n_idx - 1) * hidden_idx_stride + d_model) * e)
+    _dev(w_down, "w_down", n_idx * rank * d_model * e)
+    _dev(latent, "latent", nr * n_idx * rank * e)
     a = _latent_args(dtype=dtype, d_model=d_model, rank=rank, n_idx=n_idx,
                      n_req=n_req if n_req is not None else hidden.shape[0], hidden=hidden, w_down=w_down,
                      latent=latent, hidden_req_stride=hidden_req_stride, hidden_idx_stride=hidden_idx_stride,
@@ -345,6 +406,11 @@ def lsa_label_denoise(*, logits, n_blk, n_blk_dev, labels, n_pos, top_p=0.6, min
                       layer_sets=None, workspace=None, ev_begin=None, ev_end=None, stream=None) -> None:
     """Label denoising of logits [n_layers][n_windows][stride] (fp32 device tensor): per-layer top-p
     sets, then the min_votes vote; labels [n_windows][W] int64 bit words, n_pos / n_naive [n_windows]."""
+    n_win = len(np.atleast_1d(n_blk))
+    for name, x, need in (("logits", logits, 0), ("n_blk_dev", n_blk_dev, n_win * 4), ("labels", labels, 0),
+                          ("n_pos", n_pos, n_win * 4), ("n_naive", n_naive, n_win * 4),
+                          ("layer_sets", layer_sets, 0), ("workspace", workspace, 0)):
+        _dev(x, name, need)
     a, keep = _denoise_args(n_layers=logits.shape[0], n_blk=n_blk, top_p=top_p, min_votes=min_votes,
                             logits=logits, logit_stride=logits.shape[2], n_blk_dev=n_blk_dev,
                             layer_sets=layer_sets, labels=labels, n_pos=n_pos, n_naive=n_naive,
@@ -360,6 +426,10 @@ def lsa_gather_blocks(*, n_blocks, n_slots_total, block_bytes, cold, hot, new_id
     for name, arr in (("slot_of_block", slot_of_block), ("free_slots", free_slots), ("n_free", n_free)):
         if not (isinstance(arr, np.ndarray) and arr.dtype == np.int32 and arr.flags.c_contiguous):
             raise TypeError(f"{name} must be a C-contiguous int32 NumPy array (updated in place)")
+    _pinned_or_dev(cold, "cold", int(n_blocks) * int(block_bytes))
+    _dev(hot, "hot", int(n_slots_total) * int(block_bytes))
+    _pinned_or_dev(stage, "stage", 4 * 4 * len(ids), pinned_only=True)
+    _dev(table_dev, "table_dev", 8 * int(capacity))
     n_copied = np.zeros(1, dtype=np.int32)
     n_kept = np.zeros(1, dtype=np.int32)
     a = GatherArgs()
@@ -411,6 +481,17 @@ def lsa_sparse_decode_workspace(*, dtype, n_heads, head_dim, win_cap, n_req, max
 def lsa_sparse_decode(*, dtype, n_heads, head_dim, win_cap, q, ring, out, workspace, tbl_off, n_sel, seq_len,
                       window, pool=None, n_slots_total=0, table=None, k_new=None, v_new=None, scale=None,
                       max_groups=0, ev_attn_begin=None, ev_attn_end=None, n_sel_dev=None, stream=None) -> None:
+    R, e = len(np.atleast_1d(seq_len)), _elt(dtype)
+    bb = lsa_block_bytes(dtype, head_dim)
+    _dev(q, "q", R * n_heads * head_dim * e)
+    _dev(k_new, "k_new", R * head_dim * e)
+    _dev(v_new, "v_new", R * head_dim * e)
+    _dev(ring, "ring", R * (int(win_cap) // BLOCK_TOKENS) * bb)
+    _dev(pool, "pool", int(n_slots_total) * bb)
+    _dev(table, "table")
+    _dev(out, "out", R * n_heads * head_dim * 4)
+    _dev(workspace, "workspace")
+    _dev(n_sel_dev, "n_sel_dev", R * 4)
     a, keep = _decode_args(dtype=dtype, n_heads=n_heads, head_dim=head_dim, win_cap=win_cap, scale=scale, q=q,
                            k_new=k_new, v_new=v_new, ring=ring, pool=pool, n_slots_total=n_slots_total,
                            table=table, tbl_off=tbl_off, n_sel=n_sel, seq_len=seq_len, window=window, out=out,

@@ -382,3 +382,63 @@ def test_device_gather_validation_before_any_hip_call(over, status):
     a, keep = _dev_gather_args(**over)
     assert L.LIB.lsa_gather_plan_device(ctypes.byref(a), None) == status
     assert L.LIB.lsa_last_error().decode()
+
+
+# ---- the Python wrappers refuse host buffers where the kernels need device memory ----------------
+def _host(n, dtype=None):
+    import torch
+    return torch.zeros(n, dtype=dtype or torch.uint8)
+
+
+@pytest.mark.parametrize("name", ["q", "ring", "out", "workspace", "pool", "table", "k_new", "v_new", "n_sel_dev"])
+def test_decode_wrapper_refuses_host_buffers(name):
+    kw = dict(dtype="bf16", n_heads=16, head_dim=128, win_cap=128, q=FAKE, ring=FAKE, out=FAKE, workspace=FAKE,
+              tbl_off=[0], n_sel=[0], seq_len=[10], window=[10])
+    kw[name] = _host(1 << 20)
+    with pytest.raises(TypeError, match=name):
+        L.lsa_sparse_decode(**kw)
+    kw[name] = np.zeros(1 << 20, dtype=np.uint8)
+    with pytest.raises(TypeError, match=name):
+        L.lsa_sparse_decode(**kw)
+
+
+@pytest.mark.parametrize("name", ["hidden", "w_q", "keys", "bias", "sel_ids", "sel_count", "masks", "workspace",
+                                  "table_out"])
+def test_refresh_wrapper_refuses_host_buffers(name):
+    kw = dict(dtype="bf16", d_model=512, d_idx=128, n_idx=3, hidden=FAKE, w_q=FAKE, keys=FAKE, blk_off=[0, 64],
+              bias=FAKE, sel_ids=FAKE, sel_count=FAKE, workspace=None)
+    kw[name] = _host(1 << 20)
+    with pytest.raises(TypeError, match=name):
+        L.lsa_index_refresh(**kw)
+
+
+@pytest.mark.parametrize("name", ["hidden", "w_down", "latent"])
+def test_latent_wrapper_refuses_host_buffers(name):
+    kw = dict(dtype="bf16", d_model=512, rank=256, n_idx=3, n_req=1, hidden=FAKE, w_down=FAKE, latent=FAKE)
+    kw[name] = _host(1 << 22)
+    with pytest.raises(TypeError, match=name):
+        L.lsa_query_latent(**kw)
+
+
+def test_gather_wrapper_wants_pinned_stage_and_cold():
+    sob = np.full(64, -1, dtype=np.int32)
+    free = np.arange(8, dtype=np.int32)
+    nf = np.array([8], dtype=np.int32)
+    kw = dict(n_blocks=64, n_slots_total=8, block_bytes=32768, cold=FAKE, hot=FAKE, new_ids=[1, 2],
+              slot_of_block=sob, free_slots=free, n_free=nf, capacity=8, stage=FAKE, table_dev=FAKE)
+    for name in ("stage", "cold"):
+        bad = dict(kw, **{name: _host(64 * 32768)})  # host memory that is not pinned
+        with pytest.raises(TypeError, match=name):
+            L.lsa_gather_blocks(**bad)
+    with pytest.raises(TypeError, match="hot"):
+        L.lsa_gather_blocks(**dict(kw, hot=_host(8 * 32768)))
+    # nothing changed in the caller's state
+    assert (sob == -1).all() and nf[0] == 8
+
+
+def test_denoise_wrapper_refuses_host_buffers():
+    import torch
+    kw = dict(logits=torch.zeros((21, 2, 64)), n_blk=[64, 64], n_blk_dev=FAKE, labels=FAKE, n_pos=FAKE,
+              workspace=FAKE)
+    with pytest.raises(TypeError, match="logits"):
+        L.lsa_label_denoise(**kw)
