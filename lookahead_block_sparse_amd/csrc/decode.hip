@@ -69,9 +69,9 @@ struct MergeParams {
 };
 
 // With device-side counts, the split of the tiles over the groups is computed by every group of both
-// kernels from the same inputs (with host-side counts the host computes it): request r's tiles are [pre[r], pre[r+1]) of T = pre[n_req] (its n_sel[r] block tiles, read
-// from the device when the counts live there, then its window tiles); G = min(launched groups, T)
-// groups, group w taking [w T / G, (w+1) T / G), so every group has at least one tile.
+// kernels from the same inputs (with host-side counts the host computes it): request r's tiles are
+// [pre[r], pre[r+1]) of T = pre[n_req] (its n_sel[r] block tiles, read from the device when the
+// counts live there, then its window tiles), split over split_groups(launched groups, T) groups.
 __device__ void tile_split(const int* n_sel_dev, const int* n_sel, const int* n_ring, int n_req, int* s_ns,
                            int* s_pre) {
     if ((int)threadIdx.x < n_req) {
@@ -89,6 +89,34 @@ __device__ void tile_split(const int* n_sel_dev, const int* n_sel, const int* n_
         s_pre[n_req] = pre;
     }
     __syncthreads();
+}
+
+// XCD-aware split.  Work-groups go to the 8 XCDs round-robin (group w runs on XCD w mod 8), and the
+// odd-numbered XCDs read HBM measurably slower than the even ones: with equal shares, per-group
+// timestamps show the groups on odd XCDs finishing 3-6 us after the others in a ~66 us launch.  So a
+// group on an odd XCD gets kOddWeight/kEvenWeight of the tiles of a group on an even one (90% was
+// the best of 85-100% measured; it shortens the launch by ~1 us).  Group w takes tiles
+// [split_bound(w), split_bound(w + 1)); with T >= 2 G every group has at least one tile.
+constexpr long long kEvenWeight = 100, kOddWeight = 90;
+__host__ __device__ __forceinline__ long long split_prefix(long long w) {
+    return kEvenWeight * w - (kEvenWeight - kOddWeight) * (w / 2);
+}
+__host__ __device__ __forceinline__ long long split_bound(long long w, long long T, long long G) {
+    return T * split_prefix(w) / split_prefix(G);
+}
+// groups used for T tiles when the host does not know T: at most n_groups, and T >= 2 G
+__host__ __device__ __forceinline__ long long split_groups(long long n_groups, long long T) {
+    return T / 2 < n_groups ? (T / 2 > 1 ? T / 2 : 1) : n_groups;
+}
+// the group whose range holds tile x (0 <= x < T): the largest w with split_bound(w) <= x
+__device__ __forceinline__ int split_group_of(long long x, long long T, long long G) {
+    int lo = 0, hi = (int)G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (split_bound(mid, T, G) <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -323,10 +351,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
     if (dev_counts) tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.n_req, s_ns, s_pre);
     // both sources are uniform: the LDS values are moved to scalar registers
     auto prefix = [&](int r) { return dev_counts ? __builtin_amdgcn_readfirstlane(s_pre[r]) : p.tile_prefix[r]; };
-    const long long T_ = prefix(p.n_req), G = min((long long)p.n_groups, T_);
+    const long long T_ = prefix(p.n_req), G = split_groups(p.n_groups, T_);
     if (w >= G) return;
-    const int a = (int)((long long)w * T_ / G);
-    const int b = (int)((long long)(w + 1) * T_ / G);
+    const int a = (int)split_bound(w, T_, G);
+    const int b = (int)split_bound(w + 1, T_, G);
     const size_t block_bytes = (size_t)2 * 64 * D * Ops::EB;
 
     int r = 0;
@@ -529,15 +557,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     const int col = threadIdx.x % kMergeCols;
     const int d = c * kMergeCols + col;
     const int sub = threadIdx.x / kMergeCols;
-    // the groups whose tile ranges meet request r's tiles: the group holding tile x is the largest w
-    // with floor(w T / G) <= x, i.e. ceil((x + 1) G / T) - 1
+    // the groups whose tile ranges meet request r's tiles
     int w0 = p.w_lo[r], w1 = p.w_hi[r];
     if (p.n_sel_dev) {
         tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.n_req, s_ns, s_pre);
-        const long long T_ = s_pre[p.n_req], G = min((long long)p.n_groups, T_);
-        auto group_of = [&](long long x) { return (int)(((x + 1) * G + T_ - 1) / T_ - 1); };
-        w0 = group_of(s_pre[r]);
-        w1 = group_of(s_pre[r + 1] - 1);
+        const long long T_ = s_pre[p.n_req], G = split_groups(p.n_groups, T_);
+        w0 = split_group_of(s_pre[r], T_, G);
+        w1 = split_group_of(s_pre[r + 1] - 1, T_, G);
     }
     float m = -INFINITY, acc = 0.f, lsum = 0.f;
     for (int w = w0 + sub; w <= w1; w += 4 * kMergeSub) {
@@ -693,9 +719,9 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
         int wcur = 0;
         for (int r = 0; r < a->n_req; ++r) {
             const long long t0 = dp.tile_prefix[r], t1 = dp.tile_prefix[r + 1];  // t1 > t0 always
-            while ((long long)(wcur + 1) * TT / G <= t0) ++wcur;  // group whose range holds t0
+            while (split_bound(wcur + 1, TT, G) <= t0) ++wcur;  // group whose range holds t0
             int wend = wcur;
-            while ((long long)(wend + 1) * TT / G < t1) ++wend;   // group whose range holds t1-1
+            while (split_bound(wend + 1, TT, G) < t1) ++wend;   // group whose range holds t1-1
             mp.w_lo[r] = wcur;
             mp.w_hi[r] = wend;
         }

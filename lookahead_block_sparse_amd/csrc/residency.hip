@@ -171,6 +171,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     }
 }
 
+// Blocks are copied once per refresh: non-temporal 16-byte loads and stores.  With ordinary stores
+// the L2 sent every written line to memory about twice (12.3M 64-byte write requests for 421 MB of
+// blocks; 6.6M with these), and the copy took 88 us instead of 67 us.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const uint4* q) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(uint4* q, uint4 v) {
+    const u32x4 t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(q));
+}
+
 // Copy c of the launch (the requests' entering blocks concatenated, layer-major) goes to group c,
 // c + G, ...: 256 threads x 16-byte vectors, every load of a block in flight before its stores.
 template <int PER>  // 16-byte vectors per thread per block (block_bytes / 4096)
@@ -200,9 +213,9 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyParams p) {
         for (int v0 = 0; v0 < PER; v0 += STEP) {
             uint4 b[STEP];
 #pragma unroll
-            for (int v = 0; v < STEP; ++v) b[v] = src[(v0 + v) * kCopyThreads + threadIdx.x];
+            for (int v = 0; v < STEP; ++v) b[v] = load_nt(src + (v0 + v) * kCopyThreads + threadIdx.x);
 #pragma unroll
-            for (int v = 0; v < STEP; ++v) dst[(v0 + v) * kCopyThreads + threadIdx.x] = b[v];
+            for (int v = 0; v < STEP; ++v) store_nt(dst + (v0 + v) * kCopyThreads + threadIdx.x, b[v]);
         }
     }
 }
