@@ -75,8 +75,10 @@ def parse():
                          "layers x --denoise-windows windows x 16,384 blocks of synthetic logits per call")
     ap.add_argument("--denoise-windows", type=int, default=64)
     ap.add_argument("--plan", choices=("device", "host"), default="host",
-                    help="where the residency plan of a refresh is made: on the device "
-                         "(lsa_gather_plan_device, no host round trip) or on the host (lsa_gather_blocks_batch)")
+                    help="where the residency plan of a refresh is made: on the host "
+                         "(lsa_gather_blocks_batch; the default, and always with --cold host, as the device "
+                         "plan copies within device memory) or on the device (lsa_gather_plan_device, no host "
+                         "round trip)")
     ap.add_argument("--reactive", action="store_true",
                     help="reactive comparator: every block resident in HBM, the index scored at every step "
                          "and the decode reading the selected blocks in place (refresh cadence 1, no "
@@ -396,7 +398,7 @@ def main():
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False,
                       n_layers=cfg.n_layers, w_down=wl.w_down,
-                      device_plan=(args.plan == "device" and not args.reactive))
+                      device_plan=(args.plan == "device" and not args.reactive and args.cold == "device"))
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
@@ -455,9 +457,18 @@ def main():
     D, H = cfg.head_dim, cfg.n_heads
     dplan = sess.device_plan
     loop = DecodeLoop(sess, wl.ctx, window, out, device_counts=dplan)
-    if not dplan and not args.reactive:
-        # the first launch of a kernel in the process loads its code, inside a timed dispatch's
-        # events: one block into request 0's hot pool and out again, before anything is timed
+    # the first launch of a kernel in the process loads its code, inside a timed dispatch's events:
+    # the copy kernels run once before anything is timed
+    if dplan:
+        # a plan over the empty union planes the session starts with changes nothing
+        import ctypes
+        from lookahead_block_sparse_amd import LIB as _lib
+        if _lib.lsa_gather_plan_device(ctypes.byref(sess._plan_args(0, wl.n_req)[0]),
+                                       ctypes.c_void_p(sess.stream.cuda_stream)) != 0:
+            raise RuntimeError(_lib.lsa_last_error().decode())
+        torch.cuda.synchronize()
+    elif not args.reactive:
+        # one block into request 0's hot pool and out again
         sess.gather_many({0: np.zeros(1, dtype=np.int32)})
         sess.gather_many({0: np.zeros(0, dtype=np.int32)})
         torch.cuda.synchronize()
@@ -497,8 +508,9 @@ def main():
             evs = ref_ev.get(t, (None, None)) if timed_ref else (None, None)
             if dplan:
                 # refresh, plan and copy on the device: nothing comes back to the host
-                sess.refresh_device(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
-                                    ev_plan=gather_ev.get(t, (None, None)))
+                pev = gather_ev.get(t, (None, None)) if timed_ref else \
+                    (first_copy_ev if t == first_refresh else (None, None))
+                sess.refresh_device(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1], ev_plan=pev)
             else:
                 sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
                                    ev_latent=lat_ev.get(t, (None, None)))
@@ -536,6 +548,8 @@ def main():
     for t in range(W):
         step(t, None)
     torch.cuda.synchronize()
+    if dplan and [t for t in range(W) if wl.refreshes_at(t)] == [first_refresh]:
+        first_blocks.append(int(sess.copied_dev.sum().item()))  # the one warm-up refresh
     note(f"timing {K} steps")
     t0 = time.perf_counter()
     for i in range(K):
@@ -626,6 +640,17 @@ def main():
                      + q_in_bytes + int(12 * n_ids) + 4 * wl.n_req)
 
     gather_copy = None
+    if dplan and len(gat_us):
+        # plan + copy kernels (events on the plan's dispatch start and the copy's end)
+        bb = sess.block_bytes * cfg.n_layers
+        gather_copy = {"source": "device memory (HBM)", "kernels": "plan_kernel + copy_kernel",
+                       "plan_and_copy_us": float(np.median(gat_us)),
+                       "bytes_last_refresh": int(sess.copied_dev.sum().item()) * bb}
+        if first_blocks:
+            fb = first_blocks[0] * bb
+            fus = 1e3 * first_copy_ev[0].elapsed_time(first_copy_ev[1])
+            gather_copy["first_refresh"] = {"blocks": int(first_blocks[0]), "bytes": int(fb), "plan_and_copy_us": fus,
+                                            "GB_per_s": fb / (fus * 1e-6) / 1e9}
     if copy_ev and gather_blocks:
         # cold-pool bytes each copy kernel reads (every layer's copy of every entering block); with
         # the cold pool in HBM the kernel writes as many again to the hot pool

@@ -108,12 +108,15 @@ __host__ __device__ __forceinline__ long long split_bound(long long w, long long
 __host__ __device__ __forceinline__ long long split_groups(long long n_groups, long long T) {
     return T / 2 < n_groups ? (T / 2 > 1 ? T / 2 : 1) : n_groups;
 }
-// the group whose range holds tile x (0 <= x < T): the largest w with split_bound(w) <= x
+// the group whose range holds tile x (0 <= x < T): the largest w with split_bound(w) <= x, where
+// floor(T P(w) / P(G)) <= x  <=>  T P(w) < (x + 1) P(G): products only (a 64-bit division is a
+// long instruction sequence on the GPU, and the search makes eight of them)
 __device__ __forceinline__ int split_group_of(long long x, long long T, long long G) {
+    const long long rhs = (x + 1) * split_prefix(G);
     int lo = 0, hi = (int)G - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (split_bound(mid, T, G) <= x) lo = mid;
+        if (T * split_prefix(mid) < rhs) lo = mid;
         else hi = mid - 1;
     }
     return lo;
