@@ -17,14 +17,21 @@ sharing one KV head of dim 128, an 8192-token window, 10% background + 10%
 planted relevant blocks.  Inputs are seeded synthetic data with those shapes
 and distributions.  With --cold device (default) the cold pool sits in HBM, so
 the timed region moves no host data except the selected ids; --cold host puts
-it in pinned host memory and the gather crosses the host link.
+it in pinned host memory and the gather crosses the host link.  The residency
+plan is made on the host (--plan host, the default) or on the device (--plan
+device: no host round trip, the decode reads the counts on the device).
 
 Prints one JSON line.  `value` is end-to-end decode tokens/s (requests x K /
 wall time of the timed steps).  `roofline` describes the attention kernel
 (the dominant kernel): algorithmic bytes per launch / mean launch time from
-HIP events that take the kernel dispatch's own start and end stamps, on every
---event-every-th timed step (default 8: the events still cost stream time, about
-4.5 us per event pair).  `cpu_baseline` times the CPU oracle on a bounded sample.
+HIP events passed to the kernel's launch, on every --event-every-th timed step
+(default 8).  The start event is the dispatch's own start stamp; the end event
+lands a few microseconds after the kernel ends, so the figure is on the low
+side, and the events cost stream time (the GPU idles ~10 us around each timed
+launch).  `decode_steady` is the decode between refreshes, from the start
+stamps of those launches; the refresh, gather and latent kernels are timed the
+same way on at most 8 refreshes.  `cpu_baseline` times the CPU oracle on a
+bounded sample.
 """
 
 from __future__ import annotations
