@@ -25,7 +25,7 @@ Prints one JSON line.  `value` is end-to-end decode tokens/s (requests x K /
 wall time of the timed steps).  `roofline` describes the attention kernel
 (the dominant kernel): algorithmic bytes per launch / mean launch time from
 HIP events passed to the kernel's launch, on every --event-every-th timed step
-(default 8).  The start event is the dispatch's own start stamp; the end event
+(default 16).  The start event is the dispatch's own start stamp; the end event
 lands a few microseconds after the kernel ends, so the figure is on the low
 side, and the events cost stream time (the GPU idles ~10 us around each timed
 launch).  `decode_steady` is the decode between refreshes, from the start
@@ -90,7 +90,7 @@ def parse():
                     help="reactive comparator: every block resident in HBM, the index scored at every step "
                          "and the decode reading the selected blocks in place (refresh cadence 1, no "
                          "gathers, no host round trip)")
-    ap.add_argument("--event-every", type=int, default=8,
+    ap.add_argument("--event-every", type=int, default=16,
                     help="time the attention kernel with HIP events on every N-th timed step (the events "
                          "take the dispatch's own stamps but still cost stream time)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
