@@ -139,3 +139,25 @@ def test_device_plan_overflow_changes_nothing():
         w0, w1 = int(sess.word_off[r]), int(sess.word_off[r + 1])
         assert torch.equal(sess.resident_dev[w0:w1], before[2][w0:w1])
         assert int(sess.n_free_dev[r]) == int(before[4][r])
+
+
+def test_device_counts_split_invariance():
+    """With the counts on the device the kernels compute the split of the tiles themselves (at most
+    half as many groups as tiles, groups on odd XCDs taking a smaller share); every group count gives
+    the oracle's outputs, and the same ones up to the rounding of the bf16 softmax weights."""
+    from workloads import get_config
+
+    cfg = get_config("ctx128k_s").scaled(steps=3)
+    wl = conditioned_workload(cfg, seed=43)
+    log("device-count split invariance")
+    outs = []
+    for mg in (1, 2, 5, 0):
+        sess = make_session(wl, cold_on_device=True, with_masks=False, device_plan=True, max_groups=mg)
+        gpu, _ = _run(wl, sess, [2], check=False)
+        outs.append(gpu[(0, 2)])
+    refs, oref = oracle.simulate(wl, steps=[2])
+    ref = np.stack([oref[(r, 2)] for r in range(wl.n_req)])
+    for o in outs:
+        e = attention_errors(o, ref)
+        assert e[0] <= ABS_TOL and e[1] <= REL_TOL, e
+        assert np.abs(o - outs[-1]).max() <= 5e-3 * np.abs(outs[-1]).max()
