@@ -80,6 +80,8 @@ __global__ __launch_bounds__(kThreads, 8) void topp_kernel(TopPParams p) {
     __shared__ int s_cid[kCand];
     __shared__ unsigned long long s_ce[kCand];
     __shared__ unsigned long long s_se[kCand];
+    __shared__ int s_crank[kCand];
+    __shared__ unsigned s_kb[kMaxBlocks / 32];  // boundary-bucket blocks that are kept, by block id
     __shared__ unsigned long long s_wsum[kWaves];
     __shared__ int s_bstar, s_pstar;
     __shared__ unsigned long long s_before;
@@ -132,6 +134,7 @@ __global__ __launch_bounds__(kThreads, 8) void topp_kernel(TopPParams p) {
     for (int k = threadIdx.x; k < kBuckets; k += kThreads) {
         s_hmass[k] = 0ull;
         s_hcnt[k] = 0u;
+        if (k < kMaxBlocks / 32) s_kb[k] = 0u;
     }
     if (threadIdx.x == 0) s_nc = 0u;
     __syncthreads();
@@ -194,9 +197,9 @@ __global__ __launch_bounds__(kThreads, 8) void topp_kernel(TopPParams p) {
         return;
     }
     if (threadIdx.x == 0) p.crowded[row] = 0;
-    int pstar = 0;
     {
-        // the boundary bucket's blocks, ranked by (logit desc, id asc), walked until the target
+        // the boundary bucket's blocks, ranked by (logit desc, id asc), walked until the target; the
+        // ones kept are marked in s_kb
         const unsigned long long need_b = target - s_before;  // > 0, <= the bucket's mass
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -209,49 +212,75 @@ __global__ __launch_bounds__(kThreads, 8) void topp_kernel(TopPParams p) {
             }
         }
         __syncthreads();
-        for (int c = threadIdx.x; c < (int)cb; c += kThreads) {
-            const unsigned kc = s_ck[c];
-            const int ic = s_cid[c];
-            int rank = 0;
-            for (int q = 0; q < (int)cb; ++q) rank += (s_ck[q] > kc || (s_ck[q] == kc && s_cid[q] < ic)) ? 1 : 0;
-            s_se[rank] = s_ce[c];
-        }
-        __syncthreads();
-        // first rank whose running mass reaches need_b: thread t owns ranks 2t, 2t+1
-        const int r0 = 2 * threadIdx.x;
-        const unsigned long long a0 = r0 < (int)cb ? s_se[r0] : 0ull, a1 = r0 + 1 < (int)cb ? s_se[r0 + 1] : 0ull;
-        const unsigned long long own = a0 + a1;
-        unsigned long long inc = own;
+        if (cb <= 64) {
+            // usually a few dozen blocks: one wave ranks them, scans their masses in rank order and
+            // marks the kept ones, with no group-wide barrier
+            if (wave == 0) {
+                const int c = lane;
+                int rank = 0, id = 0;
+                unsigned long long e = 0ull;
+                if (c < (int)cb) {
+                    const unsigned kc = s_ck[c];
+                    id = s_cid[c];
+                    e = s_ce[c];
+                    for (int q = 0; q < (int)cb; ++q) rank += (s_ck[q] > kc || (s_ck[q] == kc && s_cid[q] < id)) ? 1 : 0;
+                    s_se[rank] = e;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                const unsigned long long own = lane < (int)cb ? s_se[lane] : 0ull;  // mass of rank `lane`
+                unsigned long long inc = own;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned lo = __shfl_up((unsigned)inc, o, 64), hi = __shfl_up((unsigned)(inc >> 32), o, 64);
-            if (lane >= o) inc += ((unsigned long long)hi << 32) | lo;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned lo = __shfl_up((unsigned)inc, o, 64), hi = __shfl_up((unsigned)(inc >> 32), o, 64);
+                    if (lane >= o) inc += ((unsigned long long)hi << 32) | lo;
+                }
+                // the first rank whose running mass reaches need_b
+                const unsigned long long hit = __ballot(lane < (int)cb && inc >= need_b && inc - own < need_b);
+                const int pstar = hit ? __builtin_ctzll(hit) : (int)cb - 1;
+                if (c < (int)cb && rank <= pstar) atomicOr(&s_kb[id >> 5], 1u << (id & 31));
+            }
+        } else {
+            for (int c = threadIdx.x; c < (int)cb; c += kThreads) {
+                const unsigned kc = s_ck[c];
+                const int ic = s_cid[c];
+                int rank = 0;
+                for (int q = 0; q < (int)cb; ++q) rank += (s_ck[q] > kc || (s_ck[q] == kc && s_cid[q] < ic)) ? 1 : 0;
+                s_se[rank] = s_ce[c];
+                s_crank[c] = rank;
+            }
+            __syncthreads();
+            // first rank whose running mass reaches need_b: thread t owns ranks 2t, 2t+1
+            const int r0 = 2 * threadIdx.x;
+            const unsigned long long a0 = r0 < (int)cb ? s_se[r0] : 0ull, a1 = r0 + 1 < (int)cb ? s_se[r0 + 1] : 0ull;
+            const unsigned long long own = a0 + a1;
+            unsigned long long inc = own;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const unsigned lo = __shfl_up((unsigned)inc, o, 64), hi = __shfl_up((unsigned)(inc >> 32), o, 64);
+                if (lane >= o) inc += ((unsigned long long)hi << 32) | lo;
+            }
+            __syncthreads();  // every thread is done reading s_wsum of the bucket scan
+            if (lane == 63) s_wsum[wave] = inc;
+            __syncthreads();
+            unsigned long long run = inc - own;
+            for (int v = 0; v < wave; ++v) run += s_wsum[v];
+            if (r0 < (int)cb) {
+                if (run < need_b && run + a0 >= need_b) s_pstar = r0;
+                else if (r0 + 1 < (int)cb && run + a0 < need_b && run + a0 + a1 >= need_b) s_pstar = r0 + 1;
+            }
+            __syncthreads();
+            const int pstar = s_pstar;
+            for (int c = threadIdx.x; c < (int)cb; c += kThreads)
+                if (s_crank[c] <= pstar) atomicOr(&s_kb[s_cid[c] >> 5], 1u << (s_cid[c] & 31));
         }
-        __syncthreads();  // every thread is done reading s_wsum of the bucket scan
-        if (lane == 63) s_wsum[wave] = inc;
         __syncthreads();
-        unsigned long long run = inc - own;
-        for (int v = 0; v < wave; ++v) run += s_wsum[v];
-        if (r0 < (int)cb) {
-            if (run < need_b && run + a0 >= need_b) s_pstar = r0;
-            else if (r0 + 1 < (int)cb && run + a0 < need_b && run + a0 + a1 >= need_b) s_pstar = r0 + 1;
-        }
-        __syncthreads();
-        pstar = s_pstar;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int b = threadIdx.x + kThreads * i;
             bool keep = false;
             if (b < n) {
                 const int k = bucket_of(xv[i]);
-                if (k < bstar) {
-                    keep = true;
-                } else if (k == bstar) {
-                    int rank = 0;
-                    for (int q = 0; q < (int)cb; ++q)
-                        rank += (s_ck[q] > key_of(i) || (s_ck[q] == key_of(i) && s_cid[q] < b)) ? 1 : 0;
-                    keep = rank <= pstar;
-                }
+                keep = k < bstar || (k == bstar && ((s_kb[b >> 5] >> (b & 31)) & 1u));
             }
             const unsigned long long bits = __ballot(keep);
             const int word = kWaves * i + wave;

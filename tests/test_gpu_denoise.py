@@ -75,11 +75,29 @@ def test_denoise_matches_oracle():
 
 
 def test_denoise_ties_taken_by_block_id():
-    """Integer logits: long runs of equal logits straddle the top-p boundary."""
+    """Integer logits: long runs of equal logits straddle the top-p boundary.  The run of equal
+    logits at a row's cut (computed here in float64) is ranked in one wave when it has at most 64
+    blocks, by the whole group up to 1,024, and by the bisection kernel beyond; the two workloads'
+    rows cover all three."""
     from workloads import build_denoise_workload
 
-    dw = build_denoise_workload([16384, 5000, 777], seed=4, integer_logits=True, noise=1.5)
-    _check(dw, 0.6, 3)
+    def cut_runs(dw):
+        runs = []
+        for l in range(dw.n_layers):
+            for w in range(dw.n_windows):
+                x = dw.row(l, w).astype(np.float64)
+                o = np.argsort(-x, kind="stable")
+                pr = np.exp(x[o] - x.max())
+                cut = int(np.searchsorted(np.cumsum(pr), 0.6 * pr.sum()))
+                runs.append(int((x == x[o][cut]).sum()))
+        return runs
+
+    wide = build_denoise_workload([16384, 5000, 777], seed=4, integer_logits=True, noise=1.5)
+    narrow = build_denoise_workload([16384, 3000], seed=7, integer_logits=True, noise=0.5, n_layers=5)
+    runs = np.array(cut_runs(wide) + cut_runs(narrow))
+    assert (runs <= 64).any() and ((runs > 64) & (runs <= 1024)).any() and (runs > 1024).any(), np.unique(runs)
+    _check(wide, 0.6, 3)
+    _check(narrow, 0.6, 3)
 
 
 @pytest.mark.parametrize("top_p,min_votes", [(0.3, 1), (0.9, 21), (1.0, 3), (0.6, 11)])
