@@ -440,13 +440,13 @@ def main():
     out = torch.empty((wl.n_req, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
     window = np.full(wl.n_req, cfg.window, dtype=np.int32)
 
-    def mk_event():
+    def new_event():
         e = torch.cuda.Event(enable_timing=True)
         e.record()
         return e
 
     ev_every = max(1, args.event_every)
-    att_ev = {i: (mk_event(), mk_event()) for i in range(0, K, ev_every)}
+    att_ev = {i: (new_event(), new_event()) for i in range(0, K, ev_every)}
     ref_ev = {}
     lat_ev = {}
     gather_ev = {}
@@ -456,6 +456,13 @@ def main():
     # on the refresh's critical path): at most about 8, evenly spread over the timed steps
     refresh_steps = [t for t in range(W, W + K) if wl.refreshes_at(t)]
     timed_refresh = set(refresh_steps[::max(1, len(refresh_steps) // 8)])
+    # the refreshes' events are made and recorded once before timing: made inside the loop they
+    # cost ~60 us of host time per refresh while the GPU waits for the gather's launch
+    ev_pool = [new_event() for _ in range(8 * len(timed_refresh) + 8)]
+
+    def mk_event():
+        return ev_pool.pop() if ev_pool else new_event()
+
     first_copy_ev = (mk_event(), mk_event())  # the first refresh loads every selected block
     first_blocks = []
     torch.cuda.synchronize()

@@ -340,10 +340,17 @@ lsa_status gather_batch(const lsa_gather_args* args, int n, hipStream_t stream) 
         const GatherParams& gp = launches[k].first;
         const dim3 grid(launches[k].second), block(256);
         hipEvent_t b = k == 0 ? ev0 : nullptr, e = k + 1 == launches.size() ? ev1 : nullptr;
-        switch (gp.block_bytes / 4096) {
-            case 4: hipExtLaunchKernelGGL(gather_kernel<4>, grid, block, 0, stream, b, e, 0, gp); break;
-            case 8: hipExtLaunchKernelGGL(gather_kernel<8>, grid, block, 0, stream, b, e, 0, gp); break;
-            default: hipExtLaunchKernelGGL(gather_kernel<16>, grid, block, 0, stream, b, e, 0, gp); break;
+        // a launch that records events costs ~30 us of host time, a plain one ~3 us; after a
+        // refresh the GPU waits for this launch, so events are taken only when asked for
+        const int per = gp.block_bytes / 4096;
+        if (b || e) {
+            if (per == 4) hipExtLaunchKernelGGL(gather_kernel<4>, grid, block, 0, stream, b, e, 0, gp);
+            else if (per == 8) hipExtLaunchKernelGGL(gather_kernel<8>, grid, block, 0, stream, b, e, 0, gp);
+            else hipExtLaunchKernelGGL(gather_kernel<16>, grid, block, 0, stream, b, e, 0, gp);
+        } else {
+            if (per == 4) hipLaunchKernelGGL(gather_kernel<4>, grid, block, 0, stream, gp);
+            else if (per == 8) hipLaunchKernelGGL(gather_kernel<8>, grid, block, 0, stream, gp);
+            else hipLaunchKernelGGL(gather_kernel<16>, grid, block, 0, stream, gp);
         }
         LSA_HIP(hipGetLastError());
     }

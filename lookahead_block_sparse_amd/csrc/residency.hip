@@ -333,7 +333,11 @@ extern "C" lsa_status lsa_gather_plan_device(const lsa_device_gather_args* a, hi
         pp.slot_off[r] = a->slot_off[r];
         if (r < a->n_req) wo += (int)((a->blk_off[r + 1] - a->blk_off[r] + 63) / 64);
     }
-    hipExtLaunchKernelGGL(plan_kernel, dim3(a->n_req), dim3(kPlanThreads), 0, stream, a->ev_begin, nullptr, 0, pp);
+    // events only when asked for: a launch that records them costs ~30 us of host time
+    if (a->ev_begin)
+        hipExtLaunchKernelGGL(plan_kernel, dim3(a->n_req), dim3(kPlanThreads), 0, stream, a->ev_begin, nullptr, 0, pp);
+    else
+        hipLaunchKernelGGL(plan_kernel, dim3(a->n_req), dim3(kPlanThreads), 0, stream, pp);
     LSA_HIP(hipGetLastError());
     CopyParams cp;
     for (int r = 0; r < a->n_req; ++r) cp.cold[r] = static_cast<const char*>(a->cold[r]);
@@ -352,9 +356,18 @@ extern "C" lsa_status lsa_gather_plan_device(const lsa_device_gather_args* a, hi
     if (st != LSA_OK) return st;
     const dim3 grid(dev.cu_count * 8), block(kCopyThreads);
     switch (a->block_bytes / (kCopyThreads * 16)) {
-        case 4: hipExtLaunchKernelGGL(copy_kernel<4>, grid, block, 0, stream, nullptr, a->ev_end, 0, cp); break;
-        case 8: hipExtLaunchKernelGGL(copy_kernel<8>, grid, block, 0, stream, nullptr, a->ev_end, 0, cp); break;
-        default: hipExtLaunchKernelGGL(copy_kernel<16>, grid, block, 0, stream, nullptr, a->ev_end, 0, cp); break;
+        case 4:
+            if (a->ev_end) hipExtLaunchKernelGGL(copy_kernel<4>, grid, block, 0, stream, nullptr, a->ev_end, 0, cp);
+            else hipLaunchKernelGGL(copy_kernel<4>, grid, block, 0, stream, cp);
+            break;
+        case 8:
+            if (a->ev_end) hipExtLaunchKernelGGL(copy_kernel<8>, grid, block, 0, stream, nullptr, a->ev_end, 0, cp);
+            else hipLaunchKernelGGL(copy_kernel<8>, grid, block, 0, stream, cp);
+            break;
+        default:
+            if (a->ev_end) hipExtLaunchKernelGGL(copy_kernel<16>, grid, block, 0, stream, nullptr, a->ev_end, 0, cp);
+            else hipLaunchKernelGGL(copy_kernel<16>, grid, block, 0, stream, cp);
+            break;
     }
     LSA_HIP(hipGetLastError());
     return LSA_OK;
