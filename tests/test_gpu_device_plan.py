@@ -161,3 +161,46 @@ def test_device_counts_split_invariance():
         e = attention_errors(o, ref)
         assert e[0] <= ABS_TOL and e[1] <= REL_TOL, e
         assert np.abs(o - outs[-1]).max() <= 5e-3 * np.abs(outs[-1]).max()
+
+
+def test_device_plan_events_change_nothing():
+    """Events passed to the refresh and to the device plan (launches that record dispatch stamps)
+    time the kernels and leave every result (table, counts, resident set, free stack, hot pool) as
+    the plain launches give it, over two refreshes."""
+    from workloads import get_config
+
+    cfg = get_config("ctx128k_s").scaled(steps=70)
+    wl = conditioned_workload(cfg, seed=42)
+    R = wl.n_req
+    results = []
+    for timed in (False, True):
+        log(f"device plan, events={timed}")
+        sess = make_session(wl, cold_on_device=True, with_masks=False, device_plan=True)
+        dev = sess.device
+        bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+        pairs = []
+        for k in (0, 1):
+            hid = raw_to_torch(np.stack([wl.hidden[r][min(k, len(wl.hidden[r]) - 1)] for r in range(R)]), dev)
+            if timed:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                for e in ev:
+                    e.record()  # torch creates the HIP event at its first record
+                sess.refresh_device(list(range(R)), hid, bias, ev_begin=ev[0], ev_end=ev[1], ev_plan=(ev[2], ev[3]))
+                pairs += [(ev[0], ev[1]), (ev[2], ev[3])]
+            else:
+                sess.refresh_device(list(range(R)), hid, bias)
+        torch.cuda.synchronize()
+        for a, b in pairs:
+            assert a.elapsed_time(b) > 0
+        # the hot pool is not initialised: compare the slots the tables name
+        tbl, cnt = sess.table.view(-1, 2).cpu().numpy(), sess.table_count.cpu().numpy()
+        slots = np.concatenate([tbl[int(sess.slot_base[r]):int(sess.slot_base[r]) + int(cnt[r]), 1] for r in range(R)])
+        assert len(slots) > 0
+        hot = sess.hot[:sess.n_slots * sess.block_bytes].view(sess.n_slots, sess.block_bytes)
+        used = hot[torch.from_numpy(slots.astype(np.int64)).to(dev)]
+        results.append([t.clone() for t in (sess.table, sess.table_count, sess.resident_dev, sess.free_dev,
+                                            sess.n_free_dev, sess.slot_of_block_dev, sess.copied_dev,
+                                            sess.plan_status)] + [used])
+        del sess
+    for x, y in zip(*results):
+        assert torch.equal(x, y)
