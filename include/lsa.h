@@ -247,7 +247,9 @@ typedef struct lsa_gather_args {
                                   dispatch (of the first one, in a batch); only a[0]'s are used by
                                   lsa_gather_blocks_batch.  With nothing to launch, recorded on the
                                   stream at the call. */
-    hipEvent_t ev_end;         /* optional (NULL): the end stamp of the (last) copy kernel's dispatch */
+    hipEvent_t ev_end;         /* optional (NULL): the end stamp of the (last) copy kernel's dispatch.
+                                  A launch that records stamps costs ~30 us of host time against ~3 us
+                                  for a plain one, so leave both NULL outside measurement. */
 } lsa_gather_args;
 
 lsa_status lsa_gather_blocks(const lsa_gather_args* a, hipStream_t stream);
@@ -300,8 +302,10 @@ typedef struct lsa_device_gather_args {
                                   refresh that gave up */
     void* workspace;           /* dev, workspace_bytes >= lsa_gather_plan_device_workspace() */
     size_t workspace_bytes;
-    hipEvent_t ev_begin;       /* optional, used only when both are set: start of the plan */
-    hipEvent_t ev_end;         /* dispatch and end of the copy dispatch */
+    hipEvent_t ev_begin;       /* optional (NULL): the start stamp of the plan kernel's dispatch */
+    hipEvent_t ev_end;         /* optional (NULL): the end stamp of the copy kernel's dispatch; each is
+                                  used on its own, and a launch that records a stamp costs ~30 us of
+                                  host time against ~3 us for a plain one */
 } lsa_device_gather_args;
 
 lsa_status lsa_gather_plan_device_workspace(const lsa_device_gather_args* a, size_t* bytes);
