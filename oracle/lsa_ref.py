@@ -240,6 +240,16 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.n
     return (w @ v) / w.sum(axis=1, keepdims=True)
 
 
+def seq_len_at(n_prefill: int, t: int) -> int:
+    """Tokens in the cache at decode step t: the prefill plus the tokens of steps 0..t.
+
+    [Explained] section 2 step 4: each decode step attends with the token it is producing; that
+    token (the one of step t) sits at position n_prefill + t, so the step sees L = n_prefill + t + 1
+    positions, the last of which is its own (it is in the recent window, section 1).
+    """
+    return int(n_prefill) + int(t) + 1
+
+
 def kv_rows(prefill: np.ndarray, new_rows: np.ndarray, n_prefill: int, positions: np.ndarray) -> np.ndarray:
     """Rows of the K (or V) cache at `positions`: prefill rows below n_prefill,
     decode-time rows (new_rows[p - n_prefill]) at and above it."""
@@ -305,7 +315,7 @@ def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Seque
         v_new = decode_values(wl.v_new_of(layer)[:, r] if layer else wl.v_new[:, r], dt)
         q_all = wl.q_dec_of(layer) if layer else wl.q_dec
         for t in step_list:
-            L = n + t + 1
+            L = seq_len_at(n, t)
             k_idx = governing_refresh(t, wl.refresh_steps[r])
             pos = token_set(L, cfg.window, res[k_idx].ids, cfg.block)
             kk = kv_rows(kp, k_new, n, pos)

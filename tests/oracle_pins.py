@@ -348,6 +348,70 @@ def pin_simulate_layer_uses_its_own_inputs(O):
     assert all(np.array_equal(a.ids, b.ids) for a, b in zip(refs0[0], refs1[0]))
 
 
+def _tiny_decode_workload(seed, steps=12, bias=None):
+    """The fp32 tiny workload cut to a few steps (one refresh at step 0), optionally with every
+    indexer's bias replaced."""
+    from workloads import build_workload, get_config
+
+    wl = build_workload(get_config("tiny").scaled(steps=steps), seed=seed)
+    if bias is not None:
+        wl.bias = np.full_like(wl.bias, bias)
+    return wl
+
+
+def pin_simulate_is_decode_over_grown_cache(O):
+    """simulate() at step t equals one decode step over caches built by hand as the prefill
+    rows followed by the rows of the tokens of steps 0..t, with L = N + t + 1 positions: the
+    token being produced at step t is position N + t and attends to itself ([Explained] section 2
+    step 4; the recent window holds the newest tokens)."""
+    wl = _tiny_decode_workload(seed=21)
+    steps = [0, 1, 5, 11]
+    refs, out = O.simulate(wl, steps=steps)
+    ids = refs[0][0].ids
+    assert 0 < len(ids) < wl.n_blocks[0]
+    kp, vp = wl.kv_prefill(0)
+    N = int(wl.ctx[0])
+    for t in steps:
+        k_cache = np.concatenate([kp, wl.k_new[: t + 1, 0]]).astype(np.float64)
+        v_cache = np.concatenate([vp, wl.v_new[: t + 1, 0]]).astype(np.float64)
+        assert k_cache.shape[0] == N + t + 1
+        want = O.decode_step(wl.q_dec[t, 0].astype(np.float64), k_cache, v_cache, N + t + 1,
+                             wl.cfg.window, ids)
+        assert np.allclose(out[(0, t)], want, rtol=0, atol=1e-13), (t, np.abs(out[(0, t)] - want).max())
+
+
+def pin_simulate_decode_positions_closed_form(O):
+    """All keys zero (prefill and new tokens) gives equal weights, so o = mean of V over the
+    attended set.  V is one-hot in column 0 at one token appended during decode (step t0, position
+    N + t0), zero elsewhere.  At step t the output is 1/|T_t| in column 0 when t >= t0 (the token
+    is in the window; at t = t0 it is the current token) and exactly 0 for t < t0, where
+    |T_t| = W + (tokens of selected blocks below the window start L - W) is counted by hand."""
+    for bias, expect_all in ((-1e4, False), (1e4, True), (None, None)):
+        wl = _tiny_decode_workload(seed=22, bias=bias)
+        N, W, T = int(wl.ctx[0]), wl.cfg.window, wl.cfg.steps
+        kp, vp = wl.kv_prefill(0)
+        wl.set_kv_prefill(0, np.zeros_like(kp), np.zeros_like(vp))
+        wl.k_new = np.zeros_like(wl.k_new)
+        refs, _ = O.simulate(wl, steps=[])
+        sel = refs[0][0].ids.tolist()
+        if expect_all is not None:
+            assert len(sel) == (wl.n_blocks[0] if expect_all else 0)
+        for t0 in (0, 4, T - 1):
+            v_new = np.zeros_like(wl.v_new)
+            v_new[t0, 0, 0] = 1.0
+            wl.v_new = v_new
+            steps = sorted({0, max(0, t0 - 1), t0, min(T - 1, t0 + 3), T - 1})
+            _, out = O.simulate(wl, steps=steps)
+            for t in steps:
+                L = N + t + 1
+                ws = L - W
+                count = W + sum(max(0, min(64 * b + 64, ws) - 64 * b) for b in sel)
+                want = 1.0 / count if t >= t0 else 0.0
+                o = out[(0, t)]
+                assert np.all(np.abs(o[:, 0] - want) < 1e-15), (bias, t0, t, o[0, 0], want)
+                assert np.all(o[:, 1:] == 0.0)
+
+
 # ------------------------------------------------------------------------------------------
 def _bf16_rne_bits(x32: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 with integer arithmetic on the binary32 bits: add 0x7FFF
@@ -459,6 +523,8 @@ PINS = [
     pin_bias_monotone,
     pin_block_permutation,
     pin_simulate_layer_uses_its_own_inputs,
+    pin_simulate_is_decode_over_grown_cache,
+    pin_simulate_decode_positions_closed_form,
     pin_round_bf16,
     pin_query_latent,
     pin_lowrank_query_is_product,

@@ -172,6 +172,21 @@ def _m_simulate_ignores_latent(wl, steps=None, requests=None, layer=0):
     moved.hidden = [np.ascontiguousarray(h[:, :rank]) for h in wl.hidden]
     return _orig["simulate"](moved, steps, requests, layer)
 
+def _m_kv_rows_off_by_one(prefill, new_rows, n_prefill, positions):
+    """Decode-time rows shifted by one: position p reads the token of step p - N - 1."""
+    positions = np.asarray(positions, dtype=np.int64)
+    out = np.empty((len(positions), prefill.shape[1]), dtype=np.float64)
+    lo = positions < n_prefill
+    out[lo] = prefill[positions[lo]]
+    out[~lo] = new_rows[positions[~lo] - n_prefill - 1]
+    return out
+
+
+def _m_seq_len_no_current(n_prefill, t):
+    """The step attends to the tokens before it but not to its own."""
+    return int(n_prefill) + int(t)
+
+
 MUTATIONS = [
     ("threshold", _m_threshold_ge),
     ("threshold", _m_threshold_prob),
@@ -201,6 +216,8 @@ MUTATIONS = [
     ("query_latent", _m_latent_transposed),
     ("query_latent", _m_latent_shared_hidden),
     ("simulate", _m_simulate_ignores_latent),
+    ("kv_rows", _m_kv_rows_off_by_one),
+    ("seq_len_at", _m_seq_len_no_current),
 ]
 
 
