@@ -83,6 +83,13 @@ def parse():
                     help="measure the indexer's label-denoising pipeline instead of the decode loop: 21 "
                          "layers x --denoise-windows windows x 16,384 blocks of synthetic logits per call")
     ap.add_argument("--denoise-windows", type=int, default=64)
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="measure the cold-read ceiling of one launch at the refresh's and the attention's "
+                         "sizes with the read probe (libprobe.so) instead of the decode loop")
+    ap.add_argument("--ceiling-reps", type=int, default=10)
+    ap.add_argument("--kernel-trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="no run: per kernel and grid size, the dispatch durations of a rocprofv3 "
+                         "--kernel-trace CSV")
     ap.add_argument("--plan", choices=("device", "host"), default="host",
                     help="where the residency plan of a refresh is made: on the host "
                          "(lsa_gather_blocks_batch; the default, and always with --cold host, as the device "
@@ -348,6 +355,90 @@ def run_denoise(args) -> dict:
     return res
 
 
+def run_read_ceiling(args) -> dict:
+    """Cold-read ceilings for the two hot kernels' sizes: one launch of the read probe
+    (libprobe.so) per size, access pattern, load hint, loads per batch and launch shape, each
+    reading a region last touched more than 1 GB of reads earlier (past the 256 MB memory-side
+    cache), timed with the dispatch's own start and end stamps."""
+    import ctypes
+
+    import torch
+
+    torch.cuda.init()
+    lib = ctypes.CDLL(str(ROOT / "lookahead_block_sparse_amd" / "libprobe.so"))
+    lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    lib.probe_batches.argtypes = [ctypes.c_longlong, ctypes.c_int]
+    lib.probe_batches.restype = ctypes.c_longlong
+    lib.probe_groups_per_cu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    dev = torch.device("cuda")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream()
+    # the refresh's bytes at 4 x 1M (W_q + keys) and the attention's (4 x ~206K tokens of K and V)
+    sizes = {"refresh": 3 * 4096 * 256 * 2 + 4 * 3 * 16384 * 256 * 2, "attention": 416 << 20}
+    reps = max(3, args.ceiling_reps)
+    rows = []
+    for name, size in sizes.items():
+        stride = (size + (1 << 20) - 1) >> 20 << 20
+        n_reg = max(3, -(-(1200 << 20) // stride))
+        buf = torch.empty(n_reg * stride, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        reg = 0
+        for pattern in (0, 1):
+            for nt in (1, 0):
+                for loads in (16, 48):
+                    per_cu = lib.probe_groups_per_cu(pattern, loads, nt)
+                    nb = lib.probe_batches(size, loads)
+                    for groups in (0, cus * per_cu):
+                        g_launch = groups if groups else (nb + 3) // 4
+                        if sink.numel() < 256 * g_launch:
+                            sink = torch.zeros(256 * g_launch, dtype=torch.int32, device=dev)
+                        evs = []
+                        for _ in range(reps + 1):  # the first launch of a variant loads its code
+                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            e0.record()
+                            e1.record()
+                            ptr = buf.data_ptr() + reg * stride
+                            reg = (reg + 1) % n_reg
+                            rc = lib.probe_read(ptr, size, pattern, loads, nt, groups, sink.data_ptr(),
+                                                0xDEADBEEF, e0.cuda_event, e1.cuda_event, stream.cuda_stream)
+                            if rc != 0:
+                                raise RuntimeError(f"probe_read returned {rc}")
+                            evs.append((e0, e1))
+                        torch.cuda.synchronize()
+                        us = np.array([1e3 * a.elapsed_time(b) for a, b in evs[1:]])
+                        read = nb * loads * 1024
+                        rows.append({"size": name, "bytes": int(read), "pattern": ("runs", "rows")[pattern],
+                                     "nontemporal": bool(nt), "loads_per_batch": loads,
+                                     "shape": "one-shot" if groups == 0 else f"persistent {per_cu}/CU",
+                                     "groups": int(g_launch), "median_us": float(np.median(us)),
+                                     "min_us": float(us.min()), "TB_per_s": read / (np.median(us) * 1e-6) / 1e12})
+        del buf
+        torch.cuda.empty_cache()
+    return {"metric": "cold-read ceiling of one launch", "rows": rows, "reps": reps,
+            "note": "event-timed dispatches; each launch reads a region last read more than 1 GB earlier"}
+
+
+def kernel_trace_summary(path: str) -> dict:
+    """Per (kernel, grid size): dispatch count, mean and median duration in us, from the
+    kernel_trace.csv of a rocprofv3 --kernel-trace run."""
+    import csv
+
+    groups = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        key = (name, int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0))
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    out = []
+    for (name, grid), us in sorted(groups.items()):
+        a = np.array(us)
+        out.append({"kernel": name, "grid_x": grid, "dispatches": len(a), "mean_us": float(a.mean()),
+                    "median_us": float(np.median(a)), "min_us": float(a.min())})
+    return {"trace": path, "kernels": out}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -366,6 +457,12 @@ def main():
 
     if args.denoise:
         print(json.dumps(run_denoise(args)), flush=True)
+        return
+    if args.kernel_trace_summary:
+        print(json.dumps(kernel_trace_summary(args.kernel_trace_summary)), flush=True)
+        return
+    if args.read_ceiling:
+        print(json.dumps(run_read_ceiling(args)), flush=True)
         return
 
     import torch

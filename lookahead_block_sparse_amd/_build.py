@@ -3,7 +3,8 @@
     python lookahead_block_sparse_amd/_build.py
 
 Objects go to lookahead_block_sparse_amd/_build/, the library to
-lookahead_block_sparse_amd/liblsa.so.  Every call recompiles.
+lookahead_block_sparse_amd/liblsa.so, and the read-bandwidth probe (probe/, used only by
+bench.py --read-ceiling) to lookahead_block_sparse_amd/libprobe.so.  Every call recompiles.
 """
 
 from __future__ import annotations
@@ -20,6 +21,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "liblsa.so"
+PROBE_DIR = PKG / "probe"
+PROBE_LIB = PKG / "libprobe.so"
 ARCH = "gfx950"
 
 # Device code: no packed-fp32 instructions; -O3.  The host pass warns that it does not know the
@@ -55,11 +58,29 @@ def _compile(src: Path) -> Path:
     return obj
 
 
+def build_probe(verbose: bool = True) -> Path:
+    """libprobe.so: the read-bandwidth probe (measurement only; not part of liblsa.so)."""
+    BUILD.mkdir(exist_ok=True)
+    src = PROBE_DIR / "read_probe.hip"
+    obj = _compile(src)
+    tmp = PROBE_LIB.with_suffix(".so.tmp")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), str(obj)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"linking libprobe.so failed:\n{' '.join(cmd)}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}", file=sys.stderr)
+    return PROBE_LIB
+
+
 def build(verbose: bool = True) -> Path:
     BUILD.mkdir(exist_ok=True)
     srcs = sources()
-    with ThreadPoolExecutor(max(1, min(len(srcs), os.cpu_count() or 1))) as ex:
+    with ThreadPoolExecutor(max(1, min(len(srcs) + 1, os.cpu_count() or 1))) as ex:
+        probe = ex.submit(build_probe, verbose)
         objs = list(ex.map(_compile, srcs))
+        probe.result()
     tmp = LIB.with_suffix(".so.tmp")
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs), "-lpthread"]
     res = subprocess.run(cmd, capture_output=True, text=True)

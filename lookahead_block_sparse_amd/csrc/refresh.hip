@@ -2,20 +2,31 @@
 // ordered compaction of the loaded-block list (zhichai.net explainer of "FlashMemory-DeepSeek-V4",
 // section 2 steps 2-3, section 3 (Query Encoder, frozen KIComp keys), section 4 (OR-mode union)).
 //
-// One kernel of 4-wave groups, four roles in this order of group index:
-//   encode   q[r][i][j] = sum_m W_q[i][j][m] h[r][i][m]: two waves per pair of output rows, each
-//            W_q row read once for every request, fp32 accumulation, q kept in fp32.
-//   prefetch as many groups as fit beside the encode groups at the start: read the keys of the
-//            first score units and drop them, so HBM streams keys into the memory-side cache while
-//            q is computed.
-//   score    one wave per unit = 32 key rows of one indexer in one 64-block word.  The wave issues
-//            all loads of its rows, then waits for its q, forms z = q.k + bias in fp32, turns z > 0
-//            into 32 bits with a wavefront ballot and publishes them.  Waves never synchronise with
-//            the other waves of their group.
-//   compact  one per 64 words of a request: waits until every unit of the request up to its words
-//            has published, ORs the indexers' bits into the union words, offsets its words by the
-//            popcounts before them and a wave scan, and writes their ids in ascending order; the
-//            last one of a request writes the count.
+// One launch of 4-wave groups, three roles in this order of group index:
+//   encode   q[r][i][j] = sum_m W_q[i][j][m] h[r][i][m]: a wave owns two whole output rows of one
+//            indexer for four requests; it requests both W_q rows and the four hidden states in
+//            one batch, accumulates in fp32 and publishes the eight values of q (kept in fp32).
+//   score    one wave per half of a 64-block word (32 blocks), all indexers: for each indexer the
+//            32 key rows are contiguous and read as whole 1 KiB runs (lane l takes bytes 16 l ..
+//            16 l + 15 of each run, so a lane works on one fixed 16-byte column of its rows and
+//            needs only the matching 4 or 8 values of q).  The wave requests the rows of up to
+//            three indexers (48 KiB) at once, then waits for q, forms z = q.k + bias in fp32 (per-
+//            lane partial dot products, then a reduce-scatter across the lanes of a row), turns
+//            z > 0 into 32 bits per indexer with a wavefront ballot, ORs the indexers and publishes
+//            the 32 union bits of its half word.
+//   compact  one per 64 words of a request: waits until every half word of the request up to its
+//            words has published, offsets its words by the popcounts before them and a wave scan,
+//            and writes their ids in ascending order; the last one of a request writes the count.
+// Why the score waves hold so much: a value handed from one compute unit to another inside a
+// launch (q here) travels through the memory-side queues and, with the key stream in flight,
+// reaches the score waves ~10 us after the launch starts whatever the rest of the design does.
+// Two groups of 48 KiB waves per compute unit request about 80% of all key bytes at the start of
+// the launch, and a wave asks for q right behind its keys for all its indexers at once, so the
+// memory system streams at full rate while q is computed and the wait for q is hidden behind the
+// keys.  Measured alternatives at 4 x 1M context: one wave per 16 KiB unit at five groups per
+// compute unit (q arrives late and holds the slots: 29-33 us), two launches (encode, then score:
+// q is simply there, but the memory idles during the encode launch and the gap, 4.5 + 2.1 us:
+// 30 us), and fewer resident groups to keep the queues short (31-35 us).
 // A group only waits for groups with a lower index, which were dispatched before it, and every
 // wait is bounded: a wait that gives up marks the request, whose count is then written as -1.
 // Values that cross groups travel in 64-bit words whose upper half is the call's number and lower
@@ -33,6 +44,7 @@ namespace {
 
 constexpr int kMaxReq = LSA_MAX_REFRESH_REQ;
 constexpr int kThreads = 256;
+constexpr int kGroupsPerCU = 2;
 constexpr unsigned kSpinLimit = 1u << 16;
 constexpr unsigned long long kTagMask = 0xffffffff00000000ull;
 
@@ -46,10 +58,10 @@ struct RefreshParams {
     int* sel_count;
     unsigned long long* masks;
     unsigned long long* qw;   // [n_req][n_idx][d_idx]          tag | fp32 bits of q
-    unsigned long long* hw;   // [total words][n_idx][2]        tag | 32 bits of one unit
+    unsigned long long* hw;   // [total words][2]               tag | union bits of one half word
     unsigned long long* bad;  // [n_req]                        tag when a wait of the request gave up
     unsigned long long tag;   // call number << 32
-    int n_req, d_model, d_idx, n_idx, n_units, n_encode_groups, n_prefetch_groups, n_score_groups;
+    int n_req, d_model, d_idx, n_idx, n_halves, n_encode_waves, n_encode_groups, n_score_groups;
     long long blk_off[kMaxReq + 1];
     int word_off[kMaxReq + 1];
     int cg_off[kMaxReq + 1];  // first compaction group of each request
@@ -65,9 +77,7 @@ __device__ __forceinline__ unsigned long long get(const unsigned long long* w) {
 }
 __device__ __forceinline__ bool tagged(unsigned long long w, unsigned long long tag) { return (w & kTagMask) == tag; }
 
-// The score waves read every key once per call: non-temporal 16-byte loads (about 4% faster than
-// ordinary loads for the whole refresh; the prefetch role keeps ordinary loads, whose lines must stay
-// in the memory-side cache for the score waves).
+// Keys and W_q are read once per call: non-temporal 16-byte loads.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_nt(const uint4* q) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
@@ -96,15 +106,27 @@ struct Chunk<float> {
     }
 };
 
+// acc + sum of the 8 (bf16) or 4 (fp32) products of two 16-byte chunks, in fp32.  bf16 uses the
+// packed two-pair dot product (v_dot2_f32_bf16: products of bf16 values are exact in fp32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <typename T>
-__device__ __forceinline__ float dot_chunks(uint4 a, uint4 b) {
-    float x[Chunk<T>::N], y[Chunk<T>::N];
-    Chunk<T>::widen(a, x);
-    Chunk<T>::widen(b, y);
-    float s = x[0] * y[0];
-#pragma unroll
-    for (int e = 1; e < Chunk<T>::N; ++e) s = fmaf(x[e], y[e], s);
-    return s;
+__device__ __forceinline__ float dot_chunks(uint4 a, uint4 b, float acc);
+
+template <>
+__device__ __forceinline__ float dot_chunks<uint16_t>(uint4 a, uint4 b, float acc) {
+    auto bf2 = [](unsigned w) { return __builtin_bit_cast(bf16x2, w); };
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.x), bf2(b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.y), bf2(b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.z), bf2(b.z), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(bf2(a.w), bf2(b.w), acc, false);
+}
+
+template <>
+__device__ __forceinline__ float dot_chunks<float>(uint4 a, uint4 b, float acc) {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
 }
 
 template <typename T>
@@ -124,227 +146,237 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Query Encoder role.  A group works on rows of one indexer: group g = i*gpi + k owns the
-// kEncRows*waves/2 rows from k*kEncRows*waves/2 on; waves 2m and 2m+1 sum the two halves of rows
-// m*kEncRows ..: each wave loads the halves of kEncRows W_q rows and the matching halves of four
-// requests' hidden states in one round (a hidden-state chunk serves every row of the wave).  Lane
-// l reads 16-byte chunks l, l+64, ... of its half.
-constexpr int kEncRows = 2;  // W_q rows per wave
-constexpr int kEncReq = 4;   // requests per round
+// Query Encoder role.  Encode wave e = ((i*gpi + k)*n_quads + m) owns rows 2k and 2k+1 of indexer
+// i (gpi = d_idx/2 row pairs per indexer) for requests 4m .. 4m+3.  A row is read in chunks of
+// kEncPieces 16-byte pieces per lane (the whole row when d_model <= 4096 for bf16, 2048 for fp32);
+// per chunk the wave loads both W_q rows and the four hidden states before any is used.
+constexpr int kEncReq = 4;     // requests per encode wave
+constexpr int kEncRows = 2;    // W_q rows per encode wave
+constexpr int kEncPieces = 8;  // 16-byte pieces per lane per row and chunk
+
+// pieces c0 + lane + 64 k (k < kEncPieces) of a row of hc pieces; pieces past the row are zero
+template <bool NT>
+__device__ __forceinline__ void enc_chunk(uint4* v, const uint4* row, int c0, int hc, int lane) {
+    if (c0 + 64 * kEncPieces <= hc) {
+        // a whole chunk: every load at a fixed distance from the lane's first
+#pragma unroll
+        for (int k = 0; k < kEncPieces; ++k)
+            v[k] = NT ? load_nt(row + c0 + lane + k * 64) : row[c0 + lane + k * 64];
+    } else {
+        // the tail of a short row: loads issued one by one from clamped indices
+#pragma unroll
+        for (int k = 0; k < kEncPieces; ++k) {
+            const int idx = c0 + k * 64 + lane;
+            v[k] = NT ? load_nt(row + min(idx, hc - 1)) : row[min(idx, hc - 1)];
+            if (idx >= hc) v[k] = make_uint4(0u, 0u, 0u, 0u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
 
 template <typename T>
-__device__ void encode_role(const RefreshParams& p, int g) {
+__device__ void encode_role(const RefreshParams& p, int e) {
     using C = Chunk<T>;
-    __shared__ float s_part[8][kEncRows][kEncReq];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int quads = (int)(blockDim.x >> 7);
-    const int gpi = (p.d_idx + kEncRows * quads - 1) / (kEncRows * quads);
-    const int i = g / gpi;
-    const int j0 = ((g % gpi) * quads + (wave >> 1)) * kEncRows;
-    const int half = wave & 1;
-    const int hc = p.d_model / C::N / 2;  // 16-byte chunks per half row
+    const int n_quads = (p.n_req + kEncReq - 1) / kEncReq;
+    const int gpi = (p.d_idx + kEncRows - 1) / kEncRows;
+    const int r0 = (e % n_quads) * kEncReq;
+    const int i = e / n_quads / gpi;
+    const int j0 = (e / n_quads % gpi) * kEncRows;
+    const int hc = p.d_model / C::N;  // 16-byte pieces per row (a multiple of 32)
     const T* wbase = static_cast<const T*>(p.w_q) + (size_t)i * p.d_idx * p.d_model;
     const T* hid = static_cast<const T*>(p.hidden) + (size_t)i * p.hidden_idx_stride;
-    for (int r0 = 0; r0 < p.n_req; r0 += kEncReq) {
-        float acc[kEncRows][kEncReq] = {};
-        for (int c0 = 0; c0 < hc; c0 += 64 * 4) {
-            // unconditional loads from clamped indices (masked after loading) keep all in flight
-            uint4 wc[kEncRows][4];
-            uint4 hv[kEncReq][4];
-#pragma unroll
-            for (int jj = 0; jj < kEncRows; ++jj) {
-                const uint4* w = reinterpret_cast<const uint4*>(wbase + (size_t)min(j0 + jj, p.d_idx - 1) * p.d_model) + half * hc;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) wc[jj][k] = w[min(c0 + k * 64 + lane, hc - 1)];
-            }
-#pragma unroll
-            for (int rr = 0; rr < kEncReq; ++rr) {
-                const uint4* h = reinterpret_cast<const uint4*>(hid + (size_t)min(r0 + rr, p.n_req - 1) * p.hidden_req_stride) + half * hc;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) hv[rr][k] = h[min(c0 + k * 64 + lane, hc - 1)];
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool live = c0 + k * 64 + lane < hc;
-#pragma unroll
-                for (int jj = 0; jj < kEncRows; ++jj)
-#pragma unroll
-                    for (int rr = 0; rr < kEncReq; ++rr) {
-                        const float d = dot_chunks<T>(wc[jj][k], hv[rr][k]);
-                        acc[jj][rr] += live ? d : 0.f;
-                    }
-            }
-        }
+    float acc[kEncRows][kEncReq] = {};
+    for (int c0 = 0; c0 < hc; c0 += 64 * kEncPieces) {
+        uint4 wv[kEncRows][kEncPieces];
+        uint4 hv[kEncReq][kEncPieces];
 #pragma unroll
         for (int jj = 0; jj < kEncRows; ++jj)
+            enc_chunk<true>(wv[jj], reinterpret_cast<const uint4*>(wbase + (size_t)min(j0 + jj, p.d_idx - 1) * p.d_model),
+                            c0, hc, lane);
 #pragma unroll
-            for (int rr = 0; rr < kEncReq; ++rr) {
-                const float v = wave_sum(acc[jj][rr]);
-                if (lane == 0) s_part[wave][jj][rr] = v;
-            }
-        __syncthreads();
-        if (half == 0 && lane < kEncRows * kEncReq) {
-            const int jj = lane / kEncReq, rr = lane % kEncReq;
-            const int j = j0 + jj;
-            if (j < p.d_idx && r0 + rr < p.n_req) {
-                const float q = s_part[wave][jj][rr] + s_part[wave + 1][jj][rr];
-                put(&p.qw[((size_t)(r0 + rr) * p.n_idx + i) * p.d_idx + j], p.tag, __float_as_uint(q));
-            }
+        for (int rr = 0; rr < kEncReq; ++rr)
+            enc_chunk<false>(hv[rr], reinterpret_cast<const uint4*>(hid + (size_t)min(r0 + rr, p.n_req - 1) *
+                                                                          p.hidden_req_stride),
+                             c0, hc, lane);
+        __builtin_amdgcn_sched_barrier(0);  // every load of the chunk is issued before the first use
+#pragma unroll
+        for (int k = 0; k < kEncPieces; ++k)
+#pragma unroll
+            for (int jj = 0; jj < kEncRows; ++jj)
+#pragma unroll
+                for (int rr = 0; rr < kEncReq; ++rr) acc[jj][rr] = dot_chunks<T>(wv[jj][k], hv[rr][k], acc[jj][rr]);
+    }
+    float mine = 0.f;  // lane jj*kEncReq + rr publishes q for row j0 + jj, request r0 + rr
+#pragma unroll
+    for (int jj = 0; jj < kEncRows; ++jj)
+#pragma unroll
+        for (int rr = 0; rr < kEncReq; ++rr) {
+            const float v = wave_sum(acc[jj][rr]);
+            if (lane == jj * kEncReq + rr) mine = v;
         }
-        __syncthreads();
-    }
+    const int jj = lane / kEncReq, rr = lane % kEncReq;
+    if (lane < kEncRows * kEncReq && j0 + jj < p.d_idx && r0 + rr < p.n_req)
+        put(&p.qw[((size_t)(r0 + rr) * p.n_idx + i) * p.d_idx + j0 + jj], p.tag, __float_as_uint(mine));
 }
 
 // ------------------------------------------------------------------------------------------
-// Prefetch role: the groups dispatched with the encode groups read the keys of the first score
-// units and drop them.  The reads pass through the memory-side cache, so HBM streams keys while q
-// is being computed, and the score waves of those units later find them there.
+// Scoring role.  Score wave s takes half word s: word s/2, blocks 32*(s%2) .. +31, for every
+// indexer.  For indexer i the half word's 32 key rows (ROW bytes each) are contiguous; load j of
+// the unit reads 1 KiB run j: lane l holds 16-byte column c = l % LPR of row RPL*j + l / LPR.
+// After the loads each lane has one partial dot product per run (its column); a reduce-scatter
+// halves the partials at each step over the top lane bits of a row's lanes and sums the rest,
+// leaving lane l with the logit of run k = (l >> (LOG_LPR - LOG_P)) % P, i.e. of row
+// RPL*k + l / LPR.  Up to U units (indexers) are requested at once.
 template <typename T, int DIDX>
-__device__ void prefetch_role(const RefreshParams& p, int gp) {
-    constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
-    constexpr int LPR = ROW_BYTES / 128;
-    const int lane = threadIdx.x & 63;
-    const int unit = 4 * gp + (int)(threadIdx.x >> 6);
-    if (unit >= p.n_units) return;
-    const int word = unit / (2 * p.n_idx);
-    const int i = (unit / 2) % p.n_idx;
-    const int half = unit & 1;
-    int r = 0;
-    while (r + 1 < p.n_req && p.word_off[r + 1] <= word) ++r;
-    const long long b_first = p.blk_off[r];
-    const int n_blk = (int)(p.blk_off[r + 1] - b_first);
-    const int b0 = (word - p.word_off[r]) * 64;
-    const int n_valid = min(64, n_blk - b0);
-    const char* rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + (size_t)i * n_blk + b0) * ROW_BYTES;
-    uint4 v[4][LPR];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int rowi = min(32 * half + g * 8 + (lane >> 3), n_valid - 1);
-        const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)rowi * ROW_BYTES + (lane & 7) * 16);
-#pragma unroll
-        for (int k = 0; k < LPR; ++k) v[g][k] = src[k * 8];
-    }
-    uint4 x = v[0][0];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int k = 0; k < LPR; ++k) x ^= v[g][k];
-    asm volatile("" :: "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));  // the data arrives before the wave ends
-}
+struct ScoreShape {
+    static constexpr int ROW = DIDX * (int)sizeof(T);  // bytes per key row: 256, 512 or 1024
+    static constexpr int LPR = ROW / 16;               // lanes per row
+    static constexpr int LOG_LPR = LPR == 16 ? 4 : LPR == 32 ? 5 : 6;
+    static constexpr int RPL = 64 / LPR;               // rows per 1 KiB run
+    static constexpr int P = 32 * ROW / 1024;          // runs per unit: 8, 16 or 32
+    static constexpr int LOG_P = P == 8 ? 3 : P == 16 ? 4 : 5;
+    static constexpr int U = 48 / P;                   // units requested at once: 6, 3 or 1
+    static constexpr int E = Chunk<T>::N;              // elements of q per lane (its column)
+    static constexpr int QF = E / RPL;                 // of which the lane fetches (RPL lanes share a column)
+    static_assert(P * RPL == 32, "a unit is 32 rows");
+    static_assert(QF * RPL == E, "q split over the lanes of a column");
+    static_assert(LOG_P <= LOG_LPR, "reduce-scatter shape");
+};
 
-// ------------------------------------------------------------------------------------------
-// Scoring role: wave w of score group gs takes unit 4*gs + w = (word, indexer i, half): rows
-// 32*half .. 32*half + 31 of the word's 64 blocks for indexer i.
 template <typename T, int DIDX>
-__device__ void score_role(const RefreshParams& p, int gs) {
-    using C = Chunk<T>;
-    constexpr int ROW_BYTES = DIDX * (int)sizeof(T);
-    constexpr int LPR = ROW_BYTES / 128;  // 16-byte loads per lane per row (8 lanes per row)
-    constexpr int QPL = LPR * C::N;       // q values held per lane
-    constexpr int HALF = (LPR == 8) ? 2 : 1;
-    constexpr int GH = 4 / HALF;          // groups of 8 rows per pass (32 rows per wave)
-    constexpr int QW = DIDX / 64;         // q words fetched per lane
-    static_assert(LPR >= 1 && LPR <= 8, "row size");
-    __shared__ float s_q[kThreads / 64][DIDX];
-
+__device__ void score_role(const RefreshParams& p, int sw) {
+    using S = ScoreShape<T, DIDX>;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int unit = 4 * gs + wave;
-    if (unit >= p.n_units) return;
-    const int word = unit / (2 * p.n_idx);
-    const int i = (unit / 2) % p.n_idx;
-    const int half = unit & 1;
+    if (sw >= p.n_halves) return;
+    const int word = sw >> 1;
+    const int half = sw & 1;
     int r = 0;
     while (r + 1 < p.n_req && p.word_off[r + 1] <= word) ++r;
     const int lw = word - p.word_off[r];
     const long long b_first = p.blk_off[r];
     const int n_blk = (int)(p.blk_off[r + 1] - b_first);
-    const int b0 = lw * 64;
-    const int n_valid = min(64, n_blk - b0);
+    const int n_valid = min(64, n_blk - lw * 64);  // blocks of this word that exist (>= 1)
 
-    const int x = lane & 7;      // 16-byte column inside a 128-byte slice of the row
-    const int rsub = lane >> 3;  // row inside a group of 8 rows
-    const char* rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + (size_t)i * n_blk + b0) * ROW_BYTES;
-    const unsigned long long* qrow = p.qw + ((size_t)r * p.n_idx + i) * DIDX;
-    const float bias = p.bias[r * p.n_idx + i];
-    unsigned bits = 0u;
+    const int col = lane % S::LPR;
+    const int sub = lane / S::LPR;
+    // indexer i's rows of this word start at word_rows + i * n_blk * ROW
+    const char* word_rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + lw * 64) * S::ROW;
+    const unsigned lane_off = (unsigned)(sub * S::ROW + col * 16);
+    const int k = (lane >> (S::LOG_LPR - S::LOG_P)) & (S::P - 1);
+    const int rowi = 32 * half + S::RPL * k + sub;  // row of the word whose logit this lane ends with
+    unsigned u_bits = 0u;
     bool q_ok = true;
-    float qr[QPL];
+    for (int i0 = 0; i0 < p.n_idx; i0 += S::U) {
+        const int nu = min(S::U, p.n_idx - i0);
+        uint4 v[S::U][S::P];
 #pragma unroll
-    for (int hh = 0; hh < HALF; ++hh) {
-        // unconditional loads (rows past the request's last block re-read its last row and are
-        // masked out below), so all of them are in flight together
-        uint4 v[GH][LPR];
+        for (int u = 0; u < S::U; ++u) {
+            if (u < nu) {
+                // run j of the unit at a fixed distance from its first row
+                const char* rows = word_rows + ((size_t)(i0 + u) * n_blk + 32 * half) * S::ROW + lane_off;
+                if (n_valid == 64) {
 #pragma unroll
-        for (int g = 0; g < GH; ++g) {
-            const int rowi = min(32 * half + (hh * GH + g) * 8 + rsub, n_valid - 1);
-            const uint4* src = reinterpret_cast<const uint4*>(rows + (size_t)rowi * ROW_BYTES + x * 16);
+                    for (int j = 0; j < S::P; ++j) v[u][j] = load_nt(reinterpret_cast<const uint4*>(rows + j * 1024));
+                } else {
+                    // the request's last word: a lane whose row lies past the request's last block
+                    // loads nothing (its logit is masked below), so every access stays inside the
+                    // request's keys
 #pragma unroll
-            for (int k = 0; k < LPR; ++k) v[g][k] = load_nt(src + k * 8);
-        }
-        if (hh == 0) {
-            asm volatile("" ::: "memory");  // the key loads are issued before the wait for q
-            // wait for this (request, indexer)'s q: the wave fetches the row (lane l: words QW*l ..)
-            // right behind its key loads, checks every tag (fetching again until all are this
-            // call's) and passes the values through LDS to the lanes that use them
-            unsigned spins = 0;
-            for (;;) {
-                bool all = true;
-#pragma unroll
-                for (int k = 0; k < QW; ++k) {
-                    const unsigned long long wq = get(qrow + QW * lane + k);
-                    all = all && tagged(wq, p.tag);
-                    s_q[wave][QW * lane + k] = __uint_as_float((unsigned)wq);
+                    for (int j = 0; j < S::P; ++j) {
+                        v[u][j] = make_uint4(0u, 0u, 0u, 0u);
+                        if (32 * half + S::RPL * j + sub < n_valid)
+                            v[u][j] = load_nt(reinterpret_cast<const uint4*>(rows + j * 1024));
+                    }
                 }
-                if (__all(all)) break;
-                if (++spins > kSpinLimit) {
-                    q_ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(8);
             }
-            __builtin_amdgcn_wave_barrier();
+        }
+        asm volatile("" ::: "memory");  // every key load of the batch is issued before q is polled
+        // q of every indexer of the batch, polled together right behind the key loads: lane l
+        // fetches QF of the E values of its column (the RPL lanes of a column split them) and
+        // fetches again until every tag is this call's
+        float qf[S::U][S::QF];
+        for (unsigned spins = 0;; ++spins) {
+            bool all = true;
 #pragma unroll
-            for (int k = 0; k < LPR; ++k)
+            for (int u = 0; u < S::U; ++u) {
+                if (u < nu) {
+                    const unsigned long long* qrow = p.qw + ((size_t)r * p.n_idx + i0 + u) * DIDX + col * S::E + sub * S::QF;
 #pragma unroll
-                for (int e = 0; e < C::N; ++e) qr[k * C::N + e] = s_q[wave][(k * 128 + x * 16) / (int)sizeof(T) + e];
+                    for (int e = 0; e < S::QF; ++e) {
+                        const unsigned long long wq = get(qrow + e);
+                        all = all && tagged(wq, p.tag);
+                        qf[u][e] = __uint_as_float((unsigned)wq);
+                    }
+                }
+            }
+            if (__all(all)) break;
+            if (spins >= kSpinLimit) {
+                q_ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
         }
 #pragma unroll
-        for (int g = 0; g < GH; ++g) {
-            const int rowi = 32 * half + (hh * GH + g) * 8 + rsub;
-            float acc = 0.f;
+        for (int u = 0; u < S::U; ++u) {
+            if (u < nu) {
+                const int i = i0 + u;
+                float qv[S::E];  // the column's E values, gathered from the lanes that fetched them
 #pragma unroll
-            for (int k = 0; k < LPR; ++k) acc += dot_chunk_f32<T>(v[g][k], qr + k * C::N);
-            acc += __shfl_xor(acc, 1, 64);
-            acc += __shfl_xor(acc, 2, 64);
-            acc += __shfl_xor(acc, 4, 64);
-            const bool keep = q_ok && (rowi < n_valid) && (acc + bias > 0.f);
-            const unsigned long long m = __ballot(keep);
-            unsigned b8 = 0u;  // lanes 8j..8j+7 all hold row 8g+j: take bit 8j
+                for (int s2 = 0; s2 < S::RPL; ++s2)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) b8 |= (unsigned)((m >> (8 * j)) & 1ull) << j;
-            bits |= b8 << (8 * (hh * GH + g));
+                    for (int e = 0; e < S::QF; ++e) qv[s2 * S::QF + e] = __shfl(qf[u][e], col + s2 * S::LPR, 64);
+                float part[S::P];
+#pragma unroll
+                for (int j = 0; j < S::P; ++j) part[j] = dot_chunk_f32<T>(v[u][j], qv);
+                // reduce-scatter: step t keeps the upper half of the remaining partials on lanes
+                // whose bit (LOG_LPR - 1 - t) is set and adds the partner lane's copy of that half
+#pragma unroll
+                for (int t = 0; t < S::LOG_P; ++t) {
+                    const int n = S::P >> t;
+                    const int b = S::LOG_LPR - 1 - t;
+                    const bool up = (lane >> b) & 1;
+#pragma unroll
+                    for (int kk = 0; kk < n / 2; ++kk) {
+                        const float keep = up ? part[kk + n / 2] : part[kk];
+                        const float give = up ? part[kk] : part[kk + n / 2];
+                        part[kk] = keep + __shfl_xor(give, 1 << b, 64);
+                    }
+                }
+                float z = part[0];
+#pragma unroll
+                for (int b = S::LOG_LPR - S::LOG_P - 1; b >= 0; --b) z += __shfl_xor(z, 1 << b, 64);
+                const bool keep = q_ok && (rowi < n_valid) && (z + p.bias[r * p.n_idx + i] > 0.f);
+                const unsigned long long m = __ballot(keep);
+                // row q of the half word sits on lane (q % RPL) * LPR + ((q / RPL) << (LOG_LPR - LOG_P))
+                unsigned bits = 0u;
+#pragma unroll
+                for (int q = 0; q < 32; ++q) {
+                    const int ln = (q % S::RPL) * S::LPR + ((q / S::RPL) << (S::LOG_LPR - S::LOG_P));
+                    bits |= (unsigned)((m >> ln) & 1ull) << q;
+                }
+                u_bits |= bits;
+                if (p.masks && lane == 0) {
+                    const int n_words_r = p.word_off[r + 1] - p.word_off[r];
+                    const size_t mw = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)i * n_words_r + lw;
+                    reinterpret_cast<unsigned*>(p.masks)[2 * mw + half] = bits;
+                }
+            }
         }
     }
     if (lane == 0) {
-        if (p.masks) {
-            const int n_words_r = p.word_off[r + 1] - p.word_off[r];
-            const size_t mw = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)i * n_words_r + lw;
-            reinterpret_cast<unsigned*>(p.masks)[2 * mw + half] = bits;
-        }
         if (!q_ok) {
             put(&p.bad[r], p.tag, 1u);
-            __builtin_amdgcn_s_waitcnt(0);  // the mark is stored before the unit is published
+            __builtin_amdgcn_s_waitcnt(0);  // the mark is stored before the half word is published
         }
-        put(&p.hw[unit], p.tag, bits);
+        put(&p.hw[sw], p.tag, u_bits);
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // Compaction role: group c of a request handles the request's words [64c, 64c + 64) (its slice).
 // All 256 threads read the union words up to the slice's end (thread t: words t, t+256, ...) until
-// every unit carries this call's tag; the popcounts of the words before the slice give its base,
+// both halves of each carry this call's tag; the popcounts of the words before the slice give its base,
 // a wave scan over the slice gives each word's offset, and the four waves write the slice's ids,
 // one word at a time per wave with one lane per bit, so each store writes a word's ids contiguously.
 // The group of the last slice writes the count.
@@ -364,26 +396,16 @@ __device__ void compact_role(const RefreshParams& p, int cg) {
     const int n_words = p.word_off[r + 1] - p.word_off[r];
     const int s0 = c * kSlice;
     const int s1 = min(n_words, s0 + kSlice);
-    const int nh = 2 * p.n_idx;  // published units per word
-    const unsigned long long* hw = p.hw + (size_t)p.word_off[r] * nh;
+    const unsigned long long* hw = p.hw + (size_t)p.word_off[r] * 2;
     auto union_word = [&](int w, bool* ok) {
-        // all loads of the word first (n_idx <= 4: at most 8 units), then the checks
-        unsigned long long h[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) h[k] = get(hw + (size_t)w * nh + min(k, nh - 1));
-        unsigned long long u = 0ull;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            if (k < nh) {
-                *ok = *ok && tagged(h[k], p.tag);
-                u |= (unsigned long long)(unsigned)h[k] << (32 * (k & 1));
-            }
-        }
-        return u;
+        // the union bits of the word's two halves, published by their score waves
+        const unsigned long long lo = get(hw + 2 * (size_t)w), hi = get(hw + 2 * (size_t)w + 1);
+        *ok = *ok && tagged(lo, p.tag) && tagged(hi, p.tag);
+        return (unsigned long long)(unsigned)lo | ((unsigned long long)(unsigned)hi << 32);
     };
     // Runs of up to kKeep words per thread stay in registers: a word is read until all its units
     // carry this call's tag, then kept; requests longer than 256*kKeep words are re-read.
-    constexpr int kKeep = 4;
+    constexpr int kKeep = 2;
     const bool held = s1 <= kThreads * kKeep;
     unsigned long long keep[kKeep] = {};
     unsigned done = 0u;
@@ -488,22 +510,19 @@ __device__ void compact_role(const RefreshParams& p, int cg) {
 }
 
 template <typename T, int DIDX>
-__global__ __launch_bounds__(kThreads, 3) void refresh_kernel(RefreshParams p) {
-    int g = blockIdx.x;
+__global__ __launch_bounds__(kThreads, kGroupsPerCU) void refresh_kernel(RefreshParams p) {
+    const int g = blockIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (g < p.n_encode_groups) {
-        encode_role<T>(p, g);
+        const int e = 4 * g + wave;
+        if (e < p.n_encode_waves) encode_role<T>(p, e);
         return;
     }
-    g -= p.n_encode_groups;
-    if (g < p.n_prefetch_groups) {
-        prefetch_role<T, DIDX>(p, g);
+    if (g < p.n_encode_groups + p.n_score_groups) {
+        score_role<T, DIDX>(p, 4 * (g - p.n_encode_groups) + wave);
         return;
     }
-    g -= p.n_prefetch_groups;
-    if (g < p.n_score_groups)
-        score_role<T, DIDX>(p, g);
-    else
-        compact_role(p, g - p.n_score_groups);
+    compact_role(p, g - p.n_encode_groups - p.n_score_groups);
 }
 
 struct RefreshLayout {
@@ -535,7 +554,7 @@ lsa_status refresh_layout(const lsa_refresh_args* a, RefreshLayout* L) {
     L->qw_off = off;
     off = align_up(off + (size_t)a->n_req * a->n_idx * a->d_idx * sizeof(unsigned long long), 256);
     L->hw_off = off;
-    off = align_up(off + (size_t)words * 2 * a->n_idx * sizeof(unsigned long long), 256);
+    off = align_up(off + (size_t)words * 2 * sizeof(unsigned long long), 256);
     L->bad_off = off;
     off = align_up(off + (size_t)a->n_req * sizeof(unsigned long long), 256);
     L->total = off;
@@ -571,10 +590,11 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
     rp.d_model = a->d_model;
     rp.d_idx = a->d_idx;
     rp.n_idx = a->n_idx;
-    rp.n_units = L.total_words * 2 * a->n_idx;
-    const int rows_per_group = kEncRows * (kThreads / 128);  // two waves per kEncRows W_q rows
-    rp.n_encode_groups = a->n_idx * ((a->d_idx + rows_per_group - 1) / rows_per_group);
-    rp.n_score_groups = (rp.n_units + kThreads / 64 - 1) / (kThreads / 64);
+    rp.n_halves = L.total_words * 2;
+    // encode waves: two W_q rows of one indexer for four requests each
+    rp.n_encode_waves = a->n_idx * ((a->d_idx + kEncRows - 1) / kEncRows) * ((a->n_req + kEncReq - 1) / kEncReq);
+    rp.n_encode_groups = (rp.n_encode_waves + kThreads / 64 - 1) / (kThreads / 64);
+    rp.n_score_groups = (rp.n_halves + kThreads / 64 - 1) / (kThreads / 64);
     int wo = 0, co = 0;
     for (int r = 0; r <= a->n_req; ++r) {
         rp.blk_off[r] = a->blk_off[r];
@@ -587,16 +607,7 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
         }
     }
     auto kernel = a->d_idx == 256 ? refresh_kernel<T, 256> : refresh_kernel<T, 128>;
-    // prefetch groups fill the slots the encode groups leave free at the start
-    {
-        DeviceInfo dev;
-        lsa_status st = current_device(&dev);
-        if (st != LSA_OK) return st;
-        int per_cu = 0;
-        LSA_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0));
-        rp.n_prefetch_groups = std::max(0, std::min(rp.n_score_groups, dev.cu_count * per_cu - rp.n_encode_groups));
-    }
-    const dim3 grid(rp.n_encode_groups + rp.n_prefetch_groups + rp.n_score_groups + co), block(kThreads);
+    const dim3 grid(rp.n_encode_groups + rp.n_score_groups + co), block(kThreads);
     if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps
         hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, rp);
     else
