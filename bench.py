@@ -58,8 +58,9 @@ METRIC = "LSA decode tokens/s at 1M ctx + index-refresh µs; % of HBM roofline"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=4,
+                    help="timed steps; a step is 64 decode steps of every request (one refresh interval)")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed steps before them")
     ap.add_argument("--workload", default="ctx1m")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold", choices=("device", "host"), default="device")
@@ -90,15 +91,21 @@ def parse():
     ap.add_argument("--kernel-trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="no run: per kernel and grid size, the dispatch durations of a rocprofv3 "
                          "--kernel-trace CSV")
-    ap.add_argument("--plan", choices=("device", "host"), default="host",
-                    help="where the residency plan of a refresh is made: on the host "
-                         "(lsa_gather_blocks_batch; the default, and always with --cold host, as the device "
-                         "plan copies within device memory) or on the device (lsa_gather_plan_device, no host "
-                         "round trip)")
+    ap.add_argument("--plan", choices=("device", "host"), default="device",
+                    help="where the residency plan of a refresh is made: on the device "
+                         "(lsa_gather_plan_device, the default: no host round trip, the decode reads the counts "
+                         "on the device) or on the host (lsa_gather_blocks_batch: the ids come back to the host "
+                         "and the stream waits for them)")
     ap.add_argument("--reactive", action="store_true",
                     help="reactive comparator: every block resident in HBM, the index scored at every step "
                          "and the decode reading the selected blocks in place (refresh cadence 1, no "
                          "gathers, no host round trip)")
+    ap.add_argument("--level", type=float, default=0.5,
+                    help="selection level: keep a block when sigmoid(z) > level (0.5 on the pages); other "
+                         "levels shift every indexer's bias by -logit(level)")
+    ap.add_argument("--host-leg", type=int, default=2,
+                    help="after the timed region, continue this many steps with the cold pool's pinned host "
+                         "copy (gathers over the host link) and report that rate beside the HBM-pool one")
     ap.add_argument("--event-every", type=int, default=16,
                     help="time the attention kernel with HIP events on every N-th timed step (the events "
                          "take the dispatch's own stamps but still cost stream time)")
@@ -215,46 +222,48 @@ def host_link_peak(dev, mib: int = 512, reps: int = 5) -> float:
 
 def cpu_baseline(wl, sample_steps: int, seed: int):
     """Time the oracle on a bounded sample of the same workload: one refresh of every request and
-    `sample_steps` decode steps per request."""
+    `sample_steps` decode steps per request with the BLAS threads it finds; then one refresh and
+    `sample_steps` decode steps of one request on a single thread."""
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = 1
     cfg = wl.cfg
     dt = cfg.dtype
     w_q = oracle.decode_values(wl.w_q, dt)
-    t_ref = 0.0
-    refs = {}
-    for r in range(wl.n_req):
-        t0 = time.perf_counter()
-        keys = oracle.decode_values(wl.keys[r], dt)
-        res = oracle.refresh(oracle.decode_values(wl.hidden[r][0], dt), w_q, keys, wl.bias[r])
-        t_ref += time.perf_counter() - t0
-        refs[r] = res
     rng = np.random.default_rng(seed)
     steps = sorted(rng.choice(np.arange(1, min(cfg.steps, 64)), size=sample_steps, replace=False).tolist())
-    t_dec = 0.0
-    n = 0
-    for r in range(wl.n_req):
-        kp, vp = wl.kv_prefill(r)
-        N = int(wl.ctx[r])
-        for t in steps:
+
+    def run(reqs):
+        t_ref, t_dec, n = 0.0, 0.0, 0
+        for r in reqs:
             t0 = time.perf_counter()
-            L = N + t + 1
-            pos = oracle.token_set(L, cfg.window, refs[r].ids, cfg.block)
-            lo = pos < N
-            k = np.empty((len(pos), cfg.head_dim))
-            v = np.empty((len(pos), cfg.head_dim))
-            k[lo] = oracle.decode_values(kp[pos[lo]], dt)
-            v[lo] = oracle.decode_values(vp[pos[lo]], dt)
-            k[~lo] = oracle.decode_values(wl.k_new[pos[~lo] - N, r], dt)
-            v[~lo] = oracle.decode_values(wl.v_new[pos[~lo] - N, r], dt)
-            oracle.attention(oracle.decode_values(wl.q_dec[t, r], dt), k, v, cfg.head_dim ** -0.5)
-            t_dec += time.perf_counter() - t0
-            n += 1
-    return {
+            keys = oracle.decode_values(wl.keys[r], dt)
+            res = oracle.refresh(oracle.decode_values(wl.hidden[r][0], dt), w_q, keys, wl.bias[r])
+            t_ref += time.perf_counter() - t0
+            kp, vp = wl.kv_prefill(r)
+            N = int(wl.ctx[r])
+            for t in steps:
+                t0 = time.perf_counter()
+                pos = oracle.token_set(oracle.seq_len_at(N, t), cfg.window, res.ids, cfg.block)
+                # only the attended prefill rows are decoded (the whole 1M-token prefill in float64
+                # would be 1 GB per tensor): kv_rows reads them as a prefill of m rows, the new
+                # tokens' positions shifted to follow it
+                lo = pos < N
+                m = int(lo.sum())
+                rel = np.concatenate([np.arange(m), pos[~lo] - N + m])
+                k = oracle.kv_rows(oracle.decode_values(kp[pos[lo]], dt), oracle.decode_values(wl.k_new[:, r], dt), m, rel)
+                v = oracle.kv_rows(oracle.decode_values(vp[pos[lo]], dt), oracle.decode_values(wl.v_new[:, r], dt), m, rel)
+                oracle.attention(oracle.decode_values(wl.q_dec[t, r], dt), k, v, cfg.head_dim ** -0.5)
+                t_dec += time.perf_counter() - t0
+                n += 1
+        return t_ref, t_dec, n
+
+    t_ref, t_dec, n = run(range(wl.n_req))
+    out = {
         "value": n / t_dec,
         "unit": "tokens/s",
         "cores": int(threads),
@@ -264,6 +273,13 @@ def cpu_baseline(wl, sample_steps: int, seed: int):
         "refresh_us_per_request": 1e6 * t_ref / wl.n_req,
         "seconds": t_dec + t_ref,
     }
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1_ref, t1_dec, n1 = run([0])
+        out["single_thread"] = {"value": n1 / t1_dec, "unit": "tokens/s", "cores": 1,
+                                "refresh_us_per_request": 1e6 * t1_ref, "seconds": t1_ref + t1_dec,
+                                "sample": f"{n1} request-steps of request 0 and its first refresh"}
+    return out
 
 
 def run_denoise(args) -> dict:
@@ -465,6 +481,26 @@ def main():
         print(json.dumps(run_read_ceiling(args)), flush=True)
         return
 
+    print(json.dumps(run_loop(args)), flush=True)
+
+
+STEP_DECODE = 64  # decode steps per benchmark step: one refresh interval at the pages' cadence
+
+
+def prologue_requests(wl):
+    """Requests whose first refresh falls before step 0 (staggered phases): their selection at step
+    0 comes from that prologue refresh, which the benchmark runs before the warm-up."""
+    return [r for r in range(wl.n_req) if wl.refresh_steps[r][0] < 0]
+
+
+def max_bench_steps(cfg) -> int:
+    """Most steps (warm-up included) whose decode-time tokens all stay inside the window."""
+    return cfg.window // STEP_DECODE
+
+
+def run_loop(args) -> dict:
+    """The decode loop: K timed steps of STEP_DECODE decode steps each (one refresh interval at
+    tau = 64), after W untimed ones and the prologue refreshes of staggered requests."""
     import torch
 
     from lookahead_block_sparse_amd.session import DecodeLoop, LSASession, ResidentLoop
@@ -474,8 +510,11 @@ def main():
         print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
     cfg = get_config(args.workload)
-    W, K = args.warmup, args.steps
+    W, K = args.warmup * STEP_DECODE, args.steps * STEP_DECODE  # in decode steps
     total_steps = W + K
+    if args.warmup + args.steps > max_bench_steps(cfg):
+        raise SystemExit(f"at most {max_bench_steps(cfg)} steps in all (warm-up included): decode-time "
+                         f"tokens must stay inside the {cfg.window}-token window")
     if args.tau > 0:
         cfg = cfg.scaled(tau=args.tau)
     if args.density > 0:
@@ -483,7 +522,7 @@ def main():
     if args.layers > 1 or args.hidden_rho:
         cfg = cfg.scaled(n_layers=args.layers, hidden_rho=args.hidden_rho)
     if args.select == "all":
-        cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0)  # one refresh, at step 0
+        cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0, staggered=False)  # one refresh
     if args.q_rank > 0:
         cfg = cfg.scaled(q_rank=args.q_rank)
     if args.reactive:
@@ -497,14 +536,18 @@ def main():
         wl.condition(_planting_query(cfg.dtype), None, latent_fn=_planting_latent(cfg.dtype))
     if args.select == "all":
         wl.bias[:] = 1e4  # every logit above zero: every block selected
+    if args.level != 0.5:
+        wl.bias -= np.float32(np.log(args.level / (1.0 - args.level)))  # keep sigmoid(z) > level
     note(f"workload {cfg.name}: {wl.n_req} requests, contexts {wl.ctx.tolist()[:4]}..., built")
 
     dev = torch.device("cuda")
+    dplan = args.plan == "device" and not args.reactive
+    host_leg = args.host_leg if (args.cold == "device" and not args.reactive and args.select != "all") else 0
     sess = LSASession(dtype=cfg.dtype, n_idx=cfg.n_idx, d_model=cfg.d_model, d_idx=cfg.d_idx,
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False,
-                      n_layers=cfg.n_layers, w_down=wl.w_down,
-                      device_plan=(args.plan == "device" and not args.reactive and args.cold == "device"))
+                      n_layers=cfg.n_layers, w_down=wl.w_down, device_plan=dplan,
+                      cold_host_mirror=host_leg > 0)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
@@ -523,8 +566,12 @@ def main():
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     # every refresh's hidden state and the biases are device-resident before the timed region
-    # (stacked per refresh step, in request order)
+    # (stacked per refresh step, in request order); the prologue refreshes (staggered requests
+    # whose first refresh falls before step 0) are keyed -1
     hid_at = {}
+    prologue = prologue_requests(wl)
+    if prologue:
+        hid_at[-1] = dev_raw(np.stack([wl.hidden[r][0] for r in prologue]))
     for t in range(total_steps):
         reqs = wl.refreshes_at(t)
         if reqs:
@@ -548,29 +595,34 @@ def main():
     # half a period in: with refreshes every 16 or 64 steps from the timed region's start, the
     # event-timed launches (a costlier launch) never come right after a refresh's host round trip
     att_ev = {i: (new_event(), new_event()) for i in range(ev_every // 2, K, ev_every)}
-    ref_ev = {}
-    lat_ev = {}
-    gather_ev = {}
-    copy_ev = {}  # the copy kernel alone (host plan)
-    first_refresh = min(t for t in range(total_steps) if wl.refreshes_at(t))
+    ref_ev, lat_ev, gather_ev, copy_ev = {}, {}, {}, {}
+    copied_at = {}  # device plan: blocks entered at an event-timed refresh (copied back after the run)
+    slot_reqs = {}  # row of copied_pin -> the requests of that refresh (the other counts are stale)
+    refresh_decode_steps = [t for t in range(total_steps) if wl.refreshes_at(t)]
+    # the first refresh of a run loads every selected block (not so after a prologue refresh)
+    first_refresh = refresh_decode_steps[0] if refresh_decode_steps and not prologue else None
+    # the host-link leg replays the refresh states of the first decode steps of the timed region
+    n_leg = host_leg * STEP_DECODE if total_steps + host_leg * STEP_DECODE <= cfg.window else 0
+    leg_refreshes = [W + t for t in range(n_leg) if W + t < total_steps and wl.refreshes_at(W + t)]
     # the refreshes whose kernels are timed with events (every event costs stream time and host time
     # on the refresh's critical path): at most about 8, evenly spread over the timed steps
-    refresh_steps = [t for t in range(W, W + K) if wl.refreshes_at(t)]
-    timed_refresh = set(refresh_steps[::max(1, len(refresh_steps) // 8)])
+    timed_steps_with_refresh = [t for t in range(W, W + K) if wl.refreshes_at(t)]
+    timed_refresh = set(timed_steps_with_refresh[::max(1, len(timed_steps_with_refresh) // 8)][:8])
     # the refreshes' events are made and recorded once before timing: made inside the loop they
     # cost ~60 us of host time per refresh while the GPU waits for the gather's launch
-    ev_pool = [new_event() for _ in range(8 * len(timed_refresh) + 8)]
+    ev_pool = [new_event() for _ in range(8 * len(timed_refresh) + 2 * len(leg_refreshes) + 8)]
 
     def mk_event():
         return ev_pool.pop() if ev_pool else new_event()
 
-    first_copy_ev = (mk_event(), mk_event())  # the first refresh loads every selected block
+    first_copy_ev = (mk_event(), mk_event())  # the first refresh of a run loads every selected block
     first_blocks = []
+    copied_pin = torch.zeros((len(timed_refresh) + len(leg_refreshes) + 2, wl.n_req), dtype=torch.int32,
+                             pin_memory=True)
     torch.cuda.synchronize()
 
     e = 2 if cfg.dtype == "bf16" else 4
     D, H = cfg.head_dim, cfg.n_heads
-    dplan = sess.device_plan
     loop = DecodeLoop(sess, wl.ctx, window, out, device_counts=dplan)
     # the first launch of a kernel in the process loads its code, inside a timed dispatch's events:
     # the copy kernels run once before anything is timed
@@ -594,7 +646,28 @@ def main():
     gather_host_s = []
     gather_blocks = []
     sel_hist = {}        # (request, selection version) -> ascending ids
-    step_log = []        # (t, attended entries per request, selection version per request)
+    step_log = []        # (t, attended entries per request, selection version per request, event-timed)
+
+    def refresh_group(t, reqs, hid, ev_ref=(None, None), ev_plan=(None, None), ev_copy=(None, None),
+                      copy_slot=None):
+        """One refresh of `reqs` and its gathers.  Returns the blocks copied (host plan) or None."""
+        bias = bias_dev[reqs[0]:reqs[-1] + 1] if reqs == list(range(reqs[0], reqs[-1] + 1)) else \
+            torch.stack([bias_dev[r] for r in reqs])
+        if dplan:
+            # refresh, plan and copy on the device: nothing comes back to the host
+            sess.refresh_device(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1], ev_plan=ev_plan)
+            if copy_slot is not None:
+                slot_reqs[copy_slot] = list(reqs)
+                with torch.cuda.stream(sess.stream):
+                    copied_pin[copy_slot].copy_(sess.copied_dev, non_blocking=True)
+            return None
+        sel = sess.refresh(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1],
+                           ev_latent=lat_ev.get(t, (None, None)))
+        copied = 0
+        for r, (c, _) in sess.gather_many(sel, ev_copy=ev_copy).items():
+            copied += c
+            sel_hist[(r, int(sess.sel_version[r]))] = sess.sel_host[r]
+        return copied
 
     def reactive_step(t, timed_idx):
         evs = (None, None)
@@ -610,68 +683,64 @@ def main():
         if rloop is not None:
             return reactive_step(t, timed_idx)
         reqs = wl.refreshes_at(t)
-        timed_ref = timed_idx is not None and t in timed_refresh
         if reqs:
+            timed_ref = timed_idx is not None and t in timed_refresh
             if timed_ref:
                 ref_ev[t] = (mk_event(), mk_event())
                 gather_ev[t] = (mk_event(), mk_event())
                 if sess.rank:
                     lat_ev[t] = (mk_event(), mk_event())
-            hid = hid_at[t]
-            bias = bias_dev[reqs[0]:reqs[-1] + 1] if reqs == list(range(reqs[0], reqs[-1] + 1)) else \
-                torch.stack([bias_dev[r] for r in reqs])
-            evs = ref_ev.get(t, (None, None)) if timed_ref else (None, None)
+            evs = ref_ev.get(t, (None, None))
             if dplan:
-                # refresh, plan and copy on the device: nothing comes back to the host
-                pev = gather_ev.get(t, (None, None)) if timed_ref else \
-                    (first_copy_ev if t == first_refresh else (None, None))
-                sess.refresh_device(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1], ev_plan=pev)
+                pev = gather_ev[t] if timed_ref else (first_copy_ev if t == first_refresh else (None, None))
+                slot = None
+                if timed_ref:
+                    slot = copied_at[t] = len(copied_at)
+                elif t == first_refresh:
+                    slot = copied_at["first"] = len(copied_at)
+                refresh_group(t, reqs, hid_at[t], ev_ref=evs, ev_plan=pev, copy_slot=slot)
             else:
-                sel = sess.refresh(reqs, hid, bias, ev_begin=evs[0], ev_end=evs[1],
-                                   ev_latent=lat_ev.get(t, (None, None)))
-        if reqs and not dplan:
-            h0 = time.perf_counter()
-            if timed_ref:
-                gather_ev[t][0].record(sess.stream)
-                cev = copy_ev[t] = (mk_event(), mk_event())
-            elif t == first_refresh:
-                cev = first_copy_ev
-            else:
-                cev = (None, None)
-            copied = 0
-            for r, (c, _) in sess.gather_many(sel, ev_copy=cev).items():
-                copied += c
-                sel_hist[(r, int(sess.sel_version[r]))] = sess.sel_host[r]
-            if timed_ref:
-                gather_ev[t][1].record(sess.stream)
-                gather_host_s.append(time.perf_counter() - h0)
-                gather_blocks.append(copied)
-            elif t == first_refresh:
-                first_blocks.append(copied)
-        if timed_idx is None:
-            loop.step(t, q_all[t], kn_all[t], vn_all[t])
-            for lp, (ql, kl, vl) in zip(loops_l, layer_in):
-                lp.step(t, ql[t], kl[t], vl[t])
-        else:
-            ev = att_ev.get(timed_idx, (None, None))
-            loop.step(t, q_all[t], kn_all[t], vn_all[t], ev[0], ev[1])
-            for lp, (ql, kl, vl) in zip(loops_l, layer_in):
-                lp.step(t, ql[t], kl[t], vl[t])
+                h0 = time.perf_counter()
+                if timed_ref:
+                    gather_ev[t][0].record(sess.stream)
+                    cev = copy_ev[t] = (mk_event(), mk_event())
+                elif t == first_refresh:
+                    cev = first_copy_ev
+                else:
+                    cev = (None, None)
+                copied = refresh_group(t, reqs, hid_at[t], ev_ref=evs, ev_copy=cev)
+                if timed_ref:
+                    gather_ev[t][1].record(sess.stream)
+                    gather_host_s.append(time.perf_counter() - h0)
+                    gather_blocks.append(copied)
+                elif t == first_refresh:
+                    first_blocks.append(copied)
+        ev = att_ev.get(timed_idx, (None, None)) if timed_idx is not None else (None, None)
+        loop.step(t, q_all[t], kn_all[t], vn_all[t], ev[0], ev[1])
+        for lp, (ql, kl, vl) in zip(loops_l, layer_in):
+            lp.step(t, ql[t], kl[t], vl[t])
+        if timed_idx is not None:
             step_log.append((t, None if dplan else loop.n_sel.copy(), sess.sel_version.copy(), timed_idx in att_ev))
 
-    note(f"warm-up {W} steps")
+    if prologue:
+        note(f"prologue refresh of {len(prologue)} staggered requests")
+        refresh_group(-1, prologue, hid_at[-1])
+        torch.cuda.synchronize()
+    note(f"warm-up {W // STEP_DECODE} steps ({W} decode steps)")
     for t in range(W):
         step(t, None)
     torch.cuda.synchronize()
-    if dplan and [t for t in range(W) if wl.refreshes_at(t)] == [first_refresh]:
-        first_blocks.append(int(sess.copied_dev.sum().item()))  # the one warm-up refresh
-    note(f"timing {K} steps")
+    if dplan:
+        sess.check_plan_status()
+    note(f"timing {K // STEP_DECODE} steps ({K} decode steps)")
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     note(f"timed region {elapsed * 1e3:.2f} ms")
+    if dplan:
+        sess.check_plan_status()  # any refresh of the run that gave up or did not fit raises here
 
     attn_ms = np.array([a.elapsed_time(b) for a, b in att_ev.values()])
     sel_at = {}
@@ -695,7 +764,6 @@ def main():
         for t, _, _, timed_ev in step_log:
             if timed_ev:
                 sel_at[t] = sess.refresh(list(range(wl.n_req)), hid_at[t], bias_dev)
-        # the table entries the decode reads: every selected block of the step
         step_log = [(t, None, None, te) for t, _, _, te in step_log]
     # algorithmic bytes of every timed attention launch: window tokens + tokens of the attended
     # selected blocks (below the window start), K and V, plus q and the table entries
@@ -737,42 +805,54 @@ def main():
     ev_bytes = attn_bytes[np.array(with_ev)]  # the launches the events timed, in the same order
     achieved = ev_bytes.sum() / (attn_ms.sum() * 1e-3) / 1e9  # GB/s
 
-    # refresh algorithmic bytes for one group of all requests
-    n_blocks_total = int(wl.n_blocks.sum())
-    # (low rank: the Query Encoder reads B and the latents of every indexer instead of W_q and h)
-    q_in_bytes = (wl.n_req * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else wl.n_req * cfg.d_model * e
-    ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
-                 + q_in_bytes + 4 * sum(len(x) for x in sess.sel_host) + 4 * wl.n_req)
-    lat_bytes = (cfg.n_idx * cfg.q_rank * cfg.d_model * e + wl.n_req * cfg.d_model * e
-                 + wl.n_req * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else 0
-    if dplan and sel_at:  # ids of the recomputed selections, plus the bit planes the plan reads
-        n_ids = np.mean([sum(len(v) for v in s_.values()) for s_ in sel_at.values()])
-        ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
-                     + q_in_bytes + int(4 * n_ids) + 8 * (cfg.n_idx + 1) * int(sess.word_off[-1]) + 4 * wl.n_req)
-    if rloop is not None:  # ids and table pairs of the recomputed selections
-        n_ids = np.mean([sum(len(v) for v in s.values()) for s in sel_at.values()]) if sel_at else 0.0
-        ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_total * cfg.n_idx * cfg.d_idx * e
-                     + q_in_bytes + int(12 * n_ids) + 4 * wl.n_req)
+    # refresh algorithmic bytes: keys, W_q, the hidden states and the ids of the requests one
+    # refresh serves (all of them when aligned; the staggered mix refreshes one request at a time)
+    ref_reqs = wl.refreshes_at(sorted(ref_ev)[0]) if ref_ev else list(range(wl.n_req))
+    n_blocks_ref = int(sum(int(wl.n_blocks[r]) for r in ref_reqs))
+    q_in_bytes = (len(ref_reqs) * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else len(ref_reqs) * cfg.d_model * e
+    ids_per_refresh = None
+    if dplan and sel_at:
+        ids_per_refresh = np.mean([sum(len(v) for r, v in s_.items() if r in ref_reqs) for s_ in sel_at.values()])
+    elif rloop is not None and sel_at:
+        ids_per_refresh = np.mean([sum(len(v) for v in s_.values()) for s_ in sel_at.values()])
+    else:
+        ids_per_refresh = sum(len(sess.sel_host[r]) for r in ref_reqs)
+    ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_ref * cfg.n_idx * cfg.d_idx * e + q_in_bytes
+                 + int(4 * ids_per_refresh) + 4 * len(ref_reqs))
+    if dplan:  # the bit planes the device plan reads are written by the refresh
+        ref_bytes += 8 * (cfg.n_idx + 1) * int(sum(int(sess.word_off[r + 1] - sess.word_off[r]) for r in ref_reqs))
+    if rloop is not None:  # the table pairs the refresh writes for the resident pool
+        ref_bytes += int(8 * ids_per_refresh)
+    lat_bytes = (cfg.n_idx * cfg.q_rank * cfg.d_model * e + len(ref_reqs) * cfg.d_model * e
+                 + len(ref_reqs) * cfg.n_idx * cfg.q_rank * e) if cfg.q_rank else 0
+
+    bb = sess.block_bytes * cfg.n_layers
+    torch.cuda.synchronize()
+
+    def slot_blocks(slot):
+        return int(copied_pin[slot][slot_reqs[slot]].sum())
 
     gather_copy = None
     if dplan and len(gat_us):
         # plan + copy kernels (events on the plan's dispatch start and the copy's end)
-        bb = sess.block_bytes * cfg.n_layers
-        gather_copy = {"source": "device memory (HBM)", "kernels": "plan_kernel + copy_kernel",
-                       "plan_and_copy_us": float(np.median(gat_us)),
-                       "bytes_last_refresh": int(sess.copied_dev.sum().item()) * bb}
-        if first_blocks:
-            fb = first_blocks[0] * bb
+        blocks = np.array([slot_blocks(copied_at[t]) for t in sorted(gather_ev)], dtype=np.float64)
+        gather_copy = {"source": ("pinned host memory (host link)" if args.cold == "host" else "device memory (HBM)"),
+                       "kernels": "plan_kernel + copy_kernel", "plan_and_copy_us": float(np.median(gat_us)),
+                       "blocks_per_refresh": float(blocks.mean()), "bytes_per_refresh": float(blocks.mean() * bb),
+                       "GB_per_s": float(np.median(blocks * bb / (gat_us * 1e-6) / 1e9))}
+        if "first" in copied_at:
+            fb = slot_blocks(copied_at["first"]) * bb
             fus = 1e3 * first_copy_ev[0].elapsed_time(first_copy_ev[1])
-            gather_copy["first_refresh"] = {"blocks": int(first_blocks[0]), "bytes": int(fb), "plan_and_copy_us": fus,
+            gather_copy["first_refresh"] = {"blocks": fb // bb, "bytes": int(fb), "plan_and_copy_us": fus,
                                             "GB_per_s": fb / (fus * 1e-6) / 1e9}
-    if copy_ev and gather_blocks:
+        gather_blocks = blocks.tolist()
+    if copy_ev and gather_blocks and not dplan:
         # cold-pool bytes each copy kernel reads (every layer's copy of every entering block); with
         # the cold pool in HBM the kernel writes as many again to the hot pool
-        bb = sess.block_bytes * cfg.n_layers
         later = np.array(gather_blocks, dtype=np.float64) * bb
         gather_copy = {
             "source": "pinned host memory (host link)" if args.cold == "host" else "device memory (HBM)",
+            "kernels": "gather_kernel (host plan)",
             "bytes_per_refresh": float(later.mean()),
             "copy_us": float(np.median(copy_us)),
             "GB_per_s": float(np.median(later / (copy_us * 1e-6) / 1e9)),
@@ -782,17 +862,61 @@ def main():
             fus = 1e3 * first_copy_ev[0].elapsed_time(first_copy_ev[1])
             gather_copy["first_refresh"] = {"blocks": int(first_blocks[0]), "bytes": int(fb), "copy_us": fus,
                                             "GB_per_s": fb / (fus * 1e-6) / 1e9}
-        if args.cold == "host":
-            gather_copy["link_peak_GB_per_s"] = host_link_peak(dev)
+    if gather_copy is not None and args.cold == "host":
+        gather_copy["link_peak_GB_per_s"] = host_link_peak(dev)
+
+    # the same loop continued with the cold pool's pinned host copy: every gather crosses the host
+    # link (same blocks, same residency state); timed over whole steps by the wall clock
+    host_cold = None
+    if n_leg and leg_refreshes:
+        sess.use_cold("host")
+        leg_evs, leg_slots = [], []
+        torch.cuda.synchronize()
+        tl0 = time.perf_counter()
+        for t in range(n_leg):
+            ts = W + t  # the refresh states and decode inputs of timed step ts, replayed
+            reqs = wl.refreshes_at(ts) if ts < total_steps else []
+            if reqs:
+                ev = (mk_event(), mk_event())
+                leg_evs.append(ev)
+                if dplan:
+                    slot = len(copied_at) + len(leg_slots)
+                    leg_slots.append(slot)
+                    refresh_group(ts, reqs, hid_at[ts], ev_plan=ev, copy_slot=slot)
+                else:
+                    leg_slots.append(refresh_group(ts, reqs, hid_at[ts], ev_copy=ev))
+            tt = total_steps + t  # the window keeps growing: positions past the timed region
+            loop.step(tt, q_all[ts], kn_all[ts], vn_all[ts])
+            for lp, (ql, kl, vl) in zip(loops_l, layer_in):
+                lp.step(tt, ql[ts], kl[ts], vl[ts])
+        torch.cuda.synchronize()
+        leg_s = time.perf_counter() - tl0
+        if dplan:
+            sess.check_plan_status()
+        us = np.array([1e3 * a.elapsed_time(b) for a, b in leg_evs])
+        blocks = (np.array([slot_blocks(s_) for s_ in leg_slots], dtype=np.float64) if dplan
+                  else np.array(leg_slots, dtype=np.float64))
+        host_cold = {
+            "tokens_per_s": wl.n_req * n_leg / leg_s,
+            "steps": host_leg, "decode_steps": n_leg, "seconds": leg_s,
+            "gather_us": float(np.median(us)),
+            "gather_kernels": "plan_kernel + copy_kernel" if dplan else "gather_kernel (host plan)",
+            "gather_bytes_per_refresh": float(blocks.mean() * bb),
+            "gather_GB_per_s": float(np.median(blocks * bb / (us * 1e-6) / 1e9)),
+            "link_peak_GB_per_s": host_link_peak(dev),
+            "note": "the loop continued over whole steps with the cold pool's pinned host copy (the refresh "
+                    "states of the timed region's first steps replayed): every gather reads over the host link"}
+        sess.use_cold("device")
+
     khash = kernel_hash()
     res = {
         "metric": METRIC,
         "value": wl.n_req * K / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": elapsed * 1e3 / K,
+        "steps": K // STEP_DECODE,
+        "warmup": W // STEP_DECODE,
+        "ms_per_step": elapsed * 1e3 / (K // STEP_DECODE),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -808,12 +932,16 @@ def main():
                          + (f", hidden-state correlation {cfg.hidden_rho}" if cfg.hidden_rho else "")
                          + (", reactive comparator: every block resident, scored every step" if args.reactive
                             else "")
-                         + (f", low-rank query projection r={cfg.q_rank}" if cfg.q_rank else "")),
+                         + (f", low-rank query projection r={cfg.q_rank}" if cfg.q_rank else "")
+                         + (f", selection level sigmoid > {args.level}" if args.level != 0.5 else "")),
+            "step": f"{STEP_DECODE} decode steps of every request (one refresh interval at tau = 64): refreshes, "
+                    "gathers and sparse decode",
             "cold_pool": args.cold,
             "tau": cfg.tau,
             "layers": cfg.n_layers,
             "hidden_rho": cfg.hidden_rho,
             "select": args.select,
+            "level": args.level,
             "reactive": bool(args.reactive),
             "q_rank": cfg.q_rank,
             "residency_plan": "device" if dplan else ("none (resident)" if args.reactive else "host"),
@@ -833,16 +961,21 @@ def main():
             "timed_launches": int(len(attn_ms)),
             "mean_launch_us": float(attn_ms.mean() * 1e3),
         },
+        "decode_steps_timed": K,
         "decode_attn_us": float(attn_ms.mean() * 1e3),
         "attended_tokens_per_step": float(np.mean(attn_tokens)),
         "refresh_us": float(np.median(ref_us)) if len(ref_us) else None,
         "refresh_us_p90": float(np.percentile(ref_us, 90)) if len(ref_us) else None,
+        "refresh_timed": int(len(ref_us)),
+        "refreshes_in_timed_region": int(sum(len(wl.refreshes_at(t)) > 0 for t in range(W, W + K))),
         "decode_steady": ({"tokens_per_s": wl.n_req * sum(n for n, _ in steady) / (sum(u for _, u in steady) * 1e-6),
                            "us_per_step": sum(u for _, u in steady) / sum(n for n, _ in steady),
                            "steps": int(sum(n for n, _ in steady))} if steady else None),
-        "refresh_roofline": ({"achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+        "refresh_roofline": ({"kernel": "refresh_kernel (encode + score + compaction, one launch)",
+                              "achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                              "algorithmic_bytes": ref_bytes} if len(ref_us) else None),
+                              "algorithmic_bytes": ref_bytes, "requests_per_refresh": len(ref_reqs)}
+                             if len(ref_us) else None),
         "latent_us": float(np.median(lat_us)) if len(lat_us) else None,
         "latent_roofline": ({"achieved": lat_bytes / (np.median(lat_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": lat_bytes / (np.median(lat_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -851,6 +984,7 @@ def main():
         "gather_blocks_per_refresh": float(np.mean(gather_blocks)) if gather_blocks else None,
         "gather_host_plan_ms": float(np.median(gather_host_s) * 1e3) if gather_host_s else None,
         "gather_copy": gather_copy,
+        "cold_pool_in_pinned_host_memory": host_cold,
         "kernel_sources_sha256_16": khash,
     }
     if args.calib_copy_mib > 0:
@@ -866,7 +1000,7 @@ def main():
     if not args.no_cpu_baseline:
         note("timing the CPU oracle on a sample")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_steps, args.seed)
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":

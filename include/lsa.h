@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 9
+#define LSA_ABI_VERSION 10
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -291,7 +291,8 @@ typedef struct lsa_device_gather_args {
     int32_t* slot_of_block;    /* dev [blk_off[n_req]] state: slot of each block, or -1 */
     int32_t* free_slots;       /* dev [slot_off[n_req]] state: request r's stack at slot_off[r] */
     int32_t* n_free;           /* dev [n_req] state: entries on each stack */
-    const void* const* cold;   /* host [n_req]: dev pointer to request r's cold pool (HBM) */
+    const void* const* cold;   /* host [n_req]: request r's cold pool, device memory (HBM) or pinned
+                                  host memory (then the copy reads it over the host link) */
     int64_t cold_layer_bytes;  /* n_layers > 1: layer l of request r's cold pool at cold[r] + l*this */
     void* hot;                 /* dev: hot pool of slot_off[n_req] slots (per layer) */
     int64_t hot_layer_bytes;   /* n_layers > 1: layer l's hot pool at hot + l*this */
@@ -300,6 +301,9 @@ typedef struct lsa_device_gather_args {
     int32_t* copied;           /* dev [n_req] out: blocks that entered (copied once per layer) */
     int32_t* status;           /* dev [n_req] out: 0; 1 when the selection did not fit; 2 after a
                                   refresh that gave up */
+    int32_t* status_any;       /* dev [n_req] or NULL: OR-ed with every nonzero status of the request
+                                  (sticky until the caller clears it), so one read after many calls
+                                  shows whether any of them failed */
     void* workspace;           /* dev, workspace_bytes >= lsa_gather_plan_device_workspace() */
     size_t workspace_bytes;
     hipEvent_t ev_begin;       /* optional (NULL): the start stamp of the plan kernel's dispatch */

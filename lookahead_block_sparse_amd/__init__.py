@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -114,6 +114,7 @@ class DeviceGatherArgs(Structure):
         ("resident", c_void_p), ("slot_of_block", c_void_p), ("free_slots", c_void_p), ("n_free", c_void_p),
         ("cold", c_void_p), ("cold_layer_bytes", c_int64), ("hot", c_void_p), ("hot_layer_bytes", c_int64),
         ("table", c_void_p), ("table_count", c_void_p), ("copied", c_void_p), ("status", c_void_p),
+        ("status_any", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t), ("ev_begin", c_void_p), ("ev_end", c_void_p),
     ]
 

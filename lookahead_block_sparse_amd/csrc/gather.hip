@@ -19,6 +19,35 @@
 #include "lsa_internal.hpp"
 
 namespace lsa {
+
+// Device-visible address of a buffer that is either device memory or pinned host memory.
+lsa_status device_view(const void* ptr, const char* fn, const char* what, const void** out, bool* is_host) {
+    hipPointerAttribute_t attr{};
+    hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(LSA_ERR_INVALID, "%s: %s is neither device nor pinned host memory", fn, what);
+    }
+    if (attr.type == hipMemoryTypeDevice) {
+        *out = ptr;
+        *is_host = false;
+        return LSA_OK;
+    }
+    if (attr.type == hipMemoryTypeHost) {
+        void* dptr = nullptr;
+        e = hipHostGetDevicePointer(&dptr, const_cast<void*>(ptr), 0);
+        if (e != hipSuccess || dptr == nullptr) {
+            (void)hipGetLastError();
+            return fail(LSA_ERR_INVALID, "%s: %s is host memory that is not mapped for the device", fn, what);
+        }
+        *out = dptr;
+        *is_host = true;
+        return LSA_OK;
+    }
+    return fail(LSA_ERR_INVALID, "%s: %s has memory type %d (need device or pinned host)", fn, what,
+                (int)attr.type);
+}
+
 namespace {
 
 constexpr int kMaxBatch = 16;  // requests per copy-kernel launch
@@ -91,33 +120,6 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
     }
 }
 
-// Device-visible address of a buffer that is either device memory or pinned host memory.
-lsa_status device_view(const void* ptr, const char* what, const void** out, bool* is_host) {
-    hipPointerAttribute_t attr{};
-    hipError_t e = hipPointerGetAttributes(&attr, ptr);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(LSA_ERR_INVALID, "lsa_gather_blocks: %s is neither device nor pinned host memory", what);
-    }
-    if (attr.type == hipMemoryTypeDevice) {
-        *out = ptr;
-        *is_host = false;
-        return LSA_OK;
-    }
-    if (attr.type == hipMemoryTypeHost) {
-        void* dptr = nullptr;
-        e = hipHostGetDevicePointer(&dptr, const_cast<void*>(ptr), 0);
-        if (e != hipSuccess || dptr == nullptr) {
-            (void)hipGetLastError();
-            return fail(LSA_ERR_INVALID, "lsa_gather_blocks: %s is host memory that is not mapped for the device", what);
-        }
-        *out = dptr;
-        *is_host = true;
-        return LSA_OK;
-    }
-    return fail(LSA_ERR_INVALID, "lsa_gather_blocks: %s has memory type %d (need device or pinned host)", what,
-                (int)attr.type);
-}
 
 // Everything one request's gather decides before any state changes.
 struct GatherPlan {
@@ -219,9 +221,9 @@ lsa_status plan_gather(const lsa_gather_args* a, GatherPlan* P) {
         return fail(LSA_ERR_CAPACITY, "lsa_gather_blocks: %zu entering blocks, %d slots available", enter.size(), avail);
 
     bool cold_host = false, stage_host = false;
-    lsa_status st = device_view(a->cold, "cold", &P->cold_dev, &cold_host);
+    lsa_status st = device_view(a->cold, "lsa_gather_blocks", "cold", &P->cold_dev, &cold_host);
     if (st != LSA_OK) return st;
-    st = device_view(a->stage, "stage", &P->stage_dev, &stage_host);
+    st = device_view(a->stage, "lsa_gather_blocks", "stage", &P->stage_dev, &stage_host);
     if (st != LSA_OK) return st;
     LSA_CHECK_ARG(stage_host, "lsa_gather_blocks: stage must be pinned host memory");
 

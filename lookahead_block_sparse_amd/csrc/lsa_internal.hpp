@@ -39,6 +39,10 @@ struct DeviceInfo {
 // Properties of the current device (cached per device).
 lsa_status current_device(DeviceInfo* out);
 
+// Device-visible address of a buffer that is either device memory or pinned host memory mapped
+// for the device (is_host tells which); fn names the calling entry point in error messages.
+lsa_status device_view(const void* ptr, const char* fn, const char* what, const void** out, bool* is_host);
+
 inline size_t elem_bytes(int32_t dtype) { return dtype == LSA_BF16 ? 2 : 4; }
 inline bool dtype_ok(int32_t dtype) { return dtype == LSA_F32 || dtype == LSA_BF16; }
 

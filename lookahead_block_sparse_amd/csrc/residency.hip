@@ -35,6 +35,7 @@ struct PlanParams {
     int* table_count;
     int* copied;
     int* status;
+    int* status_any;  // optional: OR of every status of the request since the caller cleared it
     int2* clist;  // copy list: request r's entering (block, slot) pairs from pair slot_off[r]
     int n_idx;
     long long blk_off[kMaxReq + 1];
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     if (gave_up || n_enter > nf + n_leave) {  // nothing changes for this request
         if (threadIdx.x == 0) {
             p.status[r] = gave_up ? 2 : 1;
+            if (p.status_any) p.status_any[r] |= gave_up ? 2 : 1;
             p.copied[r] = 0;
         }
         return;
@@ -313,6 +315,15 @@ extern "C" lsa_status lsa_gather_plan_device(const lsa_device_gather_args* a, hi
                     a->workspace ? a->workspace_bytes : (size_t)0, P.total);
     LSA_CHECK_ARG(((uintptr_t)a->hot % 16) == 0 && ((uintptr_t)a->table % 8) == 0 && ((uintptr_t)a->workspace % 16) == 0,
                   "lsa_gather_plan_device: hot (16 B), table (8 B) and workspace (16 B) alignment");
+    // the last check, the first HIP call: each cold pool in HBM or in pinned host memory (then the copy kernel reads it over the host link)
+    const char* cold_dev[LSA_MAX_REFRESH_REQ];
+    for (int r = 0; r < a->n_req; ++r) {
+        const void* d = nullptr;
+        bool host = false;
+        st = device_view(a->cold[r], "lsa_gather_plan_device", "cold[r]", &d, &host);
+        if (st != LSA_OK) return st;
+        cold_dev[r] = static_cast<const char*>(d);
+    }
     PlanParams pp;
     pp.masks = reinterpret_cast<const unsigned long long*>(a->masks);
     pp.sel_count = a->sel_count;
@@ -324,6 +335,7 @@ extern "C" lsa_status lsa_gather_plan_device(const lsa_device_gather_args* a, hi
     pp.table_count = a->table_count;
     pp.copied = a->copied;
     pp.status = a->status;
+    pp.status_any = a->status_any;
     pp.clist = static_cast<int2*>(a->workspace);
     pp.n_idx = a->n_idx;
     int wo = 0;
@@ -340,7 +352,7 @@ extern "C" lsa_status lsa_gather_plan_device(const lsa_device_gather_args* a, hi
         hipLaunchKernelGGL(plan_kernel, dim3(a->n_req), dim3(kPlanThreads), 0, stream, pp);
     LSA_HIP(hipGetLastError());
     CopyParams cp;
-    for (int r = 0; r < a->n_req; ++r) cp.cold[r] = static_cast<const char*>(a->cold[r]);
+    for (int r = 0; r < a->n_req; ++r) cp.cold[r] = cold_dev[r];
     cp.hot = static_cast<char*>(a->hot);
     cp.cold_layer_bytes = a->n_layers > 1 ? a->cold_layer_bytes : 0;
     cp.hot_layer_bytes = a->n_layers > 1 ? a->hot_layer_bytes : 0;

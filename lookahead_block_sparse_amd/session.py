@@ -59,7 +59,7 @@ class LSASession:
                  capacity: Optional[Sequence[int]] = None, cold_on_device: bool = False,
                  with_masks: bool = False, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
                  max_groups: int = 0, n_layers: int = 1, w_down: Optional[np.ndarray] = None,
-                 device_plan: bool = False):
+                 device_plan: bool = False, cold_host_mirror: bool = False):
         self.dtype = dtype
         self.n_idx, self.d_model, self.d_idx = n_idx, d_model, d_idx
         # low-rank query projection: w_down = A [n_idx][rank][d_model], w_q = B [n_idx][d_idx][rank];
@@ -83,6 +83,10 @@ class LSASession:
             raise ValueError("unsupported dtype/head_dim")
         self.elt = 2 if dtype == "bf16" else 4
         self.cold_on_device = cold_on_device
+        # with the cold pool in HBM, an optional copy in pinned host memory: use_cold("host") then
+        # makes the gathers cross the host link, with the same blocks and the same residency state
+        self.cold_host_mirror = bool(cold_host_mirror and cold_on_device)
+        self.cold_src = "device" if cold_on_device else "host"
 
         with torch.cuda.stream(self.stream):
             self.w_q = _raw_tensor(w_q, self.device)
@@ -123,6 +127,7 @@ class LSASession:
 
             # cold pools and rings
             self.cold: List[Optional[torch.Tensor]] = [None] * self.n_req
+            self.cold_host: List[Optional[torch.Tensor]] = [None] * self.n_req  # the pinned mirror
             n_chunks = win_cap // BLOCK_TOKENS
             self.ring_layer_bytes = self.n_req * n_chunks * self.block_bytes
             self.ring = torch.zeros(self.n_layers * self.ring_layer_bytes, dtype=torch.uint8, device=self.device)
@@ -139,8 +144,6 @@ class LSASession:
         # refresh never waits for the host
         self.device_plan = bool(device_plan)
         if self.device_plan:
-            if not cold_on_device:
-                raise ValueError("device planning copies from a cold pool in HBM")
             with torch.cuda.stream(self.stream):
                 dev = self.device
                 self.resident_dev = torch.zeros(int(self.word_off[-1]), dtype=torch.int64, device=dev)
@@ -150,6 +153,7 @@ class LSASession:
                 self.table_count = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
                 self.copied_dev = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
                 self.plan_status = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
+                self.plan_status_any = torch.zeros(self.n_req, dtype=torch.int32, device=dev)
             a = self._plan_args(0, self.n_req)[0]
             ws = ctypes.c_size_t(0)
             _check(LIB.lsa_gather_plan_device_workspace(ctypes.byref(a), ctypes.byref(ws)))
@@ -173,12 +177,16 @@ class LSASession:
             self.cold[r] = (torch.empty(self.n_layers * lb, dtype=torch.uint8, device=self.device)
                             if self.cold_on_device else
                             torch.empty(self.n_layers * lb, dtype=torch.uint8, pin_memory=True))
+            if self.cold_host_mirror:
+                self.cold_host[r] = torch.empty(self.n_layers * lb, dtype=torch.uint8, pin_memory=True)
             self._gargs[r] = None
         if self.cold_on_device:
-            cold_h = torch.empty(lb, dtype=torch.uint8)
+            cold_h = (self.cold_host[r][layer * lb:(layer + 1) * lb] if self.cold_host_mirror
+                      else torch.empty(lb, dtype=torch.uint8))
             lsa_pack_blocks(self.dtype, self.head_dim, k_tok, v_tok, 0, n, cold_h, int(self.n_blocks[r]))
             with torch.cuda.stream(self.stream):
-                self.cold[r][layer * lb:(layer + 1) * lb].copy_(cold_h)  # from pageable memory: synchronous
+                self.cold[r][layer * lb:(layer + 1) * lb].copy_(cold_h)
+            self.stream.synchronize()
         else:
             lsa_pack_blocks(self.dtype, self.head_dim, k_tok, v_tok, 0, n, self.cold[r][layer * lb:(layer + 1) * lb],
                             int(self.n_blocks[r]))
@@ -189,6 +197,27 @@ class LSASession:
         lo = layer * self.ring_layer_bytes + r * n_chunks * self.block_bytes
         with torch.cuda.stream(self.stream):
             self.ring[lo:lo + len(ring_h)].copy_(torch.from_numpy(ring_h).to(self.device))
+
+    def _cold_ptr(self, r: int) -> int:
+        """Address of request r's cold pool in use (HBM or pinned host memory)."""
+        if self.cold_src == "host" and self.cold_on_device:
+            return self.cold_host[r].data_ptr()
+        return self.cold[r].data_ptr()
+
+    def use_cold(self, where: str) -> None:
+        """Gather from the HBM cold pool ("device") or from its pinned host mirror ("host"); the
+        blocks are the same, so the residency state carries over.  Order with the stream: call it
+        between refreshes."""
+        if where not in ("device", "host"):
+            raise ValueError("where is 'device' or 'host'")
+        if where == "host" and self.cold_on_device and not self.cold_host_mirror:
+            raise ValueError("the session keeps no pinned host copy of its cold pool (cold_host_mirror)")
+        if where == "device" and not self.cold_on_device:
+            raise ValueError("the cold pool of this session is in pinned host memory")
+        if where != self.cold_src:
+            self.cold_src = where
+            self._pargs.clear()
+            self._gargs = [None] * self.n_req
 
     def layer_views(self, layer: int):
         """(hot pool, window ring) of one layer."""
@@ -298,7 +327,7 @@ class LSASession:
             a.slot_of_block = self.slot_of_block_dev.data_ptr() + 4 * b0
             a.free_slots = self.free_dev.data_ptr() + 4 * s0
             a.n_free = self.n_free_dev.data_ptr() + 4 * r0
-            cold = (ctypes.c_void_p * (r1 - r0))(*[self.cold[r].data_ptr() if self.cold[r] is not None else None
+            cold = (ctypes.c_void_p * (r1 - r0))(*[self._cold_ptr(r) if self.cold[r] is not None else None
                                                    for r in range(r0, r1)])
             a.cold = ctypes.cast(cold, ctypes.c_void_p)
             if self.n_layers > 1 and r1 - r0 > 1 and len(set(self.n_blocks[r0:r1].tolist())) > 1:
@@ -309,6 +338,7 @@ class LSASession:
             a.table_count = self.table_count.data_ptr() + 4 * r0
             a.copied = self.copied_dev.data_ptr() + 4 * r0
             a.status = self.plan_status.data_ptr() + 4 * r0
+            a.status_any = self.plan_status_any.data_ptr() + 4 * r0
             ws = getattr(self, "plan_ws", None)
             a.workspace = ws.data_ptr() if ws is not None else None
             a.workspace_bytes = ws.numel() if ws is not None else 0
@@ -341,6 +371,21 @@ class LSASession:
             i = j + 1
         self.sel_version[reqs] += 1
 
+    def check_plan_status(self) -> None:
+        """Raise if any device-planned refresh since the last check gave up or did not fit its
+        request's slots (then that request kept its previous table); clears the record.  Reads
+        one small device array, so it waits for the stream."""
+        if not self.device_plan:
+            return
+        with torch.cuda.stream(self.stream):
+            st = self.plan_status_any.cpu().numpy()
+            self.plan_status_any.zero_()
+        bad = np.flatnonzero(st)
+        if len(bad):
+            what = {1: "did not fit its slots", 2: "gave up (incomplete compaction)", 3: "gave up and did not fit"}
+            raise RuntimeError("device-planned refresh failed: " +
+                               "; ".join(f"request {r} {what.get(int(st[r]), int(st[r]))}" for r in bad))
+
     def gather(self, r: int, ids: np.ndarray, stream: Optional[torch.cuda.Stream] = None):
         """Make request r's hot pool hold exactly `ids` (returns (copied, kept))."""
         return self.gather_many({r: ids}, stream)[r]
@@ -352,7 +397,7 @@ class LSASession:
             # every field but the selection is fixed for the session: built once per request
             a = GatherArgs()
             a.n_blocks, a.n_slots_total, a.block_bytes = int(self.n_blocks[r]), self.n_slots, self.block_bytes
-            a.cold, a.hot = self.cold[r].data_ptr(), self.hot.data_ptr()
+            a.cold, a.hot = self._cold_ptr(r), self.hot.data_ptr()
             a.stage_ints = self.stage[r].numel()
             a.slot_of_block = self.slot_of_block[r].ctypes.data
             a.free_slots = self.free_slots[r].ctypes.data

@@ -20,6 +20,7 @@ from .lsa_ref import (  # noqa: F401
     query_latent,
     round_bf16,
     refresh,
+    seq_len_at,
     simulate,
     threshold,
     token_set,

@@ -33,11 +33,15 @@ def _check_state(sess, r, ids):
     bt = torch.as_tensor(ids, dtype=torch.long, device=sess.device)
     for layer in range(sess.n_layers):
         hot, _ = sess.layer_views(layer)
-        cold = sess.cold[r][layer * lb:(layer + 1) * lb]
-        assert torch.equal(hot.view(-1, bb)[st], cold.view(-1, bb)[bt]), (r, layer)
+        cold = sess.cold[r][layer * lb:(layer + 1) * lb]  # HBM or pinned host memory
+        want = cold.view(-1, bb)[bt.to(cold.device)].to(sess.device)
+        assert torch.equal(hot.view(-1, bb)[st], want), (r, layer)
 
 
-def _run(wl, sess, sample, check=True):
+def _run(wl, sess, sample, check=True, switch_at=None):
+    """The benchmark's device-planned loop (refresh_device + DecodeLoop with device counts): returns
+    ({(layer, t): outputs}, {(r, k): ids}); with check, every refresh's table, device state and hot
+    pool are checked against its selection."""
     from lookahead_block_sparse_amd.session import DecodeLoop
 
     cfg = wl.cfg
@@ -65,6 +69,8 @@ def _run(wl, sess, sample, check=True):
     loops = [DecodeLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), outs[l], layer=l, device_counts=True)
              for l in range(cfg.n_layers)]
     for t in range(cfg.steps):
+        if switch_at is not None and t == switch_at:
+            sess.use_cold("host")  # the same blocks from the pinned host copy from here on
         reqs = wl.refreshes_at(t)
         if reqs:
             refresh(reqs, {r: wl.refresh_index_at(r, t) for r in reqs})
@@ -75,6 +81,7 @@ def _run(wl, sess, sample, check=True):
             for l in range(cfg.n_layers):
                 gpu[(l, t)] = outs[l].double().cpu().numpy()
     torch.cuda.synchronize()
+    sess.check_plan_status()
     return gpu, sels
 
 
@@ -204,3 +211,67 @@ def test_device_plan_events_change_nothing():
         del sess
     for x, y in zip(*results):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name,mode", [("ctx1m_s", "host"), ("ragged_s", "host"), ("ctx128k_s", "switch")])
+def test_device_plan_with_pinned_host_pool_matches_oracle(name, mode):
+    """The device plan copying from a cold pool in pinned host memory (its copy kernel reads over
+    the host link), or switching from the HBM pool to its pinned host copy between refreshes: every
+    refresh bit-exact, every slot holding its block, outputs within tolerance."""
+    from workloads import get_config
+
+    cfg = get_config(name)
+    wl = conditioned_workload(cfg, seed=44)
+    log(f"device plan, cold pool {mode}, {name}")
+    if mode == "host":
+        sess = make_session(wl, cold_on_device=False, with_masks=False, device_plan=True)
+        switch = None
+    else:
+        sess = make_session(wl, cold_on_device=True, with_masks=False, device_plan=True, cold_host_mirror=True)
+        switch = 64
+    sample = sorted({0, 63, 64, cfg.steps - 1})
+    gpu, sels = _run(wl, sess, sample, switch_at=switch)
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    refs, outs = oracle.simulate(wl, steps=sample)
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (name, r, k)
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[(0, t)], ref)))
+    log(f"  {len(sels)} refreshes; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+def test_refresh_that_gave_up_is_reported():
+    """A refresh whose compaction gave up writes its count as -1; the device plan then changes
+    nothing for that request and records status 2, which check_plan_status turns into an error.
+    The -1 is written from the host (no kernel is made to fail)."""
+    import ctypes
+
+    from lookahead_block_sparse_amd import LIB
+    from workloads import get_config
+
+    cfg = get_config("ctx512k_s").scaled(steps=70)
+    wl = conditioned_workload(cfg, seed=45)
+    R = wl.n_req
+    sess = make_session(wl, cold_on_device=True, with_masks=False, device_plan=True)
+    dev = sess.device
+    bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+    sess.refresh_device(list(range(R)), raw_to_torch(np.stack([wl.hidden[r][0] for r in range(R)]), dev), bias)
+    sess.check_plan_status()  # a good refresh reports nothing
+    before = (sess.table.clone(), sess.table_count.clone(), sess.resident_dev.clone())
+    sess.sel_count[1] = -1  # request 1's refresh "gave up"
+    a = sess._plan_args(0, R)[0]
+    a.ev_begin = a.ev_end = None
+    assert LIB.lsa_gather_plan_device(ctypes.byref(a), ctypes.c_void_p(sess.stream.cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert sess.plan_status.cpu().tolist() == [0, 2, 0]
+    with pytest.raises(RuntimeError, match="request 1 gave up"):
+        sess.check_plan_status()
+    sess.check_plan_status()  # the record was cleared
+    s0, s1 = int(sess.slot_base[1]), int(sess.slot_base[2])
+    assert torch.equal(sess.table.view(-1, 2)[s0:s1], before[0].view(-1, 2)[s0:s1])
+    assert int(sess.table_count[1]) == int(before[1][1])
+    w0, w1 = int(sess.word_off[1]), int(sess.word_off[2])
+    assert torch.equal(sess.resident_dev[w0:w1], before[2][w0:w1])

@@ -1,9 +1,11 @@
 """Parity at the full workload sizes, in the benchmark's launch configuration.
 
-Each workload runs its whole decode loop through the C-ABI the way bench.py runs it (cold pool in
-HBM, no bit planes, a work-group per CU slot, DecodeLoop's per-step call); every refresh of every
-request is compared with the oracle bit for bit, and the attention output of a few sampled steps
-(always including the last one, and a refresh step where there is one) within the fp tolerance.
+Each workload runs its whole decode loop through the C-ABI: with the residency plan on the host
+(cold pool in HBM, no bit planes, a work-group per CU slot, DecodeLoop's per-step call), and in the
+benchmark's default path, the residency plan on the device with device-side counts, the cold pool
+in pinned host memory (4 x 1M, 8 x 512K) or in HBM (the ragged mix).  Every refresh of every request
+is compared with the oracle bit for bit; the attention outputs of sampled steps (the device-plan
+runs: every refresh step, the step before it, 8 seeded steps and the last) within the fp tolerance.
 """
 
 from __future__ import annotations
@@ -144,4 +146,57 @@ def test_full_size_reactive_matches_oracle():
         ref = np.stack([outs[(r, t)] for r in range(R)])
         worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
     log(f"  reactive ctx1m: {len(sels)} selections bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+def _survey_sample(wl, seed, n_random=8):
+    """Every refresh step, the step before it and n_random seeded steps (each sampled step holds the
+    outputs of every request), plus the last step."""
+    T = wl.cfg.steps
+    s = {T - 1}
+    for r in range(wl.n_req):
+        for tk in wl.refresh_steps[r]:
+            if 0 <= tk < T:
+                s.add(tk)
+                if tk > 0:
+                    s.add(tk - 1)
+    rng = np.random.default_rng(seed)
+    s.update(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    return sorted(s)
+
+
+FULL_DEVICE_PLAN = [("ctx1m", "host"), ("ctx512k", "host"), ("ragged", "device")]
+
+
+@pytest.mark.parametrize("name,cold", FULL_DEVICE_PLAN, ids=[f"{n}-{c}" for n, c in FULL_DEVICE_PLAN])
+def test_full_size_device_plan_matches_oracle(name, cold):
+    """The benchmark's default path at full size: refresh, residency plan and copy on the device,
+    device-side counts in the decode; the cold pool in pinned host memory (4 x 1M, 8 x 512K: every
+    gather reads over the host link) or in HBM (the 32-request ragged mix).  Every refresh of every
+    request bit-exact, the hot pool holding each request's selection after every refresh, and the
+    outputs of every refresh step, the step before it, 8 seeded steps and the last step within the
+    tolerance."""
+    from test_gpu_device_plan import _run
+
+    wl = conditioned_workload(name, seed=14)
+    sample = _survey_sample(wl, seed=14)
+    if name == "ragged":  # 287 refresh steps: keep every refresh check, sample a bounded set of steps
+        rng = np.random.default_rng(15)
+        keep = set(rng.choice(sample, size=24, replace=False).tolist()) | {wl.cfg.steps - 1}
+        sample = sorted(keep)
+    log(f"full size device plan {name}, cold pool {cold}: {wl.n_req} requests, {wl.cfg.steps} steps, "
+        f"{len(sample)} sampled steps")
+    sess = make_session(wl, cold_on_device=(cold == "device"), with_masks=False, device_plan=True)
+    gpu, sels = _run(wl, sess, set(sample))
+    log(f"  {name}: GPU loop done, {len(sels)} refreshes")
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    refs, outs = oracle.simulate(wl, steps=sample)
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (name, r, k, len(ids), len(refs[r][k].ids))
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(wl.n_req)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[(0, t)], ref)))
+    log(f"  {name}: {len(sels)} selections bit-exact; {len(sample)} steps, max abs {worst[0]:.3e} "
+        f"rel {worst[1]:.3e} l2 {worst[2]:.3e}")
     assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst

@@ -151,3 +151,31 @@ def test_planted_prefill_is_what_oracle_and_session_read():
     assert np.array_equal(wl.kv_prefill(0, 1)[0], other)
     with pytest.raises(ValueError):
         wl.set_kv_prefill(0, k2[:-1], v)
+
+
+@pytest.mark.parametrize("name", ["ragged", "ctx1m", "ragged_s", "ctx512k"])
+def test_every_request_has_a_selection_before_its_first_step(name):
+    """The selection in force at step 0 comes from a refresh at step 0 or from the prologue refresh
+    before it (staggered phases): the benchmark runs the prologue refreshes of exactly the requests
+    whose first refresh step is negative, so no request decodes window-only at the start."""
+    import bench
+
+    cfg = get_config(name)
+    wl = build_workload(cfg.scaled(steps=min(cfg.steps, 128)), seed=3)
+    pro = bench.prologue_requests(wl)
+    for r in range(wl.n_req):
+        first = wl.refresh_steps[r][0]
+        assert first <= 0, (r, first)
+        assert (first < 0) == (r in pro)
+        assert sum(1 for t in wl.refresh_steps[r] if t <= 0) == 1  # exactly one governs step 0
+    if cfg.staggered:
+        assert len(pro) >= wl.n_req - 1  # at most one phase is 0
+
+
+def test_benchmark_refuses_more_steps_than_the_window_holds():
+    """Decode-time tokens never leave the window (they belong to no scored block), so the benchmark
+    refuses a run whose decode steps exceed it."""
+    import bench
+
+    cfg = get_config("ctx1m")
+    assert bench.max_bench_steps(cfg) == cfg.window // bench.STEP_DECODE
