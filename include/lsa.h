@@ -371,6 +371,17 @@ typedef struct lsa_decode_args {
 lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes);
 lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream);
 
+/* lsa_sparse_decode without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same
+ * kernels and results as lsa_sparse_decode; a->workspace and a->workspace_bytes are ignored and the
+ * split-K partials go to a static array of the library, one per device (3,194,880 bytes: up to
+ * 320 work-groups plus LSA_MAX_DECODE_REQ requests at head_dim 128), held until the process ends.
+ * A call that would need more returns LSA_ERR_WORKSPACE and enqueues nothing.  The call allocates
+ * nothing (its first call on a device looks the array's device address up once).  Every call on
+ * a device shares that device's array: calls that overlap in time on one device race, so order
+ * them on one stream. */
+lsa_status lsa_sparse_decode_noalloc(const lsa_decode_args* a, hipStream_t stream);
+
 /* --------------------------------------------------------------------------------------
  * (4) Label denoising for the indexer's training labels (zhichai.net explainer,
  * section 3, the three-step pipeline).  For layer l and token window w with the raw

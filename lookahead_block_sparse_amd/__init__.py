@@ -62,6 +62,7 @@ EXPORTED_SYMBOLS = (
     "lsa_residency_reset",
     "lsa_sparse_decode_workspace",
     "lsa_sparse_decode",
+    "lsa_sparse_decode_noalloc",
     "lsa_label_denoise_workspace",
     "lsa_label_denoise",
 )
@@ -185,8 +186,9 @@ def _load():
     lib.lsa_gather_blocks_batch.argtypes = [POINTER(GatherArgs), c_int32, c_void_p]
     lib.lsa_sparse_decode_workspace.restype = c_int32
     lib.lsa_sparse_decode_workspace.argtypes = [POINTER(DecodeArgs), POINTER(c_size_t)]
-    lib.lsa_sparse_decode.restype = c_int32
-    lib.lsa_sparse_decode.argtypes = [POINTER(DecodeArgs), c_void_p]
+    for fn in ("lsa_sparse_decode", "lsa_sparse_decode_noalloc"):
+        getattr(lib, fn).restype = c_int32
+        getattr(lib, fn).argtypes = [POINTER(DecodeArgs), c_void_p]
     if lib.lsa_abi_version() != ABI_VERSION:
         raise ImportError(f"liblsa.so ABI {lib.lsa_abi_version()} != binding ABI {ABI_VERSION}")
     for i, st in enumerate((RefreshArgs, GatherArgs, DecodeArgs, LatentArgs, DenoiseArgs, DeviceGatherArgs)):

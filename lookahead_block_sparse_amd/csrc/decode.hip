@@ -22,6 +22,8 @@
 #include <hip/hip_ext.h>
 
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "lsa_internal.hpp"
 
@@ -675,9 +677,8 @@ lsa_status decode_plan(const lsa_decode_args* a, DecodePlan* P, bool sizing_only
 }
 
 template <typename Ops, typename T, int D>
-lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStream_t stream) {
+lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, char* ws, hipStream_t stream) {
     DecodeParams dp{};
-    char* ws = static_cast<char*>(a->workspace);
     dp.q = a->q;
     dp.k_new = a->k_new;
     dp.v_new = a->v_new;
@@ -750,6 +751,65 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, hipStrea
     return LSA_OK;
 }
 
+// ---- split-K partials without a workspace ------------------------------------------------------
+// lsa_sparse_decode_noalloc keeps the partials in this array instead of a caller's workspace: one
+// copy per device, held until the process ends, sized for kScratchGroups work-groups and the most
+// requests of a call at head_dim 128.  Nothing in it needs to start at zero (every partial the
+// merge reads is written by the same call's attention kernel); calls that overlap on one device
+// share it and race.
+constexpr int kScratchGroups = 320;
+constexpr size_t kScratchBytes =
+    (size_t)(kScratchGroups + kMaxReq) * kHeads * 128 * sizeof(float) +  // partial outputs (a 256 multiple)
+    (size_t)(kScratchGroups + kMaxReq) * kHeads * 2 * sizeof(float);     // (m, l) pairs
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device: looked up once per device (each device holds
+// its own copy of the array at its own address), never the host-side name of the array.
+lsa_status scratch_address(char** out) {
+    static std::mutex mu;
+    static std::vector<char*> addr;
+    int dev = -1;
+    LSA_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        LSA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (p == nullptr) return fail(LSA_ERR_HIP, "lsa_sparse_decode_noalloc: no device address for the scratch array");
+        addr[dev] = static_cast<char*>(p);
+    }
+    *out = addr[dev];
+    return LSA_OK;
+}
+
+// Checks shared by both entry points (everything but the workspace), then the plan.
+lsa_status decode_prepare(const lsa_decode_args* a, DecodePlan* P) {
+    lsa_status st = decode_check(a);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(a->q && a->ring && a->out, "lsa_sparse_decode: null device pointer");
+    bool any_sel = false;
+    for (int r = 0; r < a->n_req; ++r) any_sel |= a->n_sel[r] > 0;
+    LSA_CHECK_ARG(!any_sel || (a->pool && a->table && a->n_slots_total > 0),
+                  "lsa_sparse_decode: selected blocks but no pool/table");
+    st = decode_plan(a, P, false);
+    if (st != LSA_OK) return st;
+    LSA_CHECK_ARG(((uintptr_t)a->q % 16) == 0 && ((uintptr_t)a->ring % 16) == 0 &&
+                      (a->pool == nullptr || ((uintptr_t)a->pool % 16) == 0) &&
+                      (a->k_new == nullptr || ((uintptr_t)a->k_new % 16) == 0) &&
+                      (a->table == nullptr || ((uintptr_t)a->table % 8) == 0),
+                  "lsa_sparse_decode: q, ring, pool, k_new must be 16-byte aligned, table 8-byte aligned");
+    return LSA_OK;
+}
+
+lsa_status decode_dispatch(const lsa_decode_args* a, const DecodePlan& P, char* ws, hipStream_t stream) {
+    if (a->dtype == LSA_BF16) {
+        if (a->head_dim == 128) return launch_decode<Bf16Ops<128>, uint16_t, 128>(a, P, ws, stream);
+        return launch_decode<Bf16Ops<64>, uint16_t, 64>(a, P, ws, stream);
+    }
+    if (a->head_dim == 128) return launch_decode<F32Ops<128>, float, 128>(a, P, ws, stream);
+    return launch_decode<F32Ops<64>, float, 64>(a, P, ws, stream);
+}
+
 }  // namespace
 }  // namespace lsa
 
@@ -765,28 +825,25 @@ extern "C" lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size
 }
 
 extern "C" lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream) {
-    lsa_status st = decode_check(a);
-    if (st != LSA_OK) return st;
-    LSA_CHECK_ARG(a->q && a->ring && a->out, "lsa_sparse_decode: null device pointer");
-    bool any_sel = false;
-    for (int r = 0; r < a->n_req; ++r) any_sel |= a->n_sel[r] > 0;
-    LSA_CHECK_ARG(!any_sel || (a->pool && a->table && a->n_slots_total > 0),
-                  "lsa_sparse_decode: selected blocks but no pool/table");
     DecodePlan P;
-    st = decode_plan(a, &P, false);
+    lsa_status st = decode_prepare(a, &P);
     if (st != LSA_OK) return st;
     if (a->workspace == nullptr || a->workspace_bytes < P.total)
         return fail(LSA_ERR_WORKSPACE, "lsa_sparse_decode: workspace of %zu bytes, need %zu",
                     a->workspace ? a->workspace_bytes : (size_t)0, P.total);
-    LSA_CHECK_ARG(((uintptr_t)a->q % 16) == 0 && ((uintptr_t)a->ring % 16) == 0 &&
-                      (a->pool == nullptr || ((uintptr_t)a->pool % 16) == 0) &&
-                      (a->k_new == nullptr || ((uintptr_t)a->k_new % 16) == 0) &&
-                      (a->table == nullptr || ((uintptr_t)a->table % 8) == 0),
-                  "lsa_sparse_decode: q, ring, pool, k_new must be 16-byte aligned, table 8-byte aligned");
-    if (a->dtype == LSA_BF16) {
-        if (a->head_dim == 128) return launch_decode<Bf16Ops<128>, uint16_t, 128>(a, P, stream);
-        return launch_decode<Bf16Ops<64>, uint16_t, 64>(a, P, stream);
-    }
-    if (a->head_dim == 128) return launch_decode<F32Ops<128>, float, 128>(a, P, stream);
-    return launch_decode<F32Ops<64>, float, 64>(a, P, stream);
+    return decode_dispatch(a, P, static_cast<char*>(a->workspace), stream);
+}
+
+extern "C" lsa_status lsa_sparse_decode_noalloc(const lsa_decode_args* a, hipStream_t stream) {
+    DecodePlan P;
+    lsa_status st = decode_prepare(a, &P);
+    if (st != LSA_OK) return st;
+    if (P.total > kScratchBytes)
+        return fail(LSA_ERR_WORKSPACE,
+                    "lsa_sparse_decode_noalloc: the call needs %zu bytes of partials, the static array holds "
+                    "%zu (at most %d work-groups)", P.total, kScratchBytes, kScratchGroups);
+    char* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != LSA_OK) return st;
+    return decode_dispatch(a, P, ws, stream);
 }
