@@ -101,8 +101,8 @@ def parse():
                          "and the decode reading the selected blocks in place (refresh cadence 1, no "
                          "gathers, no host round trip)")
     ap.add_argument("--level", type=float, default=0.5,
-                    help="selection level: keep a block when sigmoid(z) > level (0.5 on the pages); other "
-                         "levels shift every indexer's bias by -logit(level)")
+                    help="selection level: keep a block when sigmoid(z) > level (0.5 on the pages; the "
+                         "refresh's select_level)")
     ap.add_argument("--host-leg", type=int, default=2,
                     help="after the timed region, continue this many steps with the cold pool's pinned host "
                          "copy (gathers over the host link) and report that rate beside the HBM-pool one")
@@ -525,6 +525,8 @@ def run_loop(args) -> dict:
         cfg = cfg.scaled(tau=max(cfg.tau, total_steps + 1), planted_frac=0.0, staggered=False)  # one refresh
     if args.q_rank > 0:
         cfg = cfg.scaled(q_rank=args.q_rank)
+    if args.level != 0.5:
+        cfg = cfg.scaled(level=args.level)
     if args.reactive:
         if args.select == "all" or cfg.n_layers > 1 or args.cold != "device":
             raise SystemExit("--reactive runs one layer with the default selection and the pool in HBM")
@@ -536,8 +538,6 @@ def run_loop(args) -> dict:
         wl.condition(_planting_query(cfg.dtype), None, latent_fn=_planting_latent(cfg.dtype))
     if args.select == "all":
         wl.bias[:] = 1e4  # every logit above zero: every block selected
-    if args.level != 0.5:
-        wl.bias -= np.float32(np.log(args.level / (1.0 - args.level)))  # keep sigmoid(z) > level
     note(f"workload {cfg.name}: {wl.n_req} requests, contexts {wl.ctx.tolist()[:4]}..., built")
 
     dev = torch.device("cuda")
@@ -547,7 +547,7 @@ def run_loop(args) -> dict:
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, cold_on_device=(args.cold == "device"), with_masks=False,
                       n_layers=cfg.n_layers, w_down=wl.w_down, device_plan=dplan,
-                      cold_host_mirror=host_leg > 0)
+                      cold_host_mirror=host_leg > 0, select_level=cfg.level)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)
@@ -908,6 +908,17 @@ def run_loop(args) -> dict:
                     "states of the timed region's first steps replayed): every gather reads over the host link"}
         sess.use_cold("device")
 
+    # recall of the planted relevant blocks (4 x 1M): the share of them in the selections in force at
+    # the event-timed steps
+    planted_recall = None
+    if cfg.planted_frac > 0 and sel_at:
+        rec = [np.isin(wl.planted[r], s_[r]).mean() for s_ in sel_at.values() for r in range(wl.n_req)
+               if len(wl.planted[r])]
+        planted_recall = float(np.mean(rec)) if rec else None
+    elif cfg.planted_frac > 0 and sel_hist:
+        rec = [np.isin(wl.planted[r], ids).mean() for (r, _), ids in sel_hist.items() if len(wl.planted[r])]
+        planted_recall = float(np.mean(rec)) if rec else None
+
     khash = kernel_hash()
     res = {
         "metric": METRIC,
@@ -964,6 +975,7 @@ def run_loop(args) -> dict:
         "decode_steps_timed": K,
         "decode_attn_us": float(attn_ms.mean() * 1e3),
         "attended_tokens_per_step": float(np.mean(attn_tokens)),
+        "planted_recall": planted_recall,
         "refresh_us": float(np.median(ref_us)) if len(ref_us) else None,
         "refresh_us_p90": float(np.percentile(ref_us, 90)) if len(ref_us) else None,
         "refresh_timed": int(len(ref_us)),

@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 10
+#define LSA_ABI_VERSION 11
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -116,7 +116,7 @@ lsa_status lsa_pack_blocks(int32_t dtype, int32_t head_dim, const void* k_tok, c
  *   q[i]     = W_q[i] h                        Query Encoder, fp32 accumulation,
  *                                              kept in fp32 (never rounded)
  *   z[i][b]  = q[i] . keys[i][b] + bias[i]      dual-encoder block logit (fp32)
- *   s[i][b]  = z[i][b] > 0                      sigmoid(z) > 0.5, decided on z
+ *   s[i][b]  = z[i][b] > logit(level)           sigmoid(z) > level (0.5 by default: z > 0), decided on z
  *   u[b]     = OR_i s[i][b]                     OR-mode union
  *   sel_ids  = ascending b with u[b], sel_count = their number
  * ------------------------------------------------------------------------------------ */
@@ -126,7 +126,10 @@ typedef struct lsa_refresh_args {
     int32_t d_idx;             /* index dim: 128 or 256 */
     int32_t n_idx;             /* indexers: 1..4 (the method uses 3) */
     int32_t dtype;             /* lsa_dtype of hidden, w_q and keys */
-    int32_t reserved0;         /* must be 0 */
+    float select_level;        /* keep a block when sigmoid(z) > select_level, decided on the logit as
+                                  z > log(level / (1 - level)) in fp32; 0 means the pages' 0.5
+                                  (z > 0), else 0 < select_level < 1 (the explainer, section 7, calls
+                                  0.5 a preliminary choice) */
     const void* hidden;        /* dev: request r, indexer i reads d_model elements at
                                   r*hidden_req_stride + i*hidden_idx_stride */
     int64_t hidden_req_stride; /* elements between requests (>= d_model) */

@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -78,7 +78,7 @@ class LSAError(RuntimeError):
 class RefreshArgs(Structure):
     _fields_ = [
         ("n_req", c_int32), ("d_model", c_int32), ("d_idx", c_int32), ("n_idx", c_int32),
-        ("dtype", c_int32), ("reserved0", c_int32),
+        ("dtype", c_int32), ("select_level", c_float),
         ("hidden", c_void_p), ("hidden_req_stride", c_int64), ("hidden_idx_stride", c_int64),
         ("w_q", c_void_p), ("keys", c_void_p), ("blk_off", POINTER(c_int64)), ("bias", c_void_p),
         ("sel_ids", c_void_p), ("sel_count", c_void_p), ("masks", c_void_p),
@@ -301,7 +301,7 @@ def _refresh_args(*, dtype, d_model, d_idx, n_idx, hidden, hidden_req_stride, hi
     a = RefreshArgs()
     a.n_req = len(blk) - 1
     a.d_model, a.d_idx, a.n_idx, a.dtype = int(d_model), int(d_idx), int(n_idx), _dtype_code(dtype)
-    a.reserved0 = 0
+    a.select_level = 0.0
     a.hidden = _ptr(hidden)
     a.hidden_req_stride = int(hidden_req_stride)
     a.hidden_idx_stride = int(hidden_idx_stride)
@@ -324,7 +324,7 @@ def lsa_index_refresh_workspace(*, dtype, d_model, d_idx, n_idx, blk_off) -> int
 
 def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_off, bias, sel_ids, sel_count,
                       workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, ev_begin=None,
-                      ev_end=None, table_out=None, table_slot_base=None, stream=None) -> None:
+                      ev_end=None, table_out=None, table_slot_base=None, stream=None, select_level=0.5) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     blk = np.asarray(blk_off, dtype=np.int64)
     n_req, n_blk, e = len(blk) - 1, int(blk[-1]), _elt(dtype)
@@ -348,6 +348,7 @@ def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_of
     a.ev_end = ev_end.cuda_event if ev_end is not None else None
     tsb = _i32(table_slot_base) if table_slot_base is not None else None
     a.table_out, a.table_slot_base = _ptr(table_out), _ptr(tsb)
+    a.select_level = float(select_level)
     _check(LIB.lsa_index_refresh(ctypes.byref(a), _stream(stream)))
 
 

@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 
 #include "lsa_internal.hpp"
 
@@ -61,6 +62,7 @@ struct RefreshParams {
     unsigned long long* hw;   // [total words][2]               tag | union bits of one half word
     unsigned long long* bad;  // [n_req]                        tag when a wait of the request gave up
     unsigned long long tag;   // call number << 32
+    float select_logit;       // a block is kept when z > this (logit of the selection level)
     int n_req, d_model, d_idx, n_idx, n_halves, n_encode_waves, n_encode_groups, n_score_groups;
     long long blk_off[kMaxReq + 1];
     int word_off[kMaxReq + 1];
@@ -346,7 +348,7 @@ __device__ void score_role(const RefreshParams& p, int sw) {
                 float z = part[0];
 #pragma unroll
                 for (int b = S::LOG_LPR - S::LOG_P - 1; b >= 0; --b) z += __shfl_xor(z, 1 << b, 64);
-                const bool keep = q_ok && (rowi < n_valid) && (z + p.bias[r * p.n_idx + i] > 0.f);
+                const bool keep = q_ok && (rowi < n_valid) && (z + p.bias[r * p.n_idx + i] > p.select_logit);
                 const unsigned long long m = __ballot(keep);
                 // row q of the half word sits on lane (q % RPL) * LPR + ((q / RPL) << (LOG_LPR - LOG_P))
                 unsigned bits = 0u;
@@ -539,7 +541,9 @@ lsa_status refresh_layout(const lsa_refresh_args* a, RefreshLayout* L) {
     LSA_CHECK_SUP(a->n_idx >= 1 && a->n_idx <= 4, "lsa_index_refresh: n_idx=%d (1..4)", a->n_idx);
     LSA_CHECK_SUP(a->d_model >= 256 && a->d_model % 256 == 0 && a->d_model <= 16384,
                   "lsa_index_refresh: d_model=%d (multiple of 256, <= 16384)", a->d_model);
-    LSA_CHECK_ARG(a->reserved0 == 0, "lsa_index_refresh: reserved0 must be 0");
+    LSA_CHECK_ARG(a->select_level == 0.f || (a->select_level > 0.f && a->select_level < 1.f),
+                  "lsa_index_refresh: select_level=%g (0 for 0.5, else strictly between 0 and 1)",
+                  (double)a->select_level);
     LSA_CHECK_ARG(a->blk_off != nullptr, "lsa_index_refresh: blk_off is null");
     LSA_CHECK_ARG(a->blk_off[0] == 0, "lsa_index_refresh: blk_off[0] must be 0");
     long long words = 0;
@@ -586,6 +590,9 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
     rp.hw = reinterpret_cast<unsigned long long*>(ws + L.hw_off);
     rp.bad = reinterpret_cast<unsigned long long*>(ws + L.bad_off);
     rp.tag = (unsigned long long)call << 32;
+    // the level's logit in double, then fp32 for the comparison with the fp32 logit (0 for 0.5)
+    const double lev = a->select_level == 0.f ? 0.5 : (double)a->select_level;
+    rp.select_logit = (float)std::log(lev / (1.0 - lev));
     rp.n_req = a->n_req;
     rp.d_model = a->d_model;
     rp.d_idx = a->d_idx;

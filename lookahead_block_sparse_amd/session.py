@@ -59,8 +59,9 @@ class LSASession:
                  capacity: Optional[Sequence[int]] = None, cold_on_device: bool = False,
                  with_masks: bool = False, device: str = "cuda", stream: Optional[torch.cuda.Stream] = None,
                  max_groups: int = 0, n_layers: int = 1, w_down: Optional[np.ndarray] = None,
-                 device_plan: bool = False, cold_host_mirror: bool = False):
+                 device_plan: bool = False, cold_host_mirror: bool = False, select_level: float = 0.5):
         self.dtype = dtype
+        self.select_level = float(select_level)  # keep a block when sigmoid(logit) > this
         self.n_idx, self.d_model, self.d_idx = n_idx, d_model, d_idx
         # low-rank query projection: w_down = A [n_idx][rank][d_model], w_q = B [n_idx][d_idx][rank];
         # every refresh first forms the latents c_i = A_i h, and the Query Encoder reads them
@@ -301,7 +302,7 @@ class LSASession:
                           workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
                           table_out=(self.table[2 * int(self.slot_base[r0]):] if table_out else None),
                           table_slot_base=(self.slot_base[r0:r1] if table_out else None),
-                          stream=self.stream)
+                          stream=self.stream, select_level=self.select_level)
 
     def masks_of(self, r: int) -> np.ndarray:
         """Request r's bit planes [n_idx+1][words] (after a refresh with masks enabled)."""

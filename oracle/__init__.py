@@ -16,6 +16,7 @@ from .lsa_ref import (  # noqa: F401
     decode_values,
     governing_refresh,
     kv_rows,
+    level_logit,
     query_encoder,
     query_latent,
     round_bf16,

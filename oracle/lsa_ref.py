@@ -143,12 +143,22 @@ def block_logits(q: np.ndarray, keys: np.ndarray, bias: np.ndarray) -> np.ndarra
     return np.stack([keys[i] @ q[i] + bias[i] for i in range(keys.shape[0])])
 
 
-def threshold(z: np.ndarray) -> np.ndarray:
-    """Per-indexer selection: keep block b iff sigmoid(z) > 0.5, i.e. iff z > 0.
+def level_logit(level: float) -> float:
+    """The logit at which sigmoid equals `level`: log(level / (1 - level)); 0 for the pages' 0.5."""
+    level = float(level)
+    if not 0.0 < level < 1.0:
+        raise ValueError("the selection level lies strictly between 0 and 1")
+    return float(np.log(level / (1.0 - level)))
 
-    [Explained] section 2 step 3 (blocks with sigmoid score above 0.5 are loaded).
+
+def threshold(z: np.ndarray, level: float = 0.5) -> np.ndarray:
+    """Per-indexer selection: keep block b iff sigmoid(z) > level, i.e. iff z > logit(level).
+
+    [Explained] section 2 step 3 (blocks with sigmoid score above 0.5 are loaded); section 7 calls
+    the 0.5 a preliminary choice, so the level is a parameter.  The sigmoid is monotone, so the
+    comparison is made on the logit.
     """
-    return np.asarray(z, dtype=np.float64) > 0.0
+    return np.asarray(z, dtype=np.float64) > level_logit(level)
 
 
 def union(s: np.ndarray) -> np.ndarray:
@@ -177,11 +187,12 @@ class RefreshResult:
         return int(len(self.ids))
 
 
-def refresh(h: np.ndarray, w_q: np.ndarray, keys: np.ndarray, bias: np.ndarray) -> RefreshResult:
+def refresh(h: np.ndarray, w_q: np.ndarray, keys: np.ndarray, bias: np.ndarray,
+            level: float = 0.5) -> RefreshResult:
     """One index refresh: [Explained] section 2 steps 2-3 with section 4's union."""
     q = query_encoder(h, w_q)
     z = block_logits(q, keys, bias)
-    s = threshold(z)
+    s = threshold(z, level)
     u = union(s)
     return RefreshResult(q=q, z=z, s=s, u=u, ids=compact(u))
 
@@ -303,7 +314,7 @@ def simulate(wl, steps: Optional[Sequence[int]] = None, requests: Optional[Seque
         hs = [decode_values(wl.hidden[r][k], dt) for k in range(len(wl.refresh_steps[r]))]
         if w_down is not None:  # low-rank query projection: the Query Encoder reads the latents
             hs = [query_latent(h, w_down, dt) for h in hs]
-        res = [refresh(h, w_q, keys, bias) for h in hs]
+        res = [refresh(h, w_q, keys, bias, getattr(cfg, "level", 0.5)) for h in hs]
         refreshes[r] = res
         if not step_list:
             continue

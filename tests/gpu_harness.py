@@ -45,14 +45,16 @@ def oracle_latent_fn(dtype):
     return fn
 
 
-def oracle_logits_fn(dtype):
-    return lambda q, keys, bias: oracle.block_logits(q, oracle.decode_values(keys, dtype), bias)
+def oracle_logits_fn(dtype, level=0.5):
+    """Logits relative to the selection level's logit (the decision point the margin keeps away from)."""
+    off = oracle.level_logit(level)
+    return lambda q, keys, bias: oracle.block_logits(q, oracle.decode_values(keys, dtype), bias) - off
 
 
 def conditioned_workload(name_or_cfg, seed=0, steps=None):
     wl = build_workload(name_or_cfg, seed=seed, steps=steps)
     dt = wl.cfg.dtype
-    rep = wl.condition(oracle_query_fn(dt), oracle_logits_fn(dt), latent_fn=oracle_latent_fn(dt))
+    rep = wl.condition(oracle_query_fn(dt), oracle_logits_fn(dt, wl.cfg.level), latent_fn=oracle_latent_fn(dt))
     assert rep.min_abs_logit >= 2e-3, rep
     return wl
 
@@ -73,7 +75,7 @@ def make_session(wl, capacity=None, cold_on_device=False, with_masks=True, max_g
                       n_heads=cfg.n_heads, head_dim=cfg.head_dim, win_cap=cfg.window, n_blocks=wl.n_blocks,
                       w_q=wl.w_q, keys=wl.keys, capacity=capacity, cold_on_device=cold_on_device,
                       with_masks=with_masks, max_groups=max_groups, w_down=wl.w_down, device_plan=device_plan,
-                      n_layers=wl.cfg.n_layers, cold_host_mirror=cold_host_mirror)
+                      n_layers=wl.cfg.n_layers, cold_host_mirror=cold_host_mirror, select_level=wl.cfg.level)
     for r in range(wl.n_req):
         k, v = wl.kv_prefill(r)
         sess.load_prefill(r, k, v)

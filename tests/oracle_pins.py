@@ -108,6 +108,25 @@ def pin_threshold_is_sigmoid_half(O):
     assert np.array_equal(got, want)
 
 
+def pin_threshold_levels(O):
+    """At other selection levels the rule is still sigmoid(z) > level, computed with math.exp, on
+    logits on either side of the level's logit (offsets 1e-6 .. 30) and at a few fixed values; the
+    default level is 0.5."""
+    for level in (0.1, 0.3, 0.5, 0.7, 0.9):
+        lg = math.log(level / (1.0 - level))
+        mags = np.logspace(-6, np.log10(30), 120)
+        z = np.concatenate([lg + mags, lg - mags, [-3.0, -0.5, 0.0, 0.4, 2.5]])
+        want = np.array([1.0 / (1.0 + math.exp(-v)) > level for v in z])
+        assert np.array_equal(O.threshold(z, level), want), level
+    z = np.linspace(-4, 4, 81)
+    assert np.array_equal(O.threshold(z), O.threshold(z, 0.5))
+    # a higher level keeps fewer blocks: the selections are nested
+    rng = _rng(13)
+    z = rng.standard_normal((3, 400))
+    sets = [O.threshold(z, lv) for lv in (0.2, 0.5, 0.8)]
+    assert (sets[1] <= sets[0]).all() and (sets[2] <= sets[1]).all() and sets[0].sum() > sets[2].sum()
+
+
 def pin_union_is_set_union(O):
     """Loaded ids = sorted(set union of the per-indexer selections)."""
     rng = _rng(4)
@@ -510,6 +529,7 @@ PINS = [
     pin_query_encoder_brute,
     pin_block_logits,
     pin_threshold_is_sigmoid_half,
+    pin_threshold_levels,
     pin_union_is_set_union,
     pin_golden_or_union,
     pin_golden_cadence,

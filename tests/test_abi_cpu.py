@@ -442,3 +442,19 @@ def test_denoise_wrapper_refuses_host_buffers():
               workspace=FAKE)
     with pytest.raises(TypeError, match="logits"):
         L.lsa_label_denoise(**kw)
+
+
+@pytest.mark.parametrize("level,ok", [(0.0, True), (0.5, True), (0.05, True), (0.95, True), (1.0, False),
+                                      (-0.2, False), (1.5, False), (float("nan"), False)])
+def test_refresh_select_level_validation(level, ok):
+    """select_level: 0 (the pages' 0.5) or strictly between 0 and 1; anything else is refused before
+    any HIP call."""
+    a, keep = L._refresh_args(dtype="bf16", d_model=4096, d_idx=256, n_idx=3, hidden=None, hidden_req_stride=4096,
+                              hidden_idx_stride=0, w_q=None, keys=None, blk_off=[0, 2048], bias=None,
+                              sel_ids=None, sel_count=None, masks=None, workspace=None, workspace_bytes=0)
+    a.select_level = level
+    n = ctypes.c_size_t(0)
+    st = L.LIB.lsa_index_refresh_workspace(ctypes.byref(a), ctypes.byref(n))
+    assert (st == L.LSA_OK) == ok, (level, st)
+    if not ok:
+        assert st == L.LSA_ERR_INVALID and b"select_level" in L.LIB.lsa_last_error()

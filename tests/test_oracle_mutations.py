@@ -17,12 +17,21 @@ from oracle_pins import PINS
 _orig = {name: getattr(ref, name) for name in dir(ref) if not name.startswith("_")}
 
 
-def _m_threshold_ge(z):
-    return np.asarray(z, dtype=np.float64) >= 0.0
+def _m_threshold_ge(z, level=0.5):
+    return np.asarray(z, dtype=np.float64) >= ref.level_logit(level)
 
 
-def _m_threshold_prob(z):
-    return np.asarray(z, dtype=np.float64) > 0.5
+def _m_threshold_prob(z, level=0.5):
+    return np.asarray(z, dtype=np.float64) > level
+
+
+def _m_threshold_ignores_level(z, level=0.5):
+    return np.asarray(z, dtype=np.float64) > 0.0
+
+
+def _m_level_logit_flipped(level):
+    level = float(level)
+    return float(np.log((1.0 - level) / level))
 
 
 def _m_union_and(s):
@@ -190,6 +199,8 @@ def _m_seq_len_no_current(n_prefill, t):
 MUTATIONS = [
     ("threshold", _m_threshold_ge),
     ("threshold", _m_threshold_prob),
+    ("threshold", _m_threshold_ignores_level),
+    ("level_logit", _m_level_logit_flipped),
     ("union", _m_union_and),
     ("union", _m_union_first),
     ("compact", _m_compact_desc),

@@ -43,6 +43,8 @@ class LSAConfig:
     n_layers: int = 1
     # correlation of successive refresh hidden states: h_k = rho h_{k-1} + sqrt(1 - rho^2) eps_k
     hidden_rho: float = 0.0
+    # selection level: a block is kept when sigmoid(logit) > level (0.5 on the pages)
+    level: float = 0.5
     # low-rank query projection: 0 = full rank (W_q [n_idx][d_idx][d_model]); r > 0 = each indexer
     # projects the latent c_i = A_i h (A_i [r][d_model]) with B_i [d_idx][r] (w_q holds B)
     q_rank: int = 0
