@@ -114,7 +114,9 @@ def parse():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no run: turn the counter_collection.csv files of a FETCH_SIZE and a WRITE_SIZE "
                          "rocprofv3 pass (both taken with --calib-copy-mib) into "
-                         "profiles/attn_kernel_<workload>_traffic.json")
+                         "profiles/<kernel>_<workload>_traffic.json")
+    ap.add_argument("--traffic-kernel", default="attn_kernel", choices=sorted(KERNEL_SOURCES),
+                    help="the kernel --traffic-summary summarises")
     return ap.parse_args()
 
 
@@ -144,17 +146,21 @@ def _planting_latent(dtype):
     return fn
 
 
-def kernel_hash() -> str:
-    """Hash of the sources the attention kernel is built from (its counters stay valid while this
-    is unchanged)."""
+KERNEL_SOURCES = {"attn_kernel": ("decode.hip", "lsa_internal.hpp"),
+                  "refresh_kernel": ("refresh.hip", "lsa_internal.hpp")}
+
+
+def kernel_hash(kernel: str = "attn_kernel") -> str:
+    """Hash of the sources a kernel is built from (its counters stay valid while this is unchanged)."""
     h = hashlib.sha256()
-    for name in ("decode.hip", "lsa_internal.hpp"):
+    for name in KERNEL_SOURCES[kernel]:
         h.update((ROOT / "lookahead_block_sparse_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 
 
-def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> dict:
-    """HBM bytes per attn_kernel launch from two rocprofv3 counter passes.  Each counter is scaled
+def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: int,
+                    kernel: str = "attn_kernel") -> dict:
+    """HBM bytes per launch of `kernel` from two rocprofv3 counter passes.  Each counter is scaled
     by what it reads for the plain device copy of calib_mib MiB in the same pass (read calib bytes,
     write calib bytes), which takes out the counters' units and any sampling of channels."""
     import csv
@@ -162,39 +168,46 @@ def traffic_summary(fetch_csv: str, write_csv: str, workload: str, calib_mib: in
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         calib = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        attn = [float(r["Counter_Value"]) for r in rows if "attn_kernel" in r["Kernel_Name"]]
-        if not attn or not calib:
-            raise SystemExit(f"{path}: no attn_kernel or copy dispatches with {counter}")
-        return float(np.mean(attn)), max(calib), len(attn)
+        mine = [r for r in rows if kernel in r["Kernel_Name"]]
+        # the launches over every request (the largest grid): a run also refreshes single requests
+        # to recompute selections, and those launches read a quarter of the keys
+        grid = max((int(r["Grid_Size"]) for r in mine), default=0)
+        vals = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == grid]
+        if not vals or not calib:
+            raise SystemExit(f"{path}: no {kernel} or copy dispatches with {counter}")
+        return float(np.mean(vals)), max(calib), len(vals)
 
     n = calib_mib << 20
-    f_attn, f_cal, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w_attn, w_cal, n_w = per_kernel(write_csv, "WRITE_SIZE")
+    f_k, f_cal, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_k, w_cal, n_w = per_kernel(write_csv, "WRITE_SIZE")
     f_scale, w_scale = n / (f_cal * 1024.0), n / (w_cal * 1024.0)
     return {
-        "kernel": "attn_kernel",
+        "kernel": kernel,
         "workload": workload,
         "dispatches": {"fetch_pass": n_f, "write_pass": n_w},
-        "fetch_size_kib_per_dispatch": f_attn,
-        "write_size_kib_per_dispatch": w_attn,
+        "launch": "the launches of the largest grid (every request of the workload)",
+        "fetch_size_kib_per_dispatch": f_k,
+        "write_size_kib_per_dispatch": w_k,
         "calib_copy_bytes": n,
         "calib_fetch_size_kib": f_cal,
         "calib_write_size_kib": w_cal,
         "fetch_scale": f_scale,
         "write_scale": w_scale,
-        "traffic_bytes_per_launch": f_attn * 1024.0 * f_scale + w_attn * 1024.0 * w_scale,
-        "kernel_sources_sha256_16": kernel_hash(),
+        "fetch_bytes_per_launch": f_k * 1024.0 * f_scale,
+        "write_bytes_per_launch": w_k * 1024.0 * w_scale,
+        "traffic_bytes_per_launch": f_k * 1024.0 * f_scale + w_k * 1024.0 * w_scale,
+        "kernel_sources_sha256_16": kernel_hash(kernel),
     }
 
 
-def stored_traffic(workload: str, khash: str):
-    """HBM traffic of the attention kernel from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
-    f = ROOT / "profiles" / f"attn_kernel_{workload}_traffic.json"
+def stored_traffic(workload: str, kernel: str = "attn_kernel"):
+    """HBM traffic per launch of a kernel from the committed counter summary, if it was taken on the
+    kernel's current sources; else None."""
+    f = ROOT / "profiles" / f"{kernel}_{workload}_traffic.json"
     if not f.exists():
         return None
     d = json.loads(f.read_text())
-    if d.get("kernel_sources_sha256_16") != khash:
+    if d.get("kernel_sources_sha256_16") != kernel_hash(kernel):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -465,8 +478,9 @@ def main():
     if args.traffic_summary:
         if args.calib_copy_mib <= 0:
             raise SystemExit("--traffic-summary needs the --calib-copy-mib the counter passes ran with")
-        d = traffic_summary(*args.traffic_summary, workload=args.workload, calib_mib=args.calib_copy_mib)
-        out = ROOT / "profiles" / f"attn_kernel_{args.workload}_traffic.json"
+        d = traffic_summary(*args.traffic_summary, workload=args.workload, calib_mib=args.calib_copy_mib,
+                            kernel=args.traffic_kernel)
+        out = ROOT / "profiles" / f"{args.traffic_kernel}_{args.workload}_traffic.json"
         out.write_text(json.dumps(d, indent=1) + "\n")
         print(json.dumps(d))
         return
@@ -967,7 +981,7 @@ def run_loop(args) -> dict:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": stored_traffic(cfg.name, khash),
+            "traffic": stored_traffic(cfg.name),
             "algorithmic_bytes_per_launch": float(ev_bytes.mean()),
             "timed_launches": int(len(attn_ms)),
             "mean_launch_us": float(attn_ms.mean() * 1e3),
@@ -986,7 +1000,8 @@ def run_loop(args) -> dict:
         "refresh_roofline": ({"kernel": "refresh_kernel (encode + score + compaction, one launch)",
                               "achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                              "algorithmic_bytes": ref_bytes, "requests_per_refresh": len(ref_reqs)}
+                              "algorithmic_bytes": ref_bytes, "requests_per_refresh": len(ref_reqs),
+                              "traffic": stored_traffic(cfg.name, "refresh_kernel")}
                              if len(ref_us) else None),
         "latent_us": float(np.median(lat_us)) if len(lat_us) else None,
         "latent_roofline": ({"achieved": lat_bytes / (np.median(lat_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
@@ -998,6 +1013,7 @@ def run_loop(args) -> dict:
         "gather_copy": gather_copy,
         "cold_pool_in_pinned_host_memory": host_cold,
         "kernel_sources_sha256_16": khash,
+        "refresh_sources_sha256_16": kernel_hash("refresh_kernel"),
     }
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20

@@ -377,7 +377,7 @@ lsa_status lsa_sparse_decode(const lsa_decode_args* a, hipStream_t stream);
 /* lsa_sparse_decode without a workspace, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The same
  * kernels and results as lsa_sparse_decode; a->workspace and a->workspace_bytes are ignored and the
- * split-K partials go to a static array of the library, one per device (3,194,880 bytes: up to
+ * split-K partials go to a static array of the library, one per device (3,195,392 bytes: up to
  * 320 work-groups plus LSA_MAX_DECODE_REQ requests at head_dim 128), held until the process ends.
  * A call that would need more returns LSA_ERR_WORKSPACE and enqueues nothing.  The call allocates
  * nothing (its first call on a device looks the array's device address up once).  Every call on

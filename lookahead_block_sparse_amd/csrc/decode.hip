@@ -46,6 +46,7 @@ struct DecodeParams {
     const int2* table;
     float* part_o;   // [P][16][D]
     float* part_ml;  // [P][16][2]
+    int* mrange;     // device-side counts: [n_req][2] first and last group of each request, for the merge
     const int* n_sel_dev;  // optional: entry counts on the device (n_sel then holds capacities)
     int n_req, n_heads, n_chunks, win_cap, n_slots, n_groups;
     float scale_log2;
@@ -61,6 +62,7 @@ struct DecodeParams {
 struct MergeParams {
     const float* part_o;
     const float* part_ml;
+    const int* mrange;  // device-side counts: each request's groups, written by the attention kernel
     float* out;
     const int* n_sel_dev;
     int n_req, n_heads, n_groups;
@@ -357,6 +359,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
     // both sources are uniform: the LDS values are moved to scalar registers
     auto prefix = [&](int r) { return dev_counts ? __builtin_amdgcn_readfirstlane(s_pre[r]) : p.tile_prefix[r]; };
     const long long T_ = prefix(p.n_req), G = split_groups(p.n_groups, T_);
+    if (dev_counts && w == 0 && (int)threadIdx.x < p.n_req) {
+        // the groups whose tile ranges meet each request's tiles, for the merge (which would otherwise
+        // repeat this split in every one of its groups before reading a partial)
+        const int rr = threadIdx.x;
+        p.mrange[2 * rr] = split_group_of(s_pre[rr], T_, G);
+        p.mrange[2 * rr + 1] = split_group_of(s_pre[rr + 1] - 1, T_, G);
+    }
     if (w >= G) return;
     const int a = (int)split_bound(w, T_, G);
     const int b = (int)split_bound(w + 1, T_, G);
@@ -552,8 +561,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     __shared__ float s_acc[kMergeSub][kMergeCols];
     __shared__ float s_l[kMergeSub][kMergeCols];
     __shared__ float s_m[kMergeSub][kMergeCols];
-    __shared__ int s_ns[kMaxReq];
-    __shared__ int s_pre[kMaxReq + 1];
     constexpr int NC = D / kMergeCols;
     const int c = blockIdx.x % NC;
     const int rh = blockIdx.x / NC;
@@ -564,11 +571,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
     const int sub = threadIdx.x / kMergeCols;
     // the groups whose tile ranges meet request r's tiles
     int w0 = p.w_lo[r], w1 = p.w_hi[r];
-    if (p.n_sel_dev) {
-        tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.n_req, s_ns, s_pre);
-        const long long T_ = s_pre[p.n_req], G = split_groups(p.n_groups, T_);
-        w0 = split_group_of(s_pre[r], T_, G);
-        w1 = split_group_of(s_pre[r + 1] - 1, T_, G);
+    if (p.n_sel_dev) {  // computed by the attention kernel from the same counts
+        w0 = p.mrange[2 * r];
+        w1 = p.mrange[2 * r + 1];
     }
     float m = -INFINITY, acc = 0.f, lsum = 0.f;
     for (int w = w0 + sub; w <= w1; w += 4 * kMergeSub) {
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
 struct DecodePlan {
     int G = 0;
     int total_tiles = 0;
-    size_t part_o_off = 0, part_ml_off = 0, total = 0;
+    size_t part_o_off = 0, part_ml_off = 0, mrange_off = 0, total = 0;
 };
 
 lsa_status decode_check(const lsa_decode_args* a) {
@@ -672,6 +677,8 @@ lsa_status decode_plan(const lsa_decode_args* a, DecodePlan* P, bool sizing_only
     off = align_up(off + (size_t)n_part * kHeads * a->head_dim * sizeof(float), 256);
     P->part_ml_off = off;
     off = align_up(off + (size_t)n_part * kHeads * 2 * sizeof(float), 256);
+    P->mrange_off = off;
+    off = align_up(off + (size_t)a->n_req * 2 * sizeof(int), 256);
     P->total = off;
     return LSA_OK;
 }
@@ -689,6 +696,7 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, char* ws
     dp.table = reinterpret_cast<const int2*>(a->table);
     dp.part_o = reinterpret_cast<float*>(ws + P.part_o_off);
     dp.part_ml = reinterpret_cast<float*>(ws + P.part_ml_off);
+    dp.mrange = reinterpret_cast<int*>(ws + P.mrange_off);
     dp.n_req = a->n_req;
     dp.n_heads = a->n_heads;
     dp.n_chunks = a->win_cap / 64;
@@ -732,6 +740,7 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, char* ws
     }
     mp.part_o = dp.part_o;
     mp.part_ml = dp.part_ml;
+    mp.mrange = dp.mrange;
     mp.out = a->out;
     mp.n_sel_dev = a->n_sel_dev;
     mp.n_req = a->n_req;
@@ -760,7 +769,8 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, char* ws
 constexpr int kScratchGroups = 320;
 constexpr size_t kScratchBytes =
     (size_t)(kScratchGroups + kMaxReq) * kHeads * 128 * sizeof(float) +  // partial outputs (a 256 multiple)
-    (size_t)(kScratchGroups + kMaxReq) * kHeads * 2 * sizeof(float);     // (m, l) pairs
+    (size_t)(kScratchGroups + kMaxReq) * kHeads * 2 * sizeof(float) +    // (m, l) pairs (a 256 multiple)
+    (size_t)kMaxReq * 2 * sizeof(int);                                   // the merge's group ranges
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 // Device address of `scratch` on the current device: looked up once per device (each device holds
