@@ -794,12 +794,10 @@ def run_loop(args) -> dict:
             toks += min(L, cfg.window)
             if rloop is not None or dplan:
                 ids = sel_at[t][r]
-                n_entries += len(ids)  # the decode reads every table entry (in-window ones masked)
-                n = int(np.searchsorted(ids, (ws + 63) // 64, side="left"))
             else:
-                ids = sel_hist[(r, int(ver[r]))] if n_att[r] > 0 else None
-                n = int(n_att[r])
-                n_entries += n
+                ids = sel_hist.get((r, int(ver[r])), np.zeros(0, dtype=np.int32))
+            n_entries += len(ids)  # the decode reads every table entry (in-window blocks are skipped)
+            n = int(np.searchsorted(ids, (ws + 63) // 64, side="left"))
             if n > 0:
                 last = int(ids[n - 1])
                 toks += 64 * (n - 1) + min(64, ws - 64 * last)

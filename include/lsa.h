@@ -353,7 +353,9 @@ typedef struct lsa_decode_args {
     int32_t reserved0;         /* must be 0 */
     const int32_t* table;      /* dev: request r's (block id, slot) pairs start at pair tbl_off[r] */
     const int32_t* tbl_off;    /* host [n_req] */
-    const int32_t* n_sel;      /* host [n_req]: entries in request r's table (ascending block id) */
+    const int32_t* n_sel;      /* host [n_req]: entries in request r's table (ascending block id);
+                                  the kernel itself leaves out the tokens of blocks at or past the
+                                  window start, so the whole table is passed */
     const int32_t* seq_len;    /* host [n_req]: L, >= 1 */
     const int32_t* window;     /* host [n_req]: W, 1..win_cap */
     float* out;                /* dev [n_req][n_heads][head_dim] fp32 */

@@ -138,9 +138,6 @@ class LSASession:
         self._gargs: List[Optional[tuple]] = [None] * self.n_req
         self._pargs = {}  # device-plan argument structs per run of requests
         self._stage_ev: List[Optional[torch.cuda.Event]] = [None] * self.n_req
-        self.last_decode_event: Optional[torch.cuda.Event] = None
-        # record an event after each decode so a gather on another stream can wait for it
-        self.track_decode = False
         # residency planned on the device (lsa_gather_plan_device): the state lives in HBM and a
         # refresh never waits for the host
         self.device_plan = bool(device_plan)
@@ -387,9 +384,9 @@ class LSASession:
             raise RuntimeError("device-planned refresh failed: " +
                                "; ".join(f"request {r} {what.get(int(st[r]), int(st[r]))}" for r in bad))
 
-    def gather(self, r: int, ids: np.ndarray, stream: Optional[torch.cuda.Stream] = None):
+    def gather(self, r: int, ids: np.ndarray):
         """Make request r's hot pool hold exactly `ids` (returns (copied, kept))."""
-        return self.gather_many({r: ids}, stream)[r]
+        return self.gather_many({r: ids})[r]
 
     def _gather_args(self, r: int):
         if self.cold[r] is None:
@@ -413,17 +410,13 @@ class LSASession:
             self._gargs[r] = (a, counts)
         return self._gargs[r]
 
-    def gather_many(self, sel: Dict[int, np.ndarray], stream: Optional[torch.cuda.Stream] = None,
-                    ev_copy=(None, None)):
+    def gather_many(self, sel: Dict[int, np.ndarray], ev_copy=(None, None)):
         """Gathers of several requests after one refresh, planned together and copied by one kernel
-        launch (lsa_gather_blocks_batch).  Returns {r: (copied, kept)}.  ev_copy (a pair of
-        torch.cuda.Event) takes the copy kernel's dispatch stamps."""
-        st = stream if stream is not None else self.stream
-        if st is not self.stream:
-            if not self.track_decode:
-                raise RuntimeError("set track_decode before gathering on a side stream")
-            if self.last_decode_event is not None:
-                st.wait_event(self.last_decode_event)  # slots of leaving blocks may still be read
+        launch (lsa_gather_blocks_batch) on the session's stream, so they follow every decode step
+        enqueued before them (slots of leaving blocks are overwritten) and precede every later one.
+        Returns {r: (copied, kept)}.  ev_copy (a pair of torch.cuda.Event) takes the copy kernel's
+        dispatch stamps."""
+        st = self.stream
         reqs = list(sel)
         ids = {r: np.ascontiguousarray(sel[r], dtype=np.int32) for r in reqs}
         arr = (GatherArgs * len(reqs))()
@@ -447,8 +440,6 @@ class LSASession:
             self.sel_host[r] = ids[r]
             self.sel_version[r] += 1
             out[r] = (int(counts[k][0]), int(counts[k][1]))
-        if st is not self.stream:
-            self.stream.wait_event(ev)
         return out
 
     def make_resident(self) -> None:
@@ -466,15 +457,6 @@ class LSASession:
         return res
 
     # ---------------------------------------------------------------------------------------
-    def attended_entries(self, seq_len: Sequence[int], window: Sequence[int]) -> np.ndarray:
-        """Per request, the number of leading table entries whose block starts before the window
-        (the only ones that contribute; the table is ascending by block id)."""
-        out = np.empty(self.n_req, dtype=np.int32)
-        for r in range(self.n_req):
-            ws = max(0, int(seq_len[r]) - int(window[r]))
-            out[r] = np.searchsorted(self.sel_host[r], (ws + BLOCK_TOKENS - 1) // BLOCK_TOKENS, side="left")
-        return out
-
     def decode(self, q: torch.Tensor, seq_len: Sequence[int], window: Sequence[int], out: torch.Tensor,
                k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
                max_groups: Optional[int] = None, ev_attn_begin=None, ev_attn_end=None, layer: int = 0) -> None:
@@ -482,24 +464,19 @@ class LSASession:
         pool, ring = self.layer_views(layer)
         lsa_sparse_decode(dtype=self.dtype, n_heads=self.n_heads, head_dim=self.head_dim, win_cap=self.win_cap,
                           q=q, ring=ring, out=out, workspace=self.decode_ws,
-                          tbl_off=self.slot_base[:-1], n_sel=self.attended_entries(seq_len, window),
+                          tbl_off=self.slot_base[:-1], n_sel=self.n_sel,
                           seq_len=seq_len, window=window,
                           pool=pool, n_slots_total=self.n_slots, table=self.table, k_new=k_new, v_new=v_new,
                           max_groups=self.max_groups if max_groups is None else max_groups,
                           ev_attn_begin=ev_attn_begin, ev_attn_end=ev_attn_end, stream=self.stream)
-        if self.track_decode:
-            # one event re-recorded every step: a later wait sees the latest decode
-            if self.last_decode_event is None:
-                self.last_decode_event = torch.cuda.Event()
-            self.last_decode_event.record(self.stream)
 
 
 class DecodeLoop:
     """Per-step decode calls with the argument struct built once.
 
     For a fixed session, window and stream, step(t) only rewrites the per-request lengths (prefill +
-    t + 1), the attended table entries and the q / k_new / v_new addresses, then calls
-    lsa_sparse_decode.  Events (torch.cuda.Event) may be passed per call to time the attention kernel.
+    t + 1), the table counts and the q / k_new / v_new addresses, then calls lsa_sparse_decode (which
+    itself leaves out the table's blocks that lie inside the window).  Events (torch.cuda.Event) may be passed per call to time the attention kernel.
     """
 
     def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor,
@@ -533,21 +510,12 @@ class DecodeLoop:
         self.args = a
         self.ref = ctypes.byref(a)
         self.stream = ctypes.c_void_p(sess.stream.cuda_stream)
-        self._bnd = np.full(sess.n_req, -1, dtype=np.int64)
-        self._ver = np.full(sess.n_req, -1, dtype=np.int64)
 
     def step(self, t: int, q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
              ev_begin=None, ev_end=None) -> None:
         np.add(self.prefill, t + 1, out=self.seq_len, casting="unsafe")
-        # attended table entries change only when a window start crosses a block boundary or a
-        # request's selection changes (device counts: the kernels mask blocks inside the window)
-        bnd = (np.maximum(0, self.seq_len - self.window) + BLOCK_TOKENS - 1) // BLOCK_TOKENS
-        changed = (bnd != self._bnd) | (self.sess.sel_version != self._ver)
-        if changed.any() and not self.device_counts:
-            for r in np.flatnonzero(changed):
-                self.n_sel[r] = np.searchsorted(self.sess.sel_host[r], bnd[r], side="left")
-            self._bnd = bnd
-            self._ver = self.sess.sel_version.copy()
+        if not self.device_counts:  # the table counts of the host-planned selections
+            self.n_sel[:] = self.sess.n_sel
         a = self.args
         a.q = q.data_ptr()
         a.k_new = k_new.data_ptr() if k_new is not None else None

@@ -33,8 +33,7 @@ def _decode_args(sess, wl, t, out, reqs_limit=None):
                          else np.ascontiguousarray(wl.q_dec[t][:R])).to(sess.device)
     seq_len = (wl.ctx[:R] + t + 1).astype(np.int32)
     window = np.full(R, wl.cfg.window, dtype=np.int32)
-    n_sel = np.ascontiguousarray(sess.attended_entries(wl.ctx + t + 1, np.full(sess.n_req, wl.cfg.window))[:R],
-                                 dtype=np.int32)
+    n_sel = np.ascontiguousarray(sess.n_sel[:R], dtype=np.int32)  # whole tables: the kernel skips in-window blocks
     tbl_off = np.ascontiguousarray(sess.slot_base[:R], dtype=np.int32)
     keep += [q, seq_len, window, n_sel, tbl_off]
     a.q, a.ring, a.pool, a.table = q.data_ptr(), ring.data_ptr(), pool.data_ptr(), sess.table.data_ptr()
