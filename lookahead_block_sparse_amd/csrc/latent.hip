@@ -4,10 +4,18 @@
 // latent with B_i.
 //
 // A GEMV over A [n_idx][rank][d_model] shared by every request, HBM-bound on A (25 M elements at
-// n_idx = 3, r = 2048, d = 4096): each wave owns kRows rows of A and reads each row once for every
-// request; lane l reads 16-byte chunks l, l+64, ... of the row; fp32 accumulation, a wavefront sum,
-// and the latent stored in the input type (bf16: round to nearest, ties to even).
+// n_idx = 3, r = 2048, d = 4096), read once per call for all requests.  A work-group owns a tile of
+// kG consecutive rows of A (all of one indexer); its waves split the row into slices of 64 16-byte
+// chunks: lane l of the wave on slice s holds chunk 64 s + l of each of the kG rows, so that one load
+// instruction reads a contiguous 1 KiB run, and all kG loads of a wave are issued before any use.
+// The A chunks stay in registers while the requests go by kQ at a time: the lane loads its chunk of
+// each request's hidden state (L2-resident, 16 bytes per request), forms the kG x kQ partial dot
+// products (fp32 accumulation), and a butterfly reduce-scatter across the wave leaves each lane one
+// of those sums; the slices' sums meet in LDS, and the latent is stored in the input type (bf16:
+// round to nearest, ties to even).
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "lsa_internal.hpp"
 
@@ -15,16 +23,26 @@ namespace lsa {
 namespace {
 
 constexpr int kMaxReq = LSA_MAX_REFRESH_REQ;
-constexpr int kThreads = 256;
-constexpr int kRows = 2;  // rows of A per wave
-constexpr int kReq = 4;   // requests per round
+constexpr int kMaxWaves = 8;  // slices handled side by side; wider rows loop over slices
+constexpr int kG = 16;        // rows of A per tile (rank is a multiple of 256: tiles never straddle indexers)
+constexpr int kQ = 2;         // requests per round
+constexpr int kN = kG * kQ;   // partial sums per lane per round (a power of two, at most 64)
+static_assert((kN & (kN - 1)) == 0 && kN <= 64, "reduce-scatter over a power of two");
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// A is read once per call: non-temporal 16-byte loads
-__device__ __forceinline__ uint4 load_nt(const uint4* q) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q));
-    return make_uint4(v.x, v.y, v.z, v.w);
+// A is read once per call, through a buffer resource over the tile: non-temporal 16-byte loads at
+// a per-row scalar offset plus the lane's offset, so that all loads of a tile share one address
+// register (and a load past the tile returns zeros instead of touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 load_nt(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2 /* nt */);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint4 load(const char* base, unsigned off) {
+    return *reinterpret_cast<const uint4*>(base + off);
 }
 
 struct LatentParams {
@@ -40,11 +58,10 @@ struct Elem;
 template <>
 struct Elem<uint16_t> {
     static constexpr int N = 8;  // elements per 16 bytes
-    // acc + a.b over 8 bf16 pairs with the packed dot of two bf16 pairs into fp32
-    // (v_dot2_f32_bf16: the products of bf16 values are exact in fp32), 4 instructions where
-    // unpacking both operands and fusing would take 24 (the unpacking made the kernel ALU-bound)
-    __device__ static float dot_acc(uint4 a, uint4 b, float acc) {
-        acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.x), bf2(b.x), acc, false);
+    // a.b over 8 bf16 pairs with the packed dot of two bf16 pairs into fp32 (v_dot2_f32_bf16: the
+    // products of bf16 values are exact in fp32), 4 instructions where unpacking and fusing take 24
+    __device__ static float dot(uint4 a, uint4 b) {
+        float acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.x), bf2(b.x), 0.0f, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.y), bf2(b.y), acc, false);
         acc = __builtin_amdgcn_fdot2_f32_bf16(bf2(a.z), bf2(b.z), acc, false);
         return __builtin_amdgcn_fdot2_f32_bf16(bf2(a.w), bf2(b.w), acc, false);
@@ -59,8 +76,8 @@ struct Elem<uint16_t> {
 template <>
 struct Elem<float> {
     static constexpr int N = 4;
-    __device__ static float dot_acc(uint4 a, uint4 b, float acc) {
-        acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    __device__ static float dot(uint4 a, uint4 b) {
+        float acc = __uint_as_float(a.x) * __uint_as_float(b.x);
         acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
         acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
         return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
@@ -68,60 +85,106 @@ struct Elem<float> {
     __device__ static float store(float x) { return x; }
 };
 
+// v[0 .. kN) summed over the 64 lanes, scattered: afterwards v[0] of lane l holds the sum of entry
+// l mod kN.  At offset o every lane pairs with a lane whose index differs in bit o and agrees in
+// the bits above it; the lane keeps the half of its 2o entries that bit o of its own index selects
+// and adds the partner's copy of that half.  The exchanges are full-rate cross-lane moves: the
+// 16-lane row swap at o = 16, the row mirror (lane ^ 15) at 8, the half-row mirror (lane ^ 7) at 4,
+// quad permutations at 2 and 1, and the half-wave swap for the final sum.
+__device__ __forceinline__ float as_f(unsigned x) { return __uint_as_float(x); }
+__device__ __forceinline__ unsigned as_u(float x) { return __float_as_uint(x); }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int O, int CTRL>
+__device__ __forceinline__ void pair_step(float (&v)[kN], int lane) {
+    const bool hi = (lane & O) != 0;
+#pragma unroll
+    for (int j = 0; j < O; ++j) {
+        const float keep = hi ? v[j + O] : v[j];
+        const float send = hi ? v[j] : v[j + O];
+        v[j] = keep + dpp<CTRL>(send);
+    }
+}
+__device__ __forceinline__ void reduce_scatter(float (&v)[kN], int lane) {
+    static_assert(kN == 32, "the exchange pattern below covers 32 entries");
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {  // odd rows of v[j] trade with even rows of v[j + 16]
+        const auto r = __builtin_amdgcn_permlane16_swap(as_u(v[j]), as_u(v[j + 16]), false, false);
+        v[j] = as_f(r[0]) + as_f(r[1]);
+    }
+    pair_step<8, 0x140>(v, lane);  // row_mirror
+    pair_step<4, 0x141>(v, lane);  // row_half_mirror
+    pair_step<2, 0x4E>(v, lane);   // quad_perm [2, 3, 0, 1]
+    pair_step<1, 0xB1>(v, lane);   // quad_perm [1, 0, 3, 2]
+    const auto r = __builtin_amdgcn_permlane32_swap(as_u(v[0]), as_u(v[0]), false, false);
+    v[0] = as_f(r[0]) + as_f(r[1]);
+}
+
+// grid: one work-group per tile of kG rows; block: 64 x min(slices, kMaxWaves) threads; LDS:
+// rounds x waves x kN floats
 template <typename T>
-__global__ __launch_bounds__(kThreads) void latent_kernel(LatentParams p) {
+__global__ __launch_bounds__(64 * kMaxWaves) void latent_kernel(LatentParams p) {
     using E = Elem<T>;
+    extern __shared__ float part[];  // [round][wave][kN]
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row0 = (blockIdx.x * (kThreads / 64) + wave) * kRows;  // over n_idx * rank rows
-    const int n_rows = p.n_idx * p.rank;
-    if (row0 >= n_rows) return;
-    const int i = row0 / p.rank;  // rank is a multiple of kRows: a wave's rows share the indexer
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_waves = blockDim.x >> 6;
     const int hc = p.d_model / E::N;  // 16-byte chunks per row
-    const uint4* a = reinterpret_cast<const uint4*>(static_cast<const T*>(p.w_down) + (size_t)row0 * p.d_model);
-    const T* hid = static_cast<const T*>(p.hidden) + (size_t)i * p.hidden_idx_stride;
-    T* out = static_cast<T*>(p.latent);
-    for (int r0 = 0; r0 < p.n_req; r0 += kReq) {
-        float acc[kRows][kReq] = {};
-        for (int c0 = 0; c0 < hc; c0 += 64 * 4) {
-            // unconditional loads from clamped indices (masked after loading) keep all in flight
-            uint4 wc[kRows][4];
-            uint4 hv[kReq][4];
+    const int n_slices = (hc + 63) / 64;
+    const int rounds = (p.n_req + kQ - 1) / kQ;
+    const int row0 = blockIdx.x * kG;  // over n_idx * rank rows
+    const int i = row0 / p.rank;
+    const size_t row_bytes = (size_t)p.d_model * sizeof(T);
+    const __amdgpu_buffer_rsrc_t a = tile_rsrc(static_cast<const char*>(p.w_down) + (size_t)row0 * row_bytes,
+                                               (unsigned)(kG * row_bytes));
+    const char* hid = static_cast<const char*>(p.hidden) + (size_t)i * p.hidden_idx_stride * sizeof(T);
+    const size_t req_bytes = (size_t)p.hidden_req_stride * sizeof(T);
+    for (int s = wave; s < n_slices; s += n_waves) {
+        const int c = s * 64 + lane;
+        const bool live = c < hc;  // a bf16 row of 256 (2k+1) elements ends in half a slice
+        const unsigned off = (unsigned)(live ? c : hc - 1) * 16u;
+        uint4 av[kG];
 #pragma unroll
-            for (int jj = 0; jj < kRows; ++jj)
+        for (int g = 0; g < kG; ++g) av[g] = load_nt(a, off, (unsigned)(g * row_bytes));
+        if (!live)  // dead lanes add exact zeros
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    wc[jj][k] = load_nt(a + (size_t)jj * hc + min(c0 + k * 64 + lane, hc - 1));
+            for (int g = 0; g < kG; ++g) av[g] = make_uint4(0, 0, 0, 0);
+        // the next round's hidden chunks are requested before this round's sums (L2 latency hidden)
+        uint4 hv[kQ], hn[kQ];
 #pragma unroll
-            for (int rr = 0; rr < kReq; ++rr) {
-                const uint4* h = reinterpret_cast<const uint4*>(hid + (size_t)min(r0 + rr, p.n_req - 1) * p.hidden_req_stride);
+        for (int q = 0; q < kQ; ++q) hv[q] = load(hid + min(q, p.n_req - 1) * req_bytes, off);
+        for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) hv[rr][k] = h[min(c0 + k * 64 + lane, hc - 1)];
+            for (int q = 0; q < kQ; ++q) hn[q] = load(hid + min((rd + 1) * kQ + q, p.n_req - 1) * req_bytes, off);
+            if (!live)
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) hv[q] = make_uint4(0, 0, 0, 0);
+            float v[kN];
+#pragma unroll
+            for (int g = 0; g < kG; ++g)
+#pragma unroll
+                for (int q = 0; q < kQ; ++q) v[g * kQ + q] = E::dot(av[g], hv[q]);
+            reduce_scatter(v, lane);
+            if (lane < kN) {
+                float* d = part + ((size_t)rd * n_waves + wave) * kN + lane;
+                *d = s == wave ? v[0] : *d + v[0];  // later slices of this wave add to their own entry
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool live = c0 + k * 64 + lane < hc;
-#pragma unroll
-                for (int jj = 0; jj < kRows; ++jj)
-#pragma unroll
-                    for (int rr = 0; rr < kReq; ++rr) {
-                        const float t = E::dot_acc(wc[jj][k], hv[rr][k], acc[jj][rr]);
-                        acc[jj][rr] = live ? t : acc[jj][rr];
-                    }
-            }
+            for (int q = 0; q < kQ; ++q) hv[q] = hn[q];
         }
-#pragma unroll
-        for (int jj = 0; jj < kRows; ++jj)
-#pragma unroll
-            for (int rr = 0; rr < kReq; ++rr) {
-                float v = acc[jj][rr];
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-                if (lane == jj * kReq + rr && r0 + rr < p.n_req) {
-                    const int k = row0 + jj - i * p.rank;
-                    out[((size_t)(r0 + rr) * p.n_idx + i) * p.rank + k] = E::store(v);
-                }
-            }
+    }
+    __syncthreads();
+    T* out = static_cast<T*>(p.latent);
+    const int k0 = row0 - i * p.rank;
+    for (int o = threadIdx.x; o < rounds * kN; o += blockDim.x) {
+        const int rd = o / kN, e = o % kN;
+        const int w_used = min(n_waves, n_slices);
+        float sum = 0.0f;
+        for (int w = 0; w < w_used; ++w) sum += part[((size_t)rd * n_waves + w) * kN + e];
+        const int g = e / kQ, r = rd * kQ + e % kQ;
+        if (r < p.n_req) out[((size_t)r * p.n_idx + i) * p.rank + k0 + g] = E::store(sum);
     }
 }
 
@@ -160,12 +223,14 @@ lsa_status launch_latent(const lsa_latent_args* a, hipStream_t stream) {
     p.d_model = a->d_model;
     p.rank = a->rank;
     p.n_idx = a->n_idx;
-    const int rows_per_group = kRows * (kThreads / 64);
-    const dim3 grid((a->n_idx * a->rank + rows_per_group - 1) / rows_per_group), block(kThreads);
+    const int slices = (a->d_model / Elem<T>::N + 63) / 64;
+    const int waves = std::min(slices, kMaxWaves);
+    const size_t lds = (size_t)((a->n_req + kQ - 1) / kQ) * waves * kN * sizeof(float);  // <= 32 KiB
+    const dim3 grid(a->n_idx * a->rank / kG), block(64 * waves);
     if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps
-        hipExtLaunchKernelGGL(latent_kernel<T>, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, p);
+        hipExtLaunchKernelGGL(latent_kernel<T>, grid, block, lds, stream, a->ev_begin, a->ev_end, 0, p);
     else
-        hipLaunchKernelGGL(latent_kernel<T>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL(latent_kernel<T>, grid, block, lds, stream, p);
     LSA_HIP(hipGetLastError());
     return LSA_OK;
 }
