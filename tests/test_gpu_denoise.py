@@ -77,7 +77,7 @@ def test_denoise_matches_oracle():
 def test_denoise_ties_taken_by_block_id():
     """Integer logits: long runs of equal logits straddle the top-p boundary.  The run of equal
     logits at a row's cut (computed here in float64) is ranked in one wave when it has at most 64
-    blocks, by the whole group up to 1,024, and by the bisection kernel beyond; the two workloads'
+    blocks, by the whole group up to 256, and by the bisection kernel beyond; the two workloads'
     rows cover all three."""
     from workloads import build_denoise_workload
 
@@ -95,7 +95,7 @@ def test_denoise_ties_taken_by_block_id():
     wide = build_denoise_workload([16384, 5000, 777], seed=4, integer_logits=True, noise=1.5)
     narrow = build_denoise_workload([16384, 3000], seed=7, integer_logits=True, noise=0.5, n_layers=5)
     runs = np.array(cut_runs(wide) + cut_runs(narrow))
-    assert (runs <= 64).any() and ((runs > 64) & (runs <= 1024)).any() and (runs > 1024).any(), np.unique(runs)
+    assert (runs <= 64).any() and ((runs > 64) & (runs <= 256)).any() and (runs > 256).any(), np.unique(runs)
     _check(wide, 0.6, 3)
     _check(narrow, 0.6, 3)
 
