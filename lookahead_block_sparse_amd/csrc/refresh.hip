@@ -26,7 +26,13 @@
 // keys.  Measured alternatives at 4 x 1M context: one wave per 16 KiB unit at five groups per
 // compute unit (q arrives late and holds the slots: 29-33 us), two launches (encode, then score:
 // q is simply there, but the memory idles during the encode launch and the gap, 4.5 + 2.1 us:
-// 30 us), and fewer resident groups to keep the queues short (31-35 us).
+// 30 us), fewer resident groups to keep the queues short (31-35 us), score waves that wait up to
+// 2 us before their key loads so that W_q is served first (no gain), and the half words beyond
+// the first round staged in LDS by direct-to-LDS loads, so that every key byte is requested at
+// the start (the stream then ran at ~4.3 TB/s and the staged words were scored after a group
+// barrier: 33-36 us).  The cross-lane moves of the scoring are row swaps and DPP (no LDS
+// crossbar); making the dot products cheaper as well saves under 0.5 us, so the launch is
+// bound by the key stream and the hand-offs, not by arithmetic.
 // A group only waits for groups with a lower index, which were dispatched before it, and every
 // wait is bounded: a wait that gives up marks the request, whose count is then written as -1.
 // Values that cross groups travel in 64-bit words whose upper half is the call's number and lower
@@ -246,133 +252,227 @@ struct ScoreShape {
     static_assert(LOG_P <= LOG_LPR, "reduce-scatter shape");
 };
 
+// Cross-lane moves for the score role, all full-rate (no LDS crossbar): the 16-lane row swap and
+// the half-wave swap exchange whole rows / halves; row mirror (lane ^ 15), half-row mirror
+// (lane ^ 7) and the quad permutations pair lanes whose index differs in bit 3, 2, 1 or 0 and
+// agrees in the bits above it.
+__device__ __forceinline__ float as_f(unsigned x) { return __uint_as_float(x); }
+__device__ __forceinline__ unsigned as_u(float x) { return __float_as_uint(x); }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int B>
+__device__ __forceinline__ float dpp_partner(float x) {  // the value of a lane differing in bit B
+    static_assert(B >= 0 && B <= 3, "row-local pairing");
+    if constexpr (B == 3) return dpp<0x140>(x);  // row_mirror
+    else if constexpr (B == 2) return dpp<0x141>(x);  // row_half_mirror
+    else if constexpr (B == 1) return dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    else return dpp<0xB1>(x);                          // quad_perm [1, 0, 3, 2]
+}
+// One reduce-scatter step over lane bit B on the n entries of v: a lane with bit B set keeps the
+// upper half, the others the lower half, each adding its partner's copy of the half it keeps.
+template <int B, int N>
+__device__ __forceinline__ void rs_step(float* v, int lane) {
+    if constexpr (B >= 4) {
+#pragma unroll
+        for (int kk = 0; kk < N / 2; ++kk) {
+            // the swap leaves each lane its own copy and its partner's copy of the half it keeps
+            const auto x = B == 4 ? __builtin_amdgcn_permlane16_swap(as_u(v[kk]), as_u(v[kk + N / 2]), false, false)
+                                  : __builtin_amdgcn_permlane32_swap(as_u(v[kk]), as_u(v[kk + N / 2]), false, false);
+            v[kk] = as_f(x[0]) + as_f(x[1]);
+        }
+    } else {
+        const bool up = (lane >> B) & 1;
+#pragma unroll
+        for (int kk = 0; kk < N / 2; ++kk) {
+            const float keep = up ? v[kk + N / 2] : v[kk];
+            const float give = up ? v[kk] : v[kk + N / 2];
+            v[kk] = keep + dpp_partner<B>(give);
+        }
+    }
+}
+template <int B, int N, int STEPS>
+__device__ __forceinline__ void rs_steps(float* v, int lane) {
+    if constexpr (STEPS > 0) {
+        rs_step<B, N>(v, lane);
+        rs_steps<B - 1, N / 2, STEPS - 1>(v, lane);
+    }
+}
+// the value of lane (l mod LPR) + s LPR for s < 64 / LPR (rows of a 1 KiB run), for every lane l
+template <int RPL>
+__device__ __forceinline__ void gather_rows(float x, float* out) {
+    if constexpr (RPL == 1) {
+        out[0] = x;
+    } else if constexpr (RPL == 2) {
+        const auto h = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+        out[0] = as_f(h[0]);  // lower half's value
+        out[1] = as_f(h[1]);  // upper half's value
+    } else {
+        static_assert(RPL == 4, "rows per run");
+        const auto h = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+        const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);  // rows 0, 1
+        const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);  // rows 2, 3
+        out[0] = as_f(a[0]);
+        out[1] = as_f(a[1]);
+        out[2] = as_f(b[0]);
+        out[3] = as_f(b[1]);
+    }
+}
+
+// Where half word sw lives: its request, word and row base.
+struct HalfWord {
+    int sw, half, r, lw, n_blk, n_valid;
+    const char* word_rows;  // indexer i's rows of the word start at word_rows + i * n_blk * ROW
+};
+template <int ROW>
+__device__ __forceinline__ HalfWord half_word(const RefreshParams& p, int sw) {
+    HalfWord h;
+    h.sw = sw;
+    const int word = sw >> 1;
+    h.half = sw & 1;
+    int r = 0;
+    while (r + 1 < p.n_req && p.word_off[r + 1] <= word) ++r;
+    h.r = r;
+    h.lw = word - p.word_off[r];
+    const long long b_first = p.blk_off[r];
+    h.n_blk = (int)(p.blk_off[r + 1] - b_first);
+    h.n_valid = min(64, h.n_blk - h.lw * 64);  // blocks of this word that exist (>= 1)
+    h.word_rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + h.lw * 64) * ROW;
+    return h;
+}
+
+// The key runs of indexers i0 .. i0 + nu - 1 of a half word into registers: run j of unit u at a
+// fixed distance from the unit's first row; in the request's last word a lane whose row lies past
+// the request's last block loads nothing (its logit is masked), so every access stays inside the
+// request's keys.
+template <typename T, int DIDX>
+__device__ __forceinline__ void load_runs(const HalfWord& h, int i0, int nu, int lane, uint4 (&v)[ScoreShape<T, DIDX>::U][ScoreShape<T, DIDX>::P]) {
+    using S = ScoreShape<T, DIDX>;
+    const int sub = lane / S::LPR;
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        if (u < nu) {
+            const char* rows = h.word_rows + ((size_t)(i0 + u) * h.n_blk + 32 * h.half) * S::ROW + lane * 16;
+            if (h.n_valid == 64) {
+#pragma unroll
+                for (int j = 0; j < S::P; ++j) v[u][j] = load_nt(reinterpret_cast<const uint4*>(rows + j * 1024));
+            } else {
+#pragma unroll
+                for (int j = 0; j < S::P; ++j) {
+                    v[u][j] = make_uint4(0u, 0u, 0u, 0u);
+                    if (32 * h.half + S::RPL * j + sub < h.n_valid)
+                        v[u][j] = load_nt(reinterpret_cast<const uint4*>(rows + j * 1024));
+                }
+            }
+        }
+    }
+}
+
+// Logits of a half word's rows for indexers i0 .. i0 + nu - 1 (keys in v), thresholded and ORed
+// into u_bits.  q of every indexer of the batch is polled together: lane l fetches QF of the E
+// values of its column (the RPL lanes of a column split them) and fetches again until every tag is
+// this call's.
+template <typename T, int DIDX>
+__device__ __forceinline__ void score_runs(const RefreshParams& p, const HalfWord& h, int i0, int nu, int lane,
+                                           const uint4 (&v)[ScoreShape<T, DIDX>::U][ScoreShape<T, DIDX>::P],
+                                           unsigned* u_bits, bool* q_ok) {
+    using S = ScoreShape<T, DIDX>;
+    const int col = lane % S::LPR;
+    const int sub = lane / S::LPR;
+    const int k = (lane >> (S::LOG_LPR - S::LOG_P)) & (S::P - 1);
+    const int rowi = 32 * h.half + S::RPL * k + sub;  // row of the word whose logit this lane ends with
+    float qf[S::U][S::QF];
+    for (unsigned spins = 0;; ++spins) {
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) {
+            if (u < nu) {
+                const unsigned long long* qrow = p.qw + ((size_t)h.r * p.n_idx + i0 + u) * DIDX + col * S::E + sub * S::QF;
+#pragma unroll
+                for (int e = 0; e < S::QF; ++e) {
+                    const unsigned long long wq = get(qrow + e);
+                    all = all && tagged(wq, p.tag);
+                    qf[u][e] = __uint_as_float((unsigned)wq);
+                }
+            }
+        }
+        if (__all(all)) break;
+        if (spins >= kSpinLimit) {
+            *q_ok = false;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        if (u < nu) {
+            const int i = i0 + u;
+            float qv[S::E];  // the column's E values, gathered from the lanes that fetched them
+#pragma unroll
+            for (int e = 0; e < S::QF; ++e) {
+                float g[S::RPL];
+                gather_rows<S::RPL>(qf[u][e], g);
+#pragma unroll
+                for (int s2 = 0; s2 < S::RPL; ++s2) qv[s2 * S::QF + e] = g[s2];
+            }
+            float part[S::P];
+#pragma unroll
+            for (int j = 0; j < S::P; ++j) part[j] = dot_chunk_f32<T>(v[u][j], qv);
+            // reduce-scatter: step t keeps the upper half of the remaining partials on lanes
+            // whose bit (LOG_LPR - 1 - t) is set and adds the partner lane's copy of that half
+            rs_steps<S::LOG_LPR - 1, S::P, S::LOG_P>(part, lane);
+            float z = part[0];
+            if constexpr (S::LOG_LPR - S::LOG_P == 2) z += dpp_partner<1>(z);
+            if constexpr (S::LOG_LPR - S::LOG_P >= 1) z += dpp_partner<0>(z);
+            static_assert(S::LOG_LPR - S::LOG_P <= 2, "row lanes left after the reduce-scatter");
+            const bool keep = *q_ok && (rowi < h.n_valid) && (z + p.bias[h.r * p.n_idx + i] > p.select_logit);
+            const unsigned long long m = __ballot(keep);
+            // row q of the half word sits on lane (q % RPL) * LPR + ((q / RPL) << (LOG_LPR - LOG_P))
+            unsigned bits = 0u;
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                const int ln = (q % S::RPL) * S::LPR + ((q / S::RPL) << (S::LOG_LPR - S::LOG_P));
+                bits |= (unsigned)((m >> ln) & 1ull) << q;
+            }
+            *u_bits |= bits;
+            if (p.masks && lane == 0) {
+                const int n_words_r = p.word_off[h.r + 1] - p.word_off[h.r];
+                const size_t mw = (size_t)(p.n_idx + 1) * p.word_off[h.r] + (size_t)i * n_words_r + h.lw;
+                reinterpret_cast<unsigned*>(p.masks)[2 * mw + h.half] = bits;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void publish_half(const RefreshParams& p, const HalfWord& h, unsigned u_bits, bool q_ok,
+                                             int lane) {
+    if (lane == 0) {
+        if (!q_ok) {
+            put(&p.bad[h.r], p.tag, 1u);
+            __builtin_amdgcn_s_waitcnt(0);  // the mark is stored before the half word is published
+        }
+        put(&p.hw[h.sw], p.tag, u_bits);
+    }
+}
+
+// Score wave: half word sw (none when sw >= n_halves), all indexers in batches of U.
 template <typename T, int DIDX>
 __device__ void score_role(const RefreshParams& p, int sw) {
     using S = ScoreShape<T, DIDX>;
     const int lane = threadIdx.x & 63;
     if (sw >= p.n_halves) return;
-    const int word = sw >> 1;
-    const int half = sw & 1;
-    int r = 0;
-    while (r + 1 < p.n_req && p.word_off[r + 1] <= word) ++r;
-    const int lw = word - p.word_off[r];
-    const long long b_first = p.blk_off[r];
-    const int n_blk = (int)(p.blk_off[r + 1] - b_first);
-    const int n_valid = min(64, n_blk - lw * 64);  // blocks of this word that exist (>= 1)
-
-    const int col = lane % S::LPR;
-    const int sub = lane / S::LPR;
-    // indexer i's rows of this word start at word_rows + i * n_blk * ROW
-    const char* word_rows = static_cast<const char*>(p.keys) + ((size_t)p.n_idx * b_first + lw * 64) * S::ROW;
-    const unsigned lane_off = (unsigned)(sub * S::ROW + col * 16);
-    const int k = (lane >> (S::LOG_LPR - S::LOG_P)) & (S::P - 1);
-    const int rowi = 32 * half + S::RPL * k + sub;  // row of the word whose logit this lane ends with
+    const HalfWord h = half_word<S::ROW>(p, sw);
+    uint4 v[S::U][S::P];
     unsigned u_bits = 0u;
     bool q_ok = true;
     for (int i0 = 0; i0 < p.n_idx; i0 += S::U) {
         const int nu = min(S::U, p.n_idx - i0);
-        uint4 v[S::U][S::P];
-#pragma unroll
-        for (int u = 0; u < S::U; ++u) {
-            if (u < nu) {
-                // run j of the unit at a fixed distance from its first row
-                const char* rows = word_rows + ((size_t)(i0 + u) * n_blk + 32 * half) * S::ROW + lane_off;
-                if (n_valid == 64) {
-#pragma unroll
-                    for (int j = 0; j < S::P; ++j) v[u][j] = load_nt(reinterpret_cast<const uint4*>(rows + j * 1024));
-                } else {
-                    // the request's last word: a lane whose row lies past the request's last block
-                    // loads nothing (its logit is masked below), so every access stays inside the
-                    // request's keys
-#pragma unroll
-                    for (int j = 0; j < S::P; ++j) {
-                        v[u][j] = make_uint4(0u, 0u, 0u, 0u);
-                        if (32 * half + S::RPL * j + sub < n_valid)
-                            v[u][j] = load_nt(reinterpret_cast<const uint4*>(rows + j * 1024));
-                    }
-                }
-            }
-        }
+        load_runs<T, DIDX>(h, i0, nu, lane, v);
         asm volatile("" ::: "memory");  // every key load of the batch is issued before q is polled
-        // q of every indexer of the batch, polled together right behind the key loads: lane l
-        // fetches QF of the E values of its column (the RPL lanes of a column split them) and
-        // fetches again until every tag is this call's
-        float qf[S::U][S::QF];
-        for (unsigned spins = 0;; ++spins) {
-            bool all = true;
-#pragma unroll
-            for (int u = 0; u < S::U; ++u) {
-                if (u < nu) {
-                    const unsigned long long* qrow = p.qw + ((size_t)r * p.n_idx + i0 + u) * DIDX + col * S::E + sub * S::QF;
-#pragma unroll
-                    for (int e = 0; e < S::QF; ++e) {
-                        const unsigned long long wq = get(qrow + e);
-                        all = all && tagged(wq, p.tag);
-                        qf[u][e] = __uint_as_float((unsigned)wq);
-                    }
-                }
-            }
-            if (__all(all)) break;
-            if (spins >= kSpinLimit) {
-                q_ok = false;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
-#pragma unroll
-        for (int u = 0; u < S::U; ++u) {
-            if (u < nu) {
-                const int i = i0 + u;
-                float qv[S::E];  // the column's E values, gathered from the lanes that fetched them
-#pragma unroll
-                for (int s2 = 0; s2 < S::RPL; ++s2)
-#pragma unroll
-                    for (int e = 0; e < S::QF; ++e) qv[s2 * S::QF + e] = __shfl(qf[u][e], col + s2 * S::LPR, 64);
-                float part[S::P];
-#pragma unroll
-                for (int j = 0; j < S::P; ++j) part[j] = dot_chunk_f32<T>(v[u][j], qv);
-                // reduce-scatter: step t keeps the upper half of the remaining partials on lanes
-                // whose bit (LOG_LPR - 1 - t) is set and adds the partner lane's copy of that half
-#pragma unroll
-                for (int t = 0; t < S::LOG_P; ++t) {
-                    const int n = S::P >> t;
-                    const int b = S::LOG_LPR - 1 - t;
-                    const bool up = (lane >> b) & 1;
-#pragma unroll
-                    for (int kk = 0; kk < n / 2; ++kk) {
-                        const float keep = up ? part[kk + n / 2] : part[kk];
-                        const float give = up ? part[kk] : part[kk + n / 2];
-                        part[kk] = keep + __shfl_xor(give, 1 << b, 64);
-                    }
-                }
-                float z = part[0];
-#pragma unroll
-                for (int b = S::LOG_LPR - S::LOG_P - 1; b >= 0; --b) z += __shfl_xor(z, 1 << b, 64);
-                const bool keep = q_ok && (rowi < n_valid) && (z + p.bias[r * p.n_idx + i] > p.select_logit);
-                const unsigned long long m = __ballot(keep);
-                // row q of the half word sits on lane (q % RPL) * LPR + ((q / RPL) << (LOG_LPR - LOG_P))
-                unsigned bits = 0u;
-#pragma unroll
-                for (int q = 0; q < 32; ++q) {
-                    const int ln = (q % S::RPL) * S::LPR + ((q / S::RPL) << (S::LOG_LPR - S::LOG_P));
-                    bits |= (unsigned)((m >> ln) & 1ull) << q;
-                }
-                u_bits |= bits;
-                if (p.masks && lane == 0) {
-                    const int n_words_r = p.word_off[r + 1] - p.word_off[r];
-                    const size_t mw = (size_t)(p.n_idx + 1) * p.word_off[r] + (size_t)i * n_words_r + lw;
-                    reinterpret_cast<unsigned*>(p.masks)[2 * mw + half] = bits;
-                }
-            }
-        }
+        score_runs<T, DIDX>(p, h, i0, nu, lane, v, &u_bits, &q_ok);
     }
-    if (lane == 0) {
-        if (!q_ok) {
-            put(&p.bad[r], p.tag, 1u);
-            __builtin_amdgcn_s_waitcnt(0);  // the mark is stored before the half word is published
-        }
-        put(&p.hw[sw], p.tag, u_bits);
-    }
+    publish_half(p, h, u_bits, q_ok, lane);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -59,6 +59,33 @@ def test_refresh_selection_bit_exact(name):
                 assert set(wl.planted[r].tolist()) <= set(got.tolist())
 
 
+# every key-row width the score role has a shape for: 256-byte rows (bf16, d_idx 128: four rows
+# per 1 KiB run), 512-byte rows (the SMALL configs) and 1 KiB rows (fp32, d_idx 256: one per run)
+WIDTHS = [("ctx128k_s", 128), ("ragged_s", 128), ("tiny", 256)]
+
+
+@pytest.mark.parametrize("name,d_idx", WIDTHS, ids=[f"{n}-didx{d}" for n, d in WIDTHS])
+def test_refresh_key_row_widths(name, d_idx):
+    from workloads import get_config
+
+    cfg = get_config(name).scaled(d_idx=d_idx, steps=130)
+    log(f"refresh {name} {cfg.dtype} d_idx {d_idx}")
+    wl = conditioned_workload(cfg, seed=2)
+    sess = make_session(wl, with_masks=True)
+    w = oracle.decode_values(wl.w_q, cfg.dtype)
+    reqs = list(range(wl.n_req))
+    for k in range(min(len(s) for s in wl.refresh_steps)):
+        got = sess.refresh(reqs, np.stack([wl.hidden[r][k] for r in reqs]), wl.bias)
+        for r in reqs:
+            keys = oracle.decode_values(wl.keys[r], cfg.dtype)
+            ref = oracle.refresh(oracle.decode_values(wl.hidden[r][k], cfg.dtype), w, keys, wl.bias[r])
+            assert np.array_equal(got[r], ref.ids), (name, d_idx, r, k, len(got[r]), len(ref.ids))
+            planes = sess.masks_of(r)
+            B = int(wl.n_blocks[r])
+            for i in range(cfg.n_idx):
+                assert np.array_equal(_unpack(planes[i], B), ref.s[i]), (name, d_idx, r, k, i)
+
+
 LEVELS = [("ctx128k_s", 0.3), ("ragged_s", 0.7), ("tiny", 0.62)]
 
 
