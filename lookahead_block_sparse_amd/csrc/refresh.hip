@@ -162,22 +162,20 @@ constexpr int kEncReq = 4;     // requests per encode wave
 constexpr int kEncRows = 2;    // W_q rows per encode wave
 constexpr int kEncPieces = 8;  // 16-byte pieces per lane per row and chunk
 
-// pieces c0 + lane + 64 k (k < kEncPieces) of a row of hc pieces; pieces past the row are zero
+// pieces c0 + lane + 64 k (k < kEncPieces) of a row of hc pieces, every load at a fixed distance
+// from the lane's first; in the last chunk of a short row the indices are clamped to the row's
+// last piece (the caller drops those pieces when it uses them, so no load waits for another)
 template <bool NT>
 __device__ __forceinline__ void enc_chunk(uint4* v, const uint4* row, int c0, int hc, int lane) {
     if (c0 + 64 * kEncPieces <= hc) {
-        // a whole chunk: every load at a fixed distance from the lane's first
 #pragma unroll
         for (int k = 0; k < kEncPieces; ++k)
             v[k] = NT ? load_nt(row + c0 + lane + k * 64) : row[c0 + lane + k * 64];
     } else {
-        // the tail of a short row: loads issued one by one from clamped indices
 #pragma unroll
         for (int k = 0; k < kEncPieces; ++k) {
-            const int idx = c0 + k * 64 + lane;
-            v[k] = NT ? load_nt(row + min(idx, hc - 1)) : row[min(idx, hc - 1)];
-            if (idx >= hc) v[k] = make_uint4(0u, 0u, 0u, 0u);
-            __builtin_amdgcn_sched_barrier(0);
+            const int idx = min(c0 + k * 64 + lane, hc - 1);
+            v[k] = NT ? load_nt(row + idx) : row[idx];
         }
     }
 }
@@ -209,11 +207,18 @@ __device__ void encode_role(const RefreshParams& p, int e) {
                              c0, hc, lane);
         __builtin_amdgcn_sched_barrier(0);  // every load of the chunk is issued before the first use
 #pragma unroll
-        for (int k = 0; k < kEncPieces; ++k)
+        for (int k = 0; k < kEncPieces; ++k) {
+            if (c0 + k * 64 + lane >= hc) {  // a clamped piece past the row's end adds nothing
+#pragma unroll
+                for (int jj = 0; jj < kEncRows; ++jj) wv[jj][k] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int rr = 0; rr < kEncReq; ++rr) hv[rr][k] = make_uint4(0u, 0u, 0u, 0u);
+            }
 #pragma unroll
             for (int jj = 0; jj < kEncRows; ++jj)
 #pragma unroll
                 for (int rr = 0; rr < kEncReq; ++rr) acc[jj][rr] = dot_chunks<T>(wv[jj][k], hv[rr][k], acc[jj][rr]);
+        }
     }
     float mine = 0.f;  // lane jj*kEncReq + rr publishes q for row j0 + jj, request r0 + rr
 #pragma unroll

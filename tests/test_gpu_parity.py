@@ -61,15 +61,17 @@ def test_refresh_selection_bit_exact(name):
 
 # every key-row width the score role has a shape for: 256-byte rows (bf16, d_idx 128: four rows
 # per 1 KiB run), 512-byte rows (the SMALL configs) and 1 KiB rows (fp32, d_idx 256: one per run)
-WIDTHS = [("ctx128k_s", 128), ("ragged_s", 128), ("tiny", 256)]
+# and hidden sizes whose rows end inside an encode chunk: 768 bf16 (96 pieces of 16 bytes: the
+# last 64-lane load half in range) and 1280 fp32 (320 pieces)
+WIDTHS = [("ctx128k_s", 128, 0), ("ragged_s", 128, 0), ("tiny", 256, 0), ("ctx128k_s", 256, 768), ("tiny", 128, 1280)]
 
 
-@pytest.mark.parametrize("name,d_idx", WIDTHS, ids=[f"{n}-didx{d}" for n, d in WIDTHS])
-def test_refresh_key_row_widths(name, d_idx):
+@pytest.mark.parametrize("name,d_idx,d_model", WIDTHS, ids=[f"{n}-didx{d}-d{m}" for n, d, m in WIDTHS])
+def test_refresh_key_row_widths(name, d_idx, d_model):
     from workloads import get_config
 
-    cfg = get_config(name).scaled(d_idx=d_idx, steps=130)
-    log(f"refresh {name} {cfg.dtype} d_idx {d_idx}")
+    cfg = get_config(name).scaled(d_idx=d_idx, steps=130, **({"d_model": d_model} if d_model else {}))
+    log(f"refresh {name} {cfg.dtype} d_idx {d_idx} d_model {cfg.d_model}")
     wl = conditioned_workload(cfg, seed=2)
     sess = make_session(wl, with_masks=True)
     w = oracle.decode_values(wl.w_q, cfg.dtype)
