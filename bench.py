@@ -633,6 +633,11 @@ def run_loop(args) -> dict:
     first_blocks = []
     copied_pin = torch.zeros((len(timed_refresh) + len(leg_refreshes) + 2, wl.n_req), dtype=torch.int32,
                              pin_memory=True)
+    # the counts go to the host on a stream of their own (same priority), off the decode stream's
+    # path; the next plan, which rewrites them, waits for that copy
+    stat_stream = torch.cuda.Stream()
+    stat_ev = [torch.cuda.Event() for _ in range(copied_pin.shape[0])]
+    stat_pending = [False]
     torch.cuda.synchronize()
 
     e = 2 if cfg.dtype == "bf16" else 4
@@ -669,11 +674,18 @@ def run_loop(args) -> dict:
             torch.stack([bias_dev[r] for r in reqs])
         if dplan:
             # refresh, plan and copy on the device: nothing comes back to the host
-            sess.refresh_device(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1], ev_plan=ev_plan)
+            if stat_pending[0]:
+                sess.stream.wait_stream(stat_stream)
+                stat_pending[0] = False
+            sess.refresh_device(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1], ev_plan=ev_plan,
+                                ev_latent=lat_ev.get(t, (None, None)))
             if copy_slot is not None:
                 slot_reqs[copy_slot] = list(reqs)
-                with torch.cuda.stream(sess.stream):
+                stat_ev[copy_slot].record(sess.stream)
+                stat_stream.wait_event(stat_ev[copy_slot])
+                with torch.cuda.stream(stat_stream):
                     copied_pin[copy_slot].copy_(sess.copied_dev, non_blocking=True)
+                stat_pending[0] = True
             return None
         sel = sess.refresh(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1],
                            ev_latent=lat_ev.get(t, (None, None)))

@@ -344,7 +344,7 @@ class LSASession:
         return self._pargs[key]
 
     def refresh_device(self, reqs: Sequence[int], hidden: torch.Tensor, bias: torch.Tensor, ev_begin=None,
-                       ev_end=None, ev_plan=(None, None)) -> None:
+                       ev_end=None, ev_plan=(None, None), ev_latent=(None, None)) -> None:
         """Index refresh of `reqs` followed by the gather planned and run on the device
         (lsa_gather_plan_device): nothing is copied back and nothing waits for the host.  The
         decode then reads the tables' counts on the device (DecodeLoop(..., device_counts=True))."""
@@ -361,7 +361,7 @@ class LSASession:
             r0, r1 = reqs[i], reqs[j] + 1
             one_run = i == 0 and j == len(reqs) - 1
             self._refresh_run(r0, r1, hid[i:j + 1], bias_d[i:j + 1], ev_begin if one_run else None,
-                              ev_end if one_run else None)
+                              ev_end if one_run else None, ev_latent=ev_latent if one_run else (None, None))
             a = self._plan_args(r0, r1)[0]
             a.ev_begin = ev_plan[0].cuda_event if (ev_plan[0] is not None and one_run) else None
             a.ev_end = ev_plan[1].cuda_event if (ev_plan[1] is not None and one_run) else None
