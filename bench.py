@@ -39,6 +39,7 @@ bounded sample.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -759,11 +760,17 @@ def run_loop(args) -> dict:
     if dplan:
         sess.check_plan_status()
     note(f"timing {K // STEP_DECODE} steps ({K} decode steps)")
+    # no garbage-collector pass inside the timed region: a full pass over this process's objects
+    # stops the host for tens of milliseconds, which a loop whose steps take microseconds of GPU
+    # time cannot hide (a serving loop would freeze its long-lived objects the same way)
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(K):
         step(W + i, i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
     note(f"timed region {elapsed * 1e3:.2f} ms")
     if dplan:
         sess.check_plan_status()  # any refresh of the run that gave up or did not fit raises here
@@ -896,6 +903,8 @@ def run_loop(args) -> dict:
         sess.use_cold("host")
         leg_evs, leg_slots = [], []
         torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
         tl0 = time.perf_counter()
         for t in range(n_leg):
             ts = W + t  # the refresh states and decode inputs of timed step ts, replayed
@@ -915,6 +924,7 @@ def run_loop(args) -> dict:
                 lp.step(tt, ql[ts], kl[ts], vl[ts])
         torch.cuda.synchronize()
         leg_s = time.perf_counter() - tl0
+        gc.enable()
         if dplan:
             sess.check_plan_status()
         us = np.array([1e3 * a.elapsed_time(b) for a, b in leg_evs])

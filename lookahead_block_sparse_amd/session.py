@@ -29,7 +29,9 @@ from . import (
     DeviceGatherArgs,
     GatherArgs,
     LIB,
+    RefreshArgs,
     _check,
+    _dtype_code,
     lsa_block_bytes,
     lsa_index_refresh,
     lsa_index_refresh_workspace,
@@ -137,6 +139,7 @@ class LSASession:
             self.decode_ws = torch.empty(ws, dtype=torch.uint8, device=self.device)
         self._gargs: List[Optional[tuple]] = [None] * self.n_req
         self._pargs = {}  # device-plan argument structs per run of requests
+        self._rargs = {}  # refresh argument structs per (run of requests, table_out)
         self._stage_ev: List[Optional[torch.cuda.Event]] = [None] * self.n_req
         # residency planned on the device (lsa_gather_plan_device): the state lives in HBM and a
         # refresh never waits for the host
@@ -278,7 +281,6 @@ class LSASession:
 
     def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor, ev_begin=None,
                      ev_end=None, table_out: bool = False, ev_latent=(None, None)) -> None:
-        off = self.blk_off[r0:r1 + 1] - self.blk_off[r0]
         stride = self.d_model
         if self.rank:
             # the latents of these requests, then the Query Encoder reads them in place of h
@@ -288,18 +290,62 @@ class LSASession:
                              ev_end=ev_latent[1], stream=self.stream)
             hid = lat
             stride = self.n_idx * self.rank
-        key_elem0 = int(self.n_idx * self.d_idx * self.blk_off[r0])
-        masks = None
-        if self.masks is not None:
-            masks = self.masks[int(self.word_off[r0]) * (self.n_idx + 1):]
-        lsa_index_refresh(dtype=self.dtype, d_model=self.q_in, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
-                          hidden_req_stride=stride, hidden_idx_stride=self.rank,
-                          w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
-                          sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
-                          workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
-                          table_out=(self.table[2 * int(self.slot_base[r0]):] if table_out else None),
-                          table_slot_base=(self.slot_base[r0:r1] if table_out else None),
-                          stream=self.stream, select_level=self.select_level)
+        key = (r0, r1, bool(table_out))
+        cached = self._rargs.get(key)
+        if cached is None:
+            # the first call of a run of requests goes through the checked wrapper; the argument
+            # struct it builds is kept, and later calls only swap the hidden states, the biases and
+            # the events (the library validates every call)
+            off = self.blk_off[r0:r1 + 1] - self.blk_off[r0]
+            key_elem0 = int(self.n_idx * self.d_idx * self.blk_off[r0])
+            masks = None
+            if self.masks is not None:
+                masks = self.masks[int(self.word_off[r0]) * (self.n_idx + 1):]
+            lsa_index_refresh(dtype=self.dtype, d_model=self.q_in, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
+                              hidden_req_stride=stride, hidden_idx_stride=self.rank,
+                              w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
+                              sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
+                              workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
+                              table_out=(self.table[2 * int(self.slot_base[r0]):] if table_out else None),
+                              table_slot_base=(self.slot_base[r0:r1] if table_out else None),
+                              stream=self.stream, select_level=self.select_level)
+            self._rargs[key] = self._refresh_struct(r0, r1, stride, table_out, masks)
+            return
+        a, _keep, need_hid, need_bias = cached
+        if not (hid.is_cuda and bias_d.is_cuda and hid.is_contiguous() and bias_d.is_contiguous()
+                and hid.numel() * hid.element_size() >= need_hid and bias_d.numel() * 4 >= need_bias):
+            raise ValueError("refresh: hidden states and biases must be contiguous device tensors of the run's size")
+        a.hidden, a.bias = hid.data_ptr(), bias_d.data_ptr()
+        a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
+        a.ev_end = ev_end.cuda_event if ev_end is not None else None
+        _check(LIB.lsa_index_refresh(ctypes.byref(a), ctypes.c_void_p(self.stream.cuda_stream)))
+
+    def _refresh_struct(self, r0: int, r1: int, stride: int, table_out: bool, masks):
+        """The refresh argument struct of a run of requests (every field but the hidden states, the
+        biases and the events), with the arrays it points into."""
+        off = np.ascontiguousarray(self.blk_off[r0:r1 + 1] - self.blk_off[r0], dtype=np.int64)
+        a = RefreshArgs()
+        a.n_req, a.d_model, a.d_idx, a.n_idx = r1 - r0, self.q_in, self.d_idx, self.n_idx
+        a.dtype = _dtype_code(self.dtype)
+        a.select_level = float(self.select_level)
+        a.hidden_req_stride, a.hidden_idx_stride = int(stride), int(self.rank)
+        a.w_q = self.w_q.data_ptr()
+        a.keys = self.keys.data_ptr() + int(self.n_idx * self.d_idx * self.blk_off[r0]) * self.keys.element_size()
+        a.blk_off = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        a.sel_ids = self.sel_ids.data_ptr() + int(self.blk_off[r0]) * 4
+        a.sel_count = self.sel_count.data_ptr() + r0 * 4
+        a.masks = masks.data_ptr() if masks is not None else None
+        a.workspace = self.refresh_ws.data_ptr()
+        a.workspace_bytes = self.refresh_ws.numel() * self.refresh_ws.element_size()
+        tsb = None
+        if table_out:
+            tsb = np.ascontiguousarray(self.slot_base[r0:r1], dtype=np.int32)
+            a.table_out = self.table.data_ptr() + 4 * 2 * int(self.slot_base[r0])
+            a.table_slot_base = tsb.ctypes.data
+        e = 2 if self.dtype == "bf16" else 4
+        need_hid = ((r1 - r0 - 1) * stride + (self.n_idx - 1) * self.rank + self.q_in) * e
+        need_bias = (r1 - r0) * self.n_idx * 4
+        return a, (off, tsb), need_hid, need_bias
 
     def masks_of(self, r: int) -> np.ndarray:
         """Request r's bit planes [n_idx+1][words] (after a refresh with masks enabled)."""
