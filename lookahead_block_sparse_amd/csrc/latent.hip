@@ -16,6 +16,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "lsa_internal.hpp"
 
@@ -188,6 +189,80 @@ __global__ __launch_bounds__(64 * kMaxWaves) void latent_kernel(LatentParams p) 
     }
 }
 
+// Matrix-core variant for batches of requests (bf16): per work-group a tile of 16 rows of A
+// against 16 requests at a time, v_mfma_f32_16x16x32_bf16 with A's rows and the requests' hidden
+// states as the two operands.  Lane l supplies row l % 16 of A and request l % 16 of the block, both
+// at the same 8 elements of each 32-element step (chunk l / 16), so every product pairs an element
+// of A with the hidden state's element of the same dimension, whatever the order inside the
+// instruction.  As in the vector kernel the waves split the row into slices of 64 chunks, whose 16
+// loads of A per lane stay in registers while the request blocks go by; the slices meet in LDS.
+// The vector kernel turns ALU-bound beyond a few requests (its dot products and reduce-scatters grow
+// with the batch), the matrix cores do not.
+constexpr int kMfmaMinReq = 12;  // batches from this size take the matrix cores
+constexpr int kMSteps = 16;     // 32-element steps per slice (64 chunks of 16 bytes)
+
+__global__ __launch_bounds__(64 * kMaxWaves) void latent_mfma_kernel(LatentParams p) {
+    extern __shared__ float mpart[];  // [request block][wave][16 rows][16 requests]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_waves = blockDim.x >> 6;
+    const int rl = lane & 15, kc = lane >> 4;
+    const int hc = p.d_model / 8;  // 16-byte chunks per row
+    const int n_slices = (hc + 63) / 64;
+    const int n_blocks = (p.n_req + 15) / 16;
+    const int row0 = blockIdx.x * 16;
+    const int i = row0 / p.rank;
+    const size_t row_bytes = (size_t)p.d_model * sizeof(uint16_t);
+    const __amdgpu_buffer_rsrc_t a = tile_rsrc(static_cast<const char*>(p.w_down) + (size_t)row0 * row_bytes,
+                                               (unsigned)(16 * row_bytes));
+    const char* hid = static_cast<const char*>(p.hidden) + (size_t)i * p.hidden_idx_stride * sizeof(uint16_t);
+    const size_t req_bytes = (size_t)p.hidden_req_stride * sizeof(uint16_t);
+    for (int s = wave; s < n_slices; s += n_waves) {
+        uint4 av[kMSteps];
+#pragma unroll
+        for (int t = 0; t < kMSteps; ++t) {
+            const int c = s * 64 + 4 * t + kc;
+            av[t] = load_nt(a, (unsigned)(rl * row_bytes) + (unsigned)min(c, hc - 1) * 16u, 0u);
+        }
+#pragma unroll
+        for (int t = 0; t < kMSteps; ++t)
+            if (s * 64 + 4 * t + kc >= hc) av[t] = make_uint4(0u, 0u, 0u, 0u);  // past a short row's end
+        for (int rb = 0; rb < n_blocks; ++rb) {
+            // lanes of requests past the batch's end compute a column that is never stored
+            const char* h = hid + (size_t)min(16 * rb + rl, p.n_req - 1) * req_bytes;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                uint4 bv[kMSteps / 2];
+#pragma unroll
+                for (int t = 0; t < kMSteps / 2; ++t) {
+                    const int c = s * 64 + 4 * (kMSteps / 2 * half + t) + kc;
+                    bv[t] = load(h, (unsigned)min(c, hc - 1) * 16u);
+                }
+#pragma unroll
+                for (int t = 0; t < kMSteps / 2; ++t)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[kMSteps / 2 * half + t]),
+                                                                   __builtin_bit_cast(bf16x8, bv[t]), acc, 0, 0, 0);
+            }
+            // lane l holds rows 4 (l / 16) .. + 3 of request column l % 16
+            float* dst = mpart + ((size_t)(rb * n_waves + wave) * 16 + 4 * kc) * 16 + rl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[16 * j] = s == wave ? acc[j] : dst[16 * j] + acc[j];
+        }
+    }
+    __syncthreads();
+    uint16_t* out = static_cast<uint16_t*>(p.latent);
+    const int k0 = row0 - i * p.rank;
+    const int w_used = min(n_waves, n_slices);
+    for (int o = threadIdx.x; o < n_blocks * 256; o += blockDim.x) {
+        const int rb = o / 256, e = o % 256, row = e / 16, col = e % 16;
+        const int r = 16 * rb + col;
+        float sum = 0.0f;
+        for (int w = 0; w < w_used; ++w) sum += mpart[((size_t)(rb * n_waves + w) * 16 + row) * 16 + col];
+        if (r < p.n_req) out[((size_t)r * p.n_idx + i) * p.rank + k0 + row] = Elem<uint16_t>::store(sum);
+    }
+}
+
 lsa_status latent_check(const lsa_latent_args* a) {
     LSA_CHECK_ARG(a != nullptr, "lsa_query_latent: null args");
     LSA_CHECK_ARG(a->n_req >= 1 && a->n_req <= kMaxReq, "lsa_query_latent: n_req=%d outside 1..%d", a->n_req, kMaxReq);
@@ -225,6 +300,16 @@ lsa_status launch_latent(const lsa_latent_args* a, hipStream_t stream) {
     p.n_idx = a->n_idx;
     const int slices = (a->d_model / Elem<T>::N + 63) / 64;
     const int waves = std::min(slices, kMaxWaves);
+    if (std::is_same<T, uint16_t>::value && a->n_req >= kMfmaMinReq) {
+        const size_t lds = (size_t)((a->n_req + 15) / 16) * waves * 256 * sizeof(float);  // <= 32 KiB
+        const dim3 grid(a->n_idx * a->rank / 16), block(64 * waves);
+        if (a->ev_begin && a->ev_end)
+            hipExtLaunchKernelGGL(latent_mfma_kernel, grid, block, lds, stream, a->ev_begin, a->ev_end, 0, p);
+        else
+            hipLaunchKernelGGL(latent_mfma_kernel, grid, block, lds, stream, p);
+        LSA_HIP(hipGetLastError());
+        return LSA_OK;
+    }
     const size_t lds = (size_t)((a->n_req + kQ - 1) / kQ) * waves * kN * sizeof(float);  // <= 32 KiB
     const dim3 grid(a->n_idx * a->rank / kG), block(64 * waves);
     if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps

@@ -13,11 +13,19 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dtype,d_model,rank,n_req,shared", [
-    ("bf16", 4096, 2048, 4, True), ("bf16", 1024, 512, 5, False), ("f32", 512, 256, 3, False)])
+    ("bf16", 4096, 2048, 4, True), ("bf16", 1024, 512, 5, False), ("f32", 512, 256, 3, False),
+    ("bf16", 4096, 2048, 16, True), ("bf16", 1280, 256, 37, False), ("f32", 1024, 256, 20, False),
+    ("bf16", 2048, 512, 11, False), ("bf16", 2048, 512, 12, True)])
 def test_latent_matches_oracle(dtype, d_model, rank, n_req, shared):
     """c_i = A_i h: bf16 latents are the oracle's (exact sum rounded to bfloat16) up to a rounding
-    decision taken on an fp32 sum instead of the exact one, i.e. equal or one bfloat16 unit
-    apart, and equal almost everywhere; fp32 latents agree to fp32 accumulation error."""
+    decision taken on an fp32 sum instead of the exact one: equal almost everywhere over the
+    batch, and elsewhere apart by at most one bfloat16 unit plus the fp32 sum's error.  That error
+    is bounded by height x 2^-24 x sum_j |A_ij h_j| for a summation tree of that height (the
+    recursive-summation bound); at these sizes every kernel sums a row in a tree of height below
+    64.  Where cancellation leaves a small latent, that error can exceed the latent's own bfloat16
+    unit.  fp32 latents agree to fp32 accumulation error.  Batches of 12 or more bf16 requests take
+    the matrix-core kernel (11 and 12: either side of the switch; 12, 16 and 37: partial, whole and
+    ragged request blocks; 1280 elements: a row ending inside a slice)."""
     from lookahead_block_sparse_amd import lsa_query_latent
     from workloads import bf16_bits_from_f32
 
@@ -37,17 +45,25 @@ def test_latent_matches_oracle(dtype, d_model, rank, n_req, shared):
     got_raw = out.cpu().numpy()
     got = oracle.decode_values(got_raw.view(np.uint16) if dtype == "bf16" else got_raw, dtype)
     A = oracle.decode_values(a_raw, dtype)
+    exact_frac, worst = [], 0.0
     for r in range(n_req):
         h = oracle.decode_values(h_raw[r, 0] if shared else h_raw[r], dtype)
         want = oracle.query_latent(h, A, dtype)
         if dtype == "bf16":
+            hh = np.broadcast_to(h, (n_idx, d_model))
+            mass = np.stack([np.abs(A[i]) @ np.abs(hh[i]) for i in range(n_idx)])
             ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(want), np.abs(got[r])))[1] - 8)
             diff = np.abs(got[r] - want)
-            assert (diff <= ulp).all(), diff.max()
-            assert (diff == 0).mean() >= 0.999, (diff == 0).mean()
+            bound = ulp + 64 * 2.0 ** -24 * mass
+            worst = max(worst, float((diff / bound).max()))
+            assert (diff <= bound).all(), (r, diff.max())
+            exact_frac.append((diff == 0).mean())
         else:
             exact = np.stack([A[i] @ (h if h.ndim == 1 else h[i]) for i in range(n_idx)])
             assert np.allclose(got[r], want, rtol=1e-5, atol=1e-5 * np.abs(exact).max())
+    if exact_frac:
+        log(f"  exact fraction {np.mean(exact_frac):.5f}; worst difference / bound {worst:.3f}")
+        assert np.mean(exact_frac) >= 0.999, np.mean(exact_frac)
 
 
 @pytest.mark.parametrize("name", ["ctx128k_s", "ragged_s"])
