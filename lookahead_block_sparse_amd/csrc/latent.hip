@@ -192,17 +192,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) void latent_kernel(LatentParams p) 
 // Matrix-core variant for batches of requests (bf16): per work-group a tile of 16 rows of A
 // against 16 requests at a time, v_mfma_f32_16x16x32_bf16 with A's rows and the requests' hidden
 // states as the two operands.  Lane l supplies row l % 16 of A and request l % 16 of the block, both
-// at the same 8 elements of each 32-element step (chunk l / 16), so every product pairs an element
-// of A with the hidden state's element of the same dimension, whatever the order inside the
-// instruction.  As in the vector kernel the waves split the row into slices of 64 chunks, whose 16
-// loads of A per lane stay in registers while the request blocks go by; the slices meet in LDS.
+// at the same 8 elements of each 32-element step (chunk l / 16 of the step's four), so every product
+// pairs an element of A with the hidden state's element of the same dimension, whatever the order
+// inside the instruction.  As in the vector kernel the waves split the row into slices of 64
+// chunks, whose 16 loads of A per lane stay in registers while the request blocks go by; the slices
+// meet in LDS.  A's operand arrives straight from memory (16 rows x 64 bytes a load, each row
+// streamed once); the hidden states, which every work-group reads, go through a per-wave LDS tile
+// instead: a quarter slice (16 chunks) of the block's 16 requests is loaded as 4 runs of 256
+// contiguous bytes per instruction, written to the tile and read back in operand order.  Loaded in
+// operand order (16 pieces of 64 bytes a load, a request stride apart) they made up most of the
+// kernel's time at 64 requests; through the tile the LDS round trip is what remains of their cost.
+// The tile's chunks are XOR-swizzled by request, so both the writes and the reads touch 16
+// distinct 16-byte bank groups per 16 lanes.  The next quarter's loads are in flight while the
+// current one is read and multiplied (a second quarter in flight measured no faster).
 // The vector kernel turns ALU-bound beyond a few requests (its dot products and reduce-scatters grow
 // with the batch), the matrix cores do not.
-constexpr int kMfmaMinReq = 12;  // batches from this size take the matrix cores
+constexpr int kMfmaMinReq = 10;  // batches from this size take the matrix cores
 constexpr int kMSteps = 16;     // 32-element steps per slice (64 chunks of 16 bytes)
+// Chunks past a short row's end load from this offset, beyond both buffer ranges (< 2^30 bytes), so
+// they read as zeros without a wait; adding up to 64 request strides (< 2^24 bytes) stays below 2^32.
+constexpr unsigned kPastEnd = 0xC0000000u;
+constexpr size_t kMfmaMaxReqBytes = (size_t)1 << 24;  // hidden-state stride bound for the matrix cores
+constexpr size_t kMfmaMaxRange = (size_t)1 << 30;     // hidden-state range bound for the matrix cores
 
 __global__ __launch_bounds__(64 * kMaxWaves) void latent_mfma_kernel(LatentParams p) {
-    extern __shared__ float mpart[];  // [request block][wave][16 rows][16 requests]
+    // [request block][wave][16 rows][16 requests] partial sums, then one 16 x 16-chunk B tile per wave
+    extern __shared__ float mpart[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n_waves = blockDim.x >> 6;
@@ -210,39 +225,52 @@ __global__ __launch_bounds__(64 * kMaxWaves) void latent_mfma_kernel(LatentParam
     const int hc = p.d_model / 8;  // 16-byte chunks per row
     const int n_slices = (hc + 63) / 64;
     const int n_blocks = (p.n_req + 15) / 16;
+    uint4* tile = reinterpret_cast<uint4*>(mpart + (size_t)n_blocks * n_waves * 256) + wave * 256;
     const int row0 = blockIdx.x * 16;
     const int i = row0 / p.rank;
     const size_t row_bytes = (size_t)p.d_model * sizeof(uint16_t);
     const __amdgpu_buffer_rsrc_t a = tile_rsrc(static_cast<const char*>(p.w_down) + (size_t)row0 * row_bytes,
                                                (unsigned)(16 * row_bytes));
-    const char* hid = static_cast<const char*>(p.hidden) + (size_t)i * p.hidden_idx_stride * sizeof(uint16_t);
-    const size_t req_bytes = (size_t)p.hidden_req_stride * sizeof(uint16_t);
+    // the hidden states of this indexer: requests past the batch's end lie beyond the range (the
+    // stride is at least a row) and read as zeros, filling columns that are never stored
+    const unsigned req_bytes = (unsigned)p.hidden_req_stride * (unsigned)sizeof(uint16_t);
+    const __amdgpu_buffer_rsrc_t hb =
+        tile_rsrc(static_cast<const char*>(p.hidden) + (size_t)i * p.hidden_idx_stride * sizeof(uint16_t),
+                  (unsigned)(p.n_req - 1) * req_bytes + (unsigned)row_bytes);
+    const unsigned lane_req = (unsigned)kc * req_bytes;
+    // instruction j of quarter q of block rb: requests 16 rb + 4 j + l / 16, chunks 16 q + l % 16 of
+    // the slice
+    auto fetch = [&](int s, int rb, int q, uint4 (&g)[4]) {
+        const int c = s * 64 + 16 * q + rl;
+        const unsigned v = c < hc ? lane_req + (unsigned)c * 16u : kPastEnd;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[j] = load_nt(hb, v + (unsigned)(16 * rb + 4 * j) * req_bytes, 0u);
+    };
     for (int s = wave; s < n_slices; s += n_waves) {
         uint4 av[kMSteps];
 #pragma unroll
         for (int t = 0; t < kMSteps; ++t) {
             const int c = s * 64 + 4 * t + kc;
-            av[t] = load_nt(a, (unsigned)(rl * row_bytes) + (unsigned)min(c, hc - 1) * 16u, 0u);
+            av[t] = load_nt(a, c < hc ? (unsigned)(rl * row_bytes) + (unsigned)c * 16u : kPastEnd, 0u);
         }
-#pragma unroll
-        for (int t = 0; t < kMSteps; ++t)
-            if (s * 64 + 4 * t + kc >= hc) av[t] = make_uint4(0u, 0u, 0u, 0u);  // past a short row's end
+        uint4 g[4];
+        fetch(s, 0, 0, g);
         for (int rb = 0; rb < n_blocks; ++rb) {
-            // lanes of requests past the batch's end compute a column that is never stored
-            const char* h = hid + (size_t)min(16 * rb + rl, p.n_req - 1) * req_bytes;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                uint4 bv[kMSteps / 2];
+            for (int q = 0; q < 4; ++q) {
 #pragma unroll
-                for (int t = 0; t < kMSteps / 2; ++t) {
-                    const int c = s * 64 + 4 * (kMSteps / 2 * half + t) + kc;
-                    bv[t] = load(h, (unsigned)min(c, hc - 1) * 16u);
-                }
+                for (int j = 0; j < 4; ++j) tile[(4 * j + kc) * 16 + (rl ^ (4 * j + kc))] = g[j];
+                __builtin_amdgcn_sched_barrier(0);  // the next loads reuse g's registers
+                if (q < 3) fetch(s, rb, q + 1, g);
+                else if (rb + 1 < n_blocks) fetch(s, rb + 1, 0, g);
+                uint4 bv[4];
 #pragma unroll
-                for (int t = 0; t < kMSteps / 2; ++t)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[kMSteps / 2 * half + t]),
-                                                                   __builtin_bit_cast(bf16x8, bv[t]), acc, 0, 0, 0);
+                for (int j = 0; j < 4; ++j) bv[j] = tile[rl * 16 + ((4 * j + kc) ^ rl)];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[4 * q + j]),
+                                                                   __builtin_bit_cast(bf16x8, bv[j]), acc, 0, 0, 0);
             }
             // lane l holds rows 4 (l / 16) .. + 3 of request column l % 16
             float* dst = mpart + ((size_t)(rb * n_waves + wave) * 16 + 4 * kc) * 16 + rl;
@@ -300,8 +328,12 @@ lsa_status launch_latent(const lsa_latent_args* a, hipStream_t stream) {
     p.n_idx = a->n_idx;
     const int slices = (a->d_model / Elem<T>::N + 63) / 64;
     const int waves = std::min(slices, kMaxWaves);
-    if (std::is_same<T, uint16_t>::value && a->n_req >= kMfmaMinReq) {
-        const size_t lds = (size_t)((a->n_req + 15) / 16) * waves * 256 * sizeof(float);  // <= 32 KiB
+    const size_t req_bytes = (size_t)a->hidden_req_stride * sizeof(T);
+    const size_t range = (size_t)(a->n_req - 1) * req_bytes + (size_t)a->d_model * sizeof(T);
+    if (std::is_same<T, uint16_t>::value && a->n_req >= kMfmaMinReq && req_bytes < kMfmaMaxReqBytes &&
+        range < kMfmaMaxRange) {
+        // per wave: partial sums (1 KiB per request block) and a B tile (4 KiB); <= 64 KiB in all
+        const size_t lds = ((size_t)((a->n_req + 15) / 16) * 256 * sizeof(float) + 256 * sizeof(uint4)) * waves;
         const dim3 grid(a->n_idx * a->rank / 16), block(64 * waves);
         if (a->ev_begin && a->ev_end)
             hipExtLaunchKernelGGL(latent_mfma_kernel, grid, block, lds, stream, a->ev_begin, a->ev_end, 0, p);
