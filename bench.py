@@ -89,6 +89,9 @@ def parse():
                     help="measure the cold-read ceiling of one launch at the refresh's and the attention's "
                          "sizes with the read probe (libprobe.so) instead of the decode loop")
     ap.add_argument("--ceiling-reps", type=int, default=10)
+    ap.add_argument("--latent-sweep", action="store_true",
+                    help="measure the low-rank latent c_i = A_i h (3 indexers x rank 2048 x d_model 4096, bf16, "
+                         "A cold) across batch sizes instead of the decode loop")
     ap.add_argument("--kernel-trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="no run: per kernel and grid size, the dispatch durations of a rocprofv3 "
                          "--kernel-trace CSV")
@@ -451,6 +454,53 @@ def run_read_ceiling(args) -> dict:
             "note": "event-timed dispatches; each launch reads a region last read more than 1 GB earlier"}
 
 
+def run_latent_sweep(args) -> dict:
+    """The latent projection of the low-rank Query Encoder (3 indexers x rank 2048 x d_model 4096,
+    bf16) at batch sizes 1-64: each launch reads one of 8 copies of A (400 MB in all, past the
+    256 MB memory-side cache, so A is cold), timed with the dispatch's own start and end stamps;
+    algorithmic bytes = A + the hidden states + the latents.  Each size's result is checked
+    against an fp32 product of the same bf16 values."""
+    import torch
+
+    from lookahead_block_sparse_amd import lsa_query_latent
+
+    dev = torch.device("cuda")
+    n_idx, rank, d = 3, 2048, 4096
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    copies = 8
+    A = [(torch.randn(n_idx, rank, d, device=dev, generator=gen) / d ** 0.5).to(torch.bfloat16) for _ in range(copies)]
+    reps = max(10, args.ceiling_reps * 4)
+    rows = []
+    for R in (1, 4, 8, 10, 12, 16, 32, 64):
+        h = torch.randn(R, d, device=dev, generator=gen).to(torch.bfloat16)
+        out = torch.empty(R, n_idx, rank, dtype=torch.int16, device=dev)
+        evs = []
+        for it in range(reps + copies):
+            a = A[it % copies]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            lsa_query_latent(dtype="bf16", d_model=d, rank=rank, n_idx=n_idx, n_req=R, hidden=h.view(torch.int16),
+                             w_down=a.view(torch.int16), latent=out, hidden_req_stride=d, hidden_idx_stride=0,
+                             ev_begin=e0, ev_end=e1)
+            if it == copies - 1:  # the latent of the last copy against an fp32 product
+                got = out.view(torch.bfloat16).float()
+                want = torch.stack([(a[i].float() @ h.float().T).T for i in range(n_idx)], 1)
+                err = ((got - want).abs().max() / want.abs().max()).item()
+                if not err < 1e-2:
+                    raise RuntimeError(f"latent at {R} requests: relative error {err:.3g}")
+            if it >= copies:
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([1e3 * x.elapsed_time(y) for x, y in evs])
+        nbytes = (n_idx * rank * d + R * d + R * n_idx * rank) * 2
+        tbs = nbytes / (np.median(us) * 1e-6) / 1e12
+        rows.append({"requests": R, "median_us": float(np.median(us)), "min_us": float(us.min()),
+                     "bytes": int(nbytes), "TB_per_s": tbs, "frac": tbs * 1e3 / HBM_PEAK_GBS})
+    return {"metric": "latent projection time across batch sizes", "rows": rows, "launches_per_size": reps,
+            "shape": {"n_idx": n_idx, "rank": rank, "d_model": d, "dtype": "bf16"}}
+
+
 def kernel_trace_summary(path: str) -> dict:
     """Per (kernel, grid size): dispatch count, mean and median duration in us, from the
     kernel_trace.csv of a rocprofv3 --kernel-trace run."""
@@ -494,6 +544,9 @@ def main():
         return
     if args.read_ceiling:
         print(json.dumps(run_read_ceiling(args)), flush=True)
+        return
+    if args.latent_sweep:
+        print(json.dumps(run_latent_sweep(args)), flush=True)
         return
 
     print(json.dumps(run_loop(args)), flush=True)
