@@ -30,9 +30,7 @@
 // 2 us before their key loads so that W_q is served first (no gain), and the half words beyond
 // the first round staged in LDS by direct-to-LDS loads, so that every key byte is requested at
 // the start (the stream then ran at ~4.3 TB/s and the staged words were scored after a group
-// barrier: 33-36 us), and three groups per compute unit (32 KiB score batches, the encode's hidden
-// states shared in LDS) so that every group is resident from the start (38 us: a wave's third
-// indexer can only be requested once q is there).  The cross-lane moves of the scoring are row swaps and DPP (no LDS
+// barrier: 33-36 us).  The cross-lane moves of the scoring are row swaps and DPP (no LDS
 // crossbar); making the dot products cheaper as well saves under 0.5 us, so the launch is
 // bound by the key stream and the hand-offs, not by arithmetic.
 // A group only waits for groups with a lower index, which were dispatched before it, and every
