@@ -685,8 +685,8 @@ def run_loop(args) -> dict:
 
     first_copy_ev = (mk_event(), mk_event())  # the first refresh of a run loads every selected block
     first_blocks = []
-    # the counts of blocks a refresh copied stay on the device while the loop runs: a copy on the
-    # decode stream into this history, read after the run.  Sent to pinned host memory from a
+    # the counts of blocks a refresh copied stay on the device while the loop runs: the plan writes
+    # them into a row of this history, read after the run.  Sent to pinned host memory from a
     # stream of their own instead, even once in the warm-up, they left every later kernel of the
     # decode stream slower (attention 66.9 -> 69.6 us per launch, 70.0 -> 74.0 us per decode step)
     copied_hist = torch.zeros((len(timed_refresh) + len(leg_refreshes) + 2, wl.n_req), dtype=torch.int32,
@@ -729,11 +729,10 @@ def run_loop(args) -> dict:
         if dplan:
             # refresh, plan and copy on the device: nothing comes back to the host
             sess.refresh_device(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1], ev_plan=ev_plan,
-                                ev_latent=lat_ev.get(t, (None, None)))
+                                ev_latent=lat_ev.get(t, (None, None)),
+                                copied_out=copied_hist[copy_slot] if copy_slot is not None else None)
             if copy_slot is not None:
                 slot_reqs[copy_slot] = list(reqs)
-                with torch.cuda.stream(sess.stream):  # before the next plan rewrites them
-                    copied_hist[copy_slot].copy_(sess.copied_dev)
             return None
         sel = sess.refresh(reqs, hid, bias, ev_begin=ev_ref[0], ev_end=ev_ref[1],
                            ev_latent=lat_ev.get(t, (None, None)))

@@ -390,12 +390,19 @@ class LSASession:
         return self._pargs[key]
 
     def refresh_device(self, reqs: Sequence[int], hidden: torch.Tensor, bias: torch.Tensor, ev_begin=None,
-                       ev_end=None, ev_plan=(None, None), ev_latent=(None, None)) -> None:
+                       ev_end=None, ev_plan=(None, None), ev_latent=(None, None),
+                       copied_out: Optional[torch.Tensor] = None) -> None:
         """Index refresh of `reqs` followed by the gather planned and run on the device
         (lsa_gather_plan_device): nothing is copied back and nothing waits for the host.  The
-        decode then reads the tables' counts on the device (DecodeLoop(..., device_counts=True))."""
+        decode then reads the tables' counts on the device (DecodeLoop(..., device_counts=True)).
+        The plan writes the number of blocks it copied for request r to entry r of `copied_out`
+        (an int32 device tensor of n_req entries) when given, else to `copied_dev`."""
         if not self.device_plan:
             raise RuntimeError("the session was built without device_plan")
+        if copied_out is not None and not (copied_out.is_cuda and copied_out.dtype == torch.int32 and
+                                           copied_out.is_contiguous() and copied_out.numel() >= self.n_req):
+            raise ValueError(f"copied_out must be a contiguous int32 device tensor of {self.n_req} entries")
+        copied_base = (copied_out if copied_out is not None else self.copied_dev).data_ptr()
         reqs = list(reqs)
         hid = hidden.reshape(len(reqs), self.d_model)
         bias_d = bias.reshape(len(reqs), self.n_idx)
@@ -409,6 +416,7 @@ class LSASession:
             self._refresh_run(r0, r1, hid[i:j + 1], bias_d[i:j + 1], ev_begin if one_run else None,
                               ev_end if one_run else None, ev_latent=ev_latent if one_run else (None, None))
             a = self._plan_args(r0, r1)[0]
+            a.copied = copied_base + 4 * r0
             a.ev_begin = ev_plan[0].cuda_event if (ev_plan[0] is not None and one_run) else None
             a.ev_end = ev_plan[1].cuda_event if (ev_plan[1] is not None and one_run) else None
             _check(LIB.lsa_gather_plan_device(ctypes.byref(a), ctypes.c_void_p(self.stream.cuda_stream)))

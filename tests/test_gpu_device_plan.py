@@ -50,17 +50,25 @@ def _run(wl, sess, sample, check=True, switch_at=None):
     bias_all = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
     sels, gpu = {}, {}
 
+    prev = {r: np.zeros(0, dtype=np.int64) for r in range(R)}  # each request's resident blocks
+
     def refresh(reqs, k_of):
         hid = raw_to_torch(np.stack([wl.hidden[r][k_of[r]] for r in reqs]), dev)
-        sess.refresh_device(reqs, hid, torch.stack([bias_all[r] for r in reqs]))
+        copied = torch.full((R,), -1, dtype=torch.int32, device=dev)  # the plan's count of copied blocks
+        sess.refresh_device(reqs, hid, torch.stack([bias_all[r] for r in reqs]), copied_out=copied)
         if check:
             counts = sess.sel_count.cpu().numpy()
             ids_all = sess.sel_ids.cpu().numpy()
+            got_copied = copied.cpu().numpy()
             for r in reqs:
                 b0 = int(sess.blk_off[r])
                 ids = ids_all[b0:b0 + counts[r]].copy()
                 sels[(r, k_of[r])] = ids
                 _check_state(sess, r, ids)
+                # the blocks that entered: selected now, not resident before
+                assert got_copied[r] == len(np.setdiff1d(ids, prev[r])), (r, got_copied[r])
+                prev[r] = ids
+            assert all(got_copied[r] == -1 for r in range(R) if r not in reqs), got_copied
 
     pro = [r for r in range(R) if wl.refresh_steps[r][0] < 0]
     if pro:
