@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 11
+#define LSA_ABI_VERSION 12
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -371,6 +371,14 @@ typedef struct lsa_decode_args {
                                   capacity, and the split of the work over the groups is computed
                                   by the kernels: the refresh's sel_count feeds the decode with no
                                   host round trip */
+    const int32_t* req_rows;   /* host [n_req] or NULL (identity).  Request r of this call is row
+                                  req_rows[r] of every device array indexed by request: q, k_new,
+                                  v_new, ring, out and n_sel_dev (the host arrays above stay this
+                                  call's own, indexed by r).  Rows must be distinct (each request
+                                  writes its own ring row and output row).  A call over some of a
+                                  batch's requests then needs no copies: two such calls over
+                                  disjoint rows, with their own workspaces, may run on two streams
+                                  at once */
 } lsa_decode_args;
 
 lsa_status lsa_sparse_decode_workspace(const lsa_decode_args* a, size_t* bytes);

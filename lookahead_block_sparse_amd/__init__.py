@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -142,7 +142,7 @@ class DecodeArgs(Structure):
         ("window", c_void_p), ("out", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("max_groups", c_int32), ("reserved1", c_int32),
         ("ev_attn_begin", c_void_p), ("ev_attn_end", c_void_p),
-        ("n_sel_dev", c_void_p),
+        ("n_sel_dev", c_void_p), ("req_rows", c_void_p),
     ]
 
 

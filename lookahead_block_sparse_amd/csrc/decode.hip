@@ -57,6 +57,7 @@ struct DecodeParams {
     int n_ring[kMaxReq];  // window tiles of each request
     int ring_first[kMaxReq];
     int tile_prefix[kMaxReq + 1];  // host-side counts: the split computed on the host
+    int row[kMaxReq];  // request r's row in q, k_new, v_new, ring and n_sel_dev
 };
 
 struct MergeParams {
@@ -70,17 +71,18 @@ struct MergeParams {
     int n_ring[kMaxReq];
     int w_lo[kMaxReq];  // host-side counts: the groups of each request, computed on the host
     int w_hi[kMaxReq];
+    int row[kMaxReq];  // request r's row in out
 };
 
 // With device-side counts, the split of the tiles over the groups is computed by every group of both
 // kernels from the same inputs (with host-side counts the host computes it): request r's tiles are
 // [pre[r], pre[r+1]) of T = pre[n_req] (its n_sel[r] block tiles, read from the device when the
 // counts live there, then its window tiles), split over split_groups(launched groups, T) groups.
-__device__ void tile_split(const int* n_sel_dev, const int* n_sel, const int* n_ring, int n_req, int* s_ns,
-                           int* s_pre) {
+__device__ void tile_split(const int* n_sel_dev, const int* n_sel, const int* n_ring, const int* row, int n_req,
+                           int* s_ns, int* s_pre) {
     if ((int)threadIdx.x < n_req) {
         int ns = n_sel[threadIdx.x];
-        if (n_sel_dev) ns = min(max(n_sel_dev[threadIdx.x], 0), ns);
+        if (n_sel_dev) ns = min(max(n_sel_dev[row[threadIdx.x]], 0), ns);
         s_ns[threadIdx.x] = ns;
     }
     __syncthreads();
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
     const int lr = lane & 15, lg = lane >> 4;
     const int w = blockIdx.x;
     const bool dev_counts = p.n_sel_dev != nullptr;
-    if (dev_counts) tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.n_req, s_ns, s_pre);
+    if (dev_counts) tile_split(p.n_sel_dev, p.n_sel, p.n_ring, p.row, p.n_req, s_ns, s_pre);
     // both sources are uniform: the LDS values are moved to scalar registers
     auto prefix = [&](int r) { return dev_counts ? __builtin_amdgcn_readfirstlane(s_pre[r]) : p.tile_prefix[r]; };
     const long long T_ = prefix(p.n_req), G = split_groups(p.n_groups, T_);
@@ -382,15 +384,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(DecodeParams p) {
         const int ws = p.ws[r];
         const int n_sel = dev_counts ? __builtin_amdgcn_readfirstlane(s_ns[r]) : p.n_sel[r];
         const int2* tbl = p.table + p.tbl_off[r];
-        char* ring_r = p.ring + (size_t)r * p.ring_req_bytes;
-        const T* kn = p.k_new ? static_cast<const T*>(p.k_new) + (size_t)r * D : nullptr;
-        const T* vn = p.v_new ? static_cast<const T*>(p.v_new) + (size_t)r * D : nullptr;
+        const int row = p.row[r];
+        char* ring_r = p.ring + (size_t)row * p.ring_req_bytes;
+        const T* kn = p.k_new ? static_cast<const T*>(p.k_new) + (size_t)row * D : nullptr;
+        const T* vn = p.v_new ? static_cast<const T*>(p.v_new) + (size_t)row * D : nullptr;
         const int cur_slot = (L - 1) % p.win_cap;
         const int cur_chunk = cur_slot >> 6;
         const int cur_row = cur_slot & 63;
 
         typename Ops::QReg q;
-        const T* q_r = static_cast<const T*>(p.q) + (size_t)r * p.n_heads * D;
+        const T* q_r = static_cast<const T*>(p.q) + (size_t)row * p.n_heads * D;
         Ops::load_q(q, q_r, p.n_heads, lane);
 
         float m_run = -INFINITY, l_run = 0.f;
@@ -619,7 +622,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p) {
             a += sc * s_acc[s][col];
             l += sc * s_l[s][col];
         }
-        p.out[((size_t)r * p.n_heads + h) * D + d] = a / l;
+        p.out[((size_t)p.row[r] * p.n_heads + h) * D + d] = a / l;
     }
 }
 
@@ -640,6 +643,13 @@ lsa_status decode_check(const lsa_decode_args* a) {
     LSA_CHECK_ARG(a->max_groups >= 0, "lsa_sparse_decode: max_groups=%d", a->max_groups);
     LSA_CHECK_ARG(a->tbl_off && a->n_sel && a->seq_len && a->window, "lsa_sparse_decode: null host array");
     LSA_CHECK_ARG((a->k_new == nullptr) == (a->v_new == nullptr), "lsa_sparse_decode: give both k_new and v_new or neither");
+    if (a->req_rows) {  // rows of distinct requests: each writes its own ring row and output row
+        for (int r = 0; r < a->n_req; ++r) {
+            LSA_CHECK_ARG(a->req_rows[r] >= 0, "lsa_sparse_decode: req_rows[%d]=%d", r, a->req_rows[r]);
+            for (int r2 = 0; r2 < r; ++r2)
+                LSA_CHECK_ARG(a->req_rows[r2] != a->req_rows[r], "lsa_sparse_decode: req_rows[%d] == req_rows[%d]", r2, r);
+        }
+    }
     LSA_CHECK_ARG(a->n_slots_total >= 0, "lsa_sparse_decode: n_slots_total=%d", a->n_slots_total);
     return LSA_OK;
 }
@@ -716,6 +726,7 @@ lsa_status launch_decode(const lsa_decode_args* a, const DecodePlan& P, char* ws
         dp.n_sel[r] = a->n_sel[r];
         dp.n_ring[r] = ring;
         dp.ring_first[r] = (wsr / 64) % dp.n_chunks;
+        dp.row[r] = mp.row[r] = a->req_rows ? a->req_rows[r] : r;
         mp.n_sel[r] = a->n_sel[r];
         mp.n_ring[r] = ring;
     }

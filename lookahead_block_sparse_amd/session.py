@@ -280,14 +280,16 @@ class LSASession:
         return out
 
     def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor, ev_begin=None,
-                     ev_end=None, table_out: bool = False, ev_latent=(None, None)) -> None:
+                     ev_end=None, table_out: bool = False, ev_latent=(None, None),
+                     stream: Optional[torch.cuda.Stream] = None) -> None:
+        st = self.stream if stream is None else stream
         stride = self.d_model
         if self.rank:
             # the latents of these requests, then the Query Encoder reads them in place of h
             lat = self.latent[r0:r1]
             lsa_query_latent(dtype=self.dtype, d_model=self.d_model, rank=self.rank, n_idx=self.n_idx,
                              n_req=r1 - r0, hidden=hid, w_down=self.w_down, latent=lat, ev_begin=ev_latent[0],
-                             ev_end=ev_latent[1], stream=self.stream)
+                             ev_end=ev_latent[1], stream=st)
             hid = lat
             stride = self.n_idx * self.rank
         key = (r0, r1, bool(table_out))
@@ -308,7 +310,7 @@ class LSASession:
                               workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
                               table_out=(self.table[2 * int(self.slot_base[r0]):] if table_out else None),
                               table_slot_base=(self.slot_base[r0:r1] if table_out else None),
-                              stream=self.stream, select_level=self.select_level)
+                              stream=st, select_level=self.select_level)
             self._rargs[key] = self._refresh_struct(r0, r1, stride, table_out, masks)
             return
         a, _keep, need_hid, need_bias = cached
@@ -318,7 +320,7 @@ class LSASession:
         a.hidden, a.bias = hid.data_ptr(), bias_d.data_ptr()
         a.ev_begin = ev_begin.cuda_event if ev_begin is not None else None
         a.ev_end = ev_end.cuda_event if ev_end is not None else None
-        _check(LIB.lsa_index_refresh(ctypes.byref(a), ctypes.c_void_p(self.stream.cuda_stream)))
+        _check(LIB.lsa_index_refresh(ctypes.byref(a), ctypes.c_void_p(st.cuda_stream)))
 
     def _refresh_struct(self, r0: int, r1: int, stride: int, table_out: bool, masks):
         """The refresh argument struct of a run of requests (every field but the hidden states, the
@@ -391,18 +393,20 @@ class LSASession:
 
     def refresh_device(self, reqs: Sequence[int], hidden: torch.Tensor, bias: torch.Tensor, ev_begin=None,
                        ev_end=None, ev_plan=(None, None), ev_latent=(None, None),
-                       copied_out: Optional[torch.Tensor] = None) -> None:
+                       copied_out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
         """Index refresh of `reqs` followed by the gather planned and run on the device
         (lsa_gather_plan_device): nothing is copied back and nothing waits for the host.  The
         decode then reads the tables' counts on the device (DecodeLoop(..., device_counts=True)).
         The plan writes the number of blocks it copied for request r to entry r of `copied_out`
-        (an int32 device tensor of n_req entries) when given, else to `copied_dev`."""
+        (an int32 device tensor of n_req entries) when given, else to `copied_dev`.  Everything is
+        enqueued on `stream` (default: the session's stream)."""
         if not self.device_plan:
             raise RuntimeError("the session was built without device_plan")
         if copied_out is not None and not (copied_out.is_cuda and copied_out.dtype == torch.int32 and
                                            copied_out.is_contiguous() and copied_out.numel() >= self.n_req):
             raise ValueError(f"copied_out must be a contiguous int32 device tensor of {self.n_req} entries")
         copied_base = (copied_out if copied_out is not None else self.copied_dev).data_ptr()
+        st = self.stream if stream is None else stream
         reqs = list(reqs)
         hid = hidden.reshape(len(reqs), self.d_model)
         bias_d = bias.reshape(len(reqs), self.n_idx)
@@ -414,12 +418,13 @@ class LSASession:
             r0, r1 = reqs[i], reqs[j] + 1
             one_run = i == 0 and j == len(reqs) - 1
             self._refresh_run(r0, r1, hid[i:j + 1], bias_d[i:j + 1], ev_begin if one_run else None,
-                              ev_end if one_run else None, ev_latent=ev_latent if one_run else (None, None))
+                              ev_end if one_run else None, ev_latent=ev_latent if one_run else (None, None),
+                              stream=st)
             a = self._plan_args(r0, r1)[0]
             a.copied = copied_base + 4 * r0
             a.ev_begin = ev_plan[0].cuda_event if (ev_plan[0] is not None and one_run) else None
             a.ev_end = ev_plan[1].cuda_event if (ev_plan[1] is not None and one_run) else None
-            _check(LIB.lsa_gather_plan_device(ctypes.byref(a), ctypes.c_void_p(self.stream.cuda_stream)))
+            _check(LIB.lsa_gather_plan_device(ctypes.byref(a), ctypes.c_void_p(st.cuda_stream)))
             i = j + 1
         self.sel_version[reqs] += 1
 
@@ -564,6 +569,45 @@ class DecodeLoop:
         self.args = a
         self.ref = ctypes.byref(a)
         self.stream = ctypes.c_void_p(sess.stream.cuda_stream)
+        self._subs = {}  # (requests, workspace) -> argument struct of a call over those rows
+
+    def _subset(self, reqs: tuple, ws: torch.Tensor):
+        key = (reqs, ws.data_ptr())
+        sub = self._subs.get(key)
+        if sub is None:
+            idx = np.asarray(reqs, dtype=np.int64)
+            a = DecodeArgs()
+            ctypes.memmove(ctypes.byref(a), ctypes.byref(self.args), ctypes.sizeof(DecodeArgs))
+            arrays = {"rows": np.ascontiguousarray(idx, dtype=np.int32),
+                      "tbl_off": np.ascontiguousarray(self.tbl_off[idx]),
+                      "n_sel": np.ascontiguousarray(self.n_sel[idx]),
+                      "window": np.ascontiguousarray(self.window[idx]),
+                      "seq_len": np.zeros(len(idx), dtype=np.int32)}
+            a.n_req = len(idx)
+            a.req_rows, a.tbl_off = arrays["rows"].ctypes.data, arrays["tbl_off"].ctypes.data
+            a.n_sel, a.window = arrays["n_sel"].ctypes.data, arrays["window"].ctypes.data
+            a.seq_len = arrays["seq_len"].ctypes.data
+            a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+            sub = self._subs[key] = (a, ctypes.byref(a), idx, arrays)
+        return sub
+
+    def step_rows(self, t: int, reqs: Sequence[int], q: torch.Tensor, k_new: Optional[torch.Tensor],
+                  v_new: Optional[torch.Tensor], stream: torch.cuda.Stream, workspace: torch.Tensor,
+                  ev_begin=None, ev_end=None) -> None:
+        """Step t for the requests `reqs` only (rows of q, k_new, v_new and out), on `stream`, with
+        its split-K partials in `workspace` (at least the session's decode workspace in size)."""
+        if workspace.numel() < self.sess.decode_ws.numel():
+            raise ValueError("step_rows: workspace smaller than the session's decode workspace")
+        a, ref, idx, arrays = self._subset(tuple(int(r) for r in reqs), workspace)
+        np.add(self.prefill[idx], t + 1, out=arrays["seq_len"], casting="unsafe")
+        if not self.device_counts:
+            arrays["n_sel"][:] = self.sess.n_sel[idx]
+        a.q = q.data_ptr()
+        a.k_new = k_new.data_ptr() if k_new is not None else None
+        a.v_new = v_new.data_ptr() if v_new is not None else None
+        a.ev_attn_begin = ev_begin.cuda_event if ev_begin is not None else None
+        a.ev_attn_end = ev_end.cuda_event if ev_end is not None else None
+        _check(LIB.lsa_sparse_decode(ref, ctypes.c_void_p(stream.cuda_stream)))
 
     def step(self, t: int, q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
              ev_begin=None, ev_end=None) -> None:
@@ -577,6 +621,56 @@ class DecodeLoop:
         a.ev_attn_begin = ev_begin.cuda_event if ev_begin is not None else None
         a.ev_attn_end = ev_end.cuda_event if ev_end is not None else None
         _check(LIB.lsa_sparse_decode(self.ref, self.stream))
+
+
+class StaggeredLoop:
+    """Decode steps of a device-planned session whose requests refresh at different steps.  At a
+    step where some requests refresh, their refresh, residency plan, block copy and their own
+    attention run on a second stream while the other requests' attention runs on the session's
+    stream; the session's stream then waits for the second one, so the next step sees every new
+    table.  No request attends over a selection before its copy has landed (both are on the second
+    stream, in that order), and the second stream starts only when the previous step's work on the
+    session's stream is done (that work still reads the refreshing requests' old slots).  Steps
+    without a refresh are one call, as in DecodeLoop."""
+
+    def __init__(self, sess: LSASession, prefill: Sequence[int], window: Sequence[int], out: torch.Tensor,
+                 side_stream: Optional[torch.cuda.Stream] = None):
+        if not sess.device_plan:
+            raise ValueError("StaggeredLoop needs a session with device_plan")
+        self.sess = sess
+        self.loop = DecodeLoop(sess, prefill, window, out, device_counts=True)
+        self.side = side_stream if side_stream is not None else torch.cuda.Stream(device=sess.device)
+        self.ws_side = torch.empty_like(sess.decode_ws)
+        self.fork, self.join = torch.cuda.Event(), torch.cuda.Event()
+
+    def step(self, t: int, q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+             refresh: Sequence[int] = (), hidden: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+             ev_begin=None, ev_end=None, ev_refresh=(None, None), ev_plan=(None, None),
+             copied_out: Optional[torch.Tensor] = None) -> None:
+        """Step t; `refresh` lists the requests that refresh first (hidden states and biases of
+        those requests, in that order).  ev_begin/ev_end time the attention of the requests that
+        do not refresh (or of all of them at a step without a refresh)."""
+        sess = self.sess
+        S = sorted(int(r) for r in refresh)
+        if not S:
+            self.loop.step(t, q, k_new, v_new, ev_begin, ev_end)
+            return
+        if S != [int(r) for r in refresh]:
+            raise ValueError("StaggeredLoop.step: list the refreshing requests in ascending order")
+        others = [r for r in range(sess.n_req) if r not in set(S)]
+        # the inputs are read on the second stream: keep the allocator from reusing them meanwhile
+        for x in (q, k_new, v_new, hidden, bias, copied_out):
+            if x is not None:
+                x.record_stream(self.side)
+        self.fork.record(sess.stream)
+        self.side.wait_event(self.fork)
+        sess.refresh_device(S, hidden, bias, ev_begin=ev_refresh[0], ev_end=ev_refresh[1], ev_plan=ev_plan,
+                            copied_out=copied_out, stream=self.side)
+        self.loop.step_rows(t, S, q, k_new, v_new, self.side, self.ws_side)
+        if others:
+            self.loop.step_rows(t, others, q, k_new, v_new, sess.stream, sess.decode_ws, ev_begin, ev_end)
+        self.join.record(self.side)
+        sess.stream.wait_event(self.join)
 
 
 class ResidentLoop:

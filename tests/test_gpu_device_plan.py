@@ -283,3 +283,66 @@ def test_refresh_that_gave_up_is_reported():
     assert int(sess.table_count[1]) == int(before[1][1])
     w0, w1 = int(sess.word_off[1]), int(sess.word_off[2])
     assert torch.equal(sess.resident_dev[w0:w1], before[2][w0:w1])
+
+
+@pytest.mark.parametrize("name", ["ragged_s"])
+def test_staggered_overlap_matches_oracle(name):
+    """Staggered refreshes overlapped with the other requests' decode (StaggeredLoop): at a step
+    where some requests refresh, their refresh, plan, copy and attention run on a second stream
+    beside the others' attention.  Every refresh selects the oracle's blocks and leaves the tables,
+    device state and hot pool of its selection; the outputs at refresh steps and the steps after
+    them match the oracle."""
+    from workloads import get_config
+    from lookahead_block_sparse_amd.session import StaggeredLoop
+
+    cfg = get_config(name)
+    wl = conditioned_workload(cfg, seed=47)
+    R = wl.n_req
+    sess = make_session(wl, cold_on_device=True, with_masks=False, device_plan=True)
+    dev = sess.device
+    bias_all = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32)).to(dev)
+    ref_steps = [t for t in range(cfg.steps) if 0 < len(wl.refreshes_at(t)) < R]
+    assert ref_steps, "the workload has no staggered refresh"
+    sample = sorted({0, cfg.steps - 1} | set(ref_steps[:4]) | {t + 1 for t in ref_steps[:4] if t + 1 < cfg.steps})
+    log(f"staggered overlap {name}: {R} requests, {cfg.steps} steps, refresh steps {ref_steps[:6]}..., sample {sample}")
+    pro = [r for r in range(R) if wl.refresh_steps[r][0] < 0]
+    sels = {}
+    if pro:
+        sess.refresh_device(pro, raw_to_torch(np.stack([wl.hidden[r][0] for r in pro]), dev),
+                            torch.stack([bias_all[r] for r in pro]))
+        torch.cuda.synchronize()
+        for r in pro:
+            b0 = int(sess.blk_off[r])
+            sels[(r, 0)] = sess.sel_ids[b0:b0 + int(sess.sel_count[r])].cpu().numpy()
+    out = torch.empty((R, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    loop = StaggeredLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), out)
+    gpu = {}
+    for t in range(cfg.steps):
+        reqs = wl.refreshes_at(t)
+        hid = raw_to_torch(np.stack([wl.hidden[r][wl.refresh_index_at(r, t)] for r in reqs]), dev) if reqs else None
+        bias = torch.stack([bias_all[r] for r in reqs]) if reqs else None
+        loop.step(t, raw_to_torch(wl.q_dec[t], dev), raw_to_torch(wl.k_new[t], dev), raw_to_torch(wl.v_new[t], dev),
+                  refresh=reqs, hidden=hid, bias=bias)
+        if reqs:
+            torch.cuda.synchronize()
+            counts = sess.sel_count.cpu().numpy()
+            ids_all = sess.sel_ids.cpu().numpy()
+            for r in reqs:
+                b0 = int(sess.blk_off[r])
+                ids = ids_all[b0:b0 + counts[r]].copy()
+                sels[(r, wl.refresh_index_at(r, t))] = ids
+                _check_state(sess, r, ids)
+        if t in sample:
+            gpu[t] = out.double().cpu().numpy()
+    torch.cuda.synchronize()
+    sess.check_plan_status()
+    refs, outs = oracle.simulate(wl, steps=sample)
+    assert len(sels) == sum(len(s) for s in wl.refresh_steps)
+    for (r, k), ids in sels.items():
+        assert np.array_equal(ids, refs[r][k].ids), (name, r, k)
+    worst = (0.0, 0.0, 0.0)
+    for t in sample:
+        ref = np.stack([outs[(r, t)] for r in range(R)])
+        worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
+    log(f"  {name}: {len(sels)} refreshes ({len(ref_steps)} overlapped steps); max abs {worst[0]:.3e} rel {worst[1]:.3e}")
+    assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
