@@ -82,6 +82,22 @@ __device__ int group_sum(int v, int* s_w) {
     return tot;
 }
 
+// The next (up to) kBits set bits of m, lowest first, cleared from m: their positions and how many.
+// The passes below handle a word's blocks kBits at a time with every load of a batch issued before
+// its stores (one memory round trip per batch instead of one per block); entries past the count
+// repeat the first position, so those loads stay on a block of the word and their values go unused.
+constexpr int kBits = 8;
+__device__ __forceinline__ int take_bits(unsigned long long& m, int (&pos)[kBits]) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < kBits; ++k) {
+        pos[k] = m ? __ffsll((long long)m) - 1 : pos[0];
+        n += m != 0ull;
+        m &= m - 1ull;
+    }
+    return n;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     __shared__ int s_w[kPlanWaves];
     const int r = blockIdx.x;
@@ -96,8 +112,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     int2* cl = p.clist + s0;
 
     int c_new = 0, c_enter = 0, c_leave = 0;
+    // a request of at most kPlanThreads words: each thread's word is the same in every pass, so it
+    // stays in registers (one round trip fewer per pass); longer requests re-read their words
+    const bool one = W <= kPlanThreads;
+    unsigned long long u1 = 0ull, o1 = 0ull;
+    if (one && (int)threadIdx.x < W) {
+        u1 = nm[threadIdx.x];
+        o1 = res[threadIdx.x];
+    }
+    auto new_word = [&](int w) { return one ? u1 : (w < W ? nm[w] : 0ull); };
+    auto old_word = [&](int w) { return one ? o1 : (w < W ? res[w] : 0ull); };
     for (int w = threadIdx.x; w < W; w += kPlanThreads) {
-        const unsigned long long u = nm[w], o = res[w];
+        const unsigned long long u = new_word(w), o = old_word(w);
         c_new += __popcll(u);
         c_enter += __popcll(u & ~o);
         c_leave += __popcll(o & ~u);
@@ -119,14 +145,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     int base = 0;
     for (int c0 = 0; c0 < W; c0 += kPlanThreads) {
         const int w = c0 + threadIdx.x;
-        unsigned long long m = w < W ? res[w] & ~nm[w] : 0ull;
+        unsigned long long m = old_word(w) & ~new_word(w);
         int tot;
         int at = base + group_exclusive_scan(__popcll(m), s_w, &tot);
         while (m) {
-            const int id = 64 * w + __ffsll((long long)m) - 1;
-            fs[nf + at++] = sob[id];
-            sob[id] = -1;
-            m &= m - 1ull;
+            int pos[kBits];
+            const int n = take_bits(m, pos);
+            int slot[kBits];
+#pragma unroll
+            for (int k = 0; k < kBits; ++k) slot[k] = sob[64 * w + pos[k]];
+#pragma unroll
+            for (int k = 0; k < kBits; ++k) {
+                if (k < n) {
+                    fs[nf + at + k] = slot[k];
+                    sob[64 * w + pos[k]] = -1;
+                }
+            }
+            at += n;
         }
         base += tot;
     }
@@ -136,15 +171,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     base = 0;
     for (int c0 = 0; c0 < W; c0 += kPlanThreads) {
         const int w = c0 + threadIdx.x;
-        unsigned long long m = w < W ? nm[w] & ~res[w] : 0ull;
+        unsigned long long m = new_word(w) & ~old_word(w);
         int tot;
         int e = base + group_exclusive_scan(__popcll(m), s_w, &tot);
         while (m) {
-            const int id = 64 * w + __ffsll((long long)m) - 1;
-            const int slot = fs[nf2 - 1 - e];
-            sob[id] = slot;
-            cl[e++] = make_int2(id, slot);
-            m &= m - 1ull;
+            int pos[kBits];
+            const int n = take_bits(m, pos);
+            int slot[kBits];
+#pragma unroll
+            for (int k = 0; k < kBits; ++k) slot[k] = fs[nf2 - 1 - (e + min(k, n - 1))];
+#pragma unroll
+            for (int k = 0; k < kBits; ++k) {
+                if (k < n) {
+                    const int id = 64 * w + pos[k];
+                    sob[id] = slot[k];
+                    cl[e + k] = make_int2(id, slot[k]);
+                }
+            }
+            e += n;
         }
         base += tot;
     }
@@ -153,14 +197,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     base = 0;
     for (int c0 = 0; c0 < W; c0 += kPlanThreads) {
         const int w = c0 + threadIdx.x;
-        const unsigned long long u = w < W ? nm[w] : 0ull;
+        const unsigned long long u = new_word(w);
         unsigned long long m = u;
         int tot;
         int at = base + group_exclusive_scan(__popcll(m), s_w, &tot);
         while (m) {
-            const int id = 64 * w + __ffsll((long long)m) - 1;
-            tbl[at++] = make_int2(id, sob[id]);
-            m &= m - 1ull;
+            int pos[kBits];
+            const int n = take_bits(m, pos);
+            int slot[kBits];
+#pragma unroll
+            for (int k = 0; k < kBits; ++k) slot[k] = sob[64 * w + pos[k]];
+#pragma unroll
+            for (int k = 0; k < kBits; ++k)
+                if (k < n) tbl[at + k] = make_int2(64 * w + pos[k], slot[k]);
+            at += n;
         }
         if (w < W) res[w] = u;
         base += tot;
