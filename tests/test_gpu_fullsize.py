@@ -149,7 +149,7 @@ def test_full_size_reactive_matches_oracle():
     assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
 
 
-def _survey_sample(wl, seed, n_random=8):
+def _sampled_steps(wl, seed, n_random=8):
     """Every refresh step, the step before it and n_random seeded steps (each sampled step holds the
     outputs of every request), plus the last step."""
     T = wl.cfg.steps
@@ -179,7 +179,7 @@ def test_full_size_device_plan_matches_oracle(name, cold):
     from test_gpu_device_plan import _run
 
     wl = conditioned_workload(name, seed=14)
-    sample = _survey_sample(wl, seed=14)
+    sample = _sampled_steps(wl, seed=14)
     if name == "ragged":  # 287 refresh steps: keep every refresh check, sample a bounded set of steps
         rng = np.random.default_rng(15)
         keep = set(rng.choice(sample, size=24, replace=False).tolist()) | {wl.cfg.steps - 1}
