@@ -262,6 +262,23 @@ def test_decode_validation_before_any_hip_call(over, status):
     assert L.LIB.lsa_sparse_decode(ctypes.byref(a), None) == status
 
 
+@pytest.mark.parametrize("rows", [[0, 0], [2, -1], [1, 3, 1]])
+def test_decode_rejects_bad_request_rows_before_any_hip_call(rows):
+    """req_rows maps each call request to its row of the device arrays: rows must be distinct and
+    non-negative (two requests on one row would write the same ring and output rows)."""
+    n = len(rows)
+    a, keep = L._decode_args(dtype="bf16", n_heads=16, head_dim=128, win_cap=8192, scale=None, q=FAKE, k_new=None,
+                             v_new=None, ring=FAKE, pool=None, n_slots_total=0, table=None, tbl_off=[0] * n,
+                             n_sel=[0] * n, seq_len=[100] * n, window=[64] * n, out=FAKE, workspace=None,
+                             max_groups=0, ev_begin=None, ev_end=None)
+    r = np.ascontiguousarray(rows, dtype=np.int32)
+    a.req_rows = r.ctypes.data
+    a.workspace, a.workspace_bytes = FAKE, 1 << 30
+    assert L.LIB.lsa_sparse_decode(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+    assert "req_rows" in L.LIB.lsa_last_error().decode()
+    assert L.LIB.lsa_sparse_decode_noalloc(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+
+
 # ---- block format packing (pure host) ------------------------------------------------------
 def _bf16_offsets(D):
     """Element offsets of key (t, d) and value (t, d) inside a bf16 block, [64][D] each, written from
