@@ -657,6 +657,8 @@ class StaggeredLoop:
             return
         if S != [int(r) for r in refresh]:
             raise ValueError("StaggeredLoop.step: list the refreshing requests in ascending order")
+        if hidden is None or bias is None:
+            raise ValueError("StaggeredLoop.step: refreshing requests need their hidden states and biases")
         others = [r for r in range(sess.n_req) if r not in set(S)]
         # the inputs are read on the second stream: keep the allocator from reusing them meanwhile
         for x in (q, k_new, v_new, hidden, bias, copied_out):
