@@ -92,6 +92,10 @@ def parse():
     ap.add_argument("--latent-sweep", action="store_true",
                     help="measure the low-rank latent c_i = A_i h (3 indexers x rank 2048 x d_model 4096, bf16, "
                          "A cold) across batch sizes instead of the decode loop")
+    ap.add_argument("--refresh-sweep", action="store_true",
+                    help="measure one index refresh (3 indexers, d_model 4096, d_idx 256, bf16, 16,384 blocks "
+                         "per request, keys cold) across the number of 1M-context requests per call instead "
+                         "of the decode loop")
     ap.add_argument("--kernel-trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="no run: per kernel and grid size, the dispatch durations of a rocprofv3 "
                          "--kernel-trace CSV")
@@ -507,6 +511,76 @@ def run_latent_sweep(args) -> dict:
             "shape": {"n_idx": n_idx, "rank": rank, "d_model": d, "dtype": "bf16"}}
 
 
+def run_refresh_sweep(args) -> dict:
+    """One index refresh of R requests of 16,384 blocks (1M tokens) each, 3 indexers, d_model 4096,
+    d_idx 256, bf16, with the bit planes the device plan reads, at R = 1-16.  Before each timed
+    launch a 1 GiB copy pushes the keys out of the 256 MB memory-side cache, so they are read cold;
+    the launch is timed with the dispatch's own start and end stamps.  Algorithmic bytes as for the
+    decode loop's refresh: W_q + keys + hidden states + ids + counts + bit planes.  Each size's
+    counts are checked against an fp32 computation of the same bf16 values (equal up to the few
+    blocks whose logits lie within rounding of the threshold)."""
+    import torch
+
+    from lookahead_block_sparse_amd import lsa_index_refresh, lsa_index_refresh_workspace
+
+    dev = torch.device("cuda")
+    n_idx, d_idx, d, B = 3, 256, 4096, 16384
+    sizes = (1, 2, 4, 8, 16)
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    R_max = max(sizes)
+    keys = (torch.randn(R_max * n_idx * B * d_idx, device=dev, generator=gen) / d_idx ** 0.5).to(torch.bfloat16)
+    w_q = (torch.randn(n_idx * d_idx * d, device=dev, generator=gen) / d ** 0.5).to(torch.bfloat16)
+    hid = torch.randn(R_max * d, device=dev, generator=gen).to(torch.bfloat16)
+    bias_val = -1.8  # logits are ~N(0, 1): ~3.6% per indexer, ~10% union
+    flush_src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    reps = max(8, args.ceiling_reps)
+    rows = []
+    for R in sizes:
+        blk = [B * r for r in range(R + 1)]
+        words = R * B // 64
+        bias = torch.full((R * n_idx,), bias_val, device=dev)
+        sel = torch.zeros(R * B, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(R, dtype=torch.int32, device=dev)
+        masks = torch.zeros(words * (n_idx + 1), dtype=torch.int64, device=dev)
+        ws = torch.zeros(lsa_index_refresh_workspace(dtype="bf16", d_model=d, d_idx=d_idx, n_idx=n_idx, blk_off=blk),
+                         dtype=torch.uint8, device=dev)
+        evs = []
+        for it in range(reps + 2):
+            flush_dst.copy_(flush_src)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            lsa_index_refresh(dtype="bf16", d_model=d, d_idx=d_idx, n_idx=n_idx, hidden=hid.view(torch.int16),
+                              w_q=w_q.view(torch.int16), keys=keys.view(torch.int16), blk_off=blk, bias=bias,
+                              sel_ids=sel, sel_count=cnt, workspace=ws, masks=masks, ev_begin=e0, ev_end=e1)
+            if it >= 2:
+                evs.append((e0, e1))
+        torch.cuda.synchronize()
+        # counts against fp32 logits of the same bf16 values
+        wq = w_q.float().view(n_idx, d_idx, d)
+        want = np.zeros(R, dtype=np.int64)
+        for r in range(R):
+            q = torch.bmm(wq, hid[r * d:(r + 1) * d].float().view(1, d, 1).expand(n_idx, d, 1).contiguous())
+            kk = keys[r * n_idx * B * d_idx:(r + 1) * n_idx * B * d_idx].float().view(n_idx, B, d_idx)
+            z = torch.bmm(kk, q).view(n_idx, B) + bias_val  # fp32 logits [n_idx][B]
+            want[r] = int((z > 0).any(0).sum().item())
+        got = cnt.cpu().numpy()
+        if np.any(np.abs(got - want) > 0.001 * B):
+            raise RuntimeError(f"refresh at {R} requests: counts {got.tolist()} against fp32 {want.tolist()}")
+        us = np.array([1e3 * x.elapsed_time(y) for x, y in evs])
+        nbytes = 2 * (n_idx * d_idx * d + R * n_idx * B * d_idx + R * d) + 4 * int(got.sum()) + 4 * R \
+            + 8 * (n_idx + 1) * words
+        tbs = nbytes / (np.median(us) * 1e-6) / 1e12
+        rows.append({"requests": R, "median_us": float(np.median(us)), "min_us": float(us.min()),
+                     "bytes": int(nbytes), "TB_per_s": tbs, "frac": tbs * 1e3 / HBM_PEAK_GBS,
+                     "selected_per_request": float(got.mean())})
+        del bias, sel, cnt, masks, ws
+    return {"metric": "index refresh time across requests per call (1M context each)", "rows": rows,
+            "launches_per_size": reps,
+            "shape": {"n_idx": n_idx, "d_model": d, "d_idx": d_idx, "blocks_per_request": B, "dtype": "bf16"}}
+
+
 def kernel_trace_summary(path: str) -> dict:
     """Per (kernel, grid size): dispatch count, mean and median duration in us, from the
     kernel_trace.csv of a rocprofv3 --kernel-trace run."""
@@ -553,6 +627,9 @@ def main():
         return
     if args.latent_sweep:
         print(json.dumps(run_latent_sweep(args)), flush=True)
+        return
+    if args.refresh_sweep:
+        print(json.dumps(run_refresh_sweep(args)), flush=True)
         return
 
     print(json.dumps(run_loop(args)), flush=True)
