@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 12
+#define LSA_ABI_VERSION 13
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -164,6 +164,10 @@ typedef struct lsa_refresh_args {
     const int32_t* table_slot_base; /* host [n_req]: slot of block 0 of request r in that pool
                                   (block b at slot base + b); required with table_out, base + B_r
                                   <= 2^31 - 1 */
+    float* logits;             /* dev or NULL: the fp32 logits z[i][b] the threshold was applied to
+                                  (bias included), request r's [n_idx][B_r] starting at element
+                                  n_idx*blk_off[r]; 4-byte aligned.  For checking the fp32 logits
+                                  against exact ones; NULL writes nothing (the default) */
 } lsa_refresh_args;
 
 lsa_status lsa_index_refresh_workspace(const lsa_refresh_args* a, size_t* bytes);

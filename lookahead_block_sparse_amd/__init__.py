@@ -36,7 +36,7 @@ LSA_BF16 = 1
 BLOCK_TOKENS = 64
 MAX_REFRESH_REQ = 64
 MAX_DECODE_REQ = 64
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 _STATUS_NAMES = {
     LSA_ERR_INVALID: "LSA_ERR_INVALID",
@@ -84,7 +84,7 @@ class RefreshArgs(Structure):
         ("sel_ids", c_void_p), ("sel_count", c_void_p), ("masks", c_void_p),
         ("workspace", c_void_p), ("workspace_bytes", c_size_t),
         ("ev_begin", c_void_p), ("ev_end", c_void_p),
-        ("table_out", c_void_p), ("table_slot_base", c_void_p),
+        ("table_out", c_void_p), ("table_slot_base", c_void_p), ("logits", c_void_p),
     ]
 
 
@@ -324,7 +324,8 @@ def lsa_index_refresh_workspace(*, dtype, d_model, d_idx, n_idx, blk_off) -> int
 
 def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_off, bias, sel_ids, sel_count,
                       workspace, hidden_req_stride=None, hidden_idx_stride=0, masks=None, ev_begin=None,
-                      ev_end=None, table_out=None, table_slot_base=None, stream=None, select_level=0.5) -> None:
+                      ev_end=None, table_out=None, table_slot_base=None, stream=None, select_level=0.5,
+                      logits=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     blk = np.asarray(blk_off, dtype=np.int64)
     n_req, n_blk, e = len(blk) - 1, int(blk[-1]), _elt(dtype)
@@ -339,6 +340,7 @@ def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_of
     _dev(masks, "masks", (n_idx + 1) * n_words * 8)
     _dev(workspace, "workspace")
     _dev(table_out, "table_out", n_blk * 8)
+    _dev(logits, "logits", n_idx * n_blk * 4)
     a, keep = _refresh_args(dtype=dtype, d_model=d_model, d_idx=d_idx, n_idx=n_idx, hidden=hidden,
                             hidden_req_stride=d_model if hidden_req_stride is None else hidden_req_stride,
                             hidden_idx_stride=hidden_idx_stride, w_q=w_q, keys=keys, blk_off=blk_off, bias=bias,
@@ -348,6 +350,7 @@ def lsa_index_refresh(*, dtype, d_model, d_idx, n_idx, hidden, w_q, keys, blk_of
     a.ev_end = ev_end.cuda_event if ev_end is not None else None
     tsb = _i32(table_slot_base) if table_slot_base is not None else None
     a.table_out, a.table_slot_base = _ptr(table_out), _ptr(tsb)
+    a.logits = _ptr(logits)
     a.select_level = float(select_level)
     _check(LIB.lsa_index_refresh(ctypes.byref(a), _stream(stream)))
 

@@ -74,6 +74,7 @@ struct RefreshParams {
     int word_off[kMaxReq + 1];
     int cg_off[kMaxReq + 1];  // first compaction group of each request
     int2* table_out;          // optional: (id, tslot[r] + id) pairs at pair blk_off[r]
+    float* logits;            // optional: z at element n_idx * blk_off[r] + i * B_r + b
     int tslot[kMaxReq];
 };
 
@@ -431,7 +432,11 @@ __device__ __forceinline__ void score_runs(const RefreshParams& p, const HalfWor
             if constexpr (S::LOG_LPR - S::LOG_P == 2) z += dpp_partner<1>(z);
             if constexpr (S::LOG_LPR - S::LOG_P >= 1) z += dpp_partner<0>(z);
             static_assert(S::LOG_LPR - S::LOG_P <= 2, "row lanes left after the reduce-scatter");
-            const bool keep = *q_ok && (rowi < h.n_valid) && (z + p.bias[h.r * p.n_idx + i] > p.select_logit);
+            const float zb = z + p.bias[h.r * p.n_idx + i];
+            const bool keep = *q_ok && (rowi < h.n_valid) && (zb > p.select_logit);
+            // the lanes that share a row hold the same logit: the first of them stores it
+            if (p.logits && rowi < h.n_valid && (lane & ((1 << (S::LOG_LPR - S::LOG_P)) - 1)) == 0)
+                p.logits[(size_t)p.n_idx * p.blk_off[h.r] + (size_t)i * h.n_blk + h.lw * 64 + rowi] = zb;
             const unsigned long long m = __ballot(keep);
             // row q of the half word sits on lane (q % RPL) * LPR + ((q / RPL) << (LOG_LPR - LOG_P))
             unsigned bits = 0u;
@@ -690,6 +695,7 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
     rp.sel_count = a->sel_count;
     rp.masks = reinterpret_cast<unsigned long long*>(a->masks);
     rp.table_out = reinterpret_cast<int2*>(a->table_out);
+    rp.logits = a->logits;
     for (int r = 0; r < a->n_req; ++r) rp.tslot[r] = a->table_out ? a->table_slot_base[r] : 0;
     rp.qw = reinterpret_cast<unsigned long long*>(ws + L.qw_off);
     rp.hw = reinterpret_cast<unsigned long long*>(ws + L.hw_off);
@@ -763,6 +769,7 @@ extern "C" lsa_status lsa_index_refresh(const lsa_refresh_args* a, hipStream_t s
     if (a->workspace == nullptr || a->workspace_bytes < L.total)
         return fail(LSA_ERR_WORKSPACE, "lsa_index_refresh: workspace of %zu bytes, need %zu",
                     a->workspace ? a->workspace_bytes : (size_t)0, L.total);
+    LSA_CHECK_ARG(((uintptr_t)a->logits % 4) == 0, "lsa_index_refresh: logits must be 4-byte aligned");
     const size_t eb = elem_bytes(a->dtype);
     LSA_CHECK_ARG(((uintptr_t)a->hidden % 16) == 0 && ((uintptr_t)a->w_q % 16) == 0 &&
                       ((uintptr_t)a->keys % 16) == 0 && ((uintptr_t)a->workspace % 256) == 0,

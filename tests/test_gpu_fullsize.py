@@ -200,3 +200,48 @@ def test_full_size_device_plan_matches_oracle(name, cold):
     log(f"  {name}: {len(sels)} selections bit-exact; {len(sample)} steps, max abs {worst[0]:.3e} "
         f"rel {worst[1]:.3e} l2 {worst[2]:.3e}")
     assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+@pytest.mark.parametrize("name", ["tiny", "ctx128k_s", "ctx512k_s", "ctx1m"])
+def test_refresh_logits_match_oracle(name):
+    """The fp32 logits the refresh thresholds (its optional logits output) against the oracle's
+    float64 logits of the same stored inputs, on every block of every request of the first refresh
+    (4 x 1M: 196,608 logits).  Bit-exact selection rests on this error staying far below the 2e-3
+    margin the generators keep around the threshold; the bound asserted is a tenth of it."""
+    from lookahead_block_sparse_amd import lsa_index_refresh, lsa_index_refresh_workspace
+
+    wl = conditioned_workload(name, steps=1)
+    cfg, R, dev = wl.cfg, wl.n_req, "cuda"
+    blk = np.concatenate([[0], np.cumsum(wl.n_blocks)]).astype(np.int64)
+    n_blk = int(blk[-1])
+    keys = raw_to_torch(np.concatenate([np.ascontiguousarray(wl.keys[r]).reshape(-1) for r in range(R)]), dev)
+    w_q = raw_to_torch(np.ascontiguousarray(wl.w_q).reshape(-1), dev)
+    hid = raw_to_torch(np.stack([wl.hidden[r][0] for r in range(R)]).reshape(-1), dev)
+    bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32).reshape(-1)).to(dev)
+    sel = torch.zeros(n_blk, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(R, dtype=torch.int32, device=dev)
+    logits = torch.full((cfg.n_idx * n_blk,), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.zeros(lsa_index_refresh_workspace(dtype=cfg.dtype, d_model=cfg.d_model, d_idx=cfg.d_idx,
+                                                 n_idx=cfg.n_idx, blk_off=blk), dtype=torch.uint8, device=dev)
+    lsa_index_refresh(dtype=cfg.dtype, d_model=cfg.d_model, d_idx=cfg.d_idx, n_idx=cfg.n_idx, hidden=hid, w_q=w_q,
+                      keys=keys, blk_off=blk, bias=bias, sel_ids=sel, sel_count=cnt, workspace=ws, logits=logits,
+                      select_level=cfg.level)
+    torch.cuda.synchronize()
+    z_gpu = logits.cpu().numpy().astype(np.float64)
+    counts = cnt.cpu().numpy()
+    w_q64 = oracle.decode_values(wl.w_q, cfg.dtype)
+    worst, worst_rel = 0.0, 0.0
+    for r in range(R):
+        ref = oracle.refresh(oracle.decode_values(wl.hidden[r][0], cfg.dtype), w_q64,
+                             oracle.decode_values(wl.keys[r], cfg.dtype), wl.bias[r].astype(np.float64), cfg.level)
+        z_ref = ref.z
+        got = z_gpu[cfg.n_idx * blk[r]: cfg.n_idx * blk[r + 1]].reshape(cfg.n_idx, -1)
+        assert np.all(np.isfinite(got)), f"request {r}: logits not written"
+        err = np.abs(got - z_ref)
+        worst = max(worst, float(err.max()))
+        worst_rel = max(worst_rel, float((err / np.maximum(np.abs(z_ref), 1.0)).max()))
+        assert counts[r] == ref.count
+        assert np.array_equal(got > oracle.level_logit(cfg.level), ref.s)
+    log(f"{name}: max |z_gpu - z_oracle| = {worst:.3g} (relative to max(|z|, 1): {worst_rel:.3g}) "
+        f"over {cfg.n_idx * n_blk} logits")
+    assert worst <= 2e-4
