@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold", choices=("device", "host"), default="device")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the cold-read ceiling (read probe) measured after the timed region")
     ap.add_argument("--cpu-sample-steps", type=int, default=6, help="decode steps per request timed on the CPU")
     ap.add_argument("--tau", type=int, default=0,
                     help="refresh cadence in steps (default: the workload's, 64); 1 scores every step")
@@ -398,68 +400,103 @@ def run_denoise(args) -> dict:
     return res
 
 
-def run_read_ceiling(args) -> dict:
-    """Cold-read ceilings for the two hot kernels' sizes: one launch of the read probe
-    (libprobe.so) per size, access pattern, load hint, loads per batch and launch shape, each
-    reading a region last touched more than 1 GB of reads earlier (past the 256 MB memory-side
-    cache), timed with the dispatch's own start and end stamps."""
+def _probe_lib():
+    """The read probe (libprobe.so, built by __graft_entry__.build()), or None when it is not built."""
     import ctypes
 
-    import torch
-
-    torch.cuda.init()
-    lib = ctypes.CDLL(str(ROOT / "lookahead_block_sparse_amd" / "libprobe.so"))
+    path = ROOT / "lookahead_block_sparse_amd" / "libprobe.so"
+    if not path.exists():
+        return None
+    lib = ctypes.CDLL(str(path))
     lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, ctypes.c_void_p, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p,
                                ctypes.c_void_p]
     lib.probe_batches.argtypes = [ctypes.c_longlong, ctypes.c_int]
     lib.probe_batches.restype = ctypes.c_longlong
     lib.probe_groups_per_cu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+def _probe_rows(lib, name: str, size: int, variants, reps: int) -> list:
+    """One row per (pattern, nontemporal, loads, persistent) variant: `reps` event-timed launches of
+    the read probe over `size` bytes, each reading a region last read more than 1.2 GB earlier."""
+    import torch
+
     dev = torch.device("cuda")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     stream = torch.cuda.current_stream()
+    stride = (size + (1 << 20) - 1) >> 20 << 20
+    n_reg = max(3, -(-(1200 << 20) // stride))
+    buf = torch.empty(n_reg * stride, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    reg = 0
+    rows = []
+    for pattern, nt, loads, persistent in variants:
+        per_cu = lib.probe_groups_per_cu(pattern, loads, nt)
+        nb = lib.probe_batches(size, loads)
+        groups = cus * per_cu if persistent else 0
+        g_launch = groups if groups else (nb + 3) // 4
+        if sink.numel() < 256 * g_launch:
+            sink = torch.zeros(256 * g_launch, dtype=torch.int32, device=dev)
+        evs = []
+        for _ in range(reps + 1):  # the first launch of a variant loads its code
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            ptr = buf.data_ptr() + reg * stride
+            reg = (reg + 1) % n_reg
+            rc = lib.probe_read(ptr, size, pattern, loads, nt, groups, sink.data_ptr(),
+                                0xDEADBEEF, e0.cuda_event, e1.cuda_event, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"probe_read returned {rc}")
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([1e3 * a.elapsed_time(b) for a, b in evs[1:]])
+        read = nb * loads * 1024
+        rows.append({"size": name, "bytes": int(read), "pattern": ("runs", "rows")[pattern],
+                     "nontemporal": bool(nt), "loads_per_batch": loads,
+                     "shape": "one-shot" if groups == 0 else f"persistent {per_cu}/CU",
+                     "groups": int(g_launch), "median_us": float(np.median(us)),
+                     "min_us": float(us.min()), "TB_per_s": read / (np.median(us) * 1e-6) / 1e12})
+    del buf
+    torch.cuda.empty_cache()
+    return rows
+
+
+def read_ceiling_best(size: int, reps: int = 5):
+    """The measured cold-read ceiling for `size` bytes: the best median rate of the read probe over
+    the load shapes the hot kernels use (whole 1 KiB runs, non-temporal loads; 48 loads per wave
+    requested at once, or 16 per batch at as many groups as fit), or None without libprobe.so."""
+    lib = _probe_lib()
+    if lib is None:
+        return None
+    rows = _probe_rows(lib, "kernel", size, [(0, 1, 48, False), (0, 1, 16, True)], reps)
+    best = max(rows, key=lambda r: r["TB_per_s"])
+    return {"GB_per_s": best["TB_per_s"] * 1e3, "bytes": best["bytes"], "median_us": best["median_us"],
+            "shape": f"{best['loads_per_batch']} loads per wave, {best['shape']}",
+            "probe": "read probe (libprobe.so): a cold region read with whole 1 KiB runs and non-temporal loads"}
+
+
+def run_read_ceiling(args) -> dict:
+    """Cold-read ceilings for the two hot kernels' sizes: one launch of the read probe
+    (libprobe.so) per size, access pattern, load hint, loads per batch and launch shape, each
+    reading a region last touched more than 1 GB of reads earlier (past the 256 MB memory-side
+    cache), timed with the dispatch's own start and end stamps."""
+    import torch
+
+    torch.cuda.init()
+    lib = _probe_lib()
+    if lib is None:
+        raise SystemExit("libprobe.so is not built: run __graft_entry__.build()")
     # the refresh's bytes at 4 x 1M (W_q + keys) and the attention's (4 x ~206K tokens of K and V)
     sizes = {"refresh": 3 * 4096 * 256 * 2 + 4 * 3 * 16384 * 256 * 2, "attention": 416 << 20}
     reps = max(3, args.ceiling_reps)
+    variants = [(pattern, nt, loads, persistent) for pattern in (0, 1) for nt in (1, 0) for loads in (16, 48)
+                for persistent in (False, True)]
     rows = []
     for name, size in sizes.items():
-        stride = (size + (1 << 20) - 1) >> 20 << 20
-        n_reg = max(3, -(-(1200 << 20) // stride))
-        buf = torch.empty(n_reg * stride, dtype=torch.uint8, device=dev)
-        buf.fill_(1)
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        reg = 0
-        for pattern in (0, 1):
-            for nt in (1, 0):
-                for loads in (16, 48):
-                    per_cu = lib.probe_groups_per_cu(pattern, loads, nt)
-                    nb = lib.probe_batches(size, loads)
-                    for groups in (0, cus * per_cu):
-                        g_launch = groups if groups else (nb + 3) // 4
-                        if sink.numel() < 256 * g_launch:
-                            sink = torch.zeros(256 * g_launch, dtype=torch.int32, device=dev)
-                        evs = []
-                        for _ in range(reps + 1):  # the first launch of a variant loads its code
-                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                            e0.record()
-                            e1.record()
-                            ptr = buf.data_ptr() + reg * stride
-                            reg = (reg + 1) % n_reg
-                            rc = lib.probe_read(ptr, size, pattern, loads, nt, groups, sink.data_ptr(),
-                                                0xDEADBEEF, e0.cuda_event, e1.cuda_event, stream.cuda_stream)
-                            if rc != 0:
-                                raise RuntimeError(f"probe_read returned {rc}")
-                            evs.append((e0, e1))
-                        torch.cuda.synchronize()
-                        us = np.array([1e3 * a.elapsed_time(b) for a, b in evs[1:]])
-                        read = nb * loads * 1024
-                        rows.append({"size": name, "bytes": int(read), "pattern": ("runs", "rows")[pattern],
-                                     "nontemporal": bool(nt), "loads_per_batch": loads,
-                                     "shape": "one-shot" if groups == 0 else f"persistent {per_cu}/CU",
-                                     "groups": int(g_launch), "median_us": float(np.median(us)),
-                                     "min_us": float(us.min()), "TB_per_s": read / (np.median(us) * 1e-6) / 1e12})
-        del buf
-        torch.cuda.empty_cache()
+        rows += _probe_rows(lib, name, size, variants, reps)
     return {"metric": "cold-read ceiling of one launch", "rows": rows, "reps": reps,
             "note": "event-timed dispatches; each launch reads a region last read more than 1 GB earlier"}
 
@@ -1182,6 +1219,19 @@ def run_loop(args) -> dict:
         "kernel_sources_sha256_16": khash,
         "refresh_sources_sha256_16": kernel_hash("refresh_kernel"),
     }
+    if not args.no_ceiling:
+        # the same byte counts read by the read probe: the kernels' fraction of what the memory
+        # delivers to a plain cold read (measured after the timed region, outside it)
+        note("measuring the cold-read ceiling of the kernels' byte counts (read probe)")
+        c = read_ceiling_best(int(ev_bytes.mean()))
+        if c is not None:
+            c["frac"] = achieved / c["GB_per_s"]
+            res["roofline"]["measured_ceiling"] = c
+        if res["refresh_roofline"] is not None:
+            c = read_ceiling_best(int(ref_bytes))
+            if c is not None:
+                c["frac"] = res["refresh_roofline"]["achieved"] / c["GB_per_s"]
+                res["refresh_roofline"]["measured_ceiling"] = c
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
