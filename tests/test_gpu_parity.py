@@ -166,7 +166,24 @@ def test_refresh_run_to_run_deterministic():
 def test_decode_loop_matches_oracle(name):
     """The whole loop: refreshes on schedule, gathers, window appends, sparse decode."""
     log(f"decode loop {name}")
-    wl = conditioned_workload(name, seed=4)
+    _check_decode_loop(conditioned_workload(name, seed=4), name)
+
+
+def test_decode_loop_largest_call():
+    """The most requests one lsa_sparse_decode call takes (64), contexts log-uniform in [64, 8192]
+    tokens (single-block requests among them), a 64-token window and staggered refreshes: every
+    refresh and the sampled steps' outputs against the oracle."""
+    from lookahead_block_sparse_amd import MAX_DECODE_REQ
+    from workloads.configs import CONFIGS
+
+    cfg = CONFIGS["ragged"].scaled(name="ragged_max_call", n_req=MAX_DECODE_REQ, ctx=("loguniform", 64, 8192),
+                                   window=64, steps=66, tag=15)
+    wl = conditioned_workload(cfg, seed=3)
+    log(f"decode loop, {wl.n_req} requests of {int(np.min(wl.n_blocks))}..{int(np.max(wl.n_blocks))} blocks")
+    _check_decode_loop(wl, cfg.name)
+
+
+def _check_decode_loop(wl, name):
     cfg = wl.cfg
     T = cfg.steps
     rng = np.random.default_rng(0)
@@ -359,3 +376,59 @@ def test_resident_reactive_loop_matches_oracle(name):
         worst = tuple(max(a, b) for a, b in zip(worst, attention_errors(gpu[t], ref)))
     log(f"  {name}: {len(sels)} selections bit-exact; max abs {worst[0]:.3e} rel {worst[1]:.3e}")
     assert worst[0] <= ABS_TOL and worst[1] <= REL_TOL, worst
+
+
+def test_refresh_largest_call_ragged_to_single_blocks():
+    """The largest call lsa_index_refresh takes, 64 requests, with contexts log-uniform in
+    [64, 8192] tokens (1 to 128 blocks: single-block requests, words that end mid-way and tiles of
+    several requests in one launch, with more encode groups than fit on the device at once), in one
+    launch: every request's ids, count, per-indexer and union bit planes bit-exact against the
+    oracle, and its fp32 logits within 2e-4 of the oracle's."""
+    from lookahead_block_sparse_amd import MAX_REFRESH_REQ, lsa_index_refresh, lsa_index_refresh_workspace
+    from workloads.configs import CONFIGS
+
+    R = MAX_REFRESH_REQ
+    cfg = CONFIGS["ragged"].scaled(name="ragged_max_call", n_req=R, ctx=("loguniform", 64, 8192), window=64,
+                                   steps=1, tag=15)
+    wl = conditioned_workload(cfg, seed=2)
+    dev = "cuda"
+    nb = np.asarray(wl.n_blocks, dtype=np.int64)
+    blk = np.concatenate([[0], np.cumsum(nb)]).astype(np.int64)
+    words = (nb + 63) // 64
+    word_off = np.concatenate([[0], np.cumsum(words)]).astype(np.int64)
+    n_blk = int(blk[-1])
+    keys = raw_to_torch(np.concatenate([np.ascontiguousarray(wl.keys[r]).reshape(-1) for r in range(R)]), dev)
+    w_q = raw_to_torch(np.ascontiguousarray(wl.w_q).reshape(-1), dev)
+    hid = raw_to_torch(np.stack([wl.hidden[r][0] for r in range(R)]).reshape(-1), dev)
+    bias = torch.from_numpy(np.stack([wl.bias[r] for r in range(R)]).astype(np.float32).reshape(-1)).to(dev)
+    sel = torch.full((n_blk,), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((R,), -7, dtype=torch.int32, device=dev)
+    masks = torch.zeros(int(word_off[-1]) * (cfg.n_idx + 1), dtype=torch.int64, device=dev)
+    logits = torch.full((cfg.n_idx * n_blk,), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.zeros(lsa_index_refresh_workspace(dtype=cfg.dtype, d_model=cfg.d_model, d_idx=cfg.d_idx,
+                                                 n_idx=cfg.n_idx, blk_off=blk), dtype=torch.uint8, device=dev)
+    lsa_index_refresh(dtype=cfg.dtype, d_model=cfg.d_model, d_idx=cfg.d_idx, n_idx=cfg.n_idx, hidden=hid, w_q=w_q,
+                      keys=keys, blk_off=blk, bias=bias, sel_ids=sel, sel_count=cnt, workspace=ws, masks=masks,
+                      logits=logits)
+    torch.cuda.synchronize()
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    masks_h = masks.cpu().numpy().view(np.uint64)
+    z_h = logits.cpu().numpy().astype(np.float64)
+    w64 = oracle.decode_values(wl.w_q, cfg.dtype)
+    worst = 0.0
+    for r in range(R):
+        B = int(nb[r])
+        ref = oracle.refresh(oracle.decode_values(wl.hidden[r][0], cfg.dtype), w64,
+                             oracle.decode_values(wl.keys[r], cfg.dtype), wl.bias[r].astype(np.float64))
+        assert cnt_h[r] == ref.count, (r, B, cnt_h[r], ref.count)
+        assert np.array_equal(sel_h[blk[r]:blk[r] + ref.count], ref.ids), (r, B)
+        planes = masks_h[int(word_off[r]) * (cfg.n_idx + 1):int(word_off[r + 1]) * (cfg.n_idx + 1)]
+        planes = planes.reshape(cfg.n_idx + 1, int(words[r]))
+        for i in range(cfg.n_idx):
+            assert np.array_equal(_unpack(planes[i], B), ref.s[i]), (r, B, i)
+        assert np.array_equal(_unpack(planes[cfg.n_idx], B), ref.u), (r, B)
+        got_z = z_h[cfg.n_idx * blk[r]:cfg.n_idx * blk[r + 1]].reshape(cfg.n_idx, B)
+        worst = max(worst, float(np.abs(got_z - ref.z).max()))
+    log(f"64-request refresh: blocks per request {int(nb.min())}..{int(nb.max())} "
+        f"({int((nb == 1).sum())} single-block), max |dz| {worst:.3g}")
+    assert worst <= 2e-4
