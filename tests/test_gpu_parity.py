@@ -63,7 +63,10 @@ def test_refresh_selection_bit_exact(name):
 # per 1 KiB run), 512-byte rows (the SMALL configs) and 1 KiB rows (fp32, d_idx 256: one per run)
 # and hidden sizes whose rows end inside an encode chunk: 768 bf16 (96 pieces of 16 bytes: the
 # last 64-lane load half in range) and 1280 fp32 (320 pieces)
-WIDTHS = [("ctx128k_s", 128, 0), ("ragged_s", 128, 0), ("tiny", 256, 0), ("ctx128k_s", 256, 768), ("tiny", 128, 1280)]
+# the hidden sizes the refresh accepts at both ends: 256 (the smallest: a fraction of one encode
+# chunk per row) and 16,384 bf16 (the largest: four encode chunks per row)
+WIDTHS = [("ctx128k_s", 128, 0), ("ragged_s", 128, 0), ("tiny", 256, 0), ("ctx128k_s", 256, 768), ("tiny", 128, 1280),
+          ("tiny", 128, 256), ("ctx128k_s", 256, 16384)]
 
 
 @pytest.mark.parametrize("name,d_idx,d_model", WIDTHS, ids=[f"{n}-didx{d}-d{m}" for n, d, m in WIDTHS])
