@@ -112,18 +112,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     int2* cl = p.clist + s0;
 
     int c_new = 0, c_enter = 0, c_leave = 0;
-    // a request of at most kPlanThreads words: each thread's word is the same in every pass, so it
-    // stays in registers (one round trip fewer per pass); longer requests re-read their words
-    const bool one = W <= kPlanThreads;
+    // 2^lq threads per word when the request's words leave threads to spare (each takes a 64/2^lq
+    // bit slice of its word, in order), so that a dense word's blocks take fewer dependent batches
+    // in each pass; thread t handles word c0 + (t >> lq) of a chunk of wpc words
+    const int lq = 4 * W <= kPlanThreads ? 2 : (2 * W <= kPlanThreads ? 1 : 0);
+    const int wpc = kPlanThreads >> lq;
+    const int tw = (int)threadIdx.x >> lq;
+    const int sl = 64 >> lq;  // bits per slice
+    const unsigned long long slice =
+        lq == 0 ? ~0ull : (((1ull << sl) - 1ull) << (sl * ((int)threadIdx.x & ((1 << lq) - 1))));
+    // a request of at most wpc words: each thread's word is the same in every pass, so it stays in
+    // registers (one round trip fewer per pass); longer requests re-read their words
+    const bool one = W <= wpc;
     unsigned long long u1 = 0ull, o1 = 0ull;
-    if (one && (int)threadIdx.x < W) {
-        u1 = nm[threadIdx.x];
-        o1 = res[threadIdx.x];
+    if (one && tw < W) {
+        u1 = nm[tw];
+        o1 = res[tw];
     }
     auto new_word = [&](int w) { return one ? u1 : (w < W ? nm[w] : 0ull); };
     auto old_word = [&](int w) { return one ? o1 : (w < W ? res[w] : 0ull); };
-    for (int w = threadIdx.x; w < W; w += kPlanThreads) {
-        const unsigned long long u = new_word(w), o = old_word(w);
+    for (int c0 = 0; c0 < W; c0 += wpc) {
+        const int w = c0 + tw;
+        const unsigned long long u = new_word(w) & slice, o = old_word(w) & slice;
         c_new += __popcll(u);
         c_enter += __popcll(u & ~o);
         c_leave += __popcll(o & ~u);
@@ -143,9 +153,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     }
     // leaving blocks push their slots, in ascending block id
     int base = 0;
-    for (int c0 = 0; c0 < W; c0 += kPlanThreads) {
-        const int w = c0 + threadIdx.x;
-        unsigned long long m = old_word(w) & ~new_word(w);
+    for (int c0 = 0; c0 < W; c0 += wpc) {
+        const int w = c0 + tw;
+        unsigned long long m = old_word(w) & ~new_word(w) & slice;
         int tot;
         int at = base + group_exclusive_scan(__popcll(m), s_w, &tot);
         while (m) {
@@ -169,9 +179,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     // entering blocks pop slots from the top of the stack, in ascending block id
     const int nf2 = nf + n_leave;
     base = 0;
-    for (int c0 = 0; c0 < W; c0 += kPlanThreads) {
-        const int w = c0 + threadIdx.x;
-        unsigned long long m = new_word(w) & ~old_word(w);
+    for (int c0 = 0; c0 < W; c0 += wpc) {
+        const int w = c0 + tw;
+        unsigned long long m = new_word(w) & ~old_word(w) & slice;
         int tot;
         int e = base + group_exclusive_scan(__popcll(m), s_w, &tot);
         while (m) {
@@ -195,10 +205,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     __syncthreads();
     // the table in ascending block id; the resident words take the new selection
     base = 0;
-    for (int c0 = 0; c0 < W; c0 += kPlanThreads) {
-        const int w = c0 + threadIdx.x;
+    for (int c0 = 0; c0 < W; c0 += wpc) {
+        const int w = c0 + tw;
         const unsigned long long u = new_word(w);
-        unsigned long long m = u;
+        unsigned long long m = u & slice;
         int tot;
         int at = base + group_exclusive_scan(__popcll(m), s_w, &tot);
         while (m) {
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
                 if (k < n) tbl[at + k] = make_int2(64 * w + pos[k], slot[k]);
             at += n;
         }
-        if (w < W) res[w] = u;
+        if (w < W && ((int)threadIdx.x & ((1 << lq) - 1)) == 0) res[w] = u;  // the word's first slice
         base += tot;
     }
     if (threadIdx.x == 0) {
