@@ -435,3 +435,19 @@ def test_refresh_largest_call_ragged_to_single_blocks():
     log(f"64-request refresh: blocks per request {int(nb.min())}..{int(nb.max())} "
         f"({int((nb == 1).sum())} single-block), max |dz| {worst:.3g}")
     assert worst <= 2e-4
+
+
+def test_decode_contexts_shorter_than_the_window():
+    """Requests whose whole context fits in the window (seq_len < window: the ring holds every token
+    and every table entry lies inside the window) beside one that does not, through refreshes and
+    decode steps: selections exact and outputs within tolerance against the oracle, which then
+    attends over the whole context of the short requests."""
+    from workloads.configs import CONFIGS
+
+    cfg = CONFIGS["ctx512k"].scaled(name="short_contexts", n_req=4, ctx=("loguniform", 64, 32768), window=2048,
+                                    density=("uniform", 0.2, 0.5), steps=70, tag=16)
+    wl = conditioned_workload(cfg, seed=3)  # contexts of 320, 26,496, 832 and 64 tokens
+    short = int((np.asarray(wl.ctx) + cfg.steps < cfg.window).sum())
+    log(f"contexts {np.asarray(wl.ctx).tolist()} tokens, window {cfg.window}: {short} shorter throughout")
+    assert short >= 1 and short < wl.n_req
+    _check_decode_loop(wl, cfg.name)

@@ -296,8 +296,9 @@ def build_workload(cfg: LSAConfig | str, seed: int = 0, steps: Optional[int] = N
         lo, hi = cfg.ctx[1], cfg.ctx[2]
         u = rng_for(seed, cfg.tag, _T_CTX).random(R)
         ctx = (np.exp(np.log(lo) + u * (np.log(hi) - np.log(lo))).astype(np.int64) // blk) * blk
-    if (ctx < cfg.window).any():
-        raise ValueError("every context must hold at least one window of tokens")
+    if cfg.planted_frac > 0 and (ctx < cfg.window).any():
+        # the planted blocks are drawn among the blocks wholly before the window
+        raise ValueError("a workload with planted blocks needs every context to hold at least one window")
 
     # densities and bias
     if cfg.density[0] == "fixed":
