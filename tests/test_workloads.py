@@ -179,3 +179,60 @@ def test_benchmark_refuses_more_steps_than_the_window_holds():
 
     cfg = get_config("ctx1m")
     assert bench.max_bench_steps(cfg) == cfg.window // bench.STEP_DECODE
+
+
+def _write_csv(path, header, rows):
+    import csv
+
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_traffic_summary_scales_counters_by_the_copy_in_the_same_pass(tmp_path):
+    """The traffic figure the benchmark reports: per pass, the kernel's mean counter value over its
+    largest-grid launches (smaller launches of the same kernel are single-request recomputations),
+    scaled by what the counter read for the plain copy of known size in the same pass."""
+    import bench
+
+    hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    calib_mib = 1024
+    # the copy reads 2^30 bytes; FETCH_SIZE reports half of that in KiB (a factor of 2 to take out),
+    # WRITE_SIZE all of it
+    fetch = [["__amd_rocclr_copyBuffer", 4096, "FETCH_SIZE", 2 ** 30 / 1024 / 2],
+             ["lsa::refresh_kernel<unsigned short, 256>", 159744, "FETCH_SIZE", 50000.0],
+             ["lsa::refresh_kernel<unsigned short, 256>", 159744, "FETCH_SIZE", 52000.0],
+             ["lsa::refresh_kernel<unsigned short, 256>", 58368, "FETCH_SIZE", 13000.0],
+             ["lsa::attn_kernel<x>", 131072, "FETCH_SIZE", 1.0]]
+    write = [["__amd_rocclr_copyBuffer", 4096, "WRITE_SIZE", 2 ** 30 / 1024],
+             ["lsa::refresh_kernel<unsigned short, 256>", 159744, "WRITE_SIZE", 200.0],
+             ["lsa::refresh_kernel<unsigned short, 256>", 58368, "WRITE_SIZE", 50.0]]
+    _write_csv(tmp_path / "f.csv", hdr, fetch)
+    _write_csv(tmp_path / "w.csv", hdr, write)
+    d = bench.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), workload="ctx1m",
+                              calib_mib=calib_mib, kernel="refresh_kernel")
+    assert d["dispatches"] == {"fetch_pass": 2, "write_pass": 1}
+    assert d["fetch_scale"] == pytest.approx(2.0) and d["write_scale"] == pytest.approx(1.0)
+    assert d["fetch_bytes_per_launch"] == pytest.approx(51000.0 * 1024 * 2)
+    assert d["write_bytes_per_launch"] == pytest.approx(200.0 * 1024)
+    assert d["traffic_bytes_per_launch"] == pytest.approx(51000.0 * 2048 + 200.0 * 1024)
+    assert d["kernel_sources_sha256_16"] == bench.kernel_hash("refresh_kernel")
+
+
+def test_kernel_trace_summary_groups_dispatches_by_kernel_and_grid(tmp_path):
+    """Per (kernel, grid) dispatch count and durations from a kernel-trace CSV (ns stamps -> us)."""
+    import bench
+
+    hdr = ["Kernel_Name", "Grid_Size", "Start_Timestamp", "End_Timestamp"]
+    rows = [["void lsa::(anonymous namespace)::attn_kernel<A>(P)", 131072, 0, 66000],
+            ["void lsa::(anonymous namespace)::attn_kernel<A>(P)", 131072, 100000, 168000],
+            ["void lsa::(anonymous namespace)::refresh_kernel<B>(Q)", 159744, 200000, 227000],
+            ["void lsa::(anonymous namespace)::refresh_kernel<B>(Q)", 58368, 300000, 316000]]
+    _write_csv(tmp_path / "t.csv", hdr, rows)
+    d = bench.kernel_trace_summary(str(tmp_path / "t.csv"))
+    got = {(k["kernel"], k["grid_x"]): k for k in d["kernels"]}
+    a = got[("lsa::attn_kernel<A>", 131072)]
+    assert a["dispatches"] == 2 and a["mean_us"] == pytest.approx(67.0) and a["min_us"] == pytest.approx(66.0)
+    assert got[("lsa::refresh_kernel<B>", 159744)]["mean_us"] == pytest.approx(27.0)
+    assert got[("lsa::refresh_kernel<B>", 58368)]["dispatches"] == 1
