@@ -1028,10 +1028,11 @@ def run_loop(args) -> dict:
         ids_per_refresh = np.mean([sum(len(v) for v in s_.values()) for s_ in sel_at.values()])
     else:
         ids_per_refresh = sum(len(sess.sel_host[r]) for r in ref_reqs)
-    ref_bytes = (cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_ref * cfg.n_idx * cfg.d_idx * e + q_in_bytes
-                 + int(4 * ids_per_refresh) + 4 * len(ref_reqs))
-    if dplan:  # the bit planes the device plan reads are written by the refresh
+    ref_bytes = cfg.n_idx * cfg.q_in * cfg.d_idx * e + n_blocks_ref * cfg.n_idx * cfg.d_idx * e + q_in_bytes
+    if dplan:  # the bit planes the device plan reads are the refresh's whole result (no ids, no counts)
         ref_bytes += 8 * (cfg.n_idx + 1) * int(sum(int(sess.word_off[r + 1] - sess.word_off[r]) for r in ref_reqs))
+    else:  # the ids and counts
+        ref_bytes += int(4 * ids_per_refresh) + 4 * len(ref_reqs)
     if rloop is not None:  # the table pairs the refresh writes for the resident pool
         ref_bytes += int(8 * ids_per_refresh)
     lat_bytes = (cfg.n_idx * cfg.q_rank * cfg.d_model * e + len(ref_reqs) * cfg.d_model * e
@@ -1201,7 +1202,9 @@ def run_loop(args) -> dict:
         "decode_steady": ({"tokens_per_s": wl.n_req * sum(n for n, _ in steady) / (sum(u for _, u in steady) * 1e-6),
                            "us_per_step": sum(u for _, u in steady) / sum(n for n, _ in steady),
                            "steps": int(sum(n for n, _ in steady))} if steady else None),
-        "refresh_roofline": ({"kernel": "refresh_kernel (encode + score + compaction, one launch)",
+        "refresh_roofline": ({"kernel": ("refresh_kernel (encode + score + threshold + union bit planes, one launch; "
+                                         "the device plan ranks the selected blocks)" if dplan else
+                                         "refresh_kernel (encode + score + compaction, one launch)"),
                               "achieved": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": ref_bytes / (np.median(ref_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "algorithmic_bytes": ref_bytes, "requests_per_refresh": len(ref_reqs),

@@ -57,7 +57,7 @@ typedef enum { LSA_F32 = 0, LSA_BF16 = 1 } lsa_dtype;
 #define LSA_BLOCK_TOKENS 64     /* tokens per KV block: the unit scored, selected and moved */
 #define LSA_MAX_REFRESH_REQ 64  /* requests per lsa_index_refresh call */
 #define LSA_MAX_DECODE_REQ 64   /* requests per lsa_sparse_decode call */
-#define LSA_ABI_VERSION 13
+#define LSA_ABI_VERSION 14
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* lsa_last_error(void);
@@ -141,8 +141,12 @@ typedef struct lsa_refresh_args {
                                   1 <= B_r <= 2^24 */
     const float* bias;         /* dev [n_req][n_idx] */
     int32_t* sel_ids;          /* dev: request r's ascending ids written at sel_ids + blk_off[r]
-                                  (capacity B_r) */
-    int32_t* sel_count;        /* dev [n_req] */
+                                  (capacity B_r); or NULL with masks: the refresh then writes the bit
+                                  planes only and leaves the ordering of the selection to the
+                                  caller (lsa_gather_plan_device ranks the blocks from the union
+                                  plane itself), with no compaction step; table_out must be NULL */
+    int32_t* sel_count;        /* dev [n_req]: the counts, -1 for a request whose waits gave up; with
+                                  sel_ids NULL only the -1 is written (a count is left as it was) */
     uint64_t* masks;           /* dev or NULL.  Request r's n_idx+1 bit planes of W_r =
                                   ceil(B_r/64) words start at word (n_idx+1)*M_r, where M_r is
                                   the sum of W_r' over r' < r; plane i < n_idx holds s[i],
@@ -291,8 +295,11 @@ typedef struct lsa_device_gather_args {
     const int64_t* blk_off;    /* host [n_req+1], as for the refresh (B_r = blk_off[r+1]-blk_off[r]) */
     const int32_t* slot_off;   /* host [n_req+1]: request r owns hot slots slot_off[r] .. slot_off[r+1]-1 */
     const uint64_t* masks;     /* dev: the refresh's bit planes (lsa_refresh_args.masks layout) */
-    const int32_t* sel_count;  /* dev [n_req]: the refresh's counts; a negative count (a refresh that
-                                  gave up) changes nothing for the request and sets its status to 2 */
+    int32_t* sel_count;        /* dev [n_req]: the refresh's counts; a negative count (a refresh that
+                                  gave up) changes nothing for the request and sets its status to 2.
+                                  The plan then writes each request's count of selected blocks
+                                  there (0 after a refresh that gave up), so that a refresh that
+                                  wrote no counts (sel_ids NULL) leaves a valid one behind */
     uint64_t* resident;        /* dev [sum_r ceil(B_r/64)] state: request r's words start at word
                                   sum_{r'<r} ceil(B_r'/64); bit b = block b resident */
     int32_t* slot_of_block;    /* dev [blk_off[n_req]] state: slot of each block, or -1 */

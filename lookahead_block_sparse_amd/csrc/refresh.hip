@@ -17,6 +17,9 @@
 //   compact  one per 64 words of a request: waits until every half word of the request up to its
 //            words has published, offsets its words by the popcounts before them and a wave scan,
 //            and writes their ids in ascending order; the last one of a request writes the count.
+//   Without ids (sel_ids NULL: a caller that ranks the selected blocks from the union plane itself)
+//   the score waves write their 32 union bits straight into the union plane, no compaction group is
+//   launched, and the launch ends with the last score wave (~3 us earlier at 4 x 1M).
 // Why the score waves hold so much: a value handed from one compute unit to another inside a
 // launch (q here) travels through the memory-side queues and, with the key stream in flight,
 // reaches the score waves ~10 us after the launch starts whatever the rest of the design does.
@@ -75,6 +78,7 @@ struct RefreshParams {
     int cg_off[kMaxReq + 1];  // first compaction group of each request
     int2* table_out;          // optional: (id, tslot[r] + id) pairs at pair blk_off[r]
     float* logits;            // optional: z at element n_idx * blk_off[r] + i * B_r + b
+    int bits_only;            // no ids: the score waves write the union plane, no compaction groups
     int tslot[kMaxReq];
 };
 
@@ -466,6 +470,18 @@ __device__ __forceinline__ void publish_half(const RefreshParams& p, const HalfW
     }
 }
 
+// A half word's union bits straight into the union plane (the bit planes are the refresh's whole
+// result when no ids are asked for), and -1 as the request's count when q never arrived.
+__device__ __forceinline__ void write_union_half(const RefreshParams& p, const HalfWord& h, unsigned u_bits, bool q_ok,
+                                                 int lane) {
+    if (lane == 0) {
+        const int n_words_r = p.word_off[h.r + 1] - p.word_off[h.r];
+        const size_t mw = (size_t)(p.n_idx + 1) * p.word_off[h.r] + (size_t)p.n_idx * n_words_r + h.lw;
+        reinterpret_cast<unsigned*>(p.masks)[2 * mw + h.half] = u_bits;
+        if (!q_ok) p.sel_count[h.r] = -1;
+    }
+}
+
 // Score wave: half word sw (none when sw >= n_halves), all indexers in batches of U.
 template <typename T, int DIDX>
 __device__ void score_role(const RefreshParams& p, int sw) {
@@ -482,7 +498,10 @@ __device__ void score_role(const RefreshParams& p, int sw) {
         asm volatile("" ::: "memory");  // every key load of the batch is issued before q is polled
         score_runs<T, DIDX>(p, h, i0, nu, lane, v, &u_bits, &q_ok);
     }
-    publish_half(p, h, u_bits, q_ok, lane);
+    if (p.bits_only)
+        write_union_half(p, h, u_bits, q_ok, lane);
+    else
+        publish_half(p, h, u_bits, q_ok, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -696,6 +715,7 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
     rp.masks = reinterpret_cast<unsigned long long*>(a->masks);
     rp.table_out = reinterpret_cast<int2*>(a->table_out);
     rp.logits = a->logits;
+    rp.bits_only = a->sel_ids == nullptr ? 1 : 0;
     for (int r = 0; r < a->n_req; ++r) rp.tslot[r] = a->table_out ? a->table_slot_base[r] : 0;
     rp.qw = reinterpret_cast<unsigned long long*>(ws + L.qw_off);
     rp.hw = reinterpret_cast<unsigned long long*>(ws + L.hw_off);
@@ -725,7 +745,7 @@ lsa_status launch_refresh(const lsa_refresh_args* a, const RefreshLayout& L, hip
         }
     }
     auto kernel = a->d_idx == 256 ? refresh_kernel<T, 256> : refresh_kernel<T, 128>;
-    const dim3 grid(rp.n_encode_groups + rp.n_score_groups + co), block(kThreads);
+    const dim3 grid(rp.n_encode_groups + rp.n_score_groups + (rp.bits_only ? 0 : co)), block(kThreads);
     if (a->ev_begin && a->ev_end)  // the events take the dispatch's own start and end timestamps
         hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a->ev_begin, a->ev_end, 0, rp);
     else
@@ -752,8 +772,9 @@ extern "C" lsa_status lsa_index_refresh(const lsa_refresh_args* a, hipStream_t s
     RefreshLayout L;
     lsa_status st = refresh_layout(a, &L);
     if (st != LSA_OK) return st;
-    LSA_CHECK_ARG(a->hidden && a->w_q && a->keys && a->bias && a->sel_ids && a->sel_count,
-                  "lsa_index_refresh: null device pointer");
+    LSA_CHECK_ARG(a->hidden && a->w_q && a->keys && a->bias && a->sel_count, "lsa_index_refresh: null device pointer");
+    LSA_CHECK_ARG(a->sel_ids || (a->masks && !a->table_out),
+                  "lsa_index_refresh: without sel_ids the refresh needs masks (its whole result) and no table_out");
     LSA_CHECK_ARG(a->hidden_req_stride >= a->d_model || a->n_req == 1,
                   "lsa_index_refresh: hidden_req_stride=%lld < d_model", (long long)a->hidden_req_stride);
     LSA_CHECK_ARG(a->hidden_idx_stride >= 0, "lsa_index_refresh: negative hidden_idx_stride");

@@ -26,7 +26,7 @@ constexpr int kCopyThreads = 256;
 
 struct PlanParams {
     const unsigned long long* masks;
-    const int* sel_count;
+    int* sel_count;
     unsigned long long* resident;
     int* slot_of_block;
     int* free_slots;
@@ -143,8 +143,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
     const int n_leave = group_sum(c_leave, s_w);
     const int nf = p.n_free[r];
     const bool gave_up = p.sel_count[r] < 0;
+    __syncthreads();  // every thread has read the count before it is rewritten below
     if (gave_up || n_enter > nf + n_leave) {  // nothing changes for this request
         if (threadIdx.x == 0) {
+            p.sel_count[r] = gave_up ? 0 : n_new;
             p.status[r] = gave_up ? 2 : 1;
             if (p.status_any) p.status_any[r] |= gave_up ? 2 : 1;
             p.copied[r] = 0;
@@ -226,6 +228,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p) {
         base += tot;
     }
     if (threadIdx.x == 0) {
+        p.sel_count[r] = n_new;
         p.n_free[r] = nf2 - n_enter;
         p.table_count[r] = n_new;
         p.copied[r] = n_enter;

@@ -281,7 +281,7 @@ class LSASession:
 
     def _refresh_run(self, r0: int, r1: int, hid: torch.Tensor, bias_d: torch.Tensor, ev_begin=None,
                      ev_end=None, table_out: bool = False, ev_latent=(None, None),
-                     stream: Optional[torch.cuda.Stream] = None) -> None:
+                     stream: Optional[torch.cuda.Stream] = None, bits_only: bool = False) -> None:
         st = self.stream if stream is None else stream
         stride = self.d_model
         if self.rank:
@@ -292,7 +292,7 @@ class LSASession:
                              ev_end=ev_latent[1], stream=st)
             hid = lat
             stride = self.n_idx * self.rank
-        key = (r0, r1, bool(table_out))
+        key = (r0, r1, bool(table_out), bool(bits_only))
         cached = self._rargs.get(key)
         if cached is None:
             # the first call of a run of requests goes through the checked wrapper; the argument
@@ -306,12 +306,13 @@ class LSASession:
             lsa_index_refresh(dtype=self.dtype, d_model=self.q_in, d_idx=self.d_idx, n_idx=self.n_idx, hidden=hid,
                               hidden_req_stride=stride, hidden_idx_stride=self.rank,
                               w_q=self.w_q, keys=self.keys[key_elem0:], blk_off=off, bias=bias_d,
-                              sel_ids=self.sel_ids[int(self.blk_off[r0]):], sel_count=self.sel_count[r0:r1],
+                              sel_ids=None if bits_only else self.sel_ids[int(self.blk_off[r0]):],
+                              sel_count=self.sel_count[r0:r1],
                               workspace=self.refresh_ws, masks=masks, ev_begin=ev_begin, ev_end=ev_end,
                               table_out=(self.table[2 * int(self.slot_base[r0]):] if table_out else None),
                               table_slot_base=(self.slot_base[r0:r1] if table_out else None),
                               stream=st, select_level=self.select_level)
-            self._rargs[key] = self._refresh_struct(r0, r1, stride, table_out, masks)
+            self._rargs[key] = self._refresh_struct(r0, r1, stride, table_out, masks, bits_only)
             return
         a, _keep, need_hid, need_bias = cached
         if not (hid.is_cuda and bias_d.is_cuda and hid.is_contiguous() and bias_d.is_contiguous()
@@ -322,7 +323,7 @@ class LSASession:
         a.ev_end = ev_end.cuda_event if ev_end is not None else None
         _check(LIB.lsa_index_refresh(ctypes.byref(a), ctypes.c_void_p(st.cuda_stream)))
 
-    def _refresh_struct(self, r0: int, r1: int, stride: int, table_out: bool, masks):
+    def _refresh_struct(self, r0: int, r1: int, stride: int, table_out: bool, masks, bits_only: bool = False):
         """The refresh argument struct of a run of requests (every field but the hidden states, the
         biases and the events), with the arrays it points into."""
         off = np.ascontiguousarray(self.blk_off[r0:r1 + 1] - self.blk_off[r0], dtype=np.int64)
@@ -334,7 +335,7 @@ class LSASession:
         a.w_q = self.w_q.data_ptr()
         a.keys = self.keys.data_ptr() + int(self.n_idx * self.d_idx * self.blk_off[r0]) * self.keys.element_size()
         a.blk_off = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
-        a.sel_ids = self.sel_ids.data_ptr() + int(self.blk_off[r0]) * 4
+        a.sel_ids = None if bits_only else self.sel_ids.data_ptr() + int(self.blk_off[r0]) * 4
         a.sel_count = self.sel_count.data_ptr() + r0 * 4
         a.masks = masks.data_ptr() if masks is not None else None
         a.workspace = self.refresh_ws.data_ptr()
@@ -348,6 +349,12 @@ class LSASession:
         need_hid = ((r1 - r0 - 1) * stride + (self.n_idx - 1) * self.rank + self.q_in) * e
         need_bias = (r1 - r0) * self.n_idx * 4
         return a, (off, tsb), need_hid, need_bias
+
+    def union_ids(self, r: int) -> np.ndarray:
+        """Request r's selected block ids, ascending, read from the union plane of its last refresh
+        (a device-planned refresh writes the bit planes and no ids)."""
+        u = np.unpackbits(np.ascontiguousarray(self.masks_of(r)[self.n_idx]).view(np.uint8), bitorder="little")
+        return np.flatnonzero(u[:int(self.n_blocks[r])]).astype(np.int32)
 
     def masks_of(self, r: int) -> np.ndarray:
         """Request r's bit planes [n_idx+1][words] (after a refresh with masks enabled)."""
@@ -396,7 +403,9 @@ class LSASession:
                        copied_out: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
         """Index refresh of `reqs` followed by the gather planned and run on the device
         (lsa_gather_plan_device): nothing is copied back and nothing waits for the host.  The
-        decode then reads the tables' counts on the device (DecodeLoop(..., device_counts=True)).
+        refresh writes the bit planes only (the plan ranks the selected blocks from the union plane
+        and writes the counts to `sel_count`; `union_ids` reads a selection back).  The decode then
+        reads the tables' counts on the device (DecodeLoop(..., device_counts=True)).
         The plan writes the number of blocks it copied for request r to entry r of `copied_out`
         (an int32 device tensor of n_req entries) when given, else to `copied_dev`.  Everything is
         enqueued on `stream` (default: the session's stream)."""
@@ -417,9 +426,10 @@ class LSASession:
                 j += 1
             r0, r1 = reqs[i], reqs[j] + 1
             one_run = i == 0 and j == len(reqs) - 1
+            # the plan ranks the selected blocks from the union plane: the refresh writes bit planes only
             self._refresh_run(r0, r1, hid[i:j + 1], bias_d[i:j + 1], ev_begin if one_run else None,
                               ev_end if one_run else None, ev_latent=ev_latent if one_run else (None, None),
-                              stream=st)
+                              stream=st, bits_only=True)
             a = self._plan_args(r0, r1)[0]
             a.copied = copied_base + 4 * r0
             a.ev_begin = ev_plan[0].cuda_event if (ev_plan[0] is not None and one_run) else None

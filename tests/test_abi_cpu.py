@@ -475,3 +475,17 @@ def test_refresh_select_level_validation(level, ok):
     assert (st == L.LSA_OK) == ok, (level, st)
     if not ok:
         assert st == L.LSA_ERR_INVALID and b"select_level" in L.LIB.lsa_last_error()
+
+
+def test_refresh_without_ids_needs_masks_and_no_table():
+    """sel_ids NULL asks for the bit planes only: the masks must be given and table_out (built from
+    the ids) must not; both are refused before any HIP call."""
+    a, keep = L._refresh_args(dtype="bf16", d_model=4096, d_idx=256, n_idx=3, hidden=FAKE, hidden_req_stride=4096,
+                              hidden_idx_stride=0, w_q=FAKE, keys=FAKE, blk_off=[0, 2048], bias=FAKE, sel_ids=None,
+                              sel_count=FAKE, masks=None, workspace=FAKE, workspace_bytes=1 << 30)
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID
+    assert "masks" in L.LIB.lsa_last_error().decode()
+    a.masks = FAKE
+    a.table_out = FAKE
+    a.table_slot_base = FAKE
+    assert L.LIB.lsa_index_refresh(ctypes.byref(a), None) == L.LSA_ERR_INVALID

@@ -57,12 +57,12 @@ def _run(wl, sess, sample, check=True, switch_at=None):
         copied = torch.full((R,), -1, dtype=torch.int32, device=dev)  # the plan's count of copied blocks
         sess.refresh_device(reqs, hid, torch.stack([bias_all[r] for r in reqs]), copied_out=copied)
         if check:
+            # the refresh wrote bit planes only; the plan rewrote the counts
             counts = sess.sel_count.cpu().numpy()
-            ids_all = sess.sel_ids.cpu().numpy()
             got_copied = copied.cpu().numpy()
             for r in reqs:
-                b0 = int(sess.blk_off[r])
-                ids = ids_all[b0:b0 + counts[r]].copy()
+                ids = sess.union_ids(r)
+                assert counts[r] == len(ids), (r, counts[r], len(ids))
                 sels[(r, k_of[r])] = ids
                 _check_state(sess, r, ids)
                 # the blocks that entered: selected now, not resident before
@@ -312,8 +312,8 @@ def test_staggered_overlap_matches_oracle(name):
                             torch.stack([bias_all[r] for r in pro]))
         torch.cuda.synchronize()
         for r in pro:
-            b0 = int(sess.blk_off[r])
-            sels[(r, 0)] = sess.sel_ids[b0:b0 + int(sess.sel_count[r])].cpu().numpy()
+            sels[(r, 0)] = sess.union_ids(r)
+            assert int(sess.sel_count[r]) == len(sels[(r, 0)])
     out = torch.empty((R, cfg.n_heads, cfg.head_dim), dtype=torch.float32, device=dev)
     loop = StaggeredLoop(sess, wl.ctx, np.full(R, cfg.window, dtype=np.int32), out)
     gpu = {}
@@ -326,10 +326,9 @@ def test_staggered_overlap_matches_oracle(name):
         if reqs:
             torch.cuda.synchronize()
             counts = sess.sel_count.cpu().numpy()
-            ids_all = sess.sel_ids.cpu().numpy()
             for r in reqs:
-                b0 = int(sess.blk_off[r])
-                ids = ids_all[b0:b0 + counts[r]].copy()
+                ids = sess.union_ids(r)
+                assert counts[r] == len(ids), (r, counts[r], len(ids))
                 sels[(r, wl.refresh_index_at(r, t))] = ids
                 _check_state(sess, r, ids)
         if t in sample:
