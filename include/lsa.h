@@ -113,9 +113,10 @@ lsa_status lsa_pack_blocks(int32_t dtype, int32_t head_dim, const void* k_tok, c
  *
  * For request r with B_r blocks and indexers i < n_idx (zhichai.net explainer,
  * sections 2-4; 1kpapers report page, Summary):
- *   q[i]     = W_q[i] h                        Query Encoder, fp32 accumulation,
- *                                              kept in fp32 (never rounded)
- *   z[i][b]  = q[i] . keys[i][b] + bias[i]      dual-encoder block logit (fp32)
+ *   q[i]     = W_q[i] h                        Query Encoder, fp32 accumulation, kept in fp32
+ *   z[i][b]  = q[i] . keys[i][b] + bias[i]      dual-encoder block logit, fp32 accumulation (bf16
+ *                                              keys meet q as the sum of two bf16 parts, within
+ *                                              2^-18 of q relative)
  *   s[i][b]  = z[i][b] > logit(level)           sigmoid(z) > level (0.5 by default: z > 0), decided on z
  *   u[b]     = OR_i s[i][b]                     OR-mode union
  *   sel_ids  = ascending b with u[b], sel_count = their number

@@ -34,8 +34,10 @@
 // the first round staged in LDS by direct-to-LDS loads, so that every key byte is requested at
 // the start (the stream then ran at ~4.3 TB/s and the staged words were scored after a group
 // barrier: 33-36 us).  The cross-lane moves of the scoring are row swaps and DPP (no LDS
-// crossbar); making the dot products cheaper as well saves under 0.5 us, so the launch is
-// bound by the key stream and the hand-offs, not by arithmetic.
+// crossbar), and bf16 keys are dotted with q on v_dot2_f32_bf16, q taken as two bf16 parts (its
+// value rounded to nearest even plus the rounded remainder, ~2^-18 relative); the launch is bound
+// by the key stream and the hand-offs, and without compaction groups the last waves' scoring is
+// its tail (the cheaper dot products and a one-round-trip q poll took ~0.6 us off it).
 // A group only waits for groups with a lower index, which were dispatched before it, and every
 // wait is bounded: a wait that gives up marks the request, whose count is then written as -1.
 // Values that cross groups travel in 64-bit words whose upper half is the call's number and lower
@@ -330,6 +332,12 @@ __device__ __forceinline__ void gather_rows(float x, float* out) {
     }
 }
 
+// fp32 -> bf16 bits, rounded to nearest even (finite values)
+__device__ __forceinline__ unsigned bf16_rne(float x) {
+    const unsigned u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Where half word sw lives: its request, word and row base.
 struct HalfWord {
     int sw, half, r, lw, n_blk, n_valid;
@@ -394,19 +402,24 @@ __device__ __forceinline__ void score_runs(const RefreshParams& p, const HalfWor
     const int rowi = 32 * h.half + S::RPL * k + sub;  // row of the word whose logit this lane ends with
     float qf[S::U][S::QF];
     for (unsigned spins = 0;; ++spins) {
-        bool all = true;
+        // every load unconditional (units past nu read the last indexer's row, and are ignored), so
+        // that the whole poll is one round trip rather than one per unit
+        unsigned long long wq[S::U][S::QF];
 #pragma unroll
         for (int u = 0; u < S::U; ++u) {
-            if (u < nu) {
-                const unsigned long long* qrow = p.qw + ((size_t)h.r * p.n_idx + i0 + u) * DIDX + col * S::E + sub * S::QF;
+            const int iu = min(i0 + u, p.n_idx - 1);
+            const unsigned long long* qrow = p.qw + ((size_t)h.r * p.n_idx + iu) * DIDX + col * S::E + sub * S::QF;
 #pragma unroll
-                for (int e = 0; e < S::QF; ++e) {
-                    const unsigned long long wq = get(qrow + e);
-                    all = all && tagged(wq, p.tag);
-                    qf[u][e] = __uint_as_float((unsigned)wq);
-                }
-            }
+            for (int e = 0; e < S::QF; ++e) wq[u][e] = get(qrow + e);
         }
+        bool all = true;
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+#pragma unroll
+            for (int e = 0; e < S::QF; ++e) {
+                all &= u >= nu || tagged(wq[u][e], p.tag);
+                qf[u][e] = __uint_as_float((unsigned)wq[u][e]);
+            }
         if (__all(all)) break;
         if (spins >= kSpinLimit) {
             *q_ok = false;
@@ -418,17 +431,50 @@ __device__ __forceinline__ void score_runs(const RefreshParams& p, const HalfWor
     for (int u = 0; u < S::U; ++u) {
         if (u < nu) {
             const int i = i0 + u;
-            float qv[S::E];  // the column's E values, gathered from the lanes that fetched them
-#pragma unroll
-            for (int e = 0; e < S::QF; ++e) {
-                float g[S::RPL];
-                gather_rows<S::RPL>(qf[u][e], g);
-#pragma unroll
-                for (int s2 = 0; s2 < S::RPL; ++s2) qv[s2 * S::QF + e] = g[s2];
-            }
             float part[S::P];
+            if constexpr (sizeof(T) == 2) {
+                // bf16 keys: q as two bf16 parts, hi = q rounded to nearest even and lo = (q - hi)
+                // rounded likewise (hi + lo is q to ~2^-17 relative, far inside the logit margin),
+                // packed in pairs by the lane that fetched them, gathered, and dotted with the keys
+                // on v_dot2_f32_bf16 (products of bf16 values are exact in fp32)
+                constexpr int QP = S::QF / 2;  // packed pairs this lane fetched
+                unsigned ph[QP], pl[QP];
 #pragma unroll
-            for (int j = 0; j < S::P; ++j) part[j] = dot_chunk_f32<T>(v[u][j], qv);
+                for (int e2 = 0; e2 < QP; ++e2) {
+                    const float a = qf[u][2 * e2], b = qf[u][2 * e2 + 1];
+                    const unsigned ha = bf16_rne(a), hb = bf16_rne(b);
+                    const unsigned la = bf16_rne(a - __uint_as_float(ha << 16)), lb = bf16_rne(b - __uint_as_float(hb << 16));
+                    ph[e2] = ha | (hb << 16);
+                    pl[e2] = la | (lb << 16);
+                }
+                unsigned qh[S::E / 2], ql[S::E / 2];  // the column's E values as pairs, lane order
+#pragma unroll
+                for (int e2 = 0; e2 < QP; ++e2) {
+                    float gh[S::RPL], gl[S::RPL];
+                    gather_rows<S::RPL>(__uint_as_float(ph[e2]), gh);
+                    gather_rows<S::RPL>(__uint_as_float(pl[e2]), gl);
+#pragma unroll
+                    for (int s2 = 0; s2 < S::RPL; ++s2) {
+                        qh[s2 * QP + e2] = __float_as_uint(gh[s2]);
+                        ql[s2 * QP + e2] = __float_as_uint(gl[s2]);
+                    }
+                }
+                const uint4 qh4 = make_uint4(qh[0], qh[1], qh[2], qh[3]);
+                const uint4 ql4 = make_uint4(ql[0], ql[1], ql[2], ql[3]);
+#pragma unroll
+                for (int j = 0; j < S::P; ++j) part[j] = dot_chunks<T>(v[u][j], ql4, dot_chunks<T>(v[u][j], qh4, 0.f));
+            } else {
+                float qv[S::E];  // the column's E values, gathered from the lanes that fetched them
+#pragma unroll
+                for (int e = 0; e < S::QF; ++e) {
+                    float g[S::RPL];
+                    gather_rows<S::RPL>(qf[u][e], g);
+#pragma unroll
+                    for (int s2 = 0; s2 < S::RPL; ++s2) qv[s2 * S::QF + e] = g[s2];
+                }
+#pragma unroll
+                for (int j = 0; j < S::P; ++j) part[j] = dot_chunk_f32<T>(v[u][j], qv);
+            }
             // reduce-scatter: step t keeps the upper half of the remaining partials on lanes
             // whose bit (LOG_LPR - 1 - t) is set and adds the partner lane's copy of that half
             rs_steps<S::LOG_LPR - 1, S::P, S::LOG_P>(part, lane);
@@ -545,14 +591,21 @@ __device__ void compact_role(const RefreshParams& p, int cg) {
     for (unsigned spins = 0;; ++spins) {
         bool ok = true;
         if (held) {
+            // both halves of every word this thread keeps, all requested at once (indices past the
+            // slice's end clamped, their words ignored)
+            unsigned long long lo[kKeep], hi[kKeep];
+#pragma unroll
+            for (int k = 0; k < kKeep; ++k) {
+                const int w = min(t + kThreads * k, s1 - 1);
+                lo[k] = get(hw + 2 * (size_t)w);
+                hi[k] = get(hw + 2 * (size_t)w + 1);
+            }
 #pragma unroll
             for (int k = 0; k < kKeep; ++k) {
                 const int w = t + kThreads * k;
                 if (w < s1 && !((done >> k) & 1u)) {
-                    bool okw = true;
-                    const unsigned long long u = union_word(w, &okw);
-                    if (okw) {
-                        keep[k] = u;
+                    if (tagged(lo[k], p.tag) && tagged(hi[k], p.tag)) {
+                        keep[k] = (unsigned long long)(unsigned)lo[k] | ((unsigned long long)(unsigned)hi[k] << 32);
                         done |= 1u << k;
                     } else {
                         ok = false;
