@@ -59,9 +59,9 @@ METRIC = "LSA decode tokens/s at 1M ctx + index-refresh µs; % of HBM roofline"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4,
+    ap.add_argument("--steps", type=int, default=12,
                     help="timed steps; a step is 64 decode steps of every request (one refresh interval)")
-    ap.add_argument("--warmup", type=int, default=1, help="untimed steps before them")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed steps before them")
     ap.add_argument("--workload", default="ctx1m")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cold", choices=("device", "host"), default="device")
